@@ -1,0 +1,84 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each mutant is a copy of ``oracle/gn_oracle.c`` with one plausible mistake planted
+(a dropped term, a wrong sign, a wrong index or divisor, swapped outputs, a wrong
+rounding step), compiled into a temporary library. Every pin in test_oracle.py is
+then run against the mutant; at least one must fail, or the pins could not have
+told that mistake apart from the definition.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import tests.test_oracle as pins
+from oracle import oracle as O
+
+SRC = os.path.join(os.path.dirname(O.__file__), "gn_oracle.c")
+
+MUTANTS = {
+    "mean_divisor": ("const double mu = sum / (double)M;", "const double mu = sum / (double)(M + 1);"),
+    "unbiased_var": ("const double v = ss / (double)M;", "const double v = ss / (double)(M - 1);"),
+    "eps_outside_sqrt": ("1.0 / sqrt(v + (double)eps)", "1.0 / (sqrt(v) + (double)eps)"),
+    "beta_sign": ("y[base + s] = gm * xhat + bt;", "y[base + s] = gm * xhat - bt;"),
+    "forward_group_index": ("const int64_t ng = n * G + c / Cg;\n            const double gm",
+                            "const int64_t ng = n * G + c % G;\n            const double gm"),
+    "dx_c2_sign": ("dx[base + s] = rs[ng] * (gm * g_ - c1[ng] - xhat * c2[ng]);",
+                   "dx[base + s] = rs[ng] * (gm * g_ - c1[ng] + xhat * c2[ng]);"),
+    "dx_drop_c1": ("dx[base + s] = rs[ng] * (gm * g_ - c1[ng] - xhat", "dx[base + s] = rs[ng] * (gm * g_ - xhat"),
+    "dx_drop_gamma": ("dx[base + s] = rs[ng] * (gm * g_", "dx[base + s] = rs[ng] * (g_"),
+    "swap_dgamma_dbeta": ("if (dgamma) dgamma[c] = a;", "if (dgamma) dgamma[c] = b;"),
+    "c2_from_s1": ("b += gno_gamma(gamma, c) * s2[n * C + c];", "b += gno_gamma(gamma, c) * s1[n * C + c];"),
+    "c1_no_mean": ("c1[n * G + g] = a / (double)M;", "c1[n * G + g] = a;"),
+    "s2_without_xhat": ("b += g_ * xhat;", "b += g_;"),
+    "bf16_truncate": ("double k = nearbyint(ldexp(a, -q));", "double k = floor(ldexp(a, -q));"),
+    "bf16_precision": ("int q = (e - 1) - 7;", "int q = (e - 1) - 8;"),
+    "bf16_nan_payload": ("return signbit(v) ? 0xFFC0 : 0x7FC0;", "return 0x7F80;"),
+}
+
+PINS = [
+    pins.test_closed_form_mean_zero_and_variance_ratio,
+    lambda: pins.test_constant_input_maps_to_beta_exactly(0.3),
+    pins.test_single_element_groups_match_printed_rstd,
+    pins.test_nan_and_inf_stay_in_their_group,
+    lambda: pins.test_against_torch_float64_group_norm("tiny"),
+    lambda: pins.test_against_torch_float64_group_norm("ragged"),
+    pins.test_special_cases_instance_norm_and_layer_norm,
+    pins.test_exact_rational_brute_force_on_eight_elements,
+    pins.test_backward_against_central_differences_all_elements,
+    pins.test_backward_closed_forms,
+    pins.test_round_bf16_matches_torch_on_fp32_values,
+    pins.test_round_bf16_ties_double_rounding_and_specials,
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} must be unique"
+    path = tmp_path / f"{name}.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / f"lib_{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-o",
+                    str(lib), str(path), "-lm"], check=True)
+    return str(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_kill_mutant(name, tmp_path, monkeypatch):
+    old, new = MUTANTS[name]
+    lib_path = _build_mutant(tmp_path, name, old, new)
+    real = O._load()
+    mutant = ctypes.CDLL(lib_path)
+    for fn in ("gno_group_stats", "gno_forward", "gno_forward_at", "gno_backward", "gno_backward_at",
+               "gno_round_bf16", "gno_round_bf16_array", "gno_round_f32_array"):
+        getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
+        getattr(mutant, fn).restype = getattr(real, fn).restype
+    monkeypatch.setattr(O, "_lib", mutant)
+    killed_by = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError):
+            killed_by.append(getattr(pin, "__name__", "lambda"))
+    assert killed_by, f"mutant {name} survived every pin"
