@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""GroupNorm fwd+bwd throughput on one MI355X, as achieved HBM GB/s.
+
+One step is the whole hot path on one batch: gn_forward (statistics + normalize) then
+gn_backward (reduction + dx), on the 128^3, C=32, G=8 bf16 UNet site with inputs
+resident in HBM. Throughput counts the two-pass method's bytes per element:
+forward 2*b_x + b_y, backward 2*(b_x + b_dy) + b_dx (16 B/element in bf16).
+
+Printed: one JSON line with the headline value, the dominant kernel's roofline
+(timed live with HIP events on the stream the kernels run on), the fp64 CPU oracle
+timed on this host as a baseline, and side figures (per-kernel times, compulsory-byte
+rate, a run with the 256 MiB last-level cache flushed between steps, a plain copy
+kernel's rate, and the 256^3 site).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+METRIC = "GroupNorm fwd+bwd achieved HBM GB/s (% of MI355X peak), bf16 128³/256³ C=32 G=8"
+KERNEL_SOURCES = ["unet_groupnorm_amd/csrc/gn_kernels.hip", "unet_groupnorm_amd/csrc/gn_plan.cpp",
+                  "unet_groupnorm_amd/csrc/gn_plan.hpp", "unet_groupnorm_amd/csrc/gn_launch.hpp"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline, roofline and baseline only")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_per_elem(x_dtype, y_dtype, dy_dtype):
+    import torch
+    sz = {torch.bfloat16: 2, torch.float32: 4}
+    bx, by, bdy = sz[x_dtype], sz[y_dtype], sz[dy_dtype]
+    phases = {"stats": bx, "apply": bx + by, "bwd_reduce": bx + bdy, "bwd_apply": bx + bdy + bx}
+    return phases, bx + by + bdy + bx
+
+
+class Runner:
+    """Holds one workload resident on the GPU with preallocated outputs."""
+
+    def __init__(self, case):
+        import torch
+
+        import unet_groupnorm_amd as gn
+        import workloads
+        self.torch, self.gn, self.case = torch, gn, case
+        inp = workloads.make(case, "cuda")
+        self.inp = inp
+        self.x, self.dy, self.G, self.eps = inp["x"], inp["dy"], inp["G"], inp["eps"]
+        self.gamma, self.beta = inp["gamma"], inp["beta"]
+        self.y = torch.empty_like(self.x, dtype=inp["out_dtype"])
+        N = case.N
+        self.mean = torch.empty((N, self.G), dtype=torch.float32, device="cuda")
+        self.rstd = torch.empty_like(self.mean)
+        self.dx = torch.empty_like(self.x)
+        self.dgamma = torch.empty(case.C, dtype=torch.float32, device="cuda")
+        self.dbeta = torch.empty_like(self.dgamma)
+        self.ws = gn.workspace_for(self.x, self.G)
+        self.phase_bytes, self.bpe = bytes_per_elem(self.x.dtype, self.y.dtype, self.dy.dtype)
+        self.step_bytes = self.bpe * case.numel
+
+    def step(self):
+        gn = self.gn
+        gn.gn_forward(self.x, self.gamma, self.beta, self.G, self.eps, workspace=self.ws, out=self.y,
+                      mean=self.mean, rstd=self.rstd)
+        gn.gn_backward(self.dy, self.x, self.mean, self.rstd, self.gamma, self.G, workspace=self.ws,
+                       dx=self.dx, dgamma=self.dgamma, dbeta=self.dbeta)
+
+    def phases(self):
+        """The same step through the split-phase entry points, one kernel each."""
+        gn = self.gn
+        return [
+            ("stats", lambda: gn.gn_forward_stats(self.x, self.G, self.ws)),
+            ("apply", lambda: gn.gn_forward_apply(self.x, self.gamma, self.beta, self.G, self.eps,
+                                                  self.y, self.mean, self.rstd, self.ws)),
+            ("bwd_reduce", lambda: gn.gn_backward_reduce(self.dy, self.x, self.mean, self.rstd,
+                                                         self.G, self.ws)),
+            ("bwd_apply", lambda: gn.gn_backward_apply(self.dy, self.x, self.mean, self.rstd,
+                                                       self.gamma, self.G, self.dx, self.dgamma,
+                                                       self.dbeta, self.ws)),
+        ]
+
+    def timed_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            self.step()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    def timed_phases(self, reps):
+        """Average duration of each kernel, from HIP events recorded between launches on the
+        stream the kernels run on (torch's current stream, which the binding passes down)."""
+        torch = self.torch
+        ph = self.phases()
+        for _, f in ph:
+            f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ph) + 1)] for _ in range(reps)]
+        for r in range(reps):
+            ev[r][0].record()
+            for i, (_, f) in enumerate(ph):
+                f()
+                ev[r][i + 1].record()
+        torch.cuda.synchronize()
+        out = {}
+        for i, (name, _) in enumerate(ph):
+            out[name] = sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
+        return out  # ms
+
+    def flushed_steps(self, steps, flush_bytes=512 << 20):
+        """Each step timed alone after overwriting a buffer twice the size of the 256 MiB
+        last-level cache, so that no input starts the step in that cache."""
+        torch = self.torch
+        buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        total = 0.0
+        for _ in range(steps):
+            buf.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            self.step()
+            e1.record()
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+        return total / steps
+
+
+def copy_ceiling_gbps(nbytes=1 << 30, reps=20):
+    import torch
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def cpu_baseline(runner, min_seconds=10.0, max_reps=3):
+    """The fp64 oracle, as it stands, on this host: forward + backward on the same volume."""
+    import numpy as np  # noqa: F401
+
+    from oracle import oracle as O
+    x, dy = runner.x.cpu(), runner.dy.cpu()
+    gamma, beta = runner.gamma.cpu(), runner.beta.cpu()
+    G, eps = runner.G, runner.eps
+    reps, t_total = 0, 0.0
+    while reps < max_reps and (reps == 0 or t_total < min_seconds):
+        t0 = time.perf_counter()
+        O.forward(x, G, gamma, beta, eps=eps)
+        O.backward(dy, x, G, gamma, eps=eps)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per = t_total / reps
+    return {
+        "value": round(runner.step_bytes / per / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"the whole {runner.case.name} volume ({runner.case.numel} elements): fp64 "
+                   f"forward + backward (outputs in fp64), {reps} repetition(s), "
+                   f"{per:.2f} s each, one thread"),
+        "seconds_per_step": round(per, 3),
+        "host_cpu": _cpu_model(),
+        "host_cores_available": os.cpu_count(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def load_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counter runs,
+    used only while the kernel sources still hash to the value recorded with them."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None, "no counter run committed"
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    return rec, "ok"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path would shard over samples or space, which is not built here)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import workloads
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    case = workloads.SCALE7
+    log(f"workload {case.name} {case.shape}; generating inputs on the GPU")
+    run = Runner(case)
+    log(f"timing {args.steps} steps after {args.warmup} warmup steps")
+    ms, wall = run.timed_steps(args.steps, args.warmup)
+    value = run.step_bytes / (ms * 1e-3) / 1e9
+
+    log("timing each kernel with HIP events")
+    ph_ms = run.timed_phases(max(args.steps, 20))
+    dom = "bwd_apply"
+    dom_bytes = run.phase_bytes[dom] * case.numel
+    dom_gbps = dom_bytes / (ph_ms[dom] * 1e-3) / 1e9
+    traffic, traffic_note = load_traffic(case.name)
+    roofline = {
+        "bound": "hbm",
+        "kernel": "bwd_apply_kernel<bf16,bf16> (dx pass: reads x and dy, writes dx)",
+        "achieved": round(dom_gbps, 1),
+        "peak": PEAK_HBM_GBPS,
+        "unit": "GB/s",
+        "frac": round(dom_gbps / PEAK_HBM_GBPS, 4),
+        "traffic": (traffic or {}).get("bytes_per_launch"),
+        "traffic_note": traffic_note if traffic is None else traffic.get("note", "ok"),
+        "algorithmic_bytes_per_launch": dom_bytes,
+        "avg_launch_us": round(ph_ms[dom] * 1e3, 2),
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": case.name, "N": case.N, "C": case.C, "G": case.G, "spatial": list(case.spatial),
+            "x_dtype": "bf16", "y_dtype": "bf16", "dy_dtype": "bf16", "dx_dtype": "bf16",
+            "stats_dtype": "fp32", "bytes_per_step": run.step_bytes,
+            "byte_model": "two-pass method bytes: fwd 2*bx+by, bwd 2*(bx+bdy)+bdx = 16 B/element",
+        },
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "roofline": roofline,
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in ph_ms.items()},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_extras:
+        compulsory = 10 * case.numel
+        out["compulsory_bytes_gbps"] = round(compulsory / (ms * 1e-3) / 1e9, 1)
+        log("timing steps with the last-level cache flushed before each")
+        fms = run.flushed_steps(max(10, args.steps // 5))
+        out["llc_flushed"] = {"ms_per_step": round(fms, 5),
+                              "value": round(run.step_bytes / (fms * 1e-3) / 1e9, 1)}
+        log("copy kernel ceiling")
+        out["copy_kernel_gbps"] = round(copy_ceiling_gbps(), 1)
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on this host")
+        out["cpu_baseline"] = cpu_baseline(run)
+    if not args.no_extras:
+        del run
+        torch.cuda.empty_cache()
+        c8 = workloads.SCALE8
+        log(f"secondary workload {c8.name}")
+        r8 = Runner(c8)
+        ms8, _ = r8.timed_steps(max(5, args.steps // 5), 3)
+        ph8 = r8.timed_phases(10)
+        out["scale8"] = {
+            "workload": c8.name, "ms_per_step": round(ms8, 4),
+            "value": round(r8.step_bytes / (ms8 * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * r8.step_bytes / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            "kernels_us": {k: round(v * 1e3, 1) for k, v in ph8.items()},
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * gn.h -- C ABI of libgn.so: 3D GroupNorm forward and backward on MI355X (gfx950).
+ *
+ * What is computed (cited from the pages the library is built from):
+ *   - "Optimize GroupNorm" (LBANN/ScaFFold pull 93), paragraph on ATen's per-(batch,
+ *     group) statistics: GroupNorm statistics are taken per (sample n, group g) over
+ *     the group's C/G channels and every voxel; y = gamma_c * (x - mu) * rstd + beta_c.
+ *   - Same page, paragraph on the independent review: rstd = 1/sqrt(var + eps) with
+ *     the biased variance (a single-element group has rstd = 316 at eps = 1e-5, and
+ *     its input gradient is exactly zero); mean/rstd are outputs, not differentiable.
+ *   - Same page, paragraph introducing the NDHWC Triton kernel: fp32 statistics from
+ *     a corrected two-pass per tile merged with Chan's parallel formula, register-only
+ *     reductions in a fixed order with no float atomics (bitwise reproducible).
+ *   - Same page, paragraph folding seven launches into four: the statistics finalize
+ *     is folded into the normalize kernel and the backward finalize and dgamma/dbeta
+ *     reduction into the dx kernel; grid, split count, tile sizes and reduction order
+ *     are pure functions of the shape.
+ *   - "Preserve GroupNorm dtype" (LBANN/ScaFFold pull 105), first paragraph: the
+ *     normalized value is computed in fp32 and only the store narrows, so the output
+ *     is the fp32 answer rounded once; an fp32 output is available on request. Second
+ *     paragraph: the plan takes no dtype, so the backward on the same values in fp32
+ *     and in bf16 gives bitwise identical dx/dgamma/dbeta.
+ *
+ * Layout. Every tensor argument is contiguous NCDHW: element (n, c, s) of a volume
+ * with S = D*H*W voxels lives at flat index (n*C + c)*S + s. Group (n, g) is the
+ * contiguous run of M = (C/G)*S elements starting at (n*C + g*C/G)*S. mean and rstd
+ * are [N*G] fp32, indexed n*G + g. gamma, beta, dgamma, dbeta are [C] fp32.
+ *
+ * Ownership and ordering. The caller owns and allocates every buffer, including the
+ * workspace (gn_workspace_bytes). The library never allocates device memory, never
+ * synchronizes the device or the stream, and never copies device-to-host. All work is
+ * enqueued on `stream` (a hipStream_t; NULL means the null stream of the current
+ * device) in stream order, and the call returns as soon as it is enqueued. Outputs are
+ * fully overwritten (dgamma/dbeta are written, not accumulated). The workspace holds
+ * intermediate partial results only between the launches of one call; it carries
+ * nothing from one call to the next and needs no initialization.
+ *
+ * Pointers. x, y, dy, dx and the workspace must be 16-byte aligned device pointers;
+ * mean, rstd, gamma, beta, dgamma, dbeta 4-byte aligned device pointers. All of them
+ * must live on one device, the device that owns x; the kernels are launched on x's
+ * device whatever device is current, and a stream that belongs to another device is
+ * rejected.
+ *
+ * Errors. Every entry point returns an int status (gn_status). All validation runs
+ * before anything is enqueued; on any error other than GN_ERR_LAUNCH nothing has been
+ * enqueued and no output is touched. After GN_ERR_LAUNCH outputs are undefined.
+ * Nothing is thrown across the ABI and no state is kept between calls.
+ */
+#ifndef GN_H
+#define GN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of x, y, dy, dx. gamma, beta, mean, rstd, dgamma, dbeta are always fp32. */
+typedef enum gn_dtype {
+    GN_F32 = 0,  /* IEEE binary32 */
+    GN_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+} gn_dtype;
+
+typedef enum gn_status {
+    GN_OK = 0,
+    GN_ERR_NULL = 1,      /* a required pointer is NULL */
+    GN_ERR_SHAPE = 2,     /* N, C, S or G <= 0, N*(C/G)*S == 1, or N*C*S too large */
+    GN_ERR_GROUPS = 3,    /* C is not a multiple of G */
+    GN_ERR_DTYPE = 4,     /* unsupported dtype or dtype combination */
+    GN_ERR_EPS = 5,       /* eps is negative or not finite */
+    GN_ERR_WORKSPACE = 6, /* workspace smaller than gn_workspace_bytes(N, C, S, G) */
+    GN_ERR_ALIGN = 7,     /* a pointer is not aligned as stated above */
+    GN_ERR_DEVICE = 8,    /* x is not device memory, or the stream belongs to another device */
+    GN_ERR_LAUNCH = 9     /* the HIP runtime refused a launch; outputs are undefined */
+} gn_status;
+
+/*
+ * Workspace size in bytes for a volume of N samples, C channels, S = D*H*W voxels and
+ * G groups. A pure function of the shape (no dtype, no device). Returns 0 for a shape
+ * that gn_forward would reject. One workspace of this size serves gn_forward and
+ * gn_backward alike (they may share it when they are stream-ordered).
+ */
+size_t gn_workspace_bytes(int64_t N, int64_t C, int64_t S, int64_t G);
+
+/*
+ * Forward. Statistics per (n, g) in fp32 (written to mean and rstd), then
+ * y = gamma_c * (x - mean) * rstd + beta_c computed in fp32 and stored once in
+ * y_dtype. x_dtype is GN_F32 or GN_BF16; y_dtype is x_dtype or GN_F32 (the fp32-output
+ * mode). gamma == NULL means all ones, beta == NULL all zeros. eps must be finite and
+ * >= 0. Two kernels are enqueued: gn_forward_stats then gn_forward_apply.
+ */
+int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta,
+               int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+               void* y, int y_dtype, float* mean, float* rstd,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/* First half of gn_forward: per-chunk fp32 partial statistics of x into the workspace. */
+int gn_forward_stats(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Second half of gn_forward: merges the workspace partials that gn_forward_stats left
+ * (same x, same shape, stream-ordered after it) in a fixed order into mean/rstd and
+ * writes y. Same argument rules as gn_forward.
+ */
+int gn_forward_apply(const void* x, int x_dtype, const float* gamma, const float* beta,
+                     int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+                     void* y, int y_dtype, float* mean, float* rstd,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward. Recomputes xhat = (x - mean) * rstd from the mean/rstd gn_forward wrote,
+ * reduces sum(dy) and sum(dy * xhat) per (n, c) in a fixed order, then writes
+ *   dx = rstd * (gamma_c * dy - c1 - xhat * c2),  c1 = (1/M) sum_{c in g} gamma_c sum(dy),
+ *                                                 c2 = (1/M) sum_{c in g} gamma_c sum(dy*xhat)
+ * in x_dtype, and dgamma_c = sum_n sum(dy * xhat), dbeta_c = sum_n sum(dy).
+ * dy_dtype is GN_F32 or GN_BF16 independently of x_dtype; the same dy values in either
+ * dtype give bitwise identical results. gamma == NULL means all ones. dx, dgamma and
+ * dbeta may each be NULL (not computed). A group with M == 1 has dx == +0 exactly for
+ * finite inputs (NaN/Inf still propagate). Two kernels are enqueued:
+ * gn_backward_reduce then gn_backward_apply.
+ */
+int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                const float* mean, const float* rstd, const float* gamma,
+                int64_t N, int64_t C, int64_t S, int64_t G,
+                void* dx, float* dgamma, float* dbeta,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* First half of gn_backward: per-chunk fp32 partial sums of dy and dy*xhat into the workspace. */
+int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                       const float* mean, const float* rstd,
+                       int64_t N, int64_t C, int64_t S, int64_t G,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Second half of gn_backward: merges the partials gn_backward_reduce left (same inputs,
+ * stream-ordered after it) in a fixed order and writes dx, dgamma, dbeta.
+ */
+int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                      const float* mean, const float* rstd, const float* gamma,
+                      int64_t N, int64_t C, int64_t S, int64_t G,
+                      void* dx, float* dgamma, float* dbeta,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static English description of a status code (never NULL). */
+const char* gn_status_string(int status);
+
+/*
+ * The launch plan for a shape: a pure function of (N, C, S, G) with no dtype and no
+ * device input, exposed so that tests and benchmarks can see the decomposition.
+ * Every kernel works on "jobs": job j covers elements [k*chunk, min((k+1)*chunk, S))
+ * of row r = j / chunks_per_row (row r = n*C + c), k = j % chunks_per_row.
+ */
+typedef struct gn_plan_info {
+    int64_t rows;               /* N*C */
+    int64_t chunk;              /* elements per job (the last job of a row may be shorter) */
+    int64_t chunks_per_row;     /* K */
+    int64_t jobs;               /* rows * K: workgroups per launch */
+    int64_t partials_per_group; /* (C/G) * K */
+    int32_t block;              /* threads per workgroup (64, 128 or 256) */
+    int32_t vectors_per_step;   /* 8-element vectors each thread loads per step */
+    size_t workspace_bytes;     /* == gn_workspace_bytes */
+} gn_plan_info;
+
+/* Fills *out for a valid shape and returns GN_OK; otherwise returns the shape error. */
+int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out);
+
+/* ABI version of this header (incremented on any incompatible change). */
+int gn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GN_H */

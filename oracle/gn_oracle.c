@@ -305,3 +305,32 @@ void gno_round_f32_array(const double* v, int64_t n, float* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = (float)v[i];
 }
+
+/*
+ * Per-channel sums of |dy| and |dy * xhat| (xhat from the given statistics): the
+ * magnitudes that bound the rounding error of any fp32 summation of dbeta and dgamma.
+ */
+int gno_channel_abs_sums(const void* dy, int dy_dt, const void* x, int x_dt,
+                         int64_t N, int64_t C, int64_t S, int64_t G,
+                         const double* mean, const double* rstd, double* abs_dy, double* abs_dyxhat)
+{
+    if (!gno_shape_ok(N, C, S, G)) return 1;
+    const int64_t Cg = C / G;
+    for (int64_t c = 0; c < C; ++c) { abs_dy[c] = 0.0; abs_dyxhat[c] = 0.0; }
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t ng = n * G + c / Cg;
+            const int64_t base = (n * C + c) * S;
+            double a = 0.0, b = 0.0;
+            for (int64_t s = 0; s < S; ++s) {
+                const double g_ = gno_load(dy, dy_dt, base + s);
+                const double xhat = (gno_load(x, x_dt, base + s) - mean[ng]) * rstd[ng];
+                a += fabs(g_);
+                b += fabs(g_ * xhat);
+            }
+            abs_dy[c] += a;
+            abs_dyxhat[c] += b;
+        }
+    }
+    return 0;
+}

@@ -41,6 +41,8 @@ def _load():
                                  P, P, P, P, P, P, P]
     lib.gno_backward_at.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, I64, I64, I64, I64,
                                     P, P, P, P, P, I64, P]
+    lib.gno_channel_abs_sums.argtypes = [P, ctypes.c_int, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P]
+    lib.gno_channel_abs_sums.restype = ctypes.c_int
     lib.gno_round_bf16.argtypes = [ctypes.c_double]
     lib.gno_round_bf16.restype = ctypes.c_uint16
     lib.gno_round_bf16_array.argtypes = [P, I64, P]
@@ -170,6 +172,19 @@ def backward_at(dy, x, G, idx, mean, rstd, c1, c2, gamma=None, dy_tag=None, x_ta
     _load().gno_backward_at(_ptr(ga), gc, _ptr(xa), xc, _ptr(g), N, C, S, G,
                             *[_ptr(a) for a in arrs], _ptr(idx), idx.size, _ptr(out))
     return out
+
+
+def channel_abs_sums(dy, x, G, mean, rstd, dy_tag=None, x_tag=None):
+    """(sum |dy|, sum |dy * xhat|) per channel [C], xhat from the given fp64 statistics."""
+    xa, xc = _typed(x, x_tag)
+    ga, gc = _typed(dy, dy_tag)
+    N, C, S = _shape(xa)
+    a = np.empty(C); b = np.empty(C)
+    mean = np.ascontiguousarray(mean, dtype=np.float64)
+    rstd = np.ascontiguousarray(rstd, dtype=np.float64)
+    _load().gno_channel_abs_sums(_ptr(ga), gc, _ptr(xa), xc, N, C, S, G, _ptr(mean), _ptr(rstd),
+                                 _ptr(a), _ptr(b))
+    return a, b
 
 
 def round_bf16(v):

@@ -1,0 +1,92 @@
+"""The C ABI on a host without a GPU: every declared symbol is exported, and invalid
+arguments are rejected with the documented status before anything touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from unet_groupnorm_amd._lib import GN_BF16, GN_F32, STATUS_NAMES, lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(gn_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared_functions()
+    assert len(names) == 10, names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_enum_matches_header():
+    text = open(HEADER).read()
+    for code, name in STATUS_NAMES.items():
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
+    assert re.search(r"GN_F32\s*=\s*0", text) and re.search(r"GN_BF16\s*=\s*1", text)
+    assert GN_F32 == 0 and GN_BF16 == 1
+    for code in STATUS_NAMES:
+        assert lib.gn_status_string(code)
+    assert lib.gn_status_string(1234) == b"unknown status"
+    assert lib.gn_abi_version() == 1
+
+
+# Fake but aligned, non-null addresses: validation never dereferences them, and every
+# case below fails validation before the device is queried.
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+
+
+def fwd(**kw):
+    args = dict(x=A, xdt=GN_BF16, gamma=None, beta=None, N=1, C=8, S=64, G=4, eps=1e-5, y=B,
+                ydt=GN_BF16, mean=A, rstd=B, ws=A, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return lib.gn_forward(*args.values())
+
+
+def bwd(**kw):
+    args = dict(dy=A, dydt=GN_BF16, x=B, xdt=GN_BF16, mean=A, rstd=B, gamma=None, N=1, C=8, S=64,
+                G=4, dx=A, dgamma=None, dbeta=None, ws=B, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return lib.gn_backward(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(y=None), 1), (dict(mean=None), 1), (dict(ws=None), 1),
+    (dict(N=0), 2), (dict(S=-1), 2), (dict(G=0), 2), (dict(C=8, G=8, S=1), 2),
+    (dict(C=6, G=4), 3),
+    (dict(xdt=2), 4), (dict(xdt=GN_F32, ydt=GN_BF16), 4), (dict(ydt=7), 4),
+    (dict(eps=-1e-5), 5), (dict(eps=float("nan")), 5), (dict(eps=float("inf")), 5),
+    (dict(wsb=16), 6),
+    (dict(x=ctypes.c_void_p(0x10002)), 7), (dict(y=ctypes.c_void_p(0x20008)), 7),
+    (dict(ws=ctypes.c_void_p(0x10004)), 7), (dict(mean=ctypes.c_void_p(0x10001)), 7),
+])
+def test_forward_validation(kw, status):
+    assert fwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), 1), (dict(x=None), 1), (dict(rstd=None), 1), (dict(ws=None), 1),
+    (dict(C=6, G=4), 3), (dict(N=-2), 2), (dict(dydt=5), 4), (dict(xdt=3), 4),
+    (dict(wsb=0), 6), (dict(dx=ctypes.c_void_p(0x10008)), 7),
+    (dict(dgamma=ctypes.c_void_p(0x10002)), 7),
+])
+def test_backward_validation(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_split_phase_validation():
+    assert lib.gn_forward_stats(None, GN_BF16, 1, 8, 64, 4, A, 1 << 20, None) == 1
+    assert lib.gn_forward_stats(A, GN_BF16, 1, 8, 64, 3, A, 1 << 20, None) == 3
+    assert lib.gn_forward_stats(A, GN_BF16, 1, 8, 64, 4, A, 8, None) == 6
+    assert lib.gn_forward_apply(A, GN_BF16, None, None, 1, 8, 64, 4, 1e-5, None, GN_BF16, A, B, A,
+                                1 << 20, None) == 1
+    assert lib.gn_backward_reduce(A, 9, B, GN_BF16, A, B, 1, 8, 64, 4, A, 1 << 20, None) == 4
+    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, A, B, None, 1, 8, 64, 4, None, None, None,
+                                 A, 8, None) == 6

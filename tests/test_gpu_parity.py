@@ -1,0 +1,339 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Small and ragged shapes are compared element by element; the 128^3 / 256^3 sites and
+the > 2^31-element volume are compared on every statistic and parameter gradient and
+on a sample of y and dx (random elements plus the edges of jobs), at the plan and
+launch configuration the benchmark times. Tolerances are documented in tests/parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import unet_groupnorm_amd as gn
+import workloads
+from oracle import oracle as O
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def _on_gpu(inp):
+    out = dict(inp)
+    for k in ("x", "gamma", "beta", "dy"):
+        if out[k] is not None:
+            out[k] = out[k].to(DEV)
+    return out
+
+
+def _run(inp, out_dtype=None, dy=None):
+    x, G, eps = inp["x"], inp["G"], inp["eps"]
+    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, eps, out_dtype or inp["out_dtype"])
+    dy = inp["dy"] if dy is None else dy
+    dx, dg, db = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G)
+    torch.cuda.synchronize()
+    return {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dgamma": dg, "dbeta": db}
+
+
+def _beta_at(idx, x, beta):
+    S = int(np.prod(x.shape[2:])) if x.dim() > 2 else 1
+    c = (idx // S) % x.shape[1]
+    return beta.cpu().numpy().astype(np.float64)[c]
+
+
+def full_check(inp, tag):
+    """Element-by-element comparison of every output."""
+    say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} dy {inp['dy'].dtype} "
+        f"out {inp['out_dtype']} G={inp['G']} -> gn_forward + gn_backward")
+    g = _on_gpu(inp)
+    r = _run(g)
+    x, dy, G, eps = inp["x"].cpu(), inp["dy"].cpu(), inp["G"], inp["eps"]
+    gamma, beta = inp["gamma"].cpu(), inp["beta"].cpu()
+    f = O.forward(x, G, gamma, beta, eps=eps)
+    rep = P.check_stats(P.to_np(r["mean"]), P.to_np(r["rstd"]), f["mean"], f["var"], f["rstd"])
+    idx = np.arange(x.numel())
+    rep.update(P.check_y(P.to_np(r["y"]).reshape(-1), f["y"].reshape(-1), _beta_at(idx, x, beta)))
+    b = O.backward(dy, x, G, gamma, eps=eps)
+    rep.update(P.check_dx(P.to_np(r["dx"]).reshape(-1), b["dx"].reshape(-1)))
+    a_dy, a_dyx = O.channel_abs_sums(dy, x, G, b["mean"], b["rstd"])
+    N, C = x.shape[:2]
+    depth = P.reduction_depth(gn.gn_plan_query(N, C, x.numel() // (N * C), G), N)
+    rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth))
+    rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth))
+    say(f"{tag}: ok {rep}")
+    return r
+
+
+def _sample_indices(x, G, n_random, seed):
+    N, C = x.shape[:2]
+    S = x.numel() // (N * C)
+    plan = gn.gn_plan_query(N, C, S, G)
+    rng = np.random.default_rng(seed)
+    parts = [rng.integers(0, x.numel(), n_random)]
+    # edges of up to 512 jobs: first and last 64 elements of each
+    K, chunk = plan["chunks_per_row"], plan["chunk"]
+    jobs = rng.choice(plan["jobs"], min(512, plan["jobs"]), replace=False)
+    for j in jobs:
+        row, k = divmod(int(j), K)
+        lo, hi = row * S + k * chunk, row * S + min((k + 1) * chunk, S)
+        parts.append(np.arange(lo, min(lo + 64, hi)))
+        parts.append(np.arange(max(hi - 64, lo), hi))
+    parts.append(np.array([0, x.numel() - 1]))
+    return np.unique(np.concatenate(parts)).astype(np.int64)
+
+
+def sampled_check(inp, tag, n_random=1 << 20, seed=0):
+    """Full statistics and parameter gradients; y and dx on sampled elements."""
+    say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} G={inp['G']} "
+        f"(sampled) -> gn_forward + gn_backward")
+    r = _run(inp)
+    x, dy, G, eps = inp["x"].cpu(), inp["dy"].cpu(), inp["G"], inp["eps"]
+    gamma, beta = inp["gamma"].cpu(), inp["beta"].cpu()
+    say(f"{tag}: oracle statistics")
+    mean64, var64, rstd64 = O.group_stats(x, G, eps)
+    rep = P.check_stats(P.to_np(r["mean"]), P.to_np(r["rstd"]), mean64, var64, rstd64)
+    idx = _sample_indices(x, G, n_random, seed)
+    it = torch.from_numpy(idx).to(DEV)
+    y64 = O.forward_at(x, G, idx, mean64, rstd64, gamma, beta)
+    rep.update(P.check_y(P.to_np(r["y"].reshape(-1)[it]), y64, _beta_at(idx, x, beta)))
+    say(f"{tag}: oracle backward")
+    b = O.backward(dy, x, G, gamma, eps=eps, want_dx=False)
+    dx64 = O.backward_at(dy, x, G, idx, b["mean"], b["rstd"], b["c1"], b["c2"], gamma)
+    rep.update(P.check_dx(P.to_np(r["dx"].reshape(-1)[it]), dx64))
+    a_dy, a_dyx = O.channel_abs_sums(dy, x, G, b["mean"], b["rstd"])
+    N, C = x.shape[:2]
+    depth = P.reduction_depth(gn.gn_plan_query(N, C, x.numel() // (N * C), G), N)
+    rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth))
+    rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth))
+    say(f"{tag}: ok ({idx.size} sampled elements) {rep}")
+    return r
+
+
+# ----------------------------------------------------------------------------- named workloads
+
+@pytest.mark.parametrize("case", [workloads.TINY, workloads.DEEP, workloads.DEEP_F32OUT],
+                         ids=lambda c: c.name)
+def test_small_workloads_elementwise(case):
+    full_check(workloads.make(case, "cpu"), case.name)
+
+
+RAGGED = [
+    workloads.custom(2, 6, 2, (5, 7, 3), torch.bfloat16, dist="unet", seed=11),
+    workloads.custom(3, 12, 3, (17, 17, 17), torch.bfloat16, dist="normal", seed=12),
+    workloads.custom(1, 4, 2, (40, 40, 41), torch.float32, dist="tiny", seed=13),
+    workloads.custom(2, 8, 4, (33, 31, 29), torch.bfloat16, dist="deep", seed=14),
+    workloads.custom(1, 2, 1, (3 * 8192 + 5,), torch.float32, dist="unet", seed=15),
+    workloads.custom(5, 10, 5, (7, 7, 7), torch.bfloat16, dist="unet", seed=16, out_dtype=torch.float32),
+    workloads.custom(2, 3, 3, (65537,), torch.float32, dist="normal", seed=17),
+    workloads.custom(1, 16, 4, (64, 64, 65), torch.bfloat16, dist="unet", seed=18),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: c.name)
+def test_ragged_shapes_elementwise(case):
+    full_check(workloads.make(case, "cpu"), case.name)
+
+
+CENSUS = workloads.census_cases()
+
+
+@pytest.mark.parametrize("case", CENSUS, ids=lambda c: c.name)
+def test_census_sites(case):
+    if case.numel <= (1 << 23):
+        full_check(workloads.make(case, "cpu"), case.name)
+    else:
+        sampled_check(workloads.make(case, DEV), case.name, n_random=1 << 18, seed=case.seed)
+
+
+@pytest.mark.parametrize("case", [workloads.SCALE7, workloads.SCALE8], ids=lambda c: c.name)
+def test_unet_top_sites_sampled(case):
+    sampled_check(workloads.make(case, DEV), case.name, seed=case.seed)
+
+
+# ----------------------------------------------------------------------------- closed forms on the GPU
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape,G", [((2, 6, 9, 10, 11), 3), ((1, 32, 128, 128, 128), 8)])
+def test_constant_input_gives_beta_bitwise(dtype, shape, G):
+    say(f"constant input {shape} {dtype}")
+    N, C = shape[:2]
+    # one constant per group (n, g), shared by the group's C/G channels
+    consts = torch.linspace(-3.0, 100.0, N * G).view(N, G, 1).expand(N, G, C // G).reshape(N, C)
+    x = consts.view(N, C, *([1] * (len(shape) - 2))).expand(shape).to(dtype).contiguous().to(DEV)
+    beta = torch.linspace(-0.5, 0.5, C, device=DEV)
+    gamma = torch.linspace(0.5, 1.5, C, device=DEV)
+    y, mean, rstd = gn.gn_forward(x, gamma, beta, G, 1e-5)
+    torch.cuda.synchronize()
+    expect = beta.view(1, C, *([1] * (len(shape) - 2))).expand(shape).to(dtype)
+    assert torch.equal(y, expect)
+    assert torch.all(rstd == rstd.flatten()[0]).item()
+    assert abs(rstd.flatten()[0].item() - 1 / math.sqrt(np.float32(1e-5))) <= 1e-5 * 316.3
+
+
+def test_single_element_groups():
+    say("single-element groups (2, 4, 1, 1, 1), G=4")
+    rng = np.random.default_rng(3)
+    x = torch.tensor(rng.normal(size=(2, 4, 1, 1, 1)), dtype=torch.float32, device=DEV)
+    dy = torch.tensor(rng.normal(size=(2, 4, 1, 1, 1)), dtype=torch.float32, device=DEV)
+    gamma = torch.tensor([1.1, 0.9, 1.3, 0.7], device=DEV)
+    beta = torch.tensor([0.1, -0.2, 0.3, -0.4], device=DEV)
+    y, mean, rstd = gn.gn_forward(x, gamma, beta, 4, 1e-5)
+    dx, dg, db = gn.gn_backward(dy, x, mean, rstd, gamma, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(y, beta.view(1, 4, 1, 1, 1).expand(2, 4, 1, 1, 1))
+    assert torch.equal(mean, x.view(2, 4))
+    assert torch.equal(dx.view(torch.int32), torch.zeros_like(dx).view(torch.int32))  # +0 exactly
+    assert torch.equal(dg, torch.zeros_like(dg))
+    assert torch.allclose(db, dy.sum(dim=(0, 2, 3, 4)), rtol=1e-6, atol=0)
+    ref = 1 / math.sqrt(float(np.float32(1e-5)))
+    assert torch.all((rstd - ref).abs() <= 1e-5 * ref).item()
+
+
+def test_nan_and_inf_confined_to_their_group():
+    say("NaN/Inf in two groups of (2, 8, 6, 6, 6), G=4")
+    inp = workloads.make(workloads.custom(2, 8, 4, (6, 6, 6), torch.bfloat16, seed=21), "cpu")
+    x = inp["x"].clone()
+    x[0, 2, 1, 1, 1] = float("nan")
+    x[1, 7, 0, 0, 0] = float("inf")
+    inp["x"] = x
+    full_check(inp, "nan_inf")
+
+
+def test_large_mean_offset_keeps_variance():
+    """fp32 input at mu/sigma = 1e5, where E[x^2] - E[x]^2 loses the variance."""
+    say("mu/sigma = 1e5, fp32, (1, 4, 32, 32, 32), G=2")
+    rng = np.random.default_rng(7)
+    x = (1e5 + rng.normal(size=(1, 4, 32, 32, 32))).astype(np.float32)
+    xt = torch.from_numpy(x).to(DEV)
+    y, mean, rstd = gn.gn_forward(xt, None, None, 2, 1e-5)
+    torch.cuda.synchronize()
+    m64, v64, r64 = O.group_stats(x, 2, 1e-5)
+    P.check_stats(P.to_np(mean), P.to_np(rstd), m64, v64, r64)
+
+
+# ----------------------------------------------------------------------------- bitwise properties
+
+@pytest.mark.parametrize("case", [workloads.DEEP, workloads.SCALE7], ids=lambda c: c.name)
+def test_bf16_output_is_fp32_output_rounded_once(case):
+    say(f"{case.name}: bf16 output vs fp32 output rounded once")
+    inp = workloads.make(case, DEV, with_dy=False)
+    x, G = inp["x"], inp["G"]
+    y16, m16, r16 = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], torch.bfloat16)
+    y32, m32, r32 = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(m16, m32) and torch.equal(r16, r32)
+    # fp32 -> bf16 round-to-nearest-even on the host (via fp64, exact for fp32 values)
+    ref = O.round_bf16(y32.cpu().numpy().astype(np.float64).reshape(-1))
+    got = P.to_np(y16).reshape(-1)
+    nan = np.isnan(y32.cpu().numpy().reshape(-1))
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("case", [workloads.DEEP, workloads.SCALE7], ids=lambda c: c.name)
+def test_dy_dtype_does_not_change_a_bit(case):
+    say(f"{case.name}: dy bf16 vs the same values in fp32")
+    inp = workloads.make(case, DEV)
+    x, G = inp["x"], inp["G"]
+    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"])
+    a = gn.gn_backward(inp["dy"], x, mean, rstd, inp["gamma"], G)
+    b = gn.gn_backward(inp["dy"].float(), x, mean, rstd, inp["gamma"], G)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u.view(torch.int32),
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v.view(torch.int32))
+
+
+@pytest.mark.parametrize("case", [workloads.SCALE7, workloads.DEEP], ids=lambda c: c.name)
+def test_repeats_are_bitwise_identical_with_poisoned_workspace(case):
+    say(f"{case.name}: 10 repeats, workspace poisoned with NaN before every call")
+    inp = workloads.make(case, DEV)
+    x, G = inp["x"], inp["G"]
+    ws = gn.workspace_for(x, G)
+    first = None
+    for i in range(10):
+        ws.view(torch.float32).fill_(float("nan"))
+        y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], workspace=ws)
+        ws.view(torch.float32).fill_(float("nan"))
+        dx, dg, db = gn.gn_backward(inp["dy"], x, mean, rstd, inp["gamma"], G, workspace=ws)
+        torch.cuda.synchronize()
+        outs = [t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+                for t in (y, mean, rstd, dx, dg, db)]
+        if first is None:
+            first = outs
+        else:
+            for u, v in zip(outs, first):
+                assert torch.equal(u, v), f"repeat {i} differs"
+
+
+def test_split_phase_entry_points_match_fused():
+    case = workloads.SCALE7
+    say(f"{case.name}: split-phase entry points vs gn_forward/gn_backward")
+    inp = workloads.make(case, DEV)
+    x, G, gamma, beta = inp["x"], inp["G"], inp["gamma"], inp["beta"]
+    y, mean, rstd = gn.gn_forward(x, gamma, beta, G, inp["eps"])
+    dx, dg, db = gn.gn_backward(inp["dy"], x, mean, rstd, gamma, G)
+    ws = gn.workspace_for(x, G)
+    y2, mean2, rstd2 = torch.empty_like(y), torch.empty_like(mean), torch.empty_like(rstd)
+    gn.gn_forward_stats(x, G, ws)
+    gn.gn_forward_apply(x, gamma, beta, G, inp["eps"], y2, mean2, rstd2, ws)
+    dx2, dg2, db2 = torch.empty_like(dx), torch.empty_like(dg), torch.empty_like(db)
+    gn.gn_backward_reduce(inp["dy"], x, mean2, rstd2, G, ws)
+    gn.gn_backward_apply(inp["dy"], x, mean2, rstd2, gamma, G, dx2, dg2, db2, ws)
+    torch.cuda.synchronize()
+    for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2), (dg, dg2), (db, db2)):
+        assert torch.equal(u, v)
+
+
+def test_autograd_function_matches_entry_points():
+    say("GroupNormFn through autograd vs entry points (deep workload)")
+    inp = workloads.make(workloads.DEEP, DEV)
+    x = inp["x"].clone().requires_grad_(True)
+    gamma = inp["gamma"].clone().requires_grad_(True)
+    beta = inp["beta"].clone().requires_grad_(True)
+    y, mean, rstd = gn.GroupNormFn.apply(x, gamma, beta, inp["G"], inp["eps"], None)
+    assert not mean.requires_grad and not rstd.requires_grad
+    y.backward(inp["dy"])
+    y2, m2, r2 = gn.gn_forward(inp["x"], inp["gamma"], inp["beta"], inp["G"], inp["eps"])
+    dx2, dg2, db2 = gn.gn_backward(inp["dy"], inp["x"], m2, r2, inp["gamma"], inp["G"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), y2) and torch.equal(x.grad, dx2)
+    assert torch.equal(gamma.grad, dg2) and torch.equal(beta.grad, db2)
+
+
+def test_binding_rejects_bad_arguments():
+    say("argument errors")
+    x = torch.zeros((0, 4, 2, 2, 2), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gn.GnError, match="GN_ERR_SHAPE"):
+        gn.gn_forward(x, None, None, 2)
+    x = torch.zeros((1, 6, 2, 2, 2), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gn.GnError, match="GN_ERR_GROUPS"):
+        gn.gn_forward(x, None, None, 4)
+    x = torch.zeros((1, 4, 1, 1, 1), dtype=torch.float32, device=DEV)
+    with pytest.raises(gn.GnError, match="GN_ERR_SHAPE"):
+        gn.gn_forward(x, None, None, 4)
+    x = torch.zeros((1, 4, 8, 8, 8), dtype=torch.float32, device=DEV)
+    with pytest.raises(gn.GnError, match="GN_ERR_EPS"):
+        gn.gn_forward(x, None, None, 2, eps=-1.0)
+    with pytest.raises(gn.GnError, match="GN_ERR_DTYPE"):
+        gn.gn_forward(x, None, None, 2, out_dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        gn.gn_forward(x.transpose(2, 3), None, None, 2)
+    with pytest.raises(gn.GnError, match="GN_ERR_DEVICE"):
+        gn.gn_forward(x.cpu().pin_memory(), None, None, 2, out=torch.empty_like(x),
+                      mean=torch.empty(1, 2, device=DEV), rstd=torch.empty(1, 2, device=DEV),
+                      workspace=gn.workspace_for(x, 2))
+
+
+# ----------------------------------------------------------------------------- largest size
+
+def test_volume_past_int32_indexing():
+    """2^31 + 512 elements per tensor (bf16): int64 offsets, statistics of 2^28-element groups."""
+    S = (1 << 28) + 64
+    case = workloads.custom(1, 8, 8, (S,), torch.bfloat16, dist="unet", seed=31)
+    sampled_check(workloads.make(case, DEV), "int64_volume", n_random=1 << 16, seed=31)

@@ -1,0 +1,108 @@
+"""Host-side checks of the launch plan and of the kernels' index arithmetic (no GPU).
+
+The plan comes from libgn.so (gn_plan_query). The job -> element and lane -> vector
+arithmetic of gn_kernels.hip is restated here in numpy and checked for every shape:
+each element of the volume belongs to exactly one job, every vector load or store a
+kernel issues stays inside the volume, and every partial index stays inside the
+workspace. These are the conditions under which the kernels cannot touch memory
+outside their buffers.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import unet_groupnorm_amd as g
+from unet_groupnorm_amd._lib import lib
+
+VEC = 8
+
+
+def _jobs(plan, S):
+    K, chunk = plan["chunks_per_row"], plan["chunk"]
+    for j in range(plan["jobs"]):
+        row, k = divmod(j, K)
+        lo = row * S + k * chunk
+        hi = row * S + min((k + 1) * chunk, S)
+        yield j, row, k, lo, hi
+
+
+SHAPES = [
+    (1, 8, 4096, 4), (1, 32, 128 ** 3, 8), (1, 32, 256 ** 3, 8), (4, 512, 512, 32),
+    (1, 64, 64 ** 3, 8), (1, 128, 32 ** 3, 16), (1, 256, 16 ** 3, 32), (1, 512, 8 ** 3, 32),
+    (2, 6, 105, 2), (3, 4, 1, 4), (1, 4, 7, 2), (2, 12, 4913, 3), (1, 2, 3 * 8192 + 5, 1),
+    (5, 10, 333, 5), (1, 1, 2 ** 20 + 3, 1), (2, 3, 65537, 3),
+]
+
+
+@pytest.mark.parametrize("N,C,S,G", SHAPES)
+def test_plan_is_consistent(N, C, S, G):
+    p = g.gn_plan_query(N, C, S, G)
+    assert p["rows"] == N * C
+    assert p["jobs"] == p["rows"] * p["chunks_per_row"]
+    assert p["partials_per_group"] == (C // G) * p["chunks_per_row"]
+    assert p["block"] in (64, 128, 256)
+    assert (p["chunks_per_row"] - 1) * p["chunk"] < S <= p["chunks_per_row"] * p["chunk"]
+    assert p["workspace_bytes"] >= 8 * p["jobs"] and p["workspace_bytes"] % 256 == 0
+    assert g.gn_workspace_bytes(N, C, S, G) == p["workspace_bytes"]
+    if p["chunks_per_row"] > 1:
+        step = p["block"] * p["vectors_per_step"] * VEC
+        assert p["chunk"] % step == 0
+
+
+@pytest.mark.parametrize("N,C,S,G", [s for s in SHAPES if s[0] * s[1] * s[2] <= 2 ** 22])
+def test_jobs_cover_every_element_once_and_stay_in_bounds(N, C, S, G):
+    p = g.gn_plan_query(N, C, S, G)
+    total = N * C * S
+    seen = np.zeros(total, dtype=np.int32)
+    blk, U = p["block"], p["vectors_per_step"]
+    stepv = blk * U
+    for j, row, k, lo, hi in _jobs(p, S):
+        assert 0 <= lo < hi <= total
+        seen[lo:hi] += 1
+        v0 = lo // VEC
+        vf0, vf1 = (lo + VEC - 1) // VEC, hi // VEC
+        nvec = (hi + VEC - 1) // VEC - v0
+        touched = np.zeros(nvec, dtype=np.int32)
+        for sv0 in range(v0, v0 + nvec, stepv):
+            full = sv0 >= vf0 and sv0 + stepv <= vf1
+            lanes = np.arange(blk)
+            for u in range(U):
+                vi = sv0 + u * blk + lanes
+                if full:
+                    # full path: every lane loads/stores a whole vector
+                    assert vi.min() >= vf0 and vi.max() < vf1
+                    assert (vi.max() + 1) * VEC <= total
+                    touched[vi - v0] += 1
+                else:
+                    whole = (vi >= vf0) & (vi < vf1)
+                    assert ((vi[whole] + 1) * VEC <= total).all()
+                    elems = vi[~whole][:, None] * VEC + np.arange(VEC)[None, :]
+                    ok = (elems >= lo) & (elems < hi)
+                    assert (elems[ok] < total).all() and (elems[ok] >= 0).all()
+                    inside = (vi - v0 >= 0) & (vi - v0 < nvec)
+                    touched[(vi - v0)[inside]] += 1
+        assert (touched == 1).all(), "each vector of a job is visited by exactly one lane-step"
+        # the finalize reads partials (n*C + g*Cg)*K + [0, P) of the job's group
+        n, c = divmod(row, C)
+        grp = c // (C // G)
+        pbase = (n * C + grp * (C // G)) * p["chunks_per_row"]
+        assert 0 <= pbase and pbase + p["partials_per_group"] <= p["jobs"]
+    assert (seen == 1).all()
+
+
+def test_invalid_shapes_are_rejected_before_any_launch():
+    info = g.gn_plan_query  # noqa: F841
+    assert lib.gn_workspace_bytes(0, 4, 8, 2) == 0
+    assert lib.gn_workspace_bytes(1, 6, 8, 4) == 0        # C % G != 0
+    assert lib.gn_workspace_bytes(1, 4, 1, 4) == 0        # a single value per group set
+    assert lib.gn_workspace_bytes(2, 4, 1, 4) > 0         # M == 1 with N > 1 is legal
+    assert lib.gn_workspace_bytes(1, 4, 1, 2) > 0
+    assert lib.gn_workspace_bytes(1, 2 ** 20, 2 ** 30, 1) == 0  # too many elements
+
+
+def test_plan_is_a_pure_function_of_shape():
+    shapes = list(itertools.product([1, 2, 4], [8, 32, 512], [1, 343, 512, 4096, 128 ** 3], [1, 8]))
+    first = {s: g.gn_plan_query(*s) for s in shapes if s[1] % s[3] == 0 and s[0] * (s[1] // s[3]) * s[2] > 1}
+    for s in reversed(list(first)):
+        assert g.gn_plan_query(*s) == first[s]

@@ -1,0 +1,258 @@
+// gn_api.cpp -- the C ABI declared in include/gn.h: validation, planning, launches.
+//
+// Every check runs before anything is enqueued. The library keeps no state, allocates
+// nothing, never synchronizes and never reads device memory from the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "gn.h"
+#include "gn_launch.hpp"
+#include "gn_plan.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool dtype_ok(int d) { return d == GN_F32 || d == GN_BF16; }
+
+int plan_or_error(int64_t N, int64_t C, int64_t S, int64_t G, gn::Plan* p)
+{
+    const int rc = gn::make_plan(N, C, S, G, p);
+    return rc == 0 ? GN_OK : (rc == 3 ? GN_ERR_GROUPS : GN_ERR_SHAPE);
+}
+
+int workspace_check(const void* ws, size_t bytes, const gn::Plan& p)
+{
+    if (!aligned(ws, 16)) return GN_ERR_ALIGN;
+    if (bytes < p.ws_bytes) return GN_ERR_WORKSPACE;
+    return GN_OK;
+}
+
+// Makes x's device current for the duration of a call ("Optimize GroupNorm", paragraph on
+// the independent review: launching on the current device instead of the input's device
+// faulted on a tensor living on another GPU). A stream of another device is rejected.
+class DeviceScope {
+  public:
+    int enter(const void* x, void* stream)
+    {
+        hipPointerAttribute_t attr;
+        if (hipPointerGetAttributes(&attr, x) != hipSuccess) {
+            (void)hipGetLastError();
+            return GN_ERR_DEVICE;
+        }
+        if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return GN_ERR_DEVICE;
+        const int dev = attr.device;
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return GN_ERR_DEVICE;
+        if (stream) {
+            hipDevice_t sdev = -1;
+            if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) {
+                (void)hipGetLastError();
+                return GN_ERR_DEVICE;
+            }
+            if (sdev != dev) return GN_ERR_DEVICE;
+        }
+        if (cur != dev) {
+            if (hipSetDevice(dev) != hipSuccess) return GN_ERR_DEVICE;
+            prev_ = cur;
+        }
+        return GN_OK;
+    }
+    ~DeviceScope()
+    {
+        if (prev_ >= 0) (void)hipSetDevice(prev_);
+    }
+
+  private:
+    int prev_ = -1;
+};
+
+int fwd_check(const void* x, int x_dtype, const float* gamma, const float* beta, int64_t N,
+              int64_t C, int64_t S, int64_t G, float eps, const void* y, int y_dtype,
+              const float* mean, const float* rstd, const void* ws, size_t ws_bytes, gn::Plan* p)
+{
+    if (!x || !y || !mean || !rstd || !ws) return GN_ERR_NULL;
+    int rc = plan_or_error(N, C, S, G, p);
+    if (rc) return rc;
+    if (!dtype_ok(x_dtype) || !(y_dtype == x_dtype || y_dtype == GN_F32)) return GN_ERR_DTYPE;
+    if (!std::isfinite(eps) || eps < 0.0f) return GN_ERR_EPS;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mean, 4) || !aligned(rstd, 4) ||
+        !aligned(gamma, 4) || !aligned(beta, 4))
+        return GN_ERR_ALIGN;
+    return workspace_check(ws, ws_bytes, *p);
+}
+
+int bwd_check(const void* dy, int dy_dtype, const void* x, int x_dtype, const float* mean,
+              const float* rstd, const float* gamma, int64_t N, int64_t C, int64_t S, int64_t G,
+              const void* dx, const float* dgamma, const float* dbeta, const void* ws,
+              size_t ws_bytes, gn::Plan* p)
+{
+    if (!dy || !x || !mean || !rstd || !ws) return GN_ERR_NULL;
+    int rc = plan_or_error(N, C, S, G, p);
+    if (rc) return rc;
+    if (!dtype_ok(x_dtype) || !dtype_ok(dy_dtype)) return GN_ERR_DTYPE;
+    if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16) || !aligned(mean, 4) ||
+        !aligned(rstd, 4) || !aligned(gamma, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4))
+        return GN_ERR_ALIGN;
+    return workspace_check(ws, ws_bytes, *p);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? GN_OK : GN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t gn_workspace_bytes(int64_t N, int64_t C, int64_t S, int64_t G)
+{
+    gn::Plan p;
+    return gn::make_plan(N, C, S, G, &p) == 0 ? p.ws_bytes : 0;
+}
+
+int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
+{
+    if (!out) return GN_ERR_NULL;
+    gn::Plan p;
+    const int rc = plan_or_error(N, C, S, G, &p);
+    if (rc) return rc;
+    out->rows = p.rows;
+    out->chunk = p.chunk;
+    out->chunks_per_row = p.K;
+    out->jobs = p.jobs;
+    out->partials_per_group = p.P;
+    out->block = p.block;
+    out->vectors_per_step = gn::kStepVecs;
+    out->workspace_bytes = p.ws_bytes;
+    return GN_OK;
+}
+
+int gn_abi_version(void) { return 1; }
+
+const char* gn_status_string(int status)
+{
+    switch (status) {
+        case GN_OK: return "ok";
+        case GN_ERR_NULL: return "a required pointer is NULL";
+        case GN_ERR_SHAPE: return "invalid shape (N, C, S, G must be positive; N*(C/G)*S must exceed 1)";
+        case GN_ERR_GROUPS: return "C is not a multiple of G";
+        case GN_ERR_DTYPE: return "unsupported dtype or dtype combination";
+        case GN_ERR_EPS: return "eps must be finite and >= 0";
+        case GN_ERR_WORKSPACE: return "workspace smaller than gn_workspace_bytes()";
+        case GN_ERR_ALIGN: return "misaligned pointer (tensors and workspace need 16 bytes, fp32 vectors 4)";
+        case GN_ERR_DEVICE: return "x is not device memory or the stream belongs to another device";
+        case GN_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int gn_forward_stats(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!x || !workspace) return GN_ERR_NULL;
+    gn::Plan p;
+    int rc = plan_or_error(N, C, S, G, &p);
+    if (rc) return rc;
+    if (!dtype_ok(x_dtype)) return GN_ERR_DTYPE;
+    if (!aligned(x, 16)) return GN_ERR_ALIGN;
+    if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p);
+    return launch_status(gn::launch_stats(x, x_dtype, a, static_cast<float2*>(workspace),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int gn_forward_apply(const void* x, int x_dtype, const float* gamma, const float* beta,
+                     int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+                     void* y, int y_dtype, float* mean, float* rstd,
+                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = fwd_check(x, x_dtype, gamma, beta, N, C, S, G, eps, y, y_dtype, mean, rstd,
+                       workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p);
+    return launch_status(gn::launch_apply(x, x_dtype, gamma, beta,
+                                          static_cast<const float2*>(workspace), y, y_dtype, mean,
+                                          rstd, a, eps, static_cast<hipStream_t>(stream)));
+}
+
+int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta,
+               int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+               void* y, int y_dtype, float* mean, float* rstd,
+               void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = fwd_check(x, x_dtype, gamma, beta, N, C, S, G, eps, y, y_dtype, mean, rstd,
+                       workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float2* part = static_cast<float2*>(workspace);
+    if ((rc = launch_status(gn::launch_stats(x, x_dtype, a, part, st)))) return rc;
+    return launch_status(gn::launch_apply(x, x_dtype, gamma, beta, part, y, y_dtype, mean, rstd,
+                                          a, eps, st));
+}
+
+int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                       const float* mean, const float* rstd,
+                       int64_t N, int64_t C, int64_t S, int64_t G,
+                       void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, nullptr, N, C, S, G, nullptr,
+                       nullptr, nullptr, workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p);
+    return launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, a,
+                                               static_cast<float2*>(workspace),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                      const float* mean, const float* rstd, const float* gamma,
+                      int64_t N, int64_t C, int64_t S, int64_t G,
+                      void* dx, float* dgamma, float* dbeta,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, N, C, S, G, dx, dgamma, dbeta,
+                       workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p);
+    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, mean, rstd, gamma,
+                                              static_cast<const float2*>(workspace), a, dx, dgamma,
+                                              dbeta, static_cast<hipStream_t>(stream)));
+}
+
+int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                const float* mean, const float* rstd, const float* gamma,
+                int64_t N, int64_t C, int64_t S, int64_t G,
+                void* dx, float* dgamma, float* dbeta,
+                void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, N, C, S, G, dx, dgamma, dbeta,
+                       workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float2* part = static_cast<float2*>(workspace);
+    if ((rc = launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, a, part, st))))
+        return rc;
+    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, part, a,
+                                              dx, dgamma, dbeta, st));
+}
+
+}  // extern "C"

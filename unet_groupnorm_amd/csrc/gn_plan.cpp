@@ -1,0 +1,63 @@
+// gn_plan.cpp -- shape -> launch plan (see gn_plan.hpp).
+#include "gn_plan.hpp"
+
+namespace gn {
+
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+}  // namespace
+
+int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
+{
+    if (N <= 0 || C <= 0 || S <= 0 || G <= 0) return 2;
+    if (C % G != 0) return 3;
+    // N*C*S must not overflow and must stay below kMaxNumel.
+    if (N > kMaxNumel / C || N * C > kMaxNumel / S) return 2;
+    const int64_t Cg = C / G;
+    // A single value per normalization set (N == 1 and M == 1) is rejected, as the stock
+    // operator does; M == 1 with N > 1 is legal and answered exactly.
+    if (N * Cg * S == 1) return 2;
+
+    Plan q;
+    q.N = N; q.C = C; q.S = S; q.G = G;
+    q.Cg = Cg;
+    q.M = Cg * S;
+    q.rows = N * C;
+
+    // Block size: the smallest of 64/128/256 threads whose step covers a whole row, so
+    // that short rows (8^3 voxels) do not leave most lanes idle.
+    const int64_t row_vecs = ceil_div(S, kVec) + 1;  // +1: a row need not start on a vector
+    int block = 64;
+    while (block < 256 && int64_t(block) * kStepVecs < row_vecs) block *= 2;
+    const int64_t step = int64_t(block) * kStepVecs * kVec;  // elements per workgroup step
+
+    // Chunking: a whole row per job, halved while the launch has fewer than kTargetJobs
+    // jobs and a chunk still holds at least one full step. Chunks other than the last
+    // of a row are whole steps.
+    int64_t K = 1, chunk = S;
+    while (chunk > kMaxChunk) {
+        K *= 2;
+        chunk = round_up(ceil_div(S, K), step);
+        K = ceil_div(S, chunk);
+    }
+    while (q.rows * K < kTargetJobs) {
+        const int64_t c2 = round_up(ceil_div(S, K * 2), step);
+        const int64_t k2 = ceil_div(S, c2);
+        if (k2 <= K) break;
+        K = k2;
+        chunk = c2;
+    }
+    q.K = K;
+    q.chunk = chunk;
+    q.jobs = q.rows * K;
+    q.P = Cg * K;
+    q.block = block;
+    q.ws_bytes = size_t(round_up(q.jobs * 8, 256));
+    *p = q;
+    return 0;
+}
+
+}  // namespace gn

@@ -1,0 +1,45 @@
+// gn_plan.hpp -- launch plan for the GroupNorm kernels: a pure function of the shape.
+//
+// "Optimize GroupNorm" (LBANN/ScaFFold pull 93), paragraph folding seven launches into
+// four: grid, split count, tile sizes and reduction order are pure functions of the
+// shape; "Preserve GroupNorm dtype" (pull 105), second paragraph: the plan takes no
+// dtype, which is what makes the fp32 and bf16 backward bitwise identical.
+//
+// This unit is plain C++ (no HIP), so it is exercised on a host without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace gn {
+
+// Elements per lane vector: one 16-byte load of bf16, two of fp32. The element -> lane
+// assignment is defined in these units, so it is the same for both dtypes.
+constexpr int kVec = 8;
+// Vectors each lane holds per step (the register tile is kVec * kStepVecs elements).
+constexpr int kStepVecs = 4;
+// Workgroups a launch aims for: 8 per CU on the 256 CUs of an MI355X.
+constexpr int64_t kTargetJobs = 2048;
+// Upper bound on a job's element count, keeping every in-job count within 32 bits.
+constexpr int64_t kMaxChunk = int64_t(1) << 30;
+// Upper bound on N*C*S accepted (indices stay far from int64 overflow).
+constexpr int64_t kMaxNumel = int64_t(1) << 48;
+
+struct Plan {
+    int64_t N = 0, C = 0, S = 0, G = 0;
+    int64_t Cg = 0;      // channels per group
+    int64_t M = 0;       // elements per group
+    int64_t rows = 0;    // N * C
+    int64_t chunk = 0;   // elements per job
+    int64_t K = 0;       // jobs per row
+    int64_t jobs = 0;    // rows * K
+    int64_t P = 0;       // partials per group = Cg * K
+    int block = 0;       // threads per workgroup
+    size_t ws_bytes = 0; // workspace: one float2 partial per job, rounded to 256 bytes
+};
+
+// Returns 0 and fills *p for a valid shape, else a gn_status shape error code
+// (2 = GN_ERR_SHAPE, 3 = GN_ERR_GROUPS).
+int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p);
+
+}  // namespace gn
