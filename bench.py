@@ -55,7 +55,7 @@ def bytes_per_elem(x_dtype, y_dtype, dy_dtype):
     sz = {torch.bfloat16: 2, torch.float32: 4}
     bx, by, bdy = sz[x_dtype], sz[y_dtype], sz[dy_dtype]
     phases = {"stats": bx, "apply": bx + by, "bwd_reduce": bx + bdy, "bwd_apply": bx + bdy + bx}
-    return phases, bx + by + bdy + bx
+    return phases, sum(phases.values())
 
 
 class Runner:

@@ -41,10 +41,8 @@ def _run(inp, out_dtype=None, dy=None):
     return {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dgamma": dg, "dbeta": db}
 
 
-def _beta_at(idx, x, beta):
-    S = int(np.prod(x.shape[2:])) if x.dim() > 2 else 1
-    c = (idx // S) % x.shape[1]
-    return beta.cpu().numpy().astype(np.float64)[c]
+def _chan_at(idx, x, gamma, beta):
+    return P.channel_params_at(idx, tuple(x.shape), gamma.cpu().numpy(), beta.cpu().numpy())
 
 
 def full_check(inp, tag):
@@ -58,7 +56,7 @@ def full_check(inp, tag):
     f = O.forward(x, G, gamma, beta, eps=eps)
     rep = P.check_stats(P.to_np(r["mean"]), P.to_np(r["rstd"]), f["mean"], f["var"], f["rstd"])
     idx = np.arange(x.numel())
-    rep.update(P.check_y(P.to_np(r["y"]).reshape(-1), f["y"].reshape(-1), _beta_at(idx, x, beta)))
+    rep.update(P.check_y(P.to_np(r["y"]).reshape(-1), f["y"].reshape(-1), *_chan_at(idx, x, gamma, beta)))
     b = O.backward(dy, x, G, gamma, eps=eps)
     rep.update(P.check_dx(P.to_np(r["dx"]).reshape(-1), b["dx"].reshape(-1)))
     a_dy, a_dyx = O.channel_abs_sums(dy, x, G, b["mean"], b["rstd"])
@@ -101,7 +99,7 @@ def sampled_check(inp, tag, n_random=1 << 20, seed=0):
     idx = _sample_indices(x, G, n_random, seed)
     it = torch.from_numpy(idx).to(DEV)
     y64 = O.forward_at(x, G, idx, mean64, rstd64, gamma, beta)
-    rep.update(P.check_y(P.to_np(r["y"].reshape(-1)[it]), y64, _beta_at(idx, x, beta)))
+    rep.update(P.check_y(P.to_np(r["y"].reshape(-1)[it]), y64, *_chan_at(idx, x, gamma, beta)))
     say(f"{tag}: oracle backward")
     b = O.backward(dy, x, G, gamma, eps=eps, want_dx=False)
     dx64 = O.backward_at(dy, x, G, idx, b["mean"], b["rstd"], b["c1"], b["c2"], gamma)
@@ -213,8 +211,9 @@ def test_large_mean_offset_keeps_variance():
     xt = torch.from_numpy(x).to(DEV)
     y, mean, rstd = gn.gn_forward(xt, None, None, 2, 1e-5)
     torch.cuda.synchronize()
-    m64, v64, r64 = O.group_stats(x, 2, 1e-5)
-    P.check_stats(P.to_np(mean), P.to_np(rstd), m64, v64, r64)
+    f = O.forward(x, 2, eps=1e-5)
+    P.check_stats(P.to_np(mean), P.to_np(rstd), f["mean"], f["var"], f["rstd"])
+    P.check_y(P.to_np(y).reshape(-1), f["y"].reshape(-1), *P.channel_params_at(np.arange(x.size), x.shape, None, None))
 
 
 # ----------------------------------------------------------------------------- bitwise properties

@@ -138,7 +138,9 @@ struct Moments {
 
 // a <- a (+) b with Chan's parallel formula. Empty operands are skipped, so a merge
 // never mixes a zero count into the mean. With equal means (a constant group) the mean
-// is untouched and M2 stays exactly zero.
+// is untouched and M2 stays exactly zero. An infinite mean (a part holding +-Inf) stays
+// what the sum of the parts makes it (+-Inf, or NaN for opposite signs) instead of the
+// NaN that Inf - Inf would give; its M2 is already NaN.
 template <typename CT>
 __device__ __forceinline__ void chan_merge(Moments<CT>& a, CT nb, float mb, float M2b)
 {
@@ -150,7 +152,8 @@ __device__ __forceinline__ void chan_merge(Moments<CT>& a, CT nb, float mb, floa
     const CT n = a.n + nb;
     const float w = float(nb) / float(n);
     const float d = mb - a.m;
-    a.m = fmaf(d, w, a.m);
+    const bool inf = __builtin_isinf(a.m) || __builtin_isinf(mb);
+    a.m = inf ? a.m + mb : fmaf(d, w, a.m);
     a.M2 = (a.M2 + M2b) + (d * d) * (float(a.n) * w);
     a.n = n;
 }
@@ -191,18 +194,22 @@ __device__ __forceinline__ float tree_sum(float (&t)[N])
 
 constexpr int kTile = kVec * kStepVecs;  // elements per lane per step (32)
 
-// Corrected two-pass over a full register tile: m = tile mean, M2 = sum d^2 - (sum d)^2 / n
-// with d = v - m. The balanced sum makes m exact for a constant tile.
-__device__ __forceinline__ void tile_moments_full(const float (&v)[kTile], float& m, float& M2)
+// Corrected two-pass over a full register tile of values shifted by the group's shift K:
+// t = v - K, m = mean(t), M2 = sum d^2 - (sum d)^2 / n with d = t - m. The balanced sum
+// makes m exactly 0 for a constant tile equal to K.
+__device__ __forceinline__ void tile_moments_full(const float (&v)[kTile], float K, float& m, float& M2)
 {
-    float t[kTile];
+    float t[kTile], u[kTile];
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) t[i] = v[i];
-    m = tree_sum(t) * (1.0f / kTile);
+    for (int i = 0; i < kTile; ++i) {
+        t[i] = v[i] - K;
+        u[i] = t[i];
+    }
+    m = tree_sum(u) * (1.0f / kTile);
     float d[kTile], q[kTile];
 #pragma unroll
     for (int i = 0; i < kTile; ++i) {
-        d[i] = v[i] - m;
+        d[i] = t[i] - m;
         q[i] = d[i] * d[i];
     }
     const float sd = tree_sum(d);
@@ -210,26 +217,38 @@ __device__ __forceinline__ void tile_moments_full(const float (&v)[kTile], float
     M2 = sq - (sd * sd) * (1.0f / kTile);
 }
 
-// Same over a tile with a validity mask (job edges). Deviations are taken from a pivot
-// (the first valid value) so that a constant tile of any length has an exact mean.
-__device__ __forceinline__ void tile_moments_masked(const float (&v)[kTile], uint32_t valid,
+// Same over a tile with a validity mask (job edges); invalid elements contribute nothing.
+__device__ __forceinline__ void tile_moments_masked(const float (&v)[kTile], float K, uint32_t valid,
                                                     uint32_t cnt, float& m, float& M2)
 {
-    const float p = v[__builtin_ctz(valid)];
     float t[kTile];
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) t[i] = ((valid >> i) & 1u) ? v[i] - p : 0.0f;
+    for (int i = 0; i < kTile; ++i) t[i] = ((valid >> i) & 1u) ? v[i] - K : 0.0f;
     const float fc = float(cnt);
-    m = p + tree_sum(t) / fc;
+    float u[kTile];
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) u[i] = t[i];
+    m = tree_sum(u) / fc;
     float d[kTile], q[kTile];
 #pragma unroll
     for (int i = 0; i < kTile; ++i) {
-        d[i] = ((valid >> i) & 1u) ? v[i] - m : 0.0f;
+        d[i] = ((valid >> i) & 1u) ? t[i] - m : 0.0f;
         q[i] = d[i] * d[i];
     }
     const float sd = tree_sum(d);
     const float sq = tree_sum(q);
     M2 = sq - (sd * sd) / fc;
+}
+
+// The shift of group (n, g): its first element, or 0 if that is not finite. Every
+// statistic of the group is accumulated relative to it, so that means stay small next to
+// the spread even when |mean| >> sigma (fp32 resolution of a mean near 1e5 would
+// otherwise be 1e-2 of a unit sigma), and a constant group has exactly zero deviations.
+template <typename T>
+__device__ __forceinline__ float group_shift(const T* __restrict__ x, const KArgs& a, int64_t n, int64_t g)
+{
+    const float k = Io<T>::load1(x + (n * a.C + g * a.Cg) * a.S);
+    return __builtin_isfinite(k) ? k : 0.0f;
 }
 
 // Loads the lane's kStepVecs vectors of one step with per-element validity. Vectors that
@@ -332,19 +351,21 @@ stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
 
     for (int64_t j = blockIdx.x; j < a.jobs; j += gridDim.x) {
         const Job jb = job_at(a, j);
+        const int64_t n = jb.row / a.C, g = (jb.row - n * a.C) / a.Cg;
+        const float K = group_shift(x, a, n, g);
         Moments<uint32_t> acc = {0u, 0.0f, 0.0f};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
             float v[kTile];
             float m, M2;
             if (step_is_full(jb, sv0, stepv)) {
                 load_step_full(x, sv0, blk, tid, v);
-                tile_moments_full(v, m, M2);
+                tile_moments_full(v, K, m, M2);
                 chan_merge(acc, uint32_t(kTile), m, M2);
             } else {
                 const uint32_t valid = load_step_masked(x, jb, sv0, blk, tid, v);
                 if (valid) {
                     const uint32_t cnt = __builtin_popcount(valid);
-                    tile_moments_masked(v, valid, cnt, m, M2);
+                    tile_moments_masked(v, K, valid, cnt, m, M2);
                     chan_merge(acc, cnt, m, M2);
                 }
             }
@@ -371,7 +392,7 @@ __device__ __forceinline__ void finalize_stats(const float2* __restrict__ part, 
     if (threadIdx.x == 0) {
         float var = float(double(r.M2) / double(a.M));
         var = (var < 0.0f) ? 0.0f : var;  // rounding can leave a tiny negative; NaN passes through
-        s_stat[0] = r.m;
+        s_stat[0] = r.m;                  // mean relative to the group's shift
         s_stat[1] = 1.0f / __fsqrt_rn(var + eps);
     }
     __syncthreads();
@@ -398,7 +419,13 @@ apply_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
             finalize_stats(part, a, n, g, eps, s_stat, s_n, s_m, s_M);
             cached = ng;
         }
-        const float mu = s_stat[0], rstd = s_stat[1];
+        // The mean as an unevaluated sum hi + lo: hi is the fp32 mean that is published,
+        // lo what rounding it left out. x - mean is taken as (x - hi) - lo, which is exact
+        // in its first step whenever x is close to the mean.
+        const float K = group_shift(x, a, n, g);
+        const float rel = s_stat[0], rstd = s_stat[1];  // mean relative to K
+        const float mu = K + rel;
+        const float mu_lo = (K - mu) + rel;
         // The group's first job publishes the statistics.
         if (tid == 0 && jb.k == 0 && c == g * a.Cg) {
             mean_out[ng] = mu;
@@ -415,7 +442,7 @@ apply_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
                 for (int u = 0; u < kStepVecs; ++u) {
                     float o[kVec];
 #pragma unroll
-                    for (int i = 0; i < kVec; ++i) o[i] = fmaf(v[u * kVec + i] - mu, scale, shift);
+                    for (int i = 0; i < kVec; ++i) o[i] = fmaf((v[u * kVec + i] - mu) - mu_lo, scale, shift);
                     Io<TY>::store8(y + (sv0 + int64_t(u) * blk + tid) * kVec, o);
                 }
             } else {
@@ -426,13 +453,13 @@ apply_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
                         float e[kVec], o[kVec];
                         Io<TX>::load8(x + vi * kVec, e);
 #pragma unroll
-                        for (int i = 0; i < kVec; ++i) o[i] = fmaf(e[i] - mu, scale, shift);
+                        for (int i = 0; i < kVec; ++i) o[i] = fmaf((e[i] - mu) - mu_lo, scale, shift);
                         Io<TY>::store8(y + vi * kVec, o);
                     } else {
                         for (int i = 0; i < kVec; ++i) {
                             const int64_t gi = vi * kVec + i;
                             if (gi >= jb.lo && gi < jb.hi)
-                                Io<TY>::store1(y + gi, fmaf(Io<TX>::load1(x + gi) - mu, scale, shift));
+                                Io<TY>::store1(y + gi, fmaf((Io<TX>::load1(x + gi) - mu) - mu_lo, scale, shift));
                         }
                     }
                 }
