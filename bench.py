@@ -35,6 +35,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline, roofline and baseline only")
+    ap.add_argument("--workload", choices=["scale7", "scale8"], default="scale7",
+                    help="the 128^3 (default) or 256^3 C=32 G=8 bf16 site")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB bf16 device copy 5 times (a kernel of known traffic "
+                         "for scaling profiler byte counters)")
     return ap.parse_args()
 
 
@@ -171,7 +176,7 @@ def copy_ceiling_gbps(nbytes=1 << 30, reps=20):
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def cpu_baseline(runner, min_seconds=10.0, max_reps=3):
+def cpu_baseline(runner, min_seconds=10.0, max_reps=40):
     """The fp64 oracle, as it stands, on this host: forward + backward on the same volume."""
     import numpy as np  # noqa: F401
 
@@ -238,7 +243,7 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
-    case = workloads.SCALE7
+    case = workloads.SCALE7 if args.workload == "scale7" else workloads.SCALE8
     log(f"workload {case.name} {case.shape}; generating inputs on the GPU")
     run = Runner(case)
     log(f"timing {args.steps} steps after {args.warmup} warmup steps")
@@ -299,7 +304,10 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on this host")
         out["cpu_baseline"] = cpu_baseline(run)
-    if not args.no_extras:
+    if args.copy_probe:
+        log("copy probe: 5 copies of 1 GiB")
+        copy_ceiling_gbps(reps=5)
+    if not args.no_extras and args.workload == "scale7":
         del run
         torch.cuda.empty_cache()
         c8 = workloads.SCALE8
