@@ -95,17 +95,18 @@ class Runner:
                        dx=self.dx, dgamma=self.dgamma, dbeta=self.dbeta)
 
     def phases(self):
-        """The same step through the split-phase entry points, one kernel each."""
+        """The same step through the split-phase entry points. The stats and bwd_reduce
+        phases are two kernels each (the partial reduction, then the small per-group
+        finalize); apply and bwd_apply are one kernel each."""
         gn = self.gn
         return [
-            ("stats", lambda: gn.gn_forward_stats(self.x, self.G, self.ws)),
-            ("apply", lambda: gn.gn_forward_apply(self.x, self.gamma, self.beta, self.G, self.eps,
-                                                  self.y, self.mean, self.rstd, self.ws)),
+            ("stats", lambda: gn.gn_forward_stats(self.x, self.gamma, self.beta, self.G, self.eps,
+                                                  self.mean, self.rstd, self.ws)),
+            ("apply", lambda: gn.gn_forward_apply(self.x, self.G, self.y, self.ws)),
             ("bwd_reduce", lambda: gn.gn_backward_reduce(self.dy, self.x, self.mean, self.rstd,
-                                                         self.G, self.ws)),
-            ("bwd_apply", lambda: gn.gn_backward_apply(self.dy, self.x, self.mean, self.rstd,
-                                                       self.gamma, self.G, self.dx, self.dgamma,
-                                                       self.dbeta, self.ws)),
+                                                         self.gamma, self.G, self.dgamma,
+                                                         self.dbeta, self.ws)),
+            ("bwd_apply", lambda: gn.gn_backward_apply(self.dy, self.x, self.G, self.dx, self.ws)),
         ]
 
     def timed_steps(self, steps, warmup):

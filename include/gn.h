@@ -11,10 +11,10 @@
  *   - Same page, paragraph introducing the NDHWC Triton kernel: fp32 statistics from
  *     a corrected two-pass per tile merged with Chan's parallel formula, register-only
  *     reductions in a fixed order with no float atomics (bitwise reproducible).
- *   - Same page, paragraph folding seven launches into four: the statistics finalize
- *     is folded into the normalize kernel and the backward finalize and dgamma/dbeta
- *     reduction into the dx kernel; grid, split count, tile sizes and reduction order
- *     are pure functions of the shape.
+ *   - Same page, paragraph folding seven launches into four: grid, split count, tile
+ *     sizes and reduction order are pure functions of the shape. (That page folds the
+ *     finalize into the elementwise kernels; here it is a small kernel of its own, run
+ *     once per group, so that the streaming kernels can be a very large grid.)
  *   - "Preserve GroupNorm dtype" (LBANN/ScaFFold pull 105), first paragraph: the
  *     normalized value is computed in fp32 and only the store narrows, so the output
  *     is the fp32 answer rounded once; an fp32 output is available on request. Second
@@ -32,8 +32,10 @@
  * enqueued on `stream` (a hipStream_t; NULL means the null stream of the current
  * device) in stream order, and the call returns as soon as it is enqueued. Outputs are
  * fully overwritten (dgamma/dbeta are written, not accumulated). The workspace holds
- * intermediate partial results only between the launches of one call; it carries
- * nothing from one call to the next and needs no initialization.
+ * partial results and per-row coefficients from the first half of a direction to its
+ * second half (gn_forward_stats -> gn_forward_apply, gn_backward_reduce ->
+ * gn_backward_apply); nothing else carries from one call to the next, and it needs no
+ * initialization.
  *
  * Pointers. x, y, dy, dx and the workspace must be 16-byte aligned device pointers;
  * mean, rstd, gamma, beta, dgamma, dbeta 4-byte aligned device pointers. All of them
@@ -88,26 +90,29 @@ size_t gn_workspace_bytes(int64_t N, int64_t C, int64_t S, int64_t G);
  * y = gamma_c * (x - mean) * rstd + beta_c computed in fp32 and stored once in
  * y_dtype. x_dtype is GN_F32 or GN_BF16; y_dtype is x_dtype or GN_F32 (the fp32-output
  * mode). gamma == NULL means all ones, beta == NULL all zeros. eps must be finite and
- * >= 0. Two kernels are enqueued: gn_forward_stats then gn_forward_apply.
+ * >= 0. Enqueues gn_forward_stats then gn_forward_apply (three kernels).
  */
 int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta,
                int64_t N, int64_t C, int64_t S, int64_t G, float eps,
                void* y, int y_dtype, float* mean, float* rstd,
                void* workspace, size_t workspace_bytes, void* stream);
 
-/* First half of gn_forward: per-chunk fp32 partial statistics of x into the workspace. */
-int gn_forward_stats(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+/*
+ * First half of gn_forward: fp32 partial statistics of x, merged in a fixed order into
+ * mean and rstd, plus per-row normalize coefficients left in the workspace for
+ * gn_forward_apply. Two kernels.
+ */
+int gn_forward_stats(const void* x, int x_dtype, const float* gamma, const float* beta,
+                     int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+                     float* mean, float* rstd,
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Second half of gn_forward: merges the workspace partials that gn_forward_stats left
- * (same x, same shape, stream-ordered after it) in a fixed order into mean/rstd and
- * writes y. Same argument rules as gn_forward.
+ * Second half of gn_forward: writes y from x and the coefficients that gn_forward_stats
+ * left in the workspace (same x, same shape, stream-ordered after it). One kernel.
  */
-int gn_forward_apply(const void* x, int x_dtype, const float* gamma, const float* beta,
-                     int64_t N, int64_t C, int64_t S, int64_t G, float eps,
-                     void* y, int y_dtype, float* mean, float* rstd,
-                     void* workspace, size_t workspace_bytes, void* stream);
+int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                     void* y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward. Recomputes xhat = (x - mean) * rstd from the mean/rstd gn_forward wrote,
@@ -118,8 +123,8 @@ int gn_forward_apply(const void* x, int x_dtype, const float* gamma, const float
  * dy_dtype is GN_F32 or GN_BF16 independently of x_dtype; the same dy values in either
  * dtype give bitwise identical results. gamma == NULL means all ones. dx, dgamma and
  * dbeta may each be NULL (not computed). A group with M == 1 has dx == +0 exactly for
- * finite inputs (NaN/Inf still propagate). Two kernels are enqueued:
- * gn_backward_reduce then gn_backward_apply.
+ * finite inputs (NaN/Inf still propagate). Enqueues gn_backward_reduce then, unless dx is
+ * NULL, gn_backward_apply (three kernels).
  */
 int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
                 const float* mean, const float* rstd, const float* gamma,
@@ -127,20 +132,24 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
                 void* dx, float* dgamma, float* dbeta,
                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* First half of gn_backward: per-chunk fp32 partial sums of dy and dy*xhat into the workspace. */
+/*
+ * First half of gn_backward: per-job fp32 sums of dy and dy*xhat, merged in a fixed
+ * order into dgamma/dbeta (either may be NULL) and per-row dx coefficients left in the
+ * workspace for gn_backward_apply. Two kernels.
+ */
 int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
-                       const float* mean, const float* rstd,
+                       const float* mean, const float* rstd, const float* gamma,
                        int64_t N, int64_t C, int64_t S, int64_t G,
+                       float* dgamma, float* dbeta,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Second half of gn_backward: merges the partials gn_backward_reduce left (same inputs,
- * stream-ordered after it) in a fixed order and writes dx, dgamma, dbeta.
+ * Second half of gn_backward: writes dx from x, dy and the coefficients that
+ * gn_backward_reduce left in the workspace (same inputs, stream-ordered after it).
+ * One kernel.
  */
 int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
-                      const float* mean, const float* rstd, const float* gamma,
-                      int64_t N, int64_t C, int64_t S, int64_t G,
-                      void* dx, float* dgamma, float* dbeta,
+                      int64_t N, int64_t C, int64_t S, int64_t G, void* dx,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English description of a status code (never NULL). */
@@ -148,19 +157,27 @@ const char* gn_status_string(int status);
 
 /*
  * The launch plan for a shape: a pure function of (N, C, S, G) with no dtype and no
- * device input, exposed so that tests and benchmarks can see the decomposition.
- * Every kernel works on "jobs": job j covers elements [k*chunk, min((k+1)*chunk, S))
- * of row r = j / chunks_per_row (row r = n*C + c), k = j % chunks_per_row.
+ * device input, exposed so that tests and benchmarks can see the decomposition. The
+ * reductions work on jobs: reduction job j covers elements
+ * [k*chunk, min((k+1)*chunk, S)) of row r = j / chunks_per_row (row r = n*C + c),
+ * k = j % chunks_per_row, and leaves one fp32 partial; their number and length fix the
+ * reduction order. The streaming kernels (normalize, dx) cover the rows the same way
+ * with apply_chunk and apply_chunks_per_row; they reduce nothing.
  */
 typedef struct gn_plan_info {
-    int64_t rows;               /* N*C */
-    int64_t chunk;              /* elements per job (the last job of a row may be shorter) */
-    int64_t chunks_per_row;     /* K */
-    int64_t jobs;               /* rows * K: workgroups per launch */
-    int64_t partials_per_group; /* (C/G) * K */
-    int32_t block;              /* threads per workgroup (64, 128 or 256) */
-    int32_t vectors_per_step;   /* 8-element vectors each thread loads per step */
-    size_t workspace_bytes;     /* == gn_workspace_bytes */
+    int64_t rows;                 /* N*C */
+    int64_t chunk;                /* elements per reduction job (a row's last may be shorter) */
+    int64_t chunks_per_row;       /* reduction jobs per row */
+    int64_t jobs;                 /* rows * chunks_per_row: workgroups of a reduction launch */
+    int64_t partials_per_group;   /* (C/G) * chunks_per_row */
+    int32_t block;                /* threads per reduction workgroup (64, 128 or 256) */
+    int32_t vectors_per_step;     /* 8-element vectors each reduction thread loads per step */
+    int64_t apply_chunk;          /* elements per streaming job */
+    int64_t apply_chunks_per_row; /* streaming jobs per row */
+    int64_t apply_jobs;           /* rows * apply_chunks_per_row: workgroups of a streaming launch */
+    int32_t apply_block;          /* threads per streaming workgroup */
+    int32_t apply_vectors;        /* 8-element vectors each streaming thread moves */
+    size_t workspace_bytes;       /* == gn_workspace_bytes */
 } gn_plan_info;
 
 /* Fills *out for a valid shape and returns GN_OK; otherwise returns the shape error. */

@@ -34,7 +34,7 @@ def test_status_enum_matches_header():
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == 1
+    assert lib.gn_abi_version() == 2
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every
@@ -82,11 +82,16 @@ def test_backward_validation(kw, status):
 
 
 def test_split_phase_validation():
-    assert lib.gn_forward_stats(None, GN_BF16, 1, 8, 64, 4, A, 1 << 20, None) == 1
-    assert lib.gn_forward_stats(A, GN_BF16, 1, 8, 64, 3, A, 1 << 20, None) == 3
-    assert lib.gn_forward_stats(A, GN_BF16, 1, 8, 64, 4, A, 8, None) == 6
-    assert lib.gn_forward_apply(A, GN_BF16, None, None, 1, 8, 64, 4, 1e-5, None, GN_BF16, A, B, A,
-                                1 << 20, None) == 1
-    assert lib.gn_backward_reduce(A, 9, B, GN_BF16, A, B, 1, 8, 64, 4, A, 1 << 20, None) == 4
-    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, A, B, None, 1, 8, 64, 4, None, None, None,
-                                 A, 8, None) == 6
+    assert lib.gn_forward_stats(None, GN_BF16, None, None, 1, 8, 64, 4, 1e-5, A, B, A, 1 << 20, None) == 1
+    assert lib.gn_forward_stats(A, GN_BF16, None, None, 1, 8, 64, 3, 1e-5, A, B, A, 1 << 20, None) == 3
+    assert lib.gn_forward_stats(A, GN_BF16, None, None, 1, 8, 64, 4, 1e-5, A, B, A, 8, None) == 6
+    assert lib.gn_forward_stats(A, GN_BF16, None, None, 1, 8, 64, 4, -1.0, A, B, A, 1 << 20, None) == 5
+    assert lib.gn_forward_apply(A, GN_BF16, 1, 8, 64, 4, None, GN_BF16, A, 1 << 20, None) == 1
+    assert lib.gn_forward_apply(A, GN_F32, 1, 8, 64, 4, B, GN_BF16, A, 1 << 20, None) == 4
+    assert lib.gn_backward_reduce(A, 9, B, GN_BF16, A, B, None, 1, 8, 64, 4, None, None, A, 1 << 20,
+                                  None) == 4
+    assert lib.gn_backward_reduce(A, GN_BF16, B, GN_BF16, A, B, None, 1, 8, 64, 4, None, None, A, 8,
+                                  None) == 6
+    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, None, A, 1 << 20, None) == 1
+    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, ctypes.c_void_p(0x30004), A,
+                                 1 << 20, None) == 7

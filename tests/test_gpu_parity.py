@@ -279,14 +279,28 @@ def test_split_phase_entry_points_match_fused():
     dx, dg, db = gn.gn_backward(inp["dy"], x, mean, rstd, gamma, G)
     ws = gn.workspace_for(x, G)
     y2, mean2, rstd2 = torch.empty_like(y), torch.empty_like(mean), torch.empty_like(rstd)
-    gn.gn_forward_stats(x, G, ws)
-    gn.gn_forward_apply(x, gamma, beta, G, inp["eps"], y2, mean2, rstd2, ws)
+    gn.gn_forward_stats(x, gamma, beta, G, inp["eps"], mean2, rstd2, ws)
+    gn.gn_forward_apply(x, G, y2, ws)
     dx2, dg2, db2 = torch.empty_like(dx), torch.empty_like(dg), torch.empty_like(db)
-    gn.gn_backward_reduce(inp["dy"], x, mean2, rstd2, G, ws)
-    gn.gn_backward_apply(inp["dy"], x, mean2, rstd2, gamma, G, dx2, dg2, db2, ws)
+    gn.gn_backward_reduce(inp["dy"], x, mean2, rstd2, gamma, G, dg2, db2, ws)
+    gn.gn_backward_apply(inp["dy"], x, G, dx2, ws)
     torch.cuda.synchronize()
     for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2), (dg, dg2), (db, db2)):
         assert torch.equal(u, v)
+
+
+def test_optional_backward_outputs():
+    case = workloads.DEEP
+    say(f"{case.name}: backward with dx only, and with dgamma/dbeta only")
+    inp = workloads.make(case, DEV)
+    x, G, gamma = inp["x"], inp["G"], inp["gamma"]
+    y, mean, rstd = gn.gn_forward(x, gamma, inp["beta"], G, inp["eps"])
+    dx, dg, db = gn.gn_backward(inp["dy"], x, mean, rstd, gamma, G)
+    dx_only, n1, n2 = gn.gn_backward(inp["dy"], x, mean, rstd, gamma, G, need_dgamma=False, need_dbeta=False)
+    n3, dg_only, db_only = gn.gn_backward(inp["dy"], x, mean, rstd, gamma, G, need_dx=False)
+    torch.cuda.synchronize()
+    assert n1 is None and n2 is None and n3 is None
+    assert torch.equal(dx, dx_only) and torch.equal(dg, dg_only) and torch.equal(db, db_only)
 
 
 def test_autograd_function_matches_entry_points():

@@ -48,6 +48,14 @@ def test_plan_is_consistent(N, C, S, G):
     if p["chunks_per_row"] > 1:
         step = p["block"] * p["vectors_per_step"] * VEC
         assert p["chunk"] % step == 0
+    # streaming decomposition
+    assert p["apply_block"] in (64, 128, 256)
+    assert p["apply_jobs"] == p["rows"] * p["apply_chunks_per_row"]
+    assert (p["apply_chunks_per_row"] - 1) * p["apply_chunk"] < S <= p["apply_chunks_per_row"] * p["apply_chunk"]
+    assert p["apply_chunk"] <= p["apply_block"] * p["apply_vectors"] * VEC
+    # workspace: partials, then 256-byte aligned per-row float4 coefficients
+    coef_off = -(-8 * p["jobs"] // 256) * 256
+    assert p["workspace_bytes"] >= coef_off + 16 * p["rows"]
 
 
 @pytest.mark.parametrize("N,C,S,G", [s for s in SHAPES if s[0] * s[1] * s[2] <= 2 ** 22])
@@ -64,8 +72,15 @@ def test_jobs_cover_every_element_once_and_stay_in_bounds(N, C, S, G):
         vf0, vf1 = (lo + VEC - 1) // VEC, hi // VEC
         nvec = (hi + VEC - 1) // VEC - v0
         touched = np.zeros(nvec, dtype=np.int32)
-        for sv0 in range(v0, v0 + nvec, stepv):
+        # the kernels pipeline the full steps [fs, fe) with unconditional vector loads and
+        # take every other step through the masked path
+        nsteps = -(-nvec // stepv)
+        fs = 1 if v0 < vf0 else 0
+        fe = max((vf1 - v0) // stepv, fs)
+        assert nsteps - fe <= 1 and fs <= 1
+        for si, sv0 in enumerate(range(v0, v0 + nvec, stepv)):
             full = sv0 >= vf0 and sv0 + stepv <= vf1
+            assert full == (fs <= si < fe)
             lanes = np.arange(blk)
             for u in range(U):
                 vi = sv0 + u * blk + lanes
@@ -88,6 +103,35 @@ def test_jobs_cover_every_element_once_and_stay_in_bounds(N, C, S, G):
         grp = c // (C // G)
         pbase = (n * C + grp * (C // G)) * p["chunks_per_row"]
         assert 0 <= pbase and pbase + p["partials_per_group"] <= p["jobs"]
+    assert (seen == 1).all()
+
+
+@pytest.mark.parametrize("N,C,S,G", [s for s in SHAPES if s[0] * s[1] * s[2] <= 2 ** 22])
+def test_streaming_jobs_cover_every_element_once_and_stay_in_bounds(N, C, S, G):
+    p = g.gn_plan_query(N, C, S, G)
+    total = N * C * S
+    seen = np.zeros(total, dtype=np.int32)
+    blk, U = p["apply_block"], p["apply_vectors"]
+    stepv = blk * U
+    K, chunk = p["apply_chunks_per_row"], p["apply_chunk"]
+    for j in range(p["apply_jobs"]):
+        row, k = divmod(j, K)
+        lo, hi = row * S + k * chunk, row * S + min((k + 1) * chunk, S)
+        assert 0 <= lo < hi <= total and row < p["rows"]
+        v0, vf0, vf1 = lo // VEC, (lo + VEC - 1) // VEC, hi // VEC
+        nvec = (hi + VEC - 1) // VEC - v0
+        assert nvec <= 2 * stepv  # at most two steps per streaming job
+        for sv0 in range(v0, v0 + nvec, stepv):
+            for u in range(U):
+                vi = sv0 + u * blk + np.arange(blk)
+                whole = (vi >= vf0) & (vi < vf1)
+                assert ((vi[whole] + 1) * VEC <= total).all()
+                seen_v = vi[whole]
+                for e in range(VEC):
+                    np.add.at(seen, seen_v * VEC + e, 1)
+                elems = vi[~whole][:, None] * VEC + np.arange(VEC)[None, :]
+                ok = (elems >= lo) & (elems < hi)
+                np.add.at(seen, elems[ok], 1)
     assert (seen == 1).all()
 
 

@@ -27,6 +27,11 @@ class GnPlanInfo(ctypes.Structure):
         ("partials_per_group", ctypes.c_int64),
         ("block", ctypes.c_int32),
         ("vectors_per_step", ctypes.c_int32),
+        ("apply_chunk", ctypes.c_int64),
+        ("apply_chunks_per_row", ctypes.c_int64),
+        ("apply_jobs", ctypes.c_int64),
+        ("apply_block", ctypes.c_int32),
+        ("apply_vectors", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
     ]
 
@@ -36,11 +41,11 @@ def _declare(lib):
     sig = {
         "gn_workspace_bytes": (SZ, [I64, I64, I64, I64]),
         "gn_forward": (I, [P, I, P, P, I64, I64, I64, I64, F, P, I, P, P, P, SZ, P]),
-        "gn_forward_stats": (I, [P, I, I64, I64, I64, I64, P, SZ, P]),
-        "gn_forward_apply": (I, [P, I, P, P, I64, I64, I64, I64, F, P, I, P, P, P, SZ, P]),
+        "gn_forward_stats": (I, [P, I, P, P, I64, I64, I64, I64, F, P, P, P, SZ, P]),
+        "gn_forward_apply": (I, [P, I, I64, I64, I64, I64, P, I, P, SZ, P]),
         "gn_backward": (I, [P, I, P, I, P, P, P, I64, I64, I64, I64, P, P, P, P, SZ, P]),
-        "gn_backward_reduce": (I, [P, I, P, I, P, P, I64, I64, I64, I64, P, SZ, P]),
-        "gn_backward_apply": (I, [P, I, P, I, P, P, P, I64, I64, I64, I64, P, P, P, P, SZ, P]),
+        "gn_backward_reduce": (I, [P, I, P, I, P, P, P, I64, I64, I64, I64, P, P, P, SZ, P]),
+        "gn_backward_apply": (I, [P, I, P, I, I64, I64, I64, I64, P, P, SZ, P]),
         "gn_status_string": (ctypes.c_char_p, [I]),
         "gn_plan_query": (I, [I64, I64, I64, I64, ctypes.POINTER(GnPlanInfo)]),
         "gn_abi_version": (I, []),

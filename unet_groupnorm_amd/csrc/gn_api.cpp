@@ -123,11 +123,16 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     out->partials_per_group = p.P;
     out->block = p.block;
     out->vectors_per_step = gn::kStepVecs;
+    out->apply_chunk = p.chunk_a;
+    out->apply_chunks_per_row = p.K_a;
+    out->apply_jobs = p.jobs_a;
+    out->apply_block = p.block_a;
+    out->apply_vectors = gn::kApplyVecs;
     out->workspace_bytes = p.ws_bytes;
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 1; }
+int gn_abi_version(void) { return 2; }
 
 const char* gn_status_string(int status)
 {
@@ -146,38 +151,43 @@ const char* gn_status_string(int status)
     }
 }
 
-int gn_forward_stats(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+int gn_forward_stats(const void* x, int x_dtype, const float* gamma, const float* beta,
+                     int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+                     float* mean, float* rstd,
                      void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (!x || !workspace) return GN_ERR_NULL;
+    if (!x || !mean || !rstd || !workspace) return GN_ERR_NULL;
     gn::Plan p;
     int rc = plan_or_error(N, C, S, G, &p);
     if (rc) return rc;
     if (!dtype_ok(x_dtype)) return GN_ERR_DTYPE;
-    if (!aligned(x, 16)) return GN_ERR_ALIGN;
+    if (!std::isfinite(eps) || eps < 0.0f) return GN_ERR_EPS;
+    if (!aligned(x, 16) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(gamma, 4) ||
+        !aligned(beta, 4))
+        return GN_ERR_ALIGN;
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    const gn::KArgs a = gn::kargs_of(p);
-    return launch_status(gn::launch_stats(x, x_dtype, a, static_cast<float2*>(workspace),
-                                          static_cast<hipStream_t>(stream)));
+    return launch_status(gn::launch_fwd_stats(x, x_dtype, gamma, beta, eps, mean, rstd,
+                                              gn::kargs_of(p), gn::workspace_of(workspace, p),
+                                              static_cast<hipStream_t>(stream)));
 }
 
-int gn_forward_apply(const void* x, int x_dtype, const float* gamma, const float* beta,
-                     int64_t N, int64_t C, int64_t S, int64_t G, float eps,
-                     void* y, int y_dtype, float* mean, float* rstd,
-                     void* workspace, size_t workspace_bytes, void* stream)
+int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                     void* y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (!x || !y || !workspace) return GN_ERR_NULL;
     gn::Plan p;
-    int rc = fwd_check(x, x_dtype, gamma, beta, N, C, S, G, eps, y, y_dtype, mean, rstd,
-                       workspace, workspace_bytes, &p);
+    int rc = plan_or_error(N, C, S, G, &p);
     if (rc) return rc;
+    if (!dtype_ok(x_dtype) || !(y_dtype == x_dtype || y_dtype == GN_F32)) return GN_ERR_DTYPE;
+    if (!aligned(x, 16) || !aligned(y, 16)) return GN_ERR_ALIGN;
+    if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    const gn::KArgs a = gn::kargs_of(p);
-    return launch_status(gn::launch_apply(x, x_dtype, gamma, beta,
-                                          static_cast<const float2*>(workspace), y, y_dtype, mean,
-                                          rstd, a, eps, static_cast<hipStream_t>(stream)));
+    return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, gn::kargs_of(p),
+                                              gn::workspace_of(workspace, p),
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta,
@@ -192,46 +202,47 @@ int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
     const gn::KArgs a = gn::kargs_of(p);
+    const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    float2* part = static_cast<float2*>(workspace);
-    if ((rc = launch_status(gn::launch_stats(x, x_dtype, a, part, st)))) return rc;
-    return launch_status(gn::launch_apply(x, x_dtype, gamma, beta, part, y, y_dtype, mean, rstd,
-                                          a, eps, st));
+    if ((rc = launch_status(gn::launch_fwd_stats(x, x_dtype, gamma, beta, eps, mean, rstd, a, w, st))))
+        return rc;
+    return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, a, w, st));
 }
 
 int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
-                       const float* mean, const float* rstd,
+                       const float* mean, const float* rstd, const float* gamma,
                        int64_t N, int64_t C, int64_t S, int64_t G,
+                       float* dgamma, float* dbeta,
                        void* workspace, size_t workspace_bytes, void* stream)
 {
     gn::Plan p;
-    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, nullptr, N, C, S, G, nullptr,
-                       nullptr, nullptr, workspace, workspace_bytes, &p);
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, N, C, S, G, nullptr, dgamma,
+                       dbeta, workspace, workspace_bytes, &p);
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    const gn::KArgs a = gn::kargs_of(p);
-    return launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, a,
-                                               static_cast<float2*>(workspace),
+    return launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, dgamma,
+                                               dbeta, gn::kargs_of(p),
+                                               gn::workspace_of(workspace, p),
                                                static_cast<hipStream_t>(stream)));
 }
 
 int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
-                      const float* mean, const float* rstd, const float* gamma,
-                      int64_t N, int64_t C, int64_t S, int64_t G,
-                      void* dx, float* dgamma, float* dbeta,
+                      int64_t N, int64_t C, int64_t S, int64_t G, void* dx,
                       void* workspace, size_t workspace_bytes, void* stream)
 {
+    if (!dy || !x || !dx || !workspace) return GN_ERR_NULL;
     gn::Plan p;
-    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, N, C, S, G, dx, dgamma, dbeta,
-                       workspace, workspace_bytes, &p);
+    int rc = plan_or_error(N, C, S, G, &p);
     if (rc) return rc;
+    if (!dtype_ok(x_dtype) || !dtype_ok(dy_dtype)) return GN_ERR_DTYPE;
+    if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16)) return GN_ERR_ALIGN;
+    if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    const gn::KArgs a = gn::kargs_of(p);
-    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, mean, rstd, gamma,
-                                              static_cast<const float2*>(workspace), a, dx, dgamma,
-                                              dbeta, static_cast<hipStream_t>(stream)));
+    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, gn::kargs_of(p),
+                                              gn::workspace_of(workspace, p),
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
@@ -247,12 +258,13 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
     const gn::KArgs a = gn::kargs_of(p);
+    const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    float2* part = static_cast<float2*>(workspace);
-    if ((rc = launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, a, part, st))))
+    if ((rc = launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma,
+                                                  dgamma, dbeta, a, w, st))))
         return rc;
-    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, part, a,
-                                              dx, dgamma, dbeta, st));
+    if (!dx) return GN_OK;
+    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, a, w, st));
 }
 
 }  // extern "C"

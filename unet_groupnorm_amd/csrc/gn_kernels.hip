@@ -1,25 +1,36 @@
 // gn_kernels.hip -- GroupNorm forward/backward kernels for gfx950 (MI355X, CDNA4).
 //
-// Four kernels, two per direction ("Optimize GroupNorm", LBANN/ScaFFold pull 93,
-// paragraph folding seven launches into four):
-//   stats_kernel       per-job (mean, M2) of x                       [read x]
-//   apply_kernel       fixed-order merge -> mean/rstd, y = affine    [read x, write y]
-//   bwd_reduce_kernel  per-job (sum dy, sum dy*xhat)                  [read x, dy]
-//   bwd_apply_kernel   fixed-order merge -> c1, c2, dgamma, dbeta; dx [read x, dy, write dx]
+// Six kernels, three per direction:
+//   stats_kernel       per reduction job: (mean, M2) of x                   [read x]
+//   fin_fwd_kernel     per group: fixed-order merge -> mean, rstd, and per-row
+//                      normalize coefficients                               [tiny]
+//   apply_kernel       per streaming job: y = (x - mean) * gamma*rstd + beta [read x, write y]
+//   bwd_reduce_kernel  per reduction job: sum dy, sum dy*xhat               [read x, dy]
+//   fin_bwd_kernel     per group: c1, c2 -> per-row dx coefficients; per
+//                      channel: dgamma, dbeta                                [tiny]
+//   bwd_apply_kernel   per streaming job: dx                                [read x, dy, write dx]
 //
-// A job is a contiguous run of one row (row = n*C + c) given by the plan. Lane t of a
-// workgroup owns the 8-element vectors t, t + B, t + 2B, ... of its job (B = block
-// size, vectors counted on the global 8-element grid), holding kStepVecs of them per
-// step. The mapping is defined on elements, never on bytes, so the reduction order is
-// the same for fp32 and bf16 data.
+// The pages fold the finalize into the elementwise kernels ("Optimize GroupNorm",
+// LBANN/ScaFFold pull 93, paragraph folding seven launches into four) and cap the
+// elementwise grid so that the redundant partial reads stay small. On MI355X the
+// streaming kernels move data fastest as a very large grid of workgroups that each move
+// a few KiB once, which a folded finalize would multiply; so here the finalize runs once
+// per group in a small kernel of its own and the streaming kernels read 16 bytes of
+// per-row coefficients.
 //
-// Statistics are fp32 throughout. Each lane takes a corrected two-pass over its
-// register tile (tile mean, then sum of squared deviations minus the squared sum of
-// deviations over n), merges tiles with Chan's parallel formula, then lanes merge in a
-// fixed shuffle tree and waves in a fixed order through LDS ("Optimize GroupNorm",
-// paragraph introducing the NDHWC kernel: corrected two-pass per tile combined by Chan's
-// formula, register-only reductions, fixed order, no float atomics). No atomics are
-// used anywhere, so every result is bitwise reproducible run to run.
+// A reduction job is a contiguous run of one row (row = n*C + c). Lane t of a workgroup
+// owns the 8-element vectors t, t + B, t + 2B, ... of its job (B = block size, vectors
+// counted on the global 8-element grid), holding kStepVecs of them per step. The mapping
+// is defined on elements, never on bytes, so the reduction order is the same for fp32
+// and bf16 data.
+//
+// Statistics are fp32 throughout. Each lane takes a corrected two-pass over its register
+// tile (tile mean, then sum of squared deviations minus the squared sum of deviations over
+// n), merges tiles with Chan's parallel formula, then lanes merge in a fixed shuffle tree
+// and waves in a fixed order through LDS ("Optimize GroupNorm", paragraph introducing the
+// NDHWC kernel: corrected two-pass per tile combined by Chan's formula, register-only
+// reductions, fixed order, no float atomics). No atomics are used anywhere, so every
+// result is bitwise reproducible run to run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,6 +43,8 @@ namespace gn {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ element access
@@ -48,16 +61,29 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// Loads of the streamed tensors are marked nontemporal: each element is read once per
+// kernel, and on MI355X this lifts a streaming read from about 6.2 to about 7 TB/s.
 template <typename T> struct Io;
 
 template <> struct Io<uint16_t> {  // bf16 storage
+    // One 8-element vector as loaded (16 bytes), widened only where it is used.
+    struct Raw {
+        u32x4 u;
+    };
+    static __device__ __forceinline__ Raw load_raw(const uint16_t* p)
+    {
+        return Raw{__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))};
+    }
+    static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
+    {
+        v[0] = bf16_lo(r.u.x); v[1] = bf16_hi(r.u.x);
+        v[2] = bf16_lo(r.u.y); v[3] = bf16_hi(r.u.y);
+        v[4] = bf16_lo(r.u.z); v[5] = bf16_hi(r.u.z);
+        v[6] = bf16_lo(r.u.w); v[7] = bf16_hi(r.u.w);
+    }
     static __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8])
     {
-        const uint4 u = *reinterpret_cast<const uint4*>(p);
-        v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
-        v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-        v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
-        v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+        widen(load_raw(p), v);
     }
     static __device__ __forceinline__ float load1(const uint16_t* p)
     {
@@ -65,12 +91,12 @@ template <> struct Io<uint16_t> {  // bf16 storage
     }
     static __device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8])
     {
-        uint4 u;
+        u32x4 u;
         u.x = pack_bf16(v[0], v[1]);
         u.y = pack_bf16(v[2], v[3]);
         u.z = pack_bf16(v[4], v[5]);
         u.w = pack_bf16(v[6], v[7]);
-        *reinterpret_cast<uint4*>(p) = u;
+        *reinterpret_cast<u32x4*>(p) = u;
     }
     static __device__ __forceinline__ void store1(uint16_t* p, float v)
     {
@@ -79,18 +105,28 @@ template <> struct Io<uint16_t> {  // bf16 storage
 };
 
 template <> struct Io<float> {
+    struct Raw {
+        f32x4 a, b;
+    };
+    static __device__ __forceinline__ Raw load_raw(const float* p)
+    {
+        return Raw{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+                   __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
+    }
+    static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
+    {
+        v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+        v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
+    }
     static __device__ __forceinline__ void load8(const float* p, float (&v)[8])
     {
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        widen(load_raw(p), v);
     }
     static __device__ __forceinline__ float load1(const float* p) { return *p; }
     static __device__ __forceinline__ void store8(float* p, const float (&v)[8])
     {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-        *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
     static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 };
@@ -98,22 +134,22 @@ template <> struct Io<float> {
 // ------------------------------------------------------------------ job geometry
 
 struct Job {
-    int64_t row, k;   // row = n*C + c, chunk index within the row
+    int64_t row, k;   // row = n*C + c, job index within the row
     int64_t lo, hi;   // global element range [lo, hi)
     int64_t v0;       // first vector (floor(lo / 8))
     int64_t vf0, vf1; // full vectors are [vf0, vf1)
     int64_t nvec;     // vectors touched: [v0, v0 + nvec)
 };
 
-__device__ __forceinline__ Job job_at(const KArgs& a, int64_t j)
+__device__ __forceinline__ Job job_at(int64_t S, int64_t chunk, int64_t K, int64_t j)
 {
     Job b;
-    b.row = j / a.K;
-    b.k = j - b.row * a.K;
-    const int64_t base = b.row * a.S;
-    const int64_t end = (b.k + 1) * a.chunk;
-    b.lo = base + b.k * a.chunk;
-    b.hi = base + (end < a.S ? end : a.S);
+    b.row = j / K;
+    b.k = j - b.row * K;
+    const int64_t base = b.row * S;
+    const int64_t end = (b.k + 1) * chunk;
+    b.lo = base + b.k * chunk;
+    b.hi = base + (end < S ? end : S);
     b.v0 = b.lo / kVec;
     b.vf0 = (b.lo + kVec - 1) / kVec;
     b.vf1 = b.hi / kVec;
@@ -121,7 +157,7 @@ __device__ __forceinline__ Job job_at(const KArgs& a, int64_t j)
     return b;
 }
 
-// Element count of job j (the plan fixes it; it is never stored).
+// Element count of reduction job k of a row (the plan fixes it; it is never stored).
 __device__ __forceinline__ int64_t job_count(const KArgs& a, int64_t k)
 {
     const int64_t end = (k + 1) * a.chunk;
@@ -179,17 +215,50 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// Balanced pairwise sum of 2^k values (pairs i, i + half). A constant input is summed
-// exactly: every addition doubles a value.
+// Balanced pairwise sum of 2^k values (pairs i, i + half at every level), leaving the
+// input intact. A constant input is summed exactly: every addition doubles a value.
 template <int N>
-__device__ __forceinline__ float tree_sum(float (&t)[N])
+__device__ __forceinline__ float tree_sum(const float (&t)[N])
 {
+    float h[N / 2];
 #pragma unroll
-    for (int h = N / 2; h >= 1; h >>= 1) {
+    for (int i = 0; i < N / 2; ++i) h[i] = t[i] + t[i + N / 2];
 #pragma unroll
-        for (int i = 0; i < h; ++i) t[i] = t[i] + t[i + h];
+    for (int w = N / 4; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) h[i] = h[i] + h[i + w];
     }
-    return t[0];
+    return h[0];
+}
+
+// Sum of squares in the same tree shape, first level fused: d_i^2 + d_{i+half}^2.
+template <int N>
+__device__ __forceinline__ float tree_sumsq(const float (&d)[N])
+{
+    float h[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) h[i] = fmaf(d[i], d[i], d[i + N / 2] * d[i + N / 2]);
+#pragma unroll
+    for (int w = N / 4; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) h[i] = h[i] + h[i + w];
+    }
+    return h[0];
+}
+
+// Sum of products in the same tree shape, first level fused: a_i b_i + a_{i+half} b_{i+half}.
+template <int N>
+__device__ __forceinline__ float tree_sumprod(const float (&a)[N], const float (&b)[N])
+{
+    float h[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) h[i] = fmaf(a[i], b[i], a[i + N / 2] * b[i + N / 2]);
+#pragma unroll
+    for (int w = N / 4; w >= 1; w >>= 1) {
+#pragma unroll
+        for (int i = 0; i < w; ++i) h[i] = h[i] + h[i + w];
+    }
+    return h[0];
 }
 
 constexpr int kTile = kVec * kStepVecs;  // elements per lane per step (32)
@@ -197,23 +266,13 @@ constexpr int kTile = kVec * kStepVecs;  // elements per lane per step (32)
 // Corrected two-pass over a full register tile of values shifted by the group's shift K:
 // t = v - K, m = mean(t), M2 = sum d^2 - (sum d)^2 / n with d = t - m. The balanced sum
 // makes m exactly 0 for a constant tile equal to K.
-__device__ __forceinline__ void tile_moments_full(const float (&v)[kTile], float K, float& m, float& M2)
+__device__ __forceinline__ void tile_moments_full(float (&t)[kTile], float& m, float& M2)
 {
-    float t[kTile], u[kTile];
+    m = tree_sum(t) * (1.0f / kTile);
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) {
-        t[i] = v[i] - K;
-        u[i] = t[i];
-    }
-    m = tree_sum(u) * (1.0f / kTile);
-    float d[kTile], q[kTile];
-#pragma unroll
-    for (int i = 0; i < kTile; ++i) {
-        d[i] = t[i] - m;
-        q[i] = d[i] * d[i];
-    }
-    const float sd = tree_sum(d);
-    const float sq = tree_sum(q);
+    for (int i = 0; i < kTile; ++i) t[i] = t[i] - m;
+    const float sd = tree_sum(t);
+    const float sq = tree_sumsq(t);
     M2 = sq - (sd * sd) * (1.0f / kTile);
 }
 
@@ -225,18 +284,11 @@ __device__ __forceinline__ void tile_moments_masked(const float (&v)[kTile], flo
 #pragma unroll
     for (int i = 0; i < kTile; ++i) t[i] = ((valid >> i) & 1u) ? v[i] - K : 0.0f;
     const float fc = float(cnt);
-    float u[kTile];
+    m = tree_sum(t) / fc;
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) u[i] = t[i];
-    m = tree_sum(u) / fc;
-    float d[kTile], q[kTile];
-#pragma unroll
-    for (int i = 0; i < kTile; ++i) {
-        d[i] = ((valid >> i) & 1u) ? t[i] - m : 0.0f;
-        q[i] = d[i] * d[i];
-    }
-    const float sd = tree_sum(d);
-    const float sq = tree_sum(q);
+    for (int i = 0; i < kTile; ++i) t[i] = ((valid >> i) & 1u) ? t[i] - m : 0.0f;
+    const float sd = tree_sum(t);
+    const float sq = tree_sumsq(t);
     M2 = sq - (sd * sd) / fc;
 }
 
@@ -294,12 +346,6 @@ __device__ __forceinline__ void load_step_full(const T* __restrict__ p, int64_t 
     }
 }
 
-// Whole workgroup step inside the full-vector range (uniform across the workgroup).
-__device__ __forceinline__ bool step_is_full(const Job& jb, int64_t sv0, int64_t stepv)
-{
-    return sv0 >= jb.vf0 && sv0 + stepv <= jb.vf1;
-}
-
 constexpr int kMaxWaves = 4;
 
 // Merges the per-wave moments (lane 0 of each wave) in wave order; result valid in thread 0.
@@ -340,48 +386,121 @@ __device__ __forceinline__ float2 block_sum2(float a, float b, float* s_a, float
 
 // ------------------------------------------------------------------ forward
 
+// The lane's kStepVecs raw vectors of one full step.
+template <typename T>
+__device__ __forceinline__ void load_raw_step(const T* __restrict__ p, int64_t sv0, int blk, int tid,
+                                              typename Io<T>::Raw (&r)[kStepVecs])
+{
+#pragma unroll
+    for (int u = 0; u < kStepVecs; ++u) r[u] = Io<T>::load_raw(p + (sv0 + int64_t(u) * blk + tid) * kVec);
+}
+
+// Steps [fs, fe) of a job are full; step 0 when fs = 1 and step fe when fe < nsteps hold
+// the job's partial edge vectors (there is at most one partial step on each side).
+__device__ __forceinline__ void full_step_range(const Job& jb, int64_t stepv, int64_t& fs, int64_t& fe,
+                                                int64_t& nsteps)
+{
+    nsteps = (jb.nvec + stepv - 1) / stepv;
+    fs = (jb.v0 < jb.vf0) ? 1 : 0;
+    fe = (jb.vf1 - jb.v0) / stepv;
+    if (fe < fs) fe = fs;
+}
+
+template <typename TX>
+__device__ __forceinline__ void stats_full_step(const typename Io<TX>::Raw (&r)[kStepVecs], float K,
+                                                Moments<uint32_t>& acc)
+{
+    float t[kTile];
+#pragma unroll
+    for (int u = 0; u < kStepVecs; ++u) {
+        float e[kVec];
+        Io<TX>::widen(r[u], e);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) t[u * kVec + i] = e[i] - K;
+    }
+    float m, M2;
+    tile_moments_full(t, m, M2);
+    chan_merge(acc, uint32_t(kTile), m, M2);
+}
+
+template <typename TX>
+__device__ __forceinline__ void stats_masked_step(const TX* __restrict__ x, const Job& jb, int64_t sv0,
+                                                  int blk, int tid, float K, Moments<uint32_t>& acc)
+{
+    float v[kTile];
+    const uint32_t valid = load_step_masked(x, jb, sv0, blk, tid, v);
+    if (valid) {
+        const uint32_t cnt = __builtin_popcount(valid);
+        float m, M2;
+        tile_moments_masked(v, K, valid, cnt, m, M2);
+        chan_merge(acc, cnt, m, M2);
+    }
+}
+
+// The full steps are software-pipelined: the next step's vectors are requested before
+// the current step is reduced, alternating between two register sets so that waiting for
+// one set leaves the other in flight.
 template <typename TX>
 __global__ void __launch_bounds__(256)
 stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
 {
+    using Raw = typename Io<TX>::Raw;
     __shared__ uint32_t s_n[kMaxWaves];
     __shared__ float s_m[kMaxWaves], s_M[kMaxWaves];
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kStepVecs;
 
     for (int64_t j = blockIdx.x; j < a.jobs; j += gridDim.x) {
-        const Job jb = job_at(a, j);
+        const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, g = (jb.row - n * a.C) / a.Cg;
         const float K = group_shift(x, a, n, g);
         Moments<uint32_t> acc = {0u, 0.0f, 0.0f};
-        for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
-            float v[kTile];
-            float m, M2;
-            if (step_is_full(jb, sv0, stepv)) {
-                load_step_full(x, sv0, blk, tid, v);
-                tile_moments_full(v, K, m, M2);
-                chan_merge(acc, uint32_t(kTile), m, M2);
+        int64_t fs, fe, nsteps;
+        full_step_range(jb, stepv, fs, fe, nsteps);
+        // At most one partial step before and one after the full steps. They are written as
+        // conditionals: a one-trip loop over them was merged twice when built by hipcc
+        // (ROCm 7.2) for gfx950.
+        if (fs > 0) stats_masked_step(x, jb, jb.v0, blk, tid, K, acc);
+        if (fe > fs) {
+            Raw A[kStepVecs], B[kStepVecs];
+            load_raw_step(x, jb.v0 + fs * stepv, blk, tid, A);
+            int64_t s = fs;
+            for (; s + 2 < fe; s += 2) {
+                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                stats_full_step<TX>(A, K, acc);
+                load_raw_step(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
+                stats_full_step<TX>(B, K, acc);
+            }
+            if (s + 1 < fe) {
+                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                stats_full_step<TX>(A, K, acc);
+                stats_full_step<TX>(B, K, acc);
             } else {
-                const uint32_t valid = load_step_masked(x, jb, sv0, blk, tid, v);
-                if (valid) {
-                    const uint32_t cnt = __builtin_popcount(valid);
-                    tile_moments_masked(v, K, valid, cnt, m, M2);
-                    chan_merge(acc, cnt, m, M2);
-                }
+                stats_full_step<TX>(A, K, acc);
             }
         }
+        if (fe < nsteps) stats_masked_step(x, jb, jb.v0 + fe * stepv, blk, tid, K, acc);
         const Moments<uint32_t> r = block_merge(acc, s_n, s_m, s_M);
         if (tid == 0) part[j] = make_float2(r.m, r.M2);
     }
 }
 
-// Fixed-order merge of the P partials of group (n, g) into mean and rstd, broadcast
-// through LDS to the whole workgroup. Every workgroup that needs the group runs the same
-// merge on the same data and so obtains bitwise the same values.
-__device__ __forceinline__ void finalize_stats(const float2* __restrict__ part, const KArgs& a,
-                                               int64_t n, int64_t g, float eps,
-                                               float* s_stat, uint64_t* s_n, float* s_m, float* s_M)
+// One workgroup per group (n, g): merges the group's P partials in a fixed order (lane
+// t takes partials t, t + B, ... in index order, then the shuffle tree, then the waves
+// in order), publishes mean and rstd, and writes each row's normalize coefficients
+// (mean head, mean tail, gamma_c * rstd, beta_c).
+template <typename TX>
+__global__ void __launch_bounds__(256)
+fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
+               const float* __restrict__ beta, float eps, const float2* __restrict__ part,
+               float* __restrict__ mean_out, float* __restrict__ rstd_out, KArgs a,
+               float4* __restrict__ coef)
 {
+    __shared__ uint64_t s_n[kMaxWaves];
+    __shared__ float s_m[kMaxWaves], s_M[kMaxWaves];
+    __shared__ float s_stat[3];
+    const int64_t ng = blockIdx.x;
+    const int64_t n = ng / a.G, g = ng - n * a.G;
     const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
     Moments<uint64_t> acc = {0ull, 0.0f, 0.0f};
     for (int64_t j = threadIdx.x; j < a.P; j += blockDim.x) {
@@ -392,75 +511,53 @@ __device__ __forceinline__ void finalize_stats(const float2* __restrict__ part, 
     if (threadIdx.x == 0) {
         float var = float(double(r.M2) / double(a.M));
         var = (var < 0.0f) ? 0.0f : var;  // rounding can leave a tiny negative; NaN passes through
-        s_stat[0] = r.m;                  // mean relative to the group's shift
-        s_stat[1] = 1.0f / __fsqrt_rn(var + eps);
+        const float rstd = 1.0f / __fsqrt_rn(var + eps);
+        // The mean as an unevaluated sum hi + lo: hi is the fp32 mean that is published,
+        // lo what rounding it left out. The normalize takes x - mean as (x - hi) - lo,
+        // which is exact in its first step whenever x is close to the mean.
+        const float K = group_shift(x, a, n, g);
+        const float hi = K + r.m;
+        const float lo = (K - hi) + r.m;
+        mean_out[ng] = hi;
+        rstd_out[ng] = rstd;
+        s_stat[0] = hi; s_stat[1] = lo; s_stat[2] = rstd;
     }
     __syncthreads();
+    const float hi = s_stat[0], lo = s_stat[1], rstd = s_stat[2];
+    for (int64_t i = threadIdx.x; i < a.Cg; i += blockDim.x) {
+        const int64_t c = g * a.Cg + i;
+        const float gm = gamma ? gamma[c] : 1.0f;
+        const float bt = beta ? beta[c] : 0.0f;
+        coef[n * a.C + c] = make_float4(hi, lo, gm * rstd, bt);
+    }
 }
 
 template <typename TX, typename TY>
 __global__ void __launch_bounds__(256)
-apply_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
-             const float* __restrict__ beta, const float2* __restrict__ part,
-             TY* __restrict__ y, float* __restrict__ mean_out, float* __restrict__ rstd_out,
-             KArgs a, float eps)
+apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
+             const float4* __restrict__ coef)
 {
-    __shared__ uint64_t s_n[kMaxWaves];
-    __shared__ float s_m[kMaxWaves], s_M[kMaxWaves];
-    __shared__ float s_stat[2];
     const int tid = threadIdx.x, blk = blockDim.x;
-    const int64_t stepv = int64_t(blk) * kStepVecs;
-    int64_t cached = -1;
-
-    for (int64_t j = blockIdx.x; j < a.jobs; j += gridDim.x) {
-        const Job jb = job_at(a, j);
-        const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg, ng = n * a.G + g;
-        if (ng != cached) {
-            finalize_stats(part, a, n, g, eps, s_stat, s_n, s_m, s_M);
-            cached = ng;
-        }
-        // The mean as an unevaluated sum hi + lo: hi is the fp32 mean that is published,
-        // lo what rounding it left out. x - mean is taken as (x - hi) - lo, which is exact
-        // in its first step whenever x is close to the mean.
-        const float K = group_shift(x, a, n, g);
-        const float rel = s_stat[0], rstd = s_stat[1];  // mean relative to K
-        const float mu = K + rel;
-        const float mu_lo = (K - mu) + rel;
-        // The group's first job publishes the statistics.
-        if (tid == 0 && jb.k == 0 && c == g * a.Cg) {
-            mean_out[ng] = mu;
-            rstd_out[ng] = rstd;
-        }
-        const float scale = (gamma ? gamma[c] : 1.0f) * rstd;
-        const float shift = beta ? beta[c] : 0.0f;
-
+    const int64_t stepv = int64_t(blk) * kApplyVecs;
+    for (int64_t j = blockIdx.x; j < a.jobs_a; j += gridDim.x) {
+        const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
+        const float4 cf = coef[jb.row];
+        const float hi = cf.x, lo = cf.y, scale = cf.z, shift = cf.w;
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
-            if (step_is_full(jb, sv0, stepv)) {
-                float v[kTile];
-                load_step_full(x, sv0, blk, tid, v);
 #pragma unroll
-                for (int u = 0; u < kStepVecs; ++u) {
-                    float o[kVec];
+            for (int u = 0; u < kApplyVecs; ++u) {
+                const int64_t vi = sv0 + int64_t(u) * blk + tid;
+                if (vi >= jb.vf0 && vi < jb.vf1) {
+                    float e[kVec], o[kVec];
+                    Io<TX>::load8(x + vi * kVec, e);
 #pragma unroll
-                    for (int i = 0; i < kVec; ++i) o[i] = fmaf((v[u * kVec + i] - mu) - mu_lo, scale, shift);
-                    Io<TY>::store8(y + (sv0 + int64_t(u) * blk + tid) * kVec, o);
-                }
-            } else {
-#pragma unroll
-                for (int u = 0; u < kStepVecs; ++u) {
-                    const int64_t vi = sv0 + int64_t(u) * blk + tid;
-                    if (vi >= jb.vf0 && vi < jb.vf1) {
-                        float e[kVec], o[kVec];
-                        Io<TX>::load8(x + vi * kVec, e);
-#pragma unroll
-                        for (int i = 0; i < kVec; ++i) o[i] = fmaf((e[i] - mu) - mu_lo, scale, shift);
-                        Io<TY>::store8(y + vi * kVec, o);
-                    } else {
-                        for (int i = 0; i < kVec; ++i) {
-                            const int64_t gi = vi * kVec + i;
-                            if (gi >= jb.lo && gi < jb.hi)
-                                Io<TY>::store1(y + gi, fmaf((Io<TX>::load1(x + gi) - mu) - mu_lo, scale, shift));
-                        }
+                    for (int i = 0; i < kVec; ++i) o[i] = fmaf((e[i] - hi) - lo, scale, shift);
+                    Io<TY>::store8(y + vi * kVec, o);
+                } else {
+                    for (int i = 0; i < kVec; ++i) {
+                        const int64_t gi = vi * kVec + i;
+                        if (gi >= jb.lo && gi < jb.hi)
+                            Io<TY>::store1(y + gi, fmaf((Io<TX>::load1(x + gi) - hi) - lo, scale, shift));
                     }
                 }
             }
@@ -471,125 +568,178 @@ apply_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
 // ------------------------------------------------------------------ backward
 
 template <typename TX, typename TD>
+__device__ __forceinline__ void bwd_full_step(const typename Io<TX>::Raw (&rx)[kStepVecs],
+                                              const typename Io<TD>::Raw (&rd)[kStepVecs], float mu,
+                                              float& s1, float& s2)
+{
+    float d[kTile], gv[kTile];
+#pragma unroll
+    for (int u = 0; u < kStepVecs; ++u) {
+        float e[kVec], f[kVec];
+        Io<TX>::widen(rx[u], e);
+        Io<TD>::widen(rd[u], f);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+            d[u * kVec + i] = e[i] - mu;
+            gv[u * kVec + i] = f[i];
+        }
+    }
+    s1 = s1 + tree_sum(gv);
+    s2 = s2 + tree_sumprod(gv, d);
+}
+
+template <typename TX, typename TD>
+__device__ __forceinline__ void bwd_masked_step(const TD* __restrict__ dy, const TX* __restrict__ x,
+                                                const Job& jb, int64_t sv0, int blk, int tid, float mu,
+                                                float& s1, float& s2)
+{
+    float xv[kTile], gv[kTile];
+    const uint32_t valid = load_step_masked(x, jb, sv0, blk, tid, xv);
+    load_step_masked(dy, jb, sv0, blk, tid, gv);  // same mask: zeros outside
+#pragma unroll
+    for (int i = 0; i < kTile; ++i) xv[i] = ((valid >> i) & 1u) ? xv[i] - mu : 0.0f;
+    s1 = s1 + tree_sum(gv);
+    s2 = s2 + tree_sumprod(gv, xv);
+}
+
+// Per job: s1 = sum dy and s2 = rstd * sum dy * (x - mean) over the job's elements, lanes
+// summing their tiles in step order, then the shuffle tree, then the waves in order. The
+// full steps are software-pipelined as in stats_kernel.
+template <typename TX, typename TD>
 __global__ void __launch_bounds__(256)
 bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
                   const float* __restrict__ mean, const float* __restrict__ rstd,
                   KArgs a, float2* __restrict__ part)
 {
+    using RawX = typename Io<TX>::Raw;
+    using RawD = typename Io<TD>::Raw;
     __shared__ float s_a[kMaxWaves], s_b[kMaxWaves];
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kStepVecs;
 
     for (int64_t j = blockIdx.x; j < a.jobs; j += gridDim.x) {
-        const Job jb = job_at(a, j);
+        const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, ng = n * a.G + c / a.Cg;
         const float mu = mean[ng];
         float s1 = 0.0f, s2 = 0.0f;  // sum dy, sum dy * (x - mu)
-        for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
-            float xv[kTile], gv[kTile];
-            if (step_is_full(jb, sv0, stepv)) {
-                load_step_full(x, sv0, blk, tid, xv);
-                load_step_full(dy, sv0, blk, tid, gv);
-            } else {
-                const uint32_t valid = load_step_masked(x, jb, sv0, blk, tid, xv);
-                load_step_masked(dy, jb, sv0, blk, tid, gv);  // same mask: zeros outside
-#pragma unroll
-                for (int i = 0; i < kTile; ++i) xv[i] = ((valid >> i) & 1u) ? xv[i] : mu;
+        int64_t fs, fe, nsteps;
+        full_step_range(jb, stepv, fs, fe, nsteps);
+        if (fs > 0) bwd_masked_step(dy, x, jb, jb.v0, blk, tid, mu, s1, s2);
+        if (fe > fs) {
+            RawX AX[kStepVecs], BX[kStepVecs];
+            RawD AD[kStepVecs], BD[kStepVecs];
+            load_raw_step(x, jb.v0 + fs * stepv, blk, tid, AX);
+            load_raw_step(dy, jb.v0 + fs * stepv, blk, tid, AD);
+            int64_t s = fs;
+            for (; s + 2 < fe; s += 2) {
+                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
+                load_raw_step(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
+                load_raw_step(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
+                bwd_full_step<TX, TD>(BX, BD, mu, s1, s2);
             }
-            float p[kTile];
-#pragma unroll
-            for (int i = 0; i < kTile; ++i) p[i] = gv[i] * (xv[i] - mu);
-            s1 = s1 + tree_sum(gv);
-            s2 = s2 + tree_sum(p);
+            if (s + 1 < fe) {
+                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
+                bwd_full_step<TX, TD>(BX, BD, mu, s1, s2);
+            } else {
+                bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
+            }
         }
+        if (fe < nsteps) bwd_masked_step(dy, x, jb, jb.v0 + fe * stepv, blk, tid, mu, s1, s2);
         const float2 r = block_sum2(s1, s2, s_a, s_b);
         if (tid == 0) part[j] = make_float2(r.x, r.y * rstd[ng]);
     }
 }
 
-template <typename TX, typename TD>
+// Workgroups [0, ngroups) each take one group (n, g): c1 = (1/M) sum gamma_c s1,
+// c2 = (1/M) sum gamma_c s2 over the group's P partials in a fixed order, then each row's
+// dx coefficients (mean, A = rstd*gamma_c, B = -rstd*c1, E = -rstd^2*c2), so that
+// dx = rstd*(gamma_c*dy - c1 - xhat*c2) = A*dy + (B + E*(x - mean)).
+// Workgroups [ngroups, ngroups + nchan) each take one channel c: dgamma_c and dbeta_c as
+// the sums of the channel's N*K partials, n-major then k, in a fixed order.
 __global__ void __launch_bounds__(256)
-bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
-                 const float* __restrict__ mean, const float* __restrict__ rstd,
-                 const float* __restrict__ gamma, const float2* __restrict__ part, KArgs a,
-                 TX* __restrict__ dx, float* __restrict__ dgamma, float* __restrict__ dbeta)
+fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
+               const float* __restrict__ gamma, const float2* __restrict__ part, KArgs a,
+               int64_t ngroups, int64_t nchan, float4* __restrict__ coef,
+               float* __restrict__ dgamma, float* __restrict__ dbeta)
 {
     __shared__ float s_a[kMaxWaves], s_b[kMaxWaves];
     __shared__ float s_coef[2];
     const int tid = threadIdx.x, blk = blockDim.x;
-    const int64_t stepv = int64_t(blk) * kStepVecs;
-    int64_t cached = -1;
-
-    for (int64_t j = blockIdx.x; j < a.jobs; j += gridDim.x) {
-        const Job jb = job_at(a, j);
-        const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg, ng = n * a.G + g;
-
-        // dgamma_c, dbeta_c: the job (n = 0, k = 0) of channel c sums the N*K partials of
-        // the channel, n-major then k, in a fixed tree.
-        if ((dgamma || dbeta) && n == 0 && jb.k == 0) {
-            float sa = 0.0f, sb = 0.0f;
-            for (int64_t i = tid; i < a.N * a.K; i += blk) {
-                const int64_t nn = i / a.K, kk = i - nn * a.K;
-                const float2 pp = part[(nn * a.C + c) * a.K + kk];
-                sa = sa + pp.y;
-                sb = sb + pp.x;
-            }
-            const float2 r = block_sum2(sa, sb, s_a, s_b);
-            if (tid == 0) {
-                if (dgamma) dgamma[c] = r.x;
-                if (dbeta) dbeta[c] = r.y;
-            }
+    const int64_t w = blockIdx.x;
+    if (w < ngroups) {
+        const int64_t n = w / a.G, g = w - n * a.G;
+        const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
+        float t1 = 0.0f, t2 = 0.0f;
+        for (int64_t i = tid; i < a.P; i += blk) {
+            const float2 pp = part[pbase + i];
+            const float gm = gamma ? gamma[g * a.Cg + i / a.K] : 1.0f;
+            t1 = t1 + gm * pp.x;
+            t2 = t2 + gm * pp.y;
         }
-        if (!dx) continue;
-
-        if (ng != cached) {
-            // c1 = (1/M) sum_{c in g} gamma_c s1[n,c], c2 likewise with s2, over the
-            // group's P partials in a fixed order.
-            const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
-            float t1 = 0.0f, t2 = 0.0f;
-            for (int64_t i = tid; i < a.P; i += blk) {
-                const float2 pp = part[pbase + i];
-                const float gm = gamma ? gamma[g * a.Cg + i / a.K] : 1.0f;
-                t1 = t1 + gm * pp.x;
-                t2 = t2 + gm * pp.y;
-            }
-            const float2 r = block_sum2(t1, t2, s_a, s_b);
-            if (tid == 0) {
-                s_coef[0] = float(double(r.x) / double(a.M));
-                s_coef[1] = float(double(r.y) / double(a.M));
-            }
-            __syncthreads();
-            cached = ng;
+        const float2 r = block_sum2(t1, t2, s_a, s_b);
+        if (tid == 0) {
+            s_coef[0] = float(double(r.x) / double(a.M));
+            s_coef[1] = float(double(r.y) / double(a.M));
         }
-        const float mu = mean[ng], rs = rstd[ng];
-        const float gm = gamma ? gamma[c] : 1.0f;
-        // dx = rstd * (gamma*dy - c1 - xhat*c2) = A*dy + (B + E*(x - mu))
-        const float A = rs * gm;
+        __syncthreads();
+        const float mu = mean[w], rs = rstd[w];
         const float B = -(rs * s_coef[0]);
         const float E = -((rs * rs) * s_coef[1]);
-        // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
-        const bool single = (a.M == 1);
+        for (int64_t i = tid; i < a.Cg; i += blk) {
+            const int64_t c = g * a.Cg + i;
+            const float gm = gamma ? gamma[c] : 1.0f;
+            coef[n * a.C + c] = make_float4(mu, rs * gm, B, E);
+        }
+    } else if (w < ngroups + nchan) {
+        const int64_t c = w - ngroups;
+        float sa = 0.0f, sb = 0.0f;
+        for (int64_t i = tid; i < a.N * a.K; i += blk) {
+            const int64_t nn = i / a.K, kk = i - nn * a.K;
+            const float2 pp = part[(nn * a.C + c) * a.K + kk];
+            sa = sa + pp.y;
+            sb = sb + pp.x;
+        }
+        const float2 r = block_sum2(sa, sb, s_a, s_b);
+        if (tid == 0) {
+            if (dgamma) dgamma[c] = r.x;
+            if (dbeta) dbeta[c] = r.y;
+        }
+    }
+}
 
+template <typename TX, typename TD>
+__global__ void __launch_bounds__(256)
+bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
+                 const float4* __restrict__ coef, TX* __restrict__ dx)
+{
+    const int tid = threadIdx.x, blk = blockDim.x;
+    const int64_t stepv = int64_t(blk) * kApplyVecs;
+    // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
+    const bool single = (a.M == 1);
+    for (int64_t j = blockIdx.x; j < a.jobs_a; j += gridDim.x) {
+        const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
+        const float4 cf = coef[jb.row];
+        const float mu = cf.x, A = cf.y, B = cf.z, E = cf.w;
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
-            if (step_is_full(jb, sv0, stepv)) {
-                float xv[kTile], gv[kTile];
-                load_step_full(x, sv0, blk, tid, xv);
-                load_step_full(dy, sv0, blk, tid, gv);
 #pragma unroll
-                for (int u = 0; u < kStepVecs; ++u) {
-                    float o[kVec];
+            for (int u = 0; u < kApplyVecs; ++u) {
+                const int64_t vi = sv0 + int64_t(u) * blk + tid;
+                if (vi >= jb.vf0 && vi < jb.vf1) {
+                    float xv[kVec], gv[kVec], o[kVec];
+                    Io<TX>::load8(x + vi * kVec, xv);
+                    Io<TD>::load8(dy + vi * kVec, gv);
 #pragma unroll
                     for (int i = 0; i < kVec; ++i) {
-                        const int e = u * kVec + i;
-                        float t = fmaf(A, gv[e], fmaf(E, xv[e] - mu, B));
+                        float t = fmaf(A, gv[i], fmaf(E, xv[i] - mu, B));
                         if (single) t = t - t;
                         o[i] = t;
                     }
-                    Io<TX>::store8(dx + (sv0 + int64_t(u) * blk + tid) * kVec, o);
-                }
-            } else {
-                for (int u = 0; u < kStepVecs; ++u) {
-                    const int64_t vi = sv0 + int64_t(u) * blk + tid;
+                    Io<TX>::store8(dx + vi * kVec, o);
+                } else {
                     for (int i = 0; i < kVec; ++i) {
                         const int64_t gi = vi * kVec + i;
                         if (gi >= jb.lo && gi < jb.hi) {
@@ -622,76 +772,86 @@ hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... a
 template <typename T> const T* cp(const void* p) { return static_cast<const T*>(p); }
 template <typename T> T* mp(void* p) { return static_cast<T*>(p); }
 
-int64_t grid_for(const KArgs& a) { return a.jobs < kMaxGrid ? a.jobs : kMaxGrid; }
+dim3 grid_of(int64_t jobs) { return dim3(unsigned(jobs < kMaxGrid ? jobs : kMaxGrid)); }
 
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_stats(const void* x, int xdt, const KArgs& a, float2* part, hipStream_t st)
+hipError_t launch_fwd_stats(const void* x, int xdt, const float* gamma, const float* beta,
+                            float eps, float* mean, float* rstd, const KArgs& a, Workspace ws,
+                            hipStream_t st)
 {
-    const dim3 grid(unsigned(grid_for(a))), block(unsigned(a.block));
-    if (xdt == kBF16)
-        return launch(stats_kernel<uint16_t>, grid, block, st, cp<uint16_t>(x), a, part);
-    else
-        return launch(stats_kernel<float>, grid, block, st, cp<float>(x), a, part);
+    const dim3 g1 = grid_of(a.jobs), b1(unsigned(a.block));
+    const dim3 g2(unsigned(a.N * a.G)), b2(256);
+    hipError_t e;
+    if (xdt == kBF16) {
+        e = launch(stats_kernel<uint16_t>, g1, b1, st, cp<uint16_t>(x), a, ws.part);
+        if (e != hipSuccess) return e;
+        return launch(fin_fwd_kernel<uint16_t>, g2, b2, st, cp<uint16_t>(x), gamma, beta, eps,
+                      static_cast<const float2*>(ws.part), mean, rstd, a, ws.coef);
+    }
+    e = launch(stats_kernel<float>, g1, b1, st, cp<float>(x), a, ws.part);
+    if (e != hipSuccess) return e;
+    return launch(fin_fwd_kernel<float>, g2, b2, st, cp<float>(x), gamma, beta, eps,
+                  static_cast<const float2*>(ws.part), mean, rstd, a, ws.coef);
 }
 
-hipError_t launch_apply(const void* x, int xdt, const float* gamma, const float* beta,
-                        const float2* part, void* y, int ydt, float* mean, float* rstd,
-                        const KArgs& a, float eps, hipStream_t st)
+hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArgs& a,
+                            Workspace ws, hipStream_t st)
 {
-    const dim3 grid(unsigned(grid_for(a))), block(unsigned(a.block));
+    const dim3 grid = grid_of(a.jobs_a), block(unsigned(a.block_a));
+    const float4* coef = ws.coef;
     if (xdt == kBF16 && ydt == kBF16)
-        return launch(apply_kernel<uint16_t, uint16_t>, grid, block, st,
-                           cp<uint16_t>(x), gamma, beta, part, mp<uint16_t>(y), mean, rstd, a, eps);
-    else if (xdt == kBF16)
-        return launch(apply_kernel<uint16_t, float>, grid, block, st,
-                           cp<uint16_t>(x), gamma, beta, part, mp<float>(y), mean, rstd, a, eps);
-    else
-        return launch(apply_kernel<float, float>, grid, block, st,
-                           cp<float>(x), gamma, beta, part, mp<float>(y), mean, rstd, a, eps);
+        return launch(apply_kernel<uint16_t, uint16_t>, grid, block, st, cp<uint16_t>(x),
+                      mp<uint16_t>(y), a, coef);
+    if (xdt == kBF16)
+        return launch(apply_kernel<uint16_t, float>, grid, block, st, cp<uint16_t>(x), mp<float>(y),
+                      a, coef);
+    return launch(apply_kernel<float, float>, grid, block, st, cp<float>(x), mp<float>(y), a, coef);
 }
 
 hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, const float* mean,
-                             const float* rstd, const KArgs& a, float2* part, hipStream_t st)
+                             const float* rstd, const float* gamma, float* dgamma, float* dbeta,
+                             const KArgs& a, Workspace ws, hipStream_t st)
 {
-    const dim3 grid(unsigned(grid_for(a))), block(unsigned(a.block));
+    const dim3 g1 = grid_of(a.jobs), b1(unsigned(a.block));
+    hipError_t e;
     if (xdt == kBF16 && dydt == kBF16)
-        return launch(bwd_reduce_kernel<uint16_t, uint16_t>, grid, block, st,
-                           cp<uint16_t>(dy), cp<uint16_t>(x), mean, rstd, a, part);
+        e = launch(bwd_reduce_kernel<uint16_t, uint16_t>, g1, b1, st, cp<uint16_t>(dy),
+                   cp<uint16_t>(x), mean, rstd, a, ws.part);
     else if (xdt == kBF16)
-        return launch(bwd_reduce_kernel<uint16_t, float>, grid, block, st,
-                           cp<float>(dy), cp<uint16_t>(x), mean, rstd, a, part);
+        e = launch(bwd_reduce_kernel<uint16_t, float>, g1, b1, st, cp<float>(dy), cp<uint16_t>(x),
+                   mean, rstd, a, ws.part);
     else if (dydt == kBF16)
-        return launch(bwd_reduce_kernel<float, uint16_t>, grid, block, st,
-                           cp<uint16_t>(dy), cp<float>(x), mean, rstd, a, part);
+        e = launch(bwd_reduce_kernel<float, uint16_t>, g1, b1, st, cp<uint16_t>(dy), cp<float>(x),
+                   mean, rstd, a, ws.part);
     else
-        return launch(bwd_reduce_kernel<float, float>, grid, block, st,
-                           cp<float>(dy), cp<float>(x), mean, rstd, a, part);
+        e = launch(bwd_reduce_kernel<float, float>, g1, b1, st, cp<float>(dy), cp<float>(x), mean,
+                   rstd, a, ws.part);
+    if (e != hipSuccess) return e;
+    const int64_t ngroups = a.N * a.G;
+    const int64_t nchan = (dgamma || dbeta) ? a.C : 0;
+    return launch(fin_bwd_kernel, dim3(unsigned(ngroups + nchan)), dim3(256), st, mean, rstd, gamma,
+                  static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coef, dgamma, dbeta);
 }
 
-hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, const float* mean,
-                            const float* rstd, const float* gamma, const float2* part,
-                            const KArgs& a, void* dx, float* dgamma, float* dbeta, hipStream_t st)
+hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,
+                            const KArgs& a, Workspace ws, hipStream_t st)
 {
-    const dim3 grid(unsigned(grid_for(a))), block(unsigned(a.block));
+    const dim3 grid = grid_of(a.jobs_a), block(unsigned(a.block_a));
+    const float4* coef = ws.coef;
     if (xdt == kBF16 && dydt == kBF16)
-        return launch(bwd_apply_kernel<uint16_t, uint16_t>, grid, block, st,
-                           cp<uint16_t>(dy), cp<uint16_t>(x), mean, rstd, gamma, part, a,
-                           mp<uint16_t>(dx), dgamma, dbeta);
-    else if (xdt == kBF16)
-        return launch(bwd_apply_kernel<uint16_t, float>, grid, block, st,
-                           cp<float>(dy), cp<uint16_t>(x), mean, rstd, gamma, part, a,
-                           mp<uint16_t>(dx), dgamma, dbeta);
-    else if (dydt == kBF16)
-        return launch(bwd_apply_kernel<float, uint16_t>, grid, block, st,
-                           cp<uint16_t>(dy), cp<float>(x), mean, rstd, gamma, part, a,
-                           mp<float>(dx), dgamma, dbeta);
-    else
-        return launch(bwd_apply_kernel<float, float>, grid, block, st,
-                           cp<float>(dy), cp<float>(x), mean, rstd, gamma, part, a,
-                           mp<float>(dx), dgamma, dbeta);
+        return launch(bwd_apply_kernel<uint16_t, uint16_t>, grid, block, st, cp<uint16_t>(dy),
+                      cp<uint16_t>(x), a, coef, mp<uint16_t>(dx));
+    if (xdt == kBF16)
+        return launch(bwd_apply_kernel<uint16_t, float>, grid, block, st, cp<float>(dy),
+                      cp<uint16_t>(x), a, coef, mp<uint16_t>(dx));
+    if (dydt == kBF16)
+        return launch(bwd_apply_kernel<float, uint16_t>, grid, block, st, cp<uint16_t>(dy),
+                      cp<float>(x), a, coef, mp<float>(dx));
+    return launch(bwd_apply_kernel<float, float>, grid, block, st, cp<float>(dy), cp<float>(x), a,
+                  coef, mp<float>(dx));
 }
 
 }  // namespace gn

@@ -11,14 +11,15 @@ namespace gn {
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
 // Largest grid launched; kernels stride over any further jobs.
-constexpr int64_t kMaxGrid = int64_t(1) << 20;
+constexpr int64_t kMaxGrid = int64_t(1) << 30;
 
 // Plain-old-data view of a Plan, passed by value to every kernel.
 struct KArgs {
     int64_t N, C, S, G;
     int64_t Cg, M;
-    int64_t chunk, K, jobs, P;
-    int32_t block;
+    int64_t chunk, K, jobs, P;        // reduction jobs
+    int64_t chunk_a, K_a, jobs_a;     // streaming jobs
+    int32_t block, block_a;
 };
 
 inline KArgs kargs_of(const Plan& p)
@@ -27,18 +28,39 @@ inline KArgs kargs_of(const Plan& p)
     a.N = p.N; a.C = p.C; a.S = p.S; a.G = p.G;
     a.Cg = p.Cg; a.M = p.M;
     a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs; a.P = p.P;
-    a.block = p.block;
+    a.chunk_a = p.chunk_a; a.K_a = p.K_a; a.jobs_a = p.jobs_a;
+    a.block = p.block; a.block_a = p.block_a;
     return a;
 }
 
-hipError_t launch_stats(const void* x, int xdt, const KArgs& a, float2* part, hipStream_t st);
-hipError_t launch_apply(const void* x, int xdt, const float* gamma, const float* beta,
-                        const float2* part, void* y, int ydt, float* mean, float* rstd,
-                        const KArgs& a, float eps, hipStream_t st);
+// Workspace views. The partials area holds one float2 per reduction job; the coefficient
+// area one float4 per row, written by a finalize kernel and read by the streaming kernel.
+struct Workspace {
+    float2* part;
+    float4* coef;
+};
+
+inline Workspace workspace_of(void* ws, const Plan& p)
+{
+    char* b = static_cast<char*>(ws);
+    return Workspace{reinterpret_cast<float2*>(b), reinterpret_cast<float4*>(b + p.ws_coef_offset)};
+}
+
+// Forward, first half: statistics partials, then their fixed-order merge into mean/rstd
+// and the per-row normalize coefficients.
+hipError_t launch_fwd_stats(const void* x, int xdt, const float* gamma, const float* beta,
+                            float eps, float* mean, float* rstd, const KArgs& a, Workspace ws,
+                            hipStream_t st);
+// Forward, second half: y from x and the per-row coefficients.
+hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArgs& a,
+                            Workspace ws, hipStream_t st);
+// Backward, first half: per-job sums of dy and dy*xhat, then their fixed-order merge into
+// dgamma/dbeta and the per-row dx coefficients.
 hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, const float* mean,
-                             const float* rstd, const KArgs& a, float2* part, hipStream_t st);
-hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, const float* mean,
-                            const float* rstd, const float* gamma, const float2* part,
-                            const KArgs& a, void* dx, float* dgamma, float* dbeta, hipStream_t st);
+                             const float* rstd, const float* gamma, float* dgamma, float* dbeta,
+                             const KArgs& a, Workspace ws, hipStream_t st);
+// Backward, second half: dx from x, dy and the per-row coefficients.
+hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,
+                            const KArgs& a, Workspace ws, hipStream_t st);
 
 }  // namespace gn

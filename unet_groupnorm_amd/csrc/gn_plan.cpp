@@ -55,7 +55,18 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     q.jobs = q.rows * K;
     q.P = Cg * K;
     q.block = block;
-    q.ws_bytes = size_t(round_up(q.jobs * 8, 256));
+
+    // Streaming jobs: kApplyVecs vectors per lane, the block sized (64..256) to the row.
+    int block_a = 64;
+    while (block_a < 256 && int64_t(block_a) * kApplyVecs < row_vecs) block_a *= 2;
+    const int64_t step_a = int64_t(block_a) * kApplyVecs * kVec;
+    q.block_a = block_a;
+    q.chunk_a = S <= step_a ? S : step_a;
+    q.K_a = ceil_div(S, q.chunk_a);
+    q.jobs_a = q.rows * q.K_a;
+
+    q.ws_coef_offset = size_t(round_up(q.jobs * 8, 256));
+    q.ws_bytes = q.ws_coef_offset + size_t(round_up(q.rows * 16, 256));
     *p = q;
     return 0;
 }

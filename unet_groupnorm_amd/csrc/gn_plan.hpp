@@ -5,6 +5,14 @@
 // shape; "Preserve GroupNorm dtype" (pull 105), second paragraph: the plan takes no
 // dtype, which is what makes the fp32 and bf16 backward bitwise identical.
 //
+// Two decompositions of the volume, both into "jobs" that are contiguous runs of one
+// row (row = n*C + c):
+//   - reduction jobs (statistics, backward sums): few and long, one fp32 partial each;
+//     their count and length fix the reduction order;
+//   - streaming jobs (normalize, dx): one short step each, so that the grid is large
+//     and every workgroup moves a few KiB and retires. They reduce nothing, so their
+//     shape can change without moving a bit.
+//
 // This unit is plain C++ (no HIP), so it is exercised on a host without a GPU.
 #pragma once
 
@@ -16,11 +24,23 @@ namespace gn {
 // Elements per lane vector: one 16-byte load of bf16, two of fp32. The element -> lane
 // assignment is defined in these units, so it is the same for both dtypes.
 constexpr int kVec = 8;
-// Vectors each lane holds per step (the register tile is kVec * kStepVecs elements).
-constexpr int kStepVecs = 4;
-// Workgroups a launch aims for: 8 per CU on the 256 CUs of an MI355X.
-constexpr int64_t kTargetJobs = 2048;
-// Upper bound on a job's element count, keeping every in-job count within 32 bits.
+// Tuning constants (compile-time overridable for measurement builds).
+#ifndef GN_STEP_VECS
+#define GN_STEP_VECS 4
+#endif
+#ifndef GN_TARGET_JOBS
+#define GN_TARGET_JOBS 2048
+#endif
+#ifndef GN_APPLY_VECS
+#define GN_APPLY_VECS 1
+#endif
+// Vectors each lane holds per step of a reduction job (register tile = kVec * kStepVecs).
+constexpr int kStepVecs = GN_STEP_VECS;
+// Reduction workgroups a launch aims for (2048: 8 per CU on the 256 CUs of an MI355X).
+constexpr int64_t kTargetJobs = GN_TARGET_JOBS;
+// Vectors each lane moves in a streaming job.
+constexpr int kApplyVecs = GN_APPLY_VECS;
+// Upper bound on a reduction job's element count (in-job counts stay within 32 bits).
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
 // Upper bound on N*C*S accepted (indices stay far from int64 overflow).
 constexpr int64_t kMaxNumel = int64_t(1) << 48;
@@ -30,12 +50,20 @@ struct Plan {
     int64_t Cg = 0;      // channels per group
     int64_t M = 0;       // elements per group
     int64_t rows = 0;    // N * C
+    // reduction jobs
     int64_t chunk = 0;   // elements per job
     int64_t K = 0;       // jobs per row
     int64_t jobs = 0;    // rows * K
     int64_t P = 0;       // partials per group = Cg * K
     int block = 0;       // threads per workgroup
-    size_t ws_bytes = 0; // workspace: one float2 partial per job, rounded to 256 bytes
+    // streaming jobs
+    int64_t chunk_a = 0;
+    int64_t K_a = 0;
+    int64_t jobs_a = 0;
+    int block_a = 0;
+    // workspace: [partials: float2 * jobs][row coefficients: float4 * rows], 256-byte aligned
+    size_t ws_coef_offset = 0;
+    size_t ws_bytes = 0;
 };
 
 // Returns 0 and fills *p for a valid shape, else a gn_status shape error code

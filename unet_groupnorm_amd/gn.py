@@ -106,21 +106,24 @@ def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, workspace=None, o
     return y, mean, rstd
 
 
-def gn_forward_stats(x, G, workspace):
-    _contig("x", x)
-    N, C, S, G = _dims(x, G)
-    _check("gn_forward_stats", lib.gn_forward_stats(
-        _ptr(x), _dtype(x), N, C, S, G, _ptr(workspace), workspace.numel(), _stream(x.device)))
-
-
-def gn_forward_apply(x, gamma, beta, G, eps, y, mean, rstd, workspace):
+def gn_forward_stats(x, gamma, beta, G, eps, mean, rstd, workspace):
+    """First half of gn_forward: mean/rstd, and coefficients left in the workspace."""
     _contig("x", x)
     N, C, S, G = _dims(x, G)
     dev = x.device
-    _check("gn_forward_apply", lib.gn_forward_apply(
+    _check("gn_forward_stats", lib.gn_forward_stats(
         _ptr(x), _dtype(x), _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
-        N, C, S, G, float(eps), _ptr(_contig("y", y)), _dtype(y), _ptr(mean), _ptr(rstd),
-        _ptr(workspace), workspace.numel(), _stream(dev)))
+        N, C, S, G, float(eps), _ptr(mean), _ptr(rstd), _ptr(workspace), workspace.numel(),
+        _stream(dev)))
+
+
+def gn_forward_apply(x, G, y, workspace):
+    """Second half of gn_forward: y from x and the workspace coefficients."""
+    _contig("x", x)
+    N, C, S, G = _dims(x, G)
+    _check("gn_forward_apply", lib.gn_forward_apply(
+        _ptr(x), _dtype(x), N, C, S, G, _ptr(_contig("y", y)), _dtype(y), _ptr(workspace),
+        workspace.numel(), _stream(x.device)))
 
 
 def gn_backward(dy, x, mean, rstd, gamma, G, *, need_dx=True, need_dgamma=True, need_dbeta=True,
@@ -146,22 +149,25 @@ def gn_backward(dy, x, mean, rstd, gamma, G, *, need_dx=True, need_dgamma=True, 
     return (dx if need_dx else None, dgamma if need_dgamma else None, dbeta if need_dbeta else None)
 
 
-def gn_backward_reduce(dy, x, mean, rstd, G, workspace):
-    _contig("x", x); _contig("dy", dy)
-    N, C, S, G = _dims(x, G)
-    _check("gn_backward_reduce", lib.gn_backward_reduce(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd), N, C, S, G,
-        _ptr(workspace), workspace.numel(), _stream(x.device)))
-
-
-def gn_backward_apply(dy, x, mean, rstd, gamma, G, dx, dgamma, dbeta, workspace):
+def gn_backward_reduce(dy, x, mean, rstd, gamma, G, dgamma, dbeta, workspace):
+    """First half of gn_backward: dgamma/dbeta (either may be None), coefficients left in
+    the workspace."""
     _contig("x", x); _contig("dy", dy)
     N, C, S, G = _dims(x, G)
     dev = x.device
-    _check("gn_backward_apply", lib.gn_backward_apply(
+    _check("gn_backward_reduce", lib.gn_backward_reduce(
         _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), N, C, S, G, _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+        _ptr(_vec("gamma", gamma, C, dev)), N, C, S, G, _ptr(dgamma), _ptr(dbeta),
         _ptr(workspace), workspace.numel(), _stream(dev)))
+
+
+def gn_backward_apply(dy, x, G, dx, workspace):
+    """Second half of gn_backward: dx from x, dy and the workspace coefficients."""
+    _contig("x", x); _contig("dy", dy)
+    N, C, S, G = _dims(x, G)
+    _check("gn_backward_apply", lib.gn_backward_apply(
+        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), N, C, S, G, _ptr(dx), _ptr(workspace),
+        workspace.numel(), _stream(x.device)))
 
 
 class GroupNormFn(torch.autograd.Function):
