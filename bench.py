@@ -161,6 +161,42 @@ class Runner:
         return total / steps
 
 
+def census(steps=10, warmup=3):
+    """The 18 GroupNorm sites of a scale-7 UNet, fwd+bwd each, back to back: aggregate rate
+    on method bytes, and whether 10 repeats of every site are bitwise identical."""
+    import torch
+
+    import workloads
+    runs = [Runner(c) for c in workloads.census_cases()]
+    for r in runs:
+        for _ in range(warmup):
+            r.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        for r in runs:
+            r.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    total = sum(r.step_bytes for r in runs)
+    # determinism: 10 repeats per site, every output compared bitwise with the first
+    identical = True
+    for r in runs:
+        r.step()
+        ref = [t.clone() for t in (r.y, r.mean, r.rstd, r.dx, r.dgamma, r.dbeta)]
+        for _ in range(9):
+            r.step()
+            for a, b in zip(ref, (r.y, r.mean, r.rstd, r.dx, r.dgamma, r.dbeta)):
+                identical &= bool(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                                              b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)))
+    return {"sites": len(runs), "elements": sum(r.case.numel for r in runs), "ms_per_pass": round(ms, 4),
+            "value": round(total / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "pct_of_peak": round(100 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+            "bitwise_identical_10_repeats": identical}
+
+
 def copy_ceiling_gbps(nbytes=1 << 30, reps=20):
     import torch
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
@@ -316,12 +352,19 @@ def main():
         r8 = Runner(c8)
         ms8, _ = r8.timed_steps(max(5, args.steps // 5), 3)
         ph8 = r8.timed_phases(10)
+        fms8 = r8.flushed_steps(5)
         out["scale8"] = {
             "workload": c8.name, "ms_per_step": round(ms8, 4),
             "value": round(r8.step_bytes / (ms8 * 1e-3) / 1e9, 1),
             "pct_of_peak": round(100 * r8.step_bytes / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
             "kernels_us": {k: round(v * 1e3, 1) for k, v in ph8.items()},
+            "llc_flushed": {"ms_per_step": round(fms8, 4),
+                            "value": round(r8.step_bytes / (fms8 * 1e-3) / 1e9, 1)},
         }
+        del r8
+        torch.cuda.empty_cache()
+        log("census: 18 GroupNorm sites of a scale-7 UNet")
+        out["census"] = census()
     print(json.dumps(out), flush=True)
 
 

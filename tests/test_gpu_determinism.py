@@ -1,0 +1,69 @@
+"""Bitwise reproducibility on the GPU: every census site over 10 repeats, and two separate
+processes computing the same workloads ("Optimize GroupNorm" (LBANN/ScaFFold pull 93): the
+pages check determinism across separate processes by hashing outputs)."""
+import hashlib
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+import unet_groupnorm_amd as gn
+import workloads
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _run(case):
+    inp = workloads.make(case, "cuda")
+    y, mean, rstd = gn.gn_forward(inp["x"], inp["gamma"], inp["beta"], inp["G"], inp["eps"], inp["out_dtype"])
+    dx, dg, db = gn.gn_backward(inp["dy"], inp["x"], mean, rstd, inp["gamma"], inp["G"])
+    torch.cuda.synchronize()
+    return [y, mean, rstd, dx, dg, db]
+
+
+def digest(cases):
+    h = hashlib.sha256()
+    for c in cases:
+        for t in _run(c):
+            h.update(_bits(t).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+@pytest.mark.parametrize("case", workloads.census_cases(), ids=lambda c: c.name)
+def test_census_site_ten_repeats_bitwise(case):
+    print(f"[gpu-determinism] {case.name}: 10 repeats", flush=True)
+    inp = workloads.make(case, "cuda")
+    ws = gn.workspace_for(inp["x"], inp["G"])
+    first = None
+    for i in range(10):
+        ws.view(torch.uint8).fill_(0xFF)  # poison: NaN in every float the kernels could read stale
+        y, mean, rstd = gn.gn_forward(inp["x"], inp["gamma"], inp["beta"], inp["G"], inp["eps"], workspace=ws)
+        dx, dg, db = gn.gn_backward(inp["dy"], inp["x"], mean, rstd, inp["gamma"], inp["G"], workspace=ws)
+        torch.cuda.synchronize()
+        outs = [_bits(t).clone() for t in (y, mean, rstd, dx, dg, db)]
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert torch.equal(a, b), f"repeat {i} differs"
+
+
+CASES = [workloads.SCALE7, workloads.DEEP, workloads.TINY]
+
+
+def test_two_processes_agree_bitwise():
+    print("[gpu-determinism] two processes: scale-7, deep, tiny", flush=True)
+    code = ("import sys; sys.path.insert(0, %r); import tests.test_gpu_determinism as d; "
+            "print(d.digest(d.CASES))" % ROOT)
+    child = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert child.returncode == 0, child.stderr[-2000:]
+    theirs = child.stdout.strip().splitlines()[-1]
+    ours = digest(CASES)
+    assert ours == theirs

@@ -38,9 +38,31 @@
 
 #include "gn_launch.hpp"
 
+// Load cache policy per kernel (1: nontemporal) and the order of the streaming grid
+// (1: last row first); compile-time overridable for measurement builds.
+#ifndef GN_NT_STATS
+#define GN_NT_STATS 1
+#endif
+#ifndef GN_NT_BRED
+#define GN_NT_BRED 1
+#endif
+#ifndef GN_NT_APPLY
+#define GN_NT_APPLY 1
+#endif
+#ifndef GN_NT_BAPPLY
+#define GN_NT_BAPPLY 1
+#endif
+#ifndef GN_REVERSE_APPLY
+#define GN_REVERSE_APPLY 0
+#endif
+
 namespace gn {
 
 namespace {
+
+constexpr bool kNtStats = GN_NT_STATS, kNtBwdReduce = GN_NT_BRED;
+constexpr bool kNtApply = GN_NT_APPLY, kNtBwdApply = GN_NT_BAPPLY;
+constexpr bool kReverseApply = GN_REVERSE_APPLY;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -70,9 +92,11 @@ template <> struct Io<uint16_t> {  // bf16 storage
     struct Raw {
         u32x4 u;
     };
+    template <bool NT>
     static __device__ __forceinline__ Raw load_raw(const uint16_t* p)
     {
-        return Raw{__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p))};
+        const u32x4* q = reinterpret_cast<const u32x4*>(p);
+        return Raw{NT ? __builtin_nontemporal_load(q) : *q};
     }
     static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
     {
@@ -81,9 +105,10 @@ template <> struct Io<uint16_t> {  // bf16 storage
         v[4] = bf16_lo(r.u.z); v[5] = bf16_hi(r.u.z);
         v[6] = bf16_lo(r.u.w); v[7] = bf16_hi(r.u.w);
     }
+    template <bool NT>
     static __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8])
     {
-        widen(load_raw(p), v);
+        widen(load_raw<NT>(p), v);
     }
     static __device__ __forceinline__ float load1(const uint16_t* p)
     {
@@ -108,19 +133,21 @@ template <> struct Io<float> {
     struct Raw {
         f32x4 a, b;
     };
+    template <bool NT>
     static __device__ __forceinline__ Raw load_raw(const float* p)
     {
-        return Raw{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
-                   __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
+        const f32x4* q = reinterpret_cast<const f32x4*>(p);
+        return NT ? Raw{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1)} : Raw{q[0], q[1]};
     }
     static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
     {
         v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
         v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
     }
+    template <bool NT>
     static __device__ __forceinline__ void load8(const float* p, float (&v)[8])
     {
-        widen(load_raw(p), v);
+        widen(load_raw<NT>(p), v);
     }
     static __device__ __forceinline__ float load1(const float* p) { return *p; }
     static __device__ __forceinline__ void store8(float* p, const float (&v)[8])
@@ -305,7 +332,7 @@ __device__ __forceinline__ float group_shift(const T* __restrict__ x, const KArg
 
 // Loads the lane's kStepVecs vectors of one step with per-element validity. Vectors that
 // are wholly inside the job use one vector load; edge vectors are loaded element-wise.
-template <typename T>
+template <bool NT, typename T>
 __device__ __forceinline__ uint32_t load_step_masked(const T* __restrict__ p, const Job& jb,
                                                      int64_t sv0, int blk, int tid,
                                                      float (&v)[kTile])
@@ -316,7 +343,7 @@ __device__ __forceinline__ uint32_t load_step_masked(const T* __restrict__ p, co
         const int64_t vi = sv0 + int64_t(u) * blk + tid;
         float e[kVec];
         if (vi >= jb.vf0 && vi < jb.vf1) {
-            Io<T>::load8(p + vi * kVec, e);
+            Io<T>::template load8<NT>(p + vi * kVec, e);
             valid |= 0xffu << (u * kVec);
         } else {
 #pragma unroll
@@ -333,18 +360,6 @@ __device__ __forceinline__ uint32_t load_step_masked(const T* __restrict__ p, co
     return valid;
 }
 
-template <typename T>
-__device__ __forceinline__ void load_step_full(const T* __restrict__ p, int64_t sv0, int blk,
-                                               int tid, float (&v)[kTile])
-{
-#pragma unroll
-    for (int u = 0; u < kStepVecs; ++u) {
-        float e[kVec];
-        Io<T>::load8(p + (sv0 + int64_t(u) * blk + tid) * kVec, e);
-#pragma unroll
-        for (int i = 0; i < kVec; ++i) v[u * kVec + i] = e[i];
-    }
-}
 
 constexpr int kMaxWaves = 4;
 
@@ -387,12 +402,12 @@ __device__ __forceinline__ float2 block_sum2(float a, float b, float* s_a, float
 // ------------------------------------------------------------------ forward
 
 // The lane's kStepVecs raw vectors of one full step.
-template <typename T>
+template <bool NT, typename T>
 __device__ __forceinline__ void load_raw_step(const T* __restrict__ p, int64_t sv0, int blk, int tid,
                                               typename Io<T>::Raw (&r)[kStepVecs])
 {
 #pragma unroll
-    for (int u = 0; u < kStepVecs; ++u) r[u] = Io<T>::load_raw(p + (sv0 + int64_t(u) * blk + tid) * kVec);
+    for (int u = 0; u < kStepVecs; ++u) r[u] = Io<T>::template load_raw<NT>(p + (sv0 + int64_t(u) * blk + tid) * kVec);
 }
 
 // Steps [fs, fe) of a job are full; step 0 when fs = 1 and step fe when fe < nsteps hold
@@ -428,7 +443,7 @@ __device__ __forceinline__ void stats_masked_step(const TX* __restrict__ x, cons
                                                   int blk, int tid, float K, Moments<uint32_t>& acc)
 {
     float v[kTile];
-    const uint32_t valid = load_step_masked(x, jb, sv0, blk, tid, v);
+    const uint32_t valid = load_step_masked<kNtStats>(x, jb, sv0, blk, tid, v);
     if (valid) {
         const uint32_t cnt = __builtin_popcount(valid);
         float m, M2;
@@ -463,16 +478,16 @@ stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
         if (fs > 0) stats_masked_step(x, jb, jb.v0, blk, tid, K, acc);
         if (fe > fs) {
             Raw A[kStepVecs], B[kStepVecs];
-            load_raw_step(x, jb.v0 + fs * stepv, blk, tid, A);
+            load_raw_step<kNtStats>(x, jb.v0 + fs * stepv, blk, tid, A);
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                load_raw_step<kNtStats>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
                 stats_full_step<TX>(A, K, acc);
-                load_raw_step(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
+                load_raw_step<kNtStats>(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
                 stats_full_step<TX>(B, K, acc);
             }
             if (s + 1 < fe) {
-                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                load_raw_step<kNtStats>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
                 stats_full_step<TX>(A, K, acc);
                 stats_full_step<TX>(B, K, acc);
             } else {
@@ -502,6 +517,8 @@ fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
     const int64_t ng = blockIdx.x;
     const int64_t n = ng / a.G, g = ng - n * a.G;
     const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
+    // Requested before the merge so that its latency overlaps the partials' loads.
+    const float K = group_shift(x, a, n, g);
     Moments<uint64_t> acc = {0ull, 0.0f, 0.0f};
     for (int64_t j = threadIdx.x; j < a.P; j += blockDim.x) {
         const float2 pm = part[pbase + j];
@@ -515,7 +532,6 @@ fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
         // The mean as an unevaluated sum hi + lo: hi is the fp32 mean that is published,
         // lo what rounding it left out. The normalize takes x - mean as (x - hi) - lo,
         // which is exact in its first step whenever x is close to the mean.
-        const float K = group_shift(x, a, n, g);
         const float hi = K + r.m;
         const float lo = (K - hi) + r.m;
         mean_out[ng] = hi;
@@ -539,7 +555,8 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
 {
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kApplyVecs;
-    for (int64_t j = blockIdx.x; j < a.jobs_a; j += gridDim.x) {
+    for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
+        const int64_t j = kReverseApply ? a.jobs_a - 1 - jj : jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[jb.row];
         const float hi = cf.x, lo = cf.y, scale = cf.z, shift = cf.w;
@@ -549,7 +566,7 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
                 const int64_t vi = sv0 + int64_t(u) * blk + tid;
                 if (vi >= jb.vf0 && vi < jb.vf1) {
                     float e[kVec], o[kVec];
-                    Io<TX>::load8(x + vi * kVec, e);
+                    Io<TX>::template load8<kNtApply>(x + vi * kVec, e);
 #pragma unroll
                     for (int i = 0; i < kVec; ++i) o[i] = fmaf((e[i] - hi) - lo, scale, shift);
                     Io<TY>::store8(y + vi * kVec, o);
@@ -594,8 +611,8 @@ __device__ __forceinline__ void bwd_masked_step(const TD* __restrict__ dy, const
                                                 float& s1, float& s2)
 {
     float xv[kTile], gv[kTile];
-    const uint32_t valid = load_step_masked(x, jb, sv0, blk, tid, xv);
-    load_step_masked(dy, jb, sv0, blk, tid, gv);  // same mask: zeros outside
+    const uint32_t valid = load_step_masked<kNtBwdReduce>(x, jb, sv0, blk, tid, xv);
+    load_step_masked<kNtBwdReduce>(dy, jb, sv0, blk, tid, gv);  // same mask: zeros outside
 #pragma unroll
     for (int i = 0; i < kTile; ++i) xv[i] = ((valid >> i) & 1u) ? xv[i] - mu : 0.0f;
     s1 = s1 + tree_sum(gv);
@@ -628,20 +645,20 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
         if (fe > fs) {
             RawX AX[kStepVecs], BX[kStepVecs];
             RawD AD[kStepVecs], BD[kStepVecs];
-            load_raw_step(x, jb.v0 + fs * stepv, blk, tid, AX);
-            load_raw_step(dy, jb.v0 + fs * stepv, blk, tid, AD);
+            load_raw_step<kNtBwdReduce>(x, jb.v0 + fs * stepv, blk, tid, AX);
+            load_raw_step<kNtBwdReduce>(dy, jb.v0 + fs * stepv, blk, tid, AD);
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
-                load_raw_step(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
-                load_raw_step(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
+                load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
+                load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
                 bwd_full_step<TX, TD>(BX, BD, mu, s1, s2);
             }
             if (s + 1 < fe) {
-                load_raw_step(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
                 bwd_full_step<TX, TD>(BX, BD, mu, s1, s2);
             } else {
@@ -673,6 +690,7 @@ fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
     if (w < ngroups) {
         const int64_t n = w / a.G, g = w - n * a.G;
         const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
+        const float mu = mean[w], rs = rstd[w];  // requested before the merge
         float t1 = 0.0f, t2 = 0.0f;
         for (int64_t i = tid; i < a.P; i += blk) {
             const float2 pp = part[pbase + i];
@@ -686,7 +704,6 @@ fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
             s_coef[1] = float(double(r.y) / double(a.M));
         }
         __syncthreads();
-        const float mu = mean[w], rs = rstd[w];
         const float B = -(rs * s_coef[0]);
         const float E = -((rs * rs) * s_coef[1]);
         for (int64_t i = tid; i < a.Cg; i += blk) {
@@ -720,7 +737,8 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
     const int64_t stepv = int64_t(blk) * kApplyVecs;
     // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
     const bool single = (a.M == 1);
-    for (int64_t j = blockIdx.x; j < a.jobs_a; j += gridDim.x) {
+    for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
+        const int64_t j = kReverseApply ? a.jobs_a - 1 - jj : jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[jb.row];
         const float mu = cf.x, A = cf.y, B = cf.z, E = cf.w;
@@ -730,8 +748,8 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
                 const int64_t vi = sv0 + int64_t(u) * blk + tid;
                 if (vi >= jb.vf0 && vi < jb.vf1) {
                     float xv[kVec], gv[kVec], o[kVec];
-                    Io<TX>::load8(x + vi * kVec, xv);
-                    Io<TD>::load8(dy + vi * kVec, gv);
+                    Io<TX>::template load8<kNtBwdApply>(x + vi * kVec, xv);
+                    Io<TD>::template load8<kNtBwdApply>(dy + vi * kVec, gv);
 #pragma unroll
                     for (int i = 0; i < kVec; ++i) {
                         float t = fmaf(A, gv[i], fmaf(E, xv[i] - mu, B));
