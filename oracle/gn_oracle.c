@@ -17,6 +17,10 @@
  *     normalized value is the full-precision answer, rounded once to the output
  *     dtype. Here "full precision" is fp64 and the rounding helpers below round
  *     straight from fp64 (never through fp32).
+ *   - Optional ReLU after the affine ("Optimize GroupNorm", paragraphs on the rung ladder
+ *     with the fused ReLU and on the NaN-correct ReLU): relu(v) = 0 where v < 0, else v, so
+ *     NaN, +Inf and -0.0 pass unchanged and -Inf becomes 0, as torch's F.relu does; its
+ *     gradient passes where the relu result is > 0 or NaN and is 0 where it is <= 0.
  *   - The backward is the calculus of the forward (the pages print no formula):
  *       xhat = (x - mu) * rstd
  *       s1[n,c] = sum_s dy,   s2[n,c] = sum_s dy * xhat
@@ -24,6 +28,8 @@
  *       c2[n,g] = (1/M) sum_{c in g} gamma_c s2[n,c]
  *       dx = rstd * (gamma_c * dy - c1 - xhat * c2)
  *       dgamma_c = sum_n s2[n,c],  dbeta_c = sum_n s1[n,c]
+ *     With the ReLU, dy above is replaced by the gated gradient g = gate(relu(pre)) * dy,
+ *     pre = gamma_c * xhat + beta_c.
  *
  * Layout: NCDHW contiguous; S = D*H*W; group (n, g) is the contiguous run of
  * M = (C/G)*S elements that starts at (n*C + g*C/G)*S.
@@ -58,6 +64,12 @@ static double gno_load(const void* p, int dt, int64_t i)
 
 static double gno_gamma(const float* gamma, int64_t c) { return gamma ? (double)gamma[c] : 1.0; }
 static double gno_beta(const float* beta, int64_t c) { return beta ? (double)beta[c] : 0.0; }
+
+/* relu as torch's F.relu: 0 where v < 0, else v (NaN, +Inf, -0.0 unchanged). */
+static double gno_relu(double v) { return v < 0.0 ? 0.0 : v; }
+
+/* Gradient gate of the relu: blocks where the relu result r is <= 0, passes otherwise (NaN too). */
+static double gno_gate(double r, double g) { return r <= 0.0 ? 0.0 : g; }
 
 /* Shape check shared by every entry point of this file: C divisible by G, all positive. */
 static int gno_shape_ok(int64_t N, int64_t C, int64_t S, int64_t G)
@@ -97,11 +109,12 @@ int gno_group_stats(const void* x, int x_dt, int64_t N, int64_t C, int64_t S, in
 }
 
 /*
- * Forward: y[i] = gamma_c * (x[i] - mu) * rstd + beta_c for every element, in fp64.
+ * Forward: y[i] = gamma_c * (x[i] - mu) * rstd + beta_c for every element, in fp64, then
+ * relu(y) if act is non-zero.
  * y is [N*C*S] fp64; mean, var, rstd are [N*G] and may be NULL.
  */
 int gno_forward(const void* x, int x_dt, const float* gamma, const float* beta,
-                int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+                int64_t N, int64_t C, int64_t S, int64_t G, float eps, int act,
                 double* y, double* mean, double* var, double* rstd)
 {
     if (!gno_shape_ok(N, C, S, G)) return 1;
@@ -118,7 +131,8 @@ int gno_forward(const void* x, int x_dt, const float* gamma, const float* beta,
             const int64_t base = (n * C + c) * S;
             for (int64_t s = 0; s < S; ++s) {
                 const double xhat = (gno_load(x, x_dt, base + s) - mu[ng]) * rs[ng];
-                y[base + s] = gm * xhat + bt;
+                const double pre = gm * xhat + bt;
+                y[base + s] = act ? gno_relu(pre) : pre;
             }
         }
     }
@@ -136,7 +150,7 @@ int gno_forward(const void* x, int x_dt, const float* gamma, const float* beta,
  * gno_group_stats (for volumes whose fp64 output would not fit in memory).
  */
 int gno_forward_at(const void* x, int x_dt, const float* gamma, const float* beta,
-                   int64_t N, int64_t C, int64_t S, int64_t G,
+                   int64_t N, int64_t C, int64_t S, int64_t G, int act,
                    const double* mean, const double* rstd,
                    const int64_t* idx, int64_t n_idx, double* y_out)
 {
@@ -146,7 +160,8 @@ int gno_forward_at(const void* x, int x_dt, const float* gamma, const float* bet
         const int64_t i = idx[k];
         const int64_t nc = i / S, n = nc / C, c = nc % C, ng = n * G + c / Cg;
         const double xhat = (gno_load(x, x_dt, i) - mean[ng]) * rstd[ng];
-        y_out[k] = gno_gamma(gamma, c) * xhat + gno_beta(beta, c);
+        const double pre = gno_gamma(gamma, c) * xhat + gno_beta(beta, c);
+        y_out[k] = act ? gno_relu(pre) : pre;
     }
     return 0;
 }
@@ -158,6 +173,7 @@ int gno_forward_at(const void* x, int x_dt, const float* gamma, const float* bet
  * are [N*G] and may be NULL.
  */
 int gno_backward(const void* dy, int dy_dt, const void* x, int x_dt, const float* gamma,
+                 const float* beta, int act,
                  int64_t N, int64_t C, int64_t S, int64_t G, float eps,
                  double* dx, double* dgamma, double* dbeta,
                  double* mean_out, double* rstd_out, double* c1_out, double* c2_out)
@@ -181,10 +197,12 @@ int gno_backward(const void* dy, int dy_dt, const void* x, int x_dt, const float
         for (int64_t c = 0; c < C; ++c) {
             const int64_t ng = n * G + c / Cg;
             const int64_t base = (n * C + c) * S;
+            const double gm = gno_gamma(gamma, c), bt = gno_beta(beta, c);
             double a = 0.0, b = 0.0;
             for (int64_t s = 0; s < S; ++s) {
-                const double g_ = gno_load(dy, dy_dt, base + s);
                 const double xhat = (gno_load(x, x_dt, base + s) - mu[ng]) * rs[ng];
+                double g_ = gno_load(dy, dy_dt, base + s);
+                if (act) g_ = gno_gate(gno_relu(gm * xhat + bt), g_);
                 a += g_;
                 b += g_ * xhat;
             }
@@ -210,10 +228,11 @@ int gno_backward(const void* dy, int dy_dt, const void* x, int x_dt, const float
             for (int64_t c = 0; c < C; ++c) {
                 const int64_t ng = n * G + c / Cg;
                 const int64_t base = (n * C + c) * S;
-                const double gm = gno_gamma(gamma, c);
+                const double gm = gno_gamma(gamma, c), bt = gno_beta(beta, c);
                 for (int64_t s = 0; s < S; ++s) {
                     const double xhat = (gno_load(x, x_dt, base + s) - mu[ng]) * rs[ng];
-                    const double g_ = gno_load(dy, dy_dt, base + s);
+                    double g_ = gno_load(dy, dy_dt, base + s);
+                    if (act) g_ = gno_gate(gno_relu(gm * xhat + bt), g_);
                     dx[base + s] = rs[ng] * (gm * g_ - c1[ng] - xhat * c2[ng]);
                 }
             }
@@ -244,7 +263,7 @@ int gno_backward(const void* dy, int dy_dt, const void* x, int x_dt, const float
  * coefficients gno_backward returned.
  */
 int gno_backward_at(const void* dy, int dy_dt, const void* x, int x_dt, const float* gamma,
-                    int64_t N, int64_t C, int64_t S, int64_t G,
+                    const float* beta, int act, int64_t N, int64_t C, int64_t S, int64_t G,
                     const double* mean, const double* rstd, const double* c1, const double* c2,
                     const int64_t* idx, int64_t n_idx, double* dx_out)
 {
@@ -254,8 +273,10 @@ int gno_backward_at(const void* dy, int dy_dt, const void* x, int x_dt, const fl
         const int64_t i = idx[k];
         const int64_t nc = i / S, n = nc / C, c = nc % C, ng = n * G + c / Cg;
         const double xhat = (gno_load(x, x_dt, i) - mean[ng]) * rstd[ng];
-        const double g_ = gno_load(dy, dy_dt, i);
-        dx_out[k] = rstd[ng] * (gno_gamma(gamma, c) * g_ - c1[ng] - xhat * c2[ng]);
+        const double gm = gno_gamma(gamma, c);
+        double g_ = gno_load(dy, dy_dt, i);
+        if (act) g_ = gno_gate(gno_relu(gm * xhat + gno_beta(beta, c)), g_);
+        dx_out[k] = rstd[ng] * (gm * g_ - c1[ng] - xhat * c2[ng]);
     }
     return 0;
 }
@@ -307,10 +328,12 @@ void gno_round_f32_array(const double* v, int64_t n, float* out)
 }
 
 /*
- * Per-channel sums of |dy| and |dy * xhat| (xhat from the given statistics): the
- * magnitudes that bound the rounding error of any fp32 summation of dbeta and dgamma.
+ * Per-channel sums of |g| and |g * xhat| (xhat from the given statistics, g = dy or the
+ * relu-gated dy): the magnitudes that bound the rounding error of any fp32 summation of
+ * dbeta and dgamma.
  */
 int gno_channel_abs_sums(const void* dy, int dy_dt, const void* x, int x_dt,
+                         const float* gamma, const float* beta, int act,
                          int64_t N, int64_t C, int64_t S, int64_t G,
                          const double* mean, const double* rstd, double* abs_dy, double* abs_dyxhat)
 {
@@ -323,8 +346,9 @@ int gno_channel_abs_sums(const void* dy, int dy_dt, const void* x, int x_dt,
             const int64_t base = (n * C + c) * S;
             double a = 0.0, b = 0.0;
             for (int64_t s = 0; s < S; ++s) {
-                const double g_ = gno_load(dy, dy_dt, base + s);
                 const double xhat = (gno_load(x, x_dt, base + s) - mean[ng]) * rstd[ng];
+                double g_ = gno_load(dy, dy_dt, base + s);
+                if (act) g_ = gno_gate(gno_relu(gno_gamma(gamma, c) * xhat + gno_beta(beta, c)), g_);
                 a += fabs(g_);
                 b += fabs(g_ * xhat);
             }
@@ -334,3 +358,7 @@ int gno_channel_abs_sums(const void* dy, int dy_dt, const void* x, int x_dt,
     }
     return 0;
 }
+
+/* The relu and its gradient gate on single values (exposed for their own pins). */
+double gno_relu_value(double v) { return gno_relu(v); }
+double gno_gate_value(double r, double g) { return gno_gate(r, g); }

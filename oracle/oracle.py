@@ -35,14 +35,19 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float
     lib.gno_group_stats.argtypes = [P, ctypes.c_int, I64, I64, I64, I64, F, P, P, P]
-    lib.gno_forward.argtypes = [P, ctypes.c_int, P, P, I64, I64, I64, I64, F, P, P, P, P]
-    lib.gno_forward_at.argtypes = [P, ctypes.c_int, P, P, I64, I64, I64, I64, P, P, P, I64, P]
-    lib.gno_backward.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, I64, I64, I64, I64, F,
+    CI = ctypes.c_int
+    lib.gno_forward.argtypes = [P, CI, P, P, I64, I64, I64, I64, F, CI, P, P, P, P]
+    lib.gno_forward_at.argtypes = [P, CI, P, P, I64, I64, I64, I64, CI, P, P, P, I64, P]
+    lib.gno_backward.argtypes = [P, CI, P, CI, P, P, CI, I64, I64, I64, I64, F,
                                  P, P, P, P, P, P, P]
-    lib.gno_backward_at.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, I64, I64, I64, I64,
+    lib.gno_backward_at.argtypes = [P, CI, P, CI, P, P, CI, I64, I64, I64, I64,
                                     P, P, P, P, P, I64, P]
-    lib.gno_channel_abs_sums.argtypes = [P, ctypes.c_int, P, ctypes.c_int, I64, I64, I64, I64, P, P, P, P]
+    lib.gno_channel_abs_sums.argtypes = [P, CI, P, CI, P, P, CI, I64, I64, I64, I64, P, P, P, P]
     lib.gno_channel_abs_sums.restype = ctypes.c_int
+    lib.gno_relu_value.argtypes = [ctypes.c_double]
+    lib.gno_relu_value.restype = ctypes.c_double
+    lib.gno_gate_value.argtypes = [ctypes.c_double, ctypes.c_double]
+    lib.gno_gate_value.restype = ctypes.c_double
     lib.gno_round_bf16.argtypes = [ctypes.c_double]
     lib.gno_round_bf16.restype = ctypes.c_uint16
     lib.gno_round_bf16_array.argtypes = [P, I64, P]
@@ -113,21 +118,21 @@ def group_stats(x, G, eps=1e-5, tag=None):
     return mean, var, rstd
 
 
-def forward(x, G, gamma=None, beta=None, eps=1e-5, tag=None):
-    """Returns dict(y [x.shape] fp64, mean/var/rstd [N, G] fp64)."""
+def forward(x, G, gamma=None, beta=None, eps=1e-5, tag=None, relu=False):
+    """Returns dict(y [x.shape] fp64, mean/var/rstd [N, G] fp64); y = relu(GN(x)) if relu."""
     xa, code = _typed(x, tag)
     N, C, S = _shape(xa)
     y = np.empty(xa.shape, dtype=np.float64)
     mean = np.empty((N, G)); var = np.empty((N, G)); rstd = np.empty((N, G))
     g = _f32vec(gamma, C); b = _f32vec(beta, C)
-    rc = _load().gno_forward(_ptr(xa), code, _ptr(g), _ptr(b), N, C, S, G, eps,
+    rc = _load().gno_forward(_ptr(xa), code, _ptr(g), _ptr(b), N, C, S, G, eps, int(relu),
                              _ptr(y), _ptr(mean), _ptr(var), _ptr(rstd))
     if rc:
         raise ValueError(f"oracle: bad shape {xa.shape} G={G}")
     return {"y": y, "mean": mean, "var": var, "rstd": rstd}
 
 
-def forward_at(x, G, idx, mean, rstd, gamma=None, beta=None, tag=None):
+def forward_at(x, G, idx, mean, rstd, gamma=None, beta=None, tag=None, relu=False):
     """y (fp64) at flat indices ``idx`` given the oracle's own statistics."""
     xa, code = _typed(x, tag)
     N, C, S = _shape(xa)
@@ -136,13 +141,15 @@ def forward_at(x, G, idx, mean, rstd, gamma=None, beta=None, tag=None):
     mean = np.ascontiguousarray(mean, dtype=np.float64)
     rstd = np.ascontiguousarray(rstd, dtype=np.float64)
     g = _f32vec(gamma, C); b = _f32vec(beta, C)
-    _load().gno_forward_at(_ptr(xa), code, _ptr(g), _ptr(b), N, C, S, G,
+    _load().gno_forward_at(_ptr(xa), code, _ptr(g), _ptr(b), N, C, S, G, int(relu),
                            _ptr(mean), _ptr(rstd), _ptr(idx), idx.size, _ptr(out))
     return out
 
 
-def backward(dy, x, G, gamma=None, eps=1e-5, want_dx=True, dy_tag=None, x_tag=None):
-    """Returns dict(dx [x.shape] fp64 or None, dgamma/dbeta [C], mean/rstd/c1/c2 [N, G])."""
+def backward(dy, x, G, gamma=None, eps=1e-5, want_dx=True, dy_tag=None, x_tag=None, beta=None,
+             relu=False):
+    """Returns dict(dx [x.shape] fp64 or None, dgamma/dbeta [C], mean/rstd/c1/c2 [N, G]).
+    With relu, dy is the gradient of relu(GN(x)) (beta is then needed for the gate)."""
     xa, xc = _typed(x, x_tag)
     ga, gc = _typed(dy, dy_tag)
     assert ga.shape == xa.shape
@@ -150,8 +157,8 @@ def backward(dy, x, G, gamma=None, eps=1e-5, want_dx=True, dy_tag=None, x_tag=No
     dx = np.empty(xa.shape, dtype=np.float64) if want_dx else None
     dgamma = np.empty(C); dbeta = np.empty(C)
     mean = np.empty((N, G)); rstd = np.empty((N, G)); c1 = np.empty((N, G)); c2 = np.empty((N, G))
-    g = _f32vec(gamma, C)
-    rc = _load().gno_backward(_ptr(ga), gc, _ptr(xa), xc, _ptr(g), N, C, S, G, eps,
+    g = _f32vec(gamma, C); b = _f32vec(beta, C)
+    rc = _load().gno_backward(_ptr(ga), gc, _ptr(xa), xc, _ptr(g), _ptr(b), int(relu), N, C, S, G, eps,
                               _ptr(dx), _ptr(dgamma), _ptr(dbeta),
                               _ptr(mean), _ptr(rstd), _ptr(c1), _ptr(c2))
     if rc:
@@ -160,7 +167,8 @@ def backward(dy, x, G, gamma=None, eps=1e-5, want_dx=True, dy_tag=None, x_tag=No
             "mean": mean, "rstd": rstd, "c1": c1, "c2": c2}
 
 
-def backward_at(dy, x, G, idx, mean, rstd, c1, c2, gamma=None, dy_tag=None, x_tag=None):
+def backward_at(dy, x, G, idx, mean, rstd, c1, c2, gamma=None, dy_tag=None, x_tag=None, beta=None,
+                relu=False):
     """dx (fp64) at flat indices ``idx`` given the oracle's own statistics and coefficients."""
     xa, xc = _typed(x, x_tag)
     ga, gc = _typed(dy, dy_tag)
@@ -168,22 +176,24 @@ def backward_at(dy, x, G, idx, mean, rstd, c1, c2, gamma=None, dy_tag=None, x_ta
     idx = np.ascontiguousarray(idx, dtype=np.int64)
     out = np.empty(idx.shape, dtype=np.float64)
     arrs = [np.ascontiguousarray(a, dtype=np.float64) for a in (mean, rstd, c1, c2)]
-    g = _f32vec(gamma, C)
-    _load().gno_backward_at(_ptr(ga), gc, _ptr(xa), xc, _ptr(g), N, C, S, G,
+    g = _f32vec(gamma, C); b = _f32vec(beta, C)
+    _load().gno_backward_at(_ptr(ga), gc, _ptr(xa), xc, _ptr(g), _ptr(b), int(relu), N, C, S, G,
                             *[_ptr(a) for a in arrs], _ptr(idx), idx.size, _ptr(out))
     return out
 
 
-def channel_abs_sums(dy, x, G, mean, rstd, dy_tag=None, x_tag=None):
-    """(sum |dy|, sum |dy * xhat|) per channel [C], xhat from the given fp64 statistics."""
+def channel_abs_sums(dy, x, G, mean, rstd, dy_tag=None, x_tag=None, gamma=None, beta=None, relu=False):
+    """(sum |g|, sum |g * xhat|) per channel [C], xhat from the given fp64 statistics, g = dy
+    or the relu-gated dy."""
     xa, xc = _typed(x, x_tag)
     ga, gc = _typed(dy, dy_tag)
     N, C, S = _shape(xa)
     a = np.empty(C); b = np.empty(C)
     mean = np.ascontiguousarray(mean, dtype=np.float64)
     rstd = np.ascontiguousarray(rstd, dtype=np.float64)
-    _load().gno_channel_abs_sums(_ptr(ga), gc, _ptr(xa), xc, N, C, S, G, _ptr(mean), _ptr(rstd),
-                                 _ptr(a), _ptr(b))
+    gm = _f32vec(gamma, C); bt = _f32vec(beta, C)
+    _load().gno_channel_abs_sums(_ptr(ga), gc, _ptr(xa), xc, _ptr(gm), _ptr(bt), int(relu), N, C, S, G,
+                                 _ptr(mean), _ptr(rstd), _ptr(a), _ptr(b))
     return a, b
 
 

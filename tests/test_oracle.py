@@ -323,3 +323,60 @@ def test_naive_variance_formula_fails_where_the_oracle_does_not():
     naive = np.float32(np.mean(x32.astype(np.float32) ** 2, dtype=np.float32)) - \
         np.float32(np.mean(x32.astype(np.float32), dtype=np.float32)) ** 2
     assert abs(float(naive) - true_var) > 0.5 * true_var
+
+
+# ----------------------------------------------------------------------------- fused relu option
+
+def _torch_relu_ref(x64, G, gamma, beta, eps, dy64):
+    x64 = x64.clone().requires_grad_(True)
+    g = torch.from_numpy(np.asarray(gamma, dtype=np.float32)).to(torch.float64).requires_grad_(True)
+    b = torch.from_numpy(np.asarray(beta, dtype=np.float32)).to(torch.float64).requires_grad_(True)
+    y = torch.relu(F.group_norm(x64, G, g, b, float(np.float32(eps))))
+    y.backward(dy64)
+    return y.detach().numpy(), x64.grad.numpy(), g.grad.numpy(), b.grad.numpy()
+
+
+def test_relu_option_against_torch_autograd():
+    """relu(GroupNorm(x)) and its gradients ("Optimize GroupNorm", fused-ReLU paragraphs)."""
+    inp = workloads.make(workloads.custom(2, 8, 4, (6, 5, 7), torch.float32, dist="tiny", seed=41), "cpu")
+    x, dy, G, eps = inp["x"], inp["dy"], inp["G"], inp["eps"]
+    gamma, beta = inp["gamma"].numpy(), inp["beta"].numpy()
+    f = O.forward(x, G, gamma, beta, eps=eps, relu=True)
+    b = O.backward(dy, x, G, gamma, eps=eps, beta=beta, relu=True)
+    y_t, dx_t, dg_t, db_t = _torch_relu_ref(_f64(x), G, gamma, beta, eps, _f64(dy))
+    assert np.abs(f["y"] - y_t).max() <= 1e-12 * np.abs(y_t).max()
+    assert (f["y"] >= 0).all() and (f["y"] == 0).mean() > 0.3   # the relu did something
+    assert np.abs(b["dx"] - dx_t).max() <= 1e-10 * np.abs(dx_t).max()
+    assert np.abs(b["dgamma"] - dg_t).max() <= 1e-10 * np.abs(dg_t).max()
+    assert np.abs(b["dbeta"] - db_t).max() <= 1e-10 * np.abs(db_t).max()
+    idx = np.arange(0, x.numel(), 7, dtype=np.int64)
+    assert np.array_equal(O.forward_at(x, G, idx, f["mean"], f["rstd"], gamma, beta, relu=True),
+                          f["y"].reshape(-1)[idx])
+    assert np.array_equal(O.backward_at(dy, x, G, idx, b["mean"], b["rstd"], b["c1"], b["c2"], gamma,
+                                        beta=beta, relu=True), b["dx"].reshape(-1)[idx])
+
+
+def test_relu_keeps_negative_zero_and_nan_group_gradient():
+    """The relu and its gate on special values against torch's F.relu and its autograd; then a
+    NaN group, whose gradient passes the gate ("Optimize GroupNorm", NaN-correct ReLU paragraph)."""
+    lib = O._load()
+    vals = [-0.0, 0.0, float("nan"), float("inf"), float("-inf"), -1.5, 2.5, 1e-300, -1e-300]
+    t = torch.tensor(vals, dtype=torch.float64, requires_grad=True)
+    r = torch.relu(t)
+    r.backward(torch.full_like(t, 3.0))
+    for i, v in enumerate(vals):
+        ours = lib.gno_relu_value(v)
+        ref = float(r[i])
+        assert (math.isnan(ours) and math.isnan(ref)) or (ours == ref and math.copysign(1, ours) == math.copysign(1, ref))
+        assert lib.gno_gate_value(ours, 3.0) == float(t.grad[i])
+    rng = np.random.default_rng(2)
+    x = rng.normal(size=(2, 4, 12)).astype(np.float32)
+    x[1, 2, 5] = np.nan
+    dy = rng.normal(size=x.shape).astype(np.float32)
+    gamma, beta = np.ones(4, np.float32), np.full(4, 0.1, np.float32)
+    b = O.backward(dy, x, 2, gamma, eps=1e-5, beta=beta, relu=True)
+    _, dx_t, dg_t, db_t = _torch_relu_ref(torch.from_numpy(x).to(torch.float64), 2, gamma, beta, 1e-5,
+                                          torch.from_numpy(dy).to(torch.float64))
+    assert np.isfinite(db_t).all() and np.allclose(b["dbeta"], db_t, rtol=1e-12)
+    assert np.array_equal(np.isnan(b["dx"]), np.isnan(dx_t))
+    assert np.array_equal(np.isnan(b["dgamma"]), np.isnan(dg_t))

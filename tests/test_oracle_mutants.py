@@ -21,7 +21,14 @@ MUTANTS = {
     "mean_divisor": ("const double mu = sum / (double)M;", "const double mu = sum / (double)(M + 1);"),
     "unbiased_var": ("const double v = ss / (double)M;", "const double v = ss / (double)(M - 1);"),
     "eps_outside_sqrt": ("1.0 / sqrt(v + (double)eps)", "1.0 / (sqrt(v) + (double)eps)"),
-    "beta_sign": ("y[base + s] = gm * xhat + bt;", "y[base + s] = gm * xhat - bt;"),
+    "beta_sign": ("const double pre = gm * xhat + bt;\n                y[base + s]",
+                  "const double pre = gm * xhat - bt;\n                y[base + s]"),
+    "relu_eats_nan_and_negzero": ("static double gno_relu(double v) { return v < 0.0 ? 0.0 : v; }",
+                                  "static double gno_relu(double v) { return v > 0.0 ? v : 0.0; }"),
+    "gate_blocks_nan": ("static double gno_gate(double r, double g) { return r <= 0.0 ? 0.0 : g; }",
+                        "static double gno_gate(double r, double g) { return r > 0.0 ? g : 0.0; }"),
+    "gate_on_wrong_side": ("static double gno_gate(double r, double g) { return r <= 0.0 ? 0.0 : g; }",
+                           "static double gno_gate(double r, double g) { return r <= 0.0 ? g : 0.0; }"),
     "forward_group_index": ("const int64_t ng = n * G + c / Cg;\n            const double gm",
                             "const int64_t ng = n * G + c % G;\n            const double gm"),
     "dx_c2_sign": ("dx[base + s] = rs[ng] * (gm * g_ - c1[ng] - xhat * c2[ng]);",
@@ -50,6 +57,8 @@ PINS = [
     pins.test_backward_closed_forms,
     pins.test_round_bf16_matches_torch_on_fp32_values,
     pins.test_round_bf16_ties_double_rounding_and_specials,
+    pins.test_relu_option_against_torch_autograd,
+    pins.test_relu_keeps_negative_zero_and_nan_group_gradient,
 ]
 
 
@@ -71,7 +80,8 @@ def test_pins_kill_mutant(name, tmp_path, monkeypatch):
     real = O._load()
     mutant = ctypes.CDLL(lib_path)
     for fn in ("gno_group_stats", "gno_forward", "gno_forward_at", "gno_backward", "gno_backward_at",
-               "gno_round_bf16", "gno_round_bf16_array", "gno_round_f32_array"):
+               "gno_round_bf16", "gno_round_bf16_array", "gno_round_f32_array", "gno_channel_abs_sums",
+               "gno_relu_value", "gno_gate_value"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(O, "_lib", mutant)

@@ -55,6 +55,9 @@
 #ifndef GN_REVERSE_APPLY
 #define GN_REVERSE_APPLY 0
 #endif
+#ifndef GN_NT_STORE
+#define GN_NT_STORE 0
+#endif
 
 namespace gn {
 
@@ -63,6 +66,7 @@ namespace {
 constexpr bool kNtStats = GN_NT_STATS, kNtBwdReduce = GN_NT_BRED;
 constexpr bool kNtApply = GN_NT_APPLY, kNtBwdApply = GN_NT_BAPPLY;
 constexpr bool kReverseApply = GN_REVERSE_APPLY;
+constexpr bool kNtStore = GN_NT_STORE;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -121,7 +125,10 @@ template <> struct Io<uint16_t> {  // bf16 storage
         u.y = pack_bf16(v[2], v[3]);
         u.z = pack_bf16(v[4], v[5]);
         u.w = pack_bf16(v[6], v[7]);
-        *reinterpret_cast<u32x4*>(p) = u;
+        if (kNtStore)
+            __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
+        else
+            *reinterpret_cast<u32x4*>(p) = u;
     }
     static __device__ __forceinline__ void store1(uint16_t* p, float v)
     {
@@ -152,8 +159,14 @@ template <> struct Io<float> {
     static __device__ __forceinline__ float load1(const float* p) { return *p; }
     static __device__ __forceinline__ void store8(float* p, const float (&v)[8])
     {
-        *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+        if (kNtStore) {
+            __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+            __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
+        } else {
+            *reinterpret_cast<f32x4*>(p) = a;
+            *reinterpret_cast<f32x4*>(p + 4) = b;
+        }
     }
     static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 };
