@@ -66,12 +66,12 @@ def bytes_per_elem(x_dtype, y_dtype, dy_dtype):
 class Runner:
     """Holds one workload resident on the GPU with preallocated outputs."""
 
-    def __init__(self, case):
+    def __init__(self, case, activation=None):
         import torch
 
         import unet_groupnorm_amd as gn
         import workloads
-        self.torch, self.gn, self.case = torch, gn, case
+        self.torch, self.gn, self.case, self.act = torch, gn, case, activation
         inp = workloads.make(case, "cuda")
         self.inp = inp
         self.x, self.dy, self.G, self.eps = inp["x"], inp["dy"], inp["G"], inp["eps"]
@@ -89,10 +89,11 @@ class Runner:
 
     def step(self):
         gn = self.gn
-        gn.gn_forward(self.x, self.gamma, self.beta, self.G, self.eps, workspace=self.ws, out=self.y,
-                      mean=self.mean, rstd=self.rstd)
-        gn.gn_backward(self.dy, self.x, self.mean, self.rstd, self.gamma, self.G, workspace=self.ws,
-                       dx=self.dx, dgamma=self.dgamma, dbeta=self.dbeta)
+        gn.gn_forward(self.x, self.gamma, self.beta, self.G, self.eps, activation=self.act,
+                      workspace=self.ws, out=self.y, mean=self.mean, rstd=self.rstd)
+        gn.gn_backward(self.dy, self.x, self.mean, self.rstd, self.gamma, self.G, beta=self.beta,
+                       activation=self.act, workspace=self.ws, dx=self.dx, dgamma=self.dgamma,
+                       dbeta=self.dbeta)
 
     def phases(self):
         """The same step through the split-phase entry points. The stats and bwd_reduce
@@ -102,11 +103,13 @@ class Runner:
         return [
             ("stats", lambda: gn.gn_forward_stats(self.x, self.gamma, self.beta, self.G, self.eps,
                                                   self.mean, self.rstd, self.ws)),
-            ("apply", lambda: gn.gn_forward_apply(self.x, self.G, self.y, self.ws)),
+            ("apply", lambda: gn.gn_forward_apply(self.x, self.G, self.y, self.ws, self.act)),
             ("bwd_reduce", lambda: gn.gn_backward_reduce(self.dy, self.x, self.mean, self.rstd,
                                                          self.gamma, self.G, self.dgamma,
-                                                         self.dbeta, self.ws)),
-            ("bwd_apply", lambda: gn.gn_backward_apply(self.dy, self.x, self.G, self.dx, self.ws)),
+                                                         self.dbeta, self.ws, beta=self.beta,
+                                                         activation=self.act)),
+            ("bwd_apply", lambda: gn.gn_backward_apply(self.dy, self.x, self.G, self.dx, self.ws,
+                                                       self.act)),
         ]
 
     def timed_steps(self, steps, warmup):
@@ -338,6 +341,12 @@ def main():
                               "value": round(run.step_bytes / (fms * 1e-3) / 1e9, 1)}
         log("copy kernel ceiling")
         out["copy_kernel_gbps"] = round(copy_ceiling_gbps(), 1)
+        log("the same step with the relu fused into the normalize store and the backward gate")
+        run.act = "relu"
+        rms, _ = run.timed_steps(max(10, args.steps // 2), 3)
+        out["relu_fused"] = {"ms_per_step": round(rms, 5),
+                             "value": round(run.step_bytes / (rms * 1e-3) / 1e9, 1)}
+        run.act = None
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on this host")
         out["cpu_baseline"] = cpu_baseline(run)

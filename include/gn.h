@@ -74,8 +74,21 @@ typedef enum gn_status {
     GN_ERR_WORKSPACE = 6, /* workspace smaller than gn_workspace_bytes(N, C, S, G) */
     GN_ERR_ALIGN = 7,     /* a pointer is not aligned as stated above */
     GN_ERR_DEVICE = 8,    /* x is not device memory, or the stream belongs to another device */
-    GN_ERR_LAUNCH = 9     /* the HIP runtime refused a launch; outputs are undefined */
+    GN_ERR_LAUNCH = 9,    /* the HIP runtime refused a launch; outputs are undefined */
+    GN_ERR_ACTIVATION = 10 /* unknown activation code */
 } gn_status;
+
+/*
+ * Activation applied after the affine, inside the normalize store ("Optimize GroupNorm",
+ * paragraphs on the rung ladder with the fused ReLU and on the NaN-correct ReLU):
+ * relu(v) = 0 where v < 0, else v (NaN, +Inf and -0.0 pass unchanged, -Inf becomes 0), as
+ * torch's F.relu; in the backward the gradient is blocked where relu(pre) <= 0 and passes
+ * otherwise (NaN too), pre being the affine output recomputed in fp32 from x.
+ */
+typedef enum gn_activation {
+    GN_ACT_NONE = 0,
+    GN_ACT_RELU = 1
+} gn_activation;
 
 /*
  * Workspace size in bytes for a volume of N samples, C channels, S = D*H*W voxels and
@@ -87,13 +100,14 @@ size_t gn_workspace_bytes(int64_t N, int64_t C, int64_t S, int64_t G);
 
 /*
  * Forward. Statistics per (n, g) in fp32 (written to mean and rstd), then
- * y = gamma_c * (x - mean) * rstd + beta_c computed in fp32 and stored once in
+ * y = act(gamma_c * (x - mean) * rstd + beta_c) computed in fp32 and stored once in
  * y_dtype. x_dtype is GN_F32 or GN_BF16; y_dtype is x_dtype or GN_F32 (the fp32-output
  * mode). gamma == NULL means all ones, beta == NULL all zeros. eps must be finite and
- * >= 0. Enqueues gn_forward_stats then gn_forward_apply (three kernels).
+ * >= 0. activation is a gn_activation. Enqueues gn_forward_stats then gn_forward_apply
+ * (three kernels).
  */
 int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta,
-               int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+               int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
                void* y, int y_dtype, float* mean, float* rstd,
                void* workspace, size_t workspace_bytes, void* stream);
 
@@ -112,7 +126,8 @@ int gn_forward_stats(const void* x, int x_dtype, const float* gamma, const float
  * left in the workspace (same x, same shape, stream-ordered after it). One kernel.
  */
 int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
-                     void* y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream);
+                     int activation, void* y, int y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward. Recomputes xhat = (x - mean) * rstd from the mean/rstd gn_forward wrote,
@@ -123,11 +138,14 @@ int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S
  * dy_dtype is GN_F32 or GN_BF16 independently of x_dtype; the same dy values in either
  * dtype give bitwise identical results. gamma == NULL means all ones. dx, dgamma and
  * dbeta may each be NULL (not computed). A group with M == 1 has dx == +0 exactly for
- * finite inputs (NaN/Inf still propagate). Enqueues gn_backward_reduce then, unless dx is
- * NULL, gn_backward_apply (three kernels).
+ * finite inputs (NaN/Inf still propagate). With activation GN_ACT_RELU, dy is the gradient
+ * of the relu's output and is gated as stated above before all of this (beta, NULL for
+ * zeros, is then needed to recompute the pre-activation; it is ignored otherwise).
+ * Enqueues gn_backward_reduce then, unless dx is NULL, gn_backward_apply (three kernels).
  */
 int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
                 const float* mean, const float* rstd, const float* gamma,
+                const float* beta, int activation,
                 int64_t N, int64_t C, int64_t S, int64_t G,
                 void* dx, float* dgamma, float* dbeta,
                 void* workspace, size_t workspace_bytes, void* stream);
@@ -139,6 +157,7 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
  */
 int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
                        const float* mean, const float* rstd, const float* gamma,
+                       const float* beta, int activation,
                        int64_t N, int64_t C, int64_t S, int64_t G,
                        float* dgamma, float* dbeta,
                        void* workspace, size_t workspace_bytes, void* stream);
@@ -149,7 +168,7 @@ int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
  * One kernel.
  */
 int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
-                      int64_t N, int64_t C, int64_t S, int64_t G, void* dx,
+                      int64_t N, int64_t C, int64_t S, int64_t G, int activation, void* dx,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static English description of a status code (never NULL). */

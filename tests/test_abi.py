@@ -30,11 +30,12 @@ def test_status_enum_matches_header():
     for code, name in STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
     assert re.search(r"GN_F32\s*=\s*0", text) and re.search(r"GN_BF16\s*=\s*1", text)
+    assert re.search(r"GN_ACT_NONE\s*=\s*0", text) and re.search(r"GN_ACT_RELU\s*=\s*1", text)
     assert GN_F32 == 0 and GN_BF16 == 1
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == 2
+    assert lib.gn_abi_version() == 3
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every
@@ -44,15 +45,15 @@ B = ctypes.c_void_p(0x20000)
 
 
 def fwd(**kw):
-    args = dict(x=A, xdt=GN_BF16, gamma=None, beta=None, N=1, C=8, S=64, G=4, eps=1e-5, y=B,
+    args = dict(x=A, xdt=GN_BF16, gamma=None, beta=None, N=1, C=8, S=64, G=4, eps=1e-5, act=0, y=B,
                 ydt=GN_BF16, mean=A, rstd=B, ws=A, wsb=1 << 20, stream=None)
     args.update(kw)
     return lib.gn_forward(*args.values())
 
 
 def bwd(**kw):
-    args = dict(dy=A, dydt=GN_BF16, x=B, xdt=GN_BF16, mean=A, rstd=B, gamma=None, N=1, C=8, S=64,
-                G=4, dx=A, dgamma=None, dbeta=None, ws=B, wsb=1 << 20, stream=None)
+    args = dict(dy=A, dydt=GN_BF16, x=B, xdt=GN_BF16, mean=A, rstd=B, gamma=None, beta=None, act=0,
+                N=1, C=8, S=64, G=4, dx=A, dgamma=None, dbeta=None, ws=B, wsb=1 << 20, stream=None)
     args.update(kw)
     return lib.gn_backward(*args.values())
 
@@ -66,6 +67,7 @@ def bwd(**kw):
     (dict(wsb=16), 6),
     (dict(x=ctypes.c_void_p(0x10002)), 7), (dict(y=ctypes.c_void_p(0x20008)), 7),
     (dict(ws=ctypes.c_void_p(0x10004)), 7), (dict(mean=ctypes.c_void_p(0x10001)), 7),
+    (dict(act=2), 10), (dict(act=-1), 10),
 ])
 def test_forward_validation(kw, status):
     assert fwd(**kw) == status
@@ -75,7 +77,8 @@ def test_forward_validation(kw, status):
     (dict(dy=None), 1), (dict(x=None), 1), (dict(rstd=None), 1), (dict(ws=None), 1),
     (dict(C=6, G=4), 3), (dict(N=-2), 2), (dict(dydt=5), 4), (dict(xdt=3), 4),
     (dict(wsb=0), 6), (dict(dx=ctypes.c_void_p(0x10008)), 7),
-    (dict(dgamma=ctypes.c_void_p(0x10002)), 7),
+    (dict(dgamma=ctypes.c_void_p(0x10002)), 7), (dict(beta=ctypes.c_void_p(0x10002)), 7),
+    (dict(act=5), 10),
 ])
 def test_backward_validation(kw, status):
     assert bwd(**kw) == status
@@ -86,12 +89,17 @@ def test_split_phase_validation():
     assert lib.gn_forward_stats(A, GN_BF16, None, None, 1, 8, 64, 3, 1e-5, A, B, A, 1 << 20, None) == 3
     assert lib.gn_forward_stats(A, GN_BF16, None, None, 1, 8, 64, 4, 1e-5, A, B, A, 8, None) == 6
     assert lib.gn_forward_stats(A, GN_BF16, None, None, 1, 8, 64, 4, -1.0, A, B, A, 1 << 20, None) == 5
-    assert lib.gn_forward_apply(A, GN_BF16, 1, 8, 64, 4, None, GN_BF16, A, 1 << 20, None) == 1
-    assert lib.gn_forward_apply(A, GN_F32, 1, 8, 64, 4, B, GN_BF16, A, 1 << 20, None) == 4
-    assert lib.gn_backward_reduce(A, 9, B, GN_BF16, A, B, None, 1, 8, 64, 4, None, None, A, 1 << 20,
-                                  None) == 4
-    assert lib.gn_backward_reduce(A, GN_BF16, B, GN_BF16, A, B, None, 1, 8, 64, 4, None, None, A, 8,
-                                  None) == 6
-    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, None, A, 1 << 20, None) == 1
-    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, ctypes.c_void_p(0x30004), A,
+    assert lib.gn_forward_apply(A, GN_BF16, 1, 8, 64, 4, 0, None, GN_BF16, A, 1 << 20, None) == 1
+    assert lib.gn_forward_apply(A, GN_F32, 1, 8, 64, 4, 0, B, GN_BF16, A, 1 << 20, None) == 4
+    assert lib.gn_forward_apply(A, GN_BF16, 1, 8, 64, 4, 3, B, GN_BF16, A, 1 << 20, None) == 10
+    assert lib.gn_backward_reduce(A, 9, B, GN_BF16, A, B, None, None, 0, 1, 8, 64, 4, None, None, A,
+                                  1 << 20, None) == 4
+    assert lib.gn_backward_reduce(A, GN_BF16, B, GN_BF16, A, B, None, None, 0, 1, 8, 64, 4, None, None,
+                                  A, 8, None) == 6
+    assert lib.gn_backward_reduce(A, GN_BF16, B, GN_BF16, A, B, None, None, 7, 1, 8, 64, 4, None, None,
+                                  A, 1 << 20, None) == 10
+    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, 0, None, A, 1 << 20, None) == 1
+    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, 0, ctypes.c_void_p(0x30004), A,
                                  1 << 20, None) == 7
+    assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, 2, ctypes.c_void_p(0x30000), A,
+                                 1 << 20, None) == 10

@@ -32,11 +32,13 @@ def _on_gpu(inp):
     return out
 
 
-def _run(inp, out_dtype=None, dy=None):
+def _run(inp, out_dtype=None, dy=None, relu=False):
     x, G, eps = inp["x"], inp["G"], inp["eps"]
-    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, eps, out_dtype or inp["out_dtype"])
+    act = "relu" if relu else None
+    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, eps, out_dtype or inp["out_dtype"],
+                                  activation=act)
     dy = inp["dy"] if dy is None else dy
-    dx, dg, db = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G)
+    dx, dg, db = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G, beta=inp["beta"], activation=act)
     torch.cuda.synchronize()
     return {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dgamma": dg, "dbeta": db}
 
@@ -45,25 +47,30 @@ def _chan_at(idx, x, gamma, beta):
     return P.channel_params_at(idx, tuple(x.shape), gamma.cpu().numpy(), beta.cpu().numpy())
 
 
-def full_check(inp, tag):
+def full_check(inp, tag, relu=False):
     """Element-by-element comparison of every output."""
     say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} dy {inp['dy'].dtype} "
-        f"out {inp['out_dtype']} G={inp['G']} -> gn_forward + gn_backward")
+        f"out {inp['out_dtype']} G={inp['G']} relu={relu} -> gn_forward + gn_backward")
     g = _on_gpu(inp)
-    r = _run(g)
+    r = _run(g, relu=relu)
     x, dy, G, eps = inp["x"].cpu(), inp["dy"].cpu(), inp["G"], inp["eps"]
     gamma, beta = inp["gamma"].cpu(), inp["beta"].cpu()
-    f = O.forward(x, G, gamma, beta, eps=eps)
+    f = O.forward(x, G, gamma, beta, eps=eps, relu=relu)
     rep = P.check_stats(P.to_np(r["mean"]), P.to_np(r["rstd"]), f["mean"], f["var"], f["rstd"])
     idx = np.arange(x.numel())
     rep.update(P.check_y(P.to_np(r["y"]).reshape(-1), f["y"].reshape(-1), *_chan_at(idx, x, gamma, beta)))
-    b = O.backward(dy, x, G, gamma, eps=eps)
-    rep.update(P.check_dx(P.to_np(r["dx"]).reshape(-1), b["dx"].reshape(-1)))
-    a_dy, a_dyx = O.channel_abs_sums(dy, x, G, b["mean"], b["rstd"])
+    b = O.backward(dy, x, G, gamma, eps=eps, beta=beta, relu=relu)
+    dx64 = b["dx"].reshape(-1)
+    band = P.ReluBand(x, dy, G, gamma, beta, b["mean"], b["rstd"]) if relu else None
+    rep.update(P.check_dx(P.to_np(r["dx"]).reshape(-1), dx64,
+                          band=None if band is None else band.dx_terms(idx, dx64)))
+    a_dy, a_dyx = O.channel_abs_sums(dy, x, G, b["mean"], b["rstd"], gamma=gamma, beta=beta, relu=relu)
     N, C = x.shape[:2]
     depth = P.reduction_depth(gn.gn_plan_query(N, C, x.numel() // (N * C), G), N)
-    rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth))
-    rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth))
+    rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth,
+                             0.0 if band is None else band.dgamma))
+    rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth,
+                             0.0 if band is None else band.dbeta))
     say(f"{tag}: ok {rep}")
     return r
 
@@ -86,11 +93,11 @@ def _sample_indices(x, G, n_random, seed):
     return np.unique(np.concatenate(parts)).astype(np.int64)
 
 
-def sampled_check(inp, tag, n_random=1 << 20, seed=0):
+def sampled_check(inp, tag, n_random=1 << 20, seed=0, relu=False):
     """Full statistics and parameter gradients; y and dx on sampled elements."""
-    say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} G={inp['G']} "
+    say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} G={inp['G']} relu={relu} "
         f"(sampled) -> gn_forward + gn_backward")
-    r = _run(inp)
+    r = _run(inp, relu=relu)
     x, dy, G, eps = inp["x"].cpu(), inp["dy"].cpu(), inp["G"], inp["eps"]
     gamma, beta = inp["gamma"].cpu(), inp["beta"].cpu()
     say(f"{tag}: oracle statistics")
@@ -98,17 +105,23 @@ def sampled_check(inp, tag, n_random=1 << 20, seed=0):
     rep = P.check_stats(P.to_np(r["mean"]), P.to_np(r["rstd"]), mean64, var64, rstd64)
     idx = _sample_indices(x, G, n_random, seed)
     it = torch.from_numpy(idx).to(DEV)
-    y64 = O.forward_at(x, G, idx, mean64, rstd64, gamma, beta)
+    y64 = O.forward_at(x, G, idx, mean64, rstd64, gamma, beta, relu=relu)
     rep.update(P.check_y(P.to_np(r["y"].reshape(-1)[it]), y64, *_chan_at(idx, x, gamma, beta)))
     say(f"{tag}: oracle backward")
-    b = O.backward(dy, x, G, gamma, eps=eps, want_dx=False)
-    dx64 = O.backward_at(dy, x, G, idx, b["mean"], b["rstd"], b["c1"], b["c2"], gamma)
-    rep.update(P.check_dx(P.to_np(r["dx"].reshape(-1)[it]), dx64))
-    a_dy, a_dyx = O.channel_abs_sums(dy, x, G, b["mean"], b["rstd"])
+    b = O.backward(dy, x, G, gamma, eps=eps, want_dx=False, beta=beta, relu=relu)
+    dx64 = O.backward_at(dy, x, G, idx, b["mean"], b["rstd"], b["c1"], b["c2"], gamma, beta=beta, relu=relu)
+    band = P.ReluBand(x, dy, G, gamma, beta, b["mean"], b["rstd"]) if relu else None
+    rep.update(P.check_dx(P.to_np(r["dx"].reshape(-1)[it]), dx64,
+                          band=None if band is None else band.dx_terms(idx, dx64)))
+    a_dy, a_dyx = O.channel_abs_sums(dy, x, G, b["mean"], b["rstd"], gamma=gamma, beta=beta, relu=relu)
     N, C = x.shape[:2]
     depth = P.reduction_depth(gn.gn_plan_query(N, C, x.numel() // (N * C), G), N)
-    rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth))
-    rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth))
+    rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth,
+                             0.0 if band is None else band.dgamma))
+    rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth,
+                             0.0 if band is None else band.dbeta))
+    if band is not None:
+        rep["band_total"] = band.count
     say(f"{tag}: ok ({idx.size} sampled elements) {rep}")
     return r
 
@@ -287,6 +300,16 @@ def test_split_phase_entry_points_match_fused():
     torch.cuda.synchronize()
     for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2), (dg, dg2), (db, db2)):
         assert torch.equal(u, v)
+    say(f"{case.name}: split-phase entry points with relu vs fused")
+    y, mean, rstd = gn.gn_forward(x, gamma, beta, G, inp["eps"], activation="relu")
+    dx, dg, db = gn.gn_backward(inp["dy"], x, mean, rstd, gamma, G, beta=beta, activation="relu")
+    gn.gn_forward_stats(x, gamma, beta, G, inp["eps"], mean2, rstd2, ws)
+    gn.gn_forward_apply(x, G, y2, ws, activation="relu")
+    gn.gn_backward_reduce(inp["dy"], x, mean2, rstd2, gamma, G, dg2, db2, ws, beta=beta, activation="relu")
+    gn.gn_backward_apply(inp["dy"], x, G, dx2, ws, activation="relu")
+    torch.cuda.synchronize()
+    for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2), (dg, dg2), (db, db2)):
+        assert torch.equal(u, v)
 
 
 def test_optional_backward_outputs():
@@ -319,6 +342,22 @@ def test_autograd_function_matches_entry_points():
     assert torch.equal(gamma.grad, dg2) and torch.equal(beta.grad, db2)
 
 
+def test_autograd_relu_matches_entry_points():
+    say("group_norm(activation='relu') through autograd vs entry points (deep workload)")
+    inp = workloads.make(workloads.DEEP, DEV)
+    x = inp["x"].clone().requires_grad_(True)
+    gamma = inp["gamma"].clone().requires_grad_(True)
+    beta = inp["beta"].clone().requires_grad_(True)
+    y = gn.group_norm(x, inp["G"], gamma, beta, inp["eps"], activation="relu")
+    y.backward(inp["dy"])
+    y2, m2, r2 = gn.gn_forward(inp["x"], inp["gamma"], inp["beta"], inp["G"], inp["eps"], activation="relu")
+    dx2, dg2, db2 = gn.gn_backward(inp["dy"], inp["x"], m2, r2, inp["gamma"], inp["G"],
+                                   beta=inp["beta"], activation="relu")
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), y2) and torch.equal(x.grad, dx2)
+    assert torch.equal(gamma.grad, dg2) and torch.equal(beta.grad, db2)
+
+
 def test_binding_rejects_bad_arguments():
     say("argument errors")
     x = torch.zeros((0, 4, 2, 2, 2), dtype=torch.bfloat16, device=DEV)
@@ -337,10 +376,89 @@ def test_binding_rejects_bad_arguments():
         gn.gn_forward(x, None, None, 2, out_dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         gn.gn_forward(x.transpose(2, 3), None, None, 2)
+    with pytest.raises(ValueError, match="activation"):
+        gn.gn_forward(x, None, None, 2, activation="gelu")
     with pytest.raises(gn.GnError, match="GN_ERR_DEVICE"):
         gn.gn_forward(x.cpu().pin_memory(), None, None, 2, out=torch.empty_like(x),
                       mean=torch.empty(1, 2, device=DEV), rstd=torch.empty(1, 2, device=DEV),
                       workspace=gn.workspace_for(x, 2))
+
+
+# ----------------------------------------------------------------------------- fused relu
+
+RELU_CASES = [workloads.TINY, workloads.DEEP, workloads.DEEP_F32OUT, RAGGED[0], RAGGED[2], RAGGED[3],
+              RAGGED[5]]
+
+
+@pytest.mark.parametrize("case", RELU_CASES, ids=lambda c: c.name)
+def test_relu_elementwise(case):
+    full_check(workloads.make(case, "cpu"), case.name + "_relu", relu=True)
+
+
+def test_relu_nan_inf_confined_to_their_group():
+    say("relu: NaN/Inf in two groups of (2, 8, 6, 6, 6), G=4")
+    inp = workloads.make(workloads.custom(2, 8, 4, (6, 6, 6), torch.bfloat16, seed=22), "cpu")
+    x = inp["x"].clone()
+    x[0, 2, 1, 1, 1] = float("nan")
+    x[1, 7, 0, 0, 0] = float("-inf")
+    inp["x"] = x
+    r = full_check(inp, "nan_inf_relu", relu=True)
+    # relu passes NaN through (no clamp swallows it), in y and in the backward gate
+    assert torch.isnan(r["y"][0, 2:4].float()).all() and torch.isnan(r["dx"][1, 6:8].float()).all()
+    assert torch.isfinite(r["y"][0, 0:2].float()).all() and torch.isfinite(r["dx"][1, 0:6].float()).all()
+
+
+def test_relu_scale7_sampled():
+    case = workloads.SCALE7
+    sampled_check(workloads.make(case, DEV), case.name + "_relu", seed=case.seed, relu=True)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", [workloads.DEEP, workloads.SCALE7], ids=lambda c: c.name)
+def test_relu_forward_is_unfused_forward_then_relu_bitwise(case, out_dtype):
+    """The fused store equals the unfused output with negatives replaced by +0, bit for
+    bit: NaN stays NaN, -0.0 stays -0.0 (a channel with gamma = 0, beta = -0.0 makes them)."""
+    say(f"{case.name}: fused relu forward vs unfused + relu, out {out_dtype}")
+    inp = workloads.make(case, DEV, with_dy=False)
+    x, G = inp["x"], inp["G"]
+    gamma, beta = inp["gamma"].clone(), inp["beta"].clone()
+    gamma[0], beta[0] = 0.0, -0.0
+    x = x.clone()
+    x.view(x.shape[0], G, -1)[0, G - 1, 5] = float("nan")
+    y, m, r = gn.gn_forward(x, gamma, beta, G, inp["eps"], out_dtype)
+    yr, mr, rr = gn.gn_forward(x, gamma, beta, G, inp["eps"], out_dtype, activation="relu")
+    torch.cuda.synchronize()
+    assert torch.equal(m.view(torch.int32), mr.view(torch.int32))
+    assert torch.equal(r.view(torch.int32), rr.view(torch.int32))
+    ref = torch.where(y < 0, torch.zeros_like(y), y)
+    bits = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(yr.view(bits), ref.view(bits))
+    assert torch.isnan(yr).sum().item() == torch.isnan(y).sum().item() > 0
+    assert (yr.view(bits) == torch.tensor(-0.0, dtype=out_dtype).view(bits).item()).any()
+
+
+@pytest.mark.parametrize("case", [workloads.DEEP, workloads.SCALE7], ids=lambda c: c.name)
+def test_relu_gate_all_open_or_all_closed(case):
+    """beta far above every |gamma * xhat|: every gate is open and the relu path equals the
+    plain path bit for bit. beta far below: y is +0 everywhere and every gradient is 0."""
+    say(f"{case.name}: relu with every gate open, then every gate closed")
+    inp = workloads.make(case, DEV)
+    x, G, gamma, dy = inp["x"], inp["G"], inp["gamma"], inp["dy"]
+    for sign in (1.0, -1.0):
+        beta = torch.full_like(inp["beta"], sign * 1e4)
+        y, m, r = gn.gn_forward(x, gamma, beta, G, inp["eps"])
+        a = gn.gn_backward(dy, x, m, r, gamma, G, beta=beta)
+        yr, mr, rr = gn.gn_forward(x, gamma, beta, G, inp["eps"], activation="relu")
+        b = gn.gn_backward(dy, x, mr, rr, gamma, G, beta=beta, activation="relu")
+        torch.cuda.synchronize()
+        if sign > 0:
+            assert torch.equal(y.view(torch.int16), yr.view(torch.int16))
+            for u, v in zip(a, b):
+                assert torch.equal(u, v)
+        else:
+            assert torch.equal(yr.view(torch.int16), torch.zeros_like(yr).view(torch.int16))
+            for t in b:
+                assert (t == 0).all()
 
 
 # ----------------------------------------------------------------------------- largest size

@@ -53,9 +53,9 @@ def test_plan_is_consistent(N, C, S, G):
     assert p["apply_jobs"] == p["rows"] * p["apply_chunks_per_row"]
     assert (p["apply_chunks_per_row"] - 1) * p["apply_chunk"] < S <= p["apply_chunks_per_row"] * p["apply_chunk"]
     assert p["apply_chunk"] <= p["apply_block"] * p["apply_vectors"] * VEC
-    # workspace: partials, then 256-byte aligned per-row float4 coefficients
+    # workspace: partials, then 256-byte aligned per-row coefficients (two float4 per row)
     coef_off = -(-8 * p["jobs"] // 256) * 256
-    assert p["workspace_bytes"] >= coef_off + 16 * p["rows"]
+    assert p["workspace_bytes"] >= coef_off + 32 * p["rows"]
 
 
 @pytest.mark.parametrize("N,C,S,G", [s for s in SHAPES if s[0] * s[1] * s[2] <= 2 ** 22])

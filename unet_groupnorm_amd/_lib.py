@@ -12,9 +12,11 @@ LIB_PATH = os.path.join(HERE, "libgn.so")
 # Status codes and dtype codes of include/gn.h.
 GN_OK = 0
 GN_F32, GN_BF16 = 0, 1
+GN_ACT_NONE, GN_ACT_RELU = 0, 1
 STATUS_NAMES = {
     0: "GN_OK", 1: "GN_ERR_NULL", 2: "GN_ERR_SHAPE", 3: "GN_ERR_GROUPS", 4: "GN_ERR_DTYPE",
     5: "GN_ERR_EPS", 6: "GN_ERR_WORKSPACE", 7: "GN_ERR_ALIGN", 8: "GN_ERR_DEVICE", 9: "GN_ERR_LAUNCH",
+    10: "GN_ERR_ACTIVATION",
 }
 
 
@@ -40,12 +42,12 @@ def _declare(lib):
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "gn_workspace_bytes": (SZ, [I64, I64, I64, I64]),
-        "gn_forward": (I, [P, I, P, P, I64, I64, I64, I64, F, P, I, P, P, P, SZ, P]),
+        "gn_forward": (I, [P, I, P, P, I64, I64, I64, I64, F, I, P, I, P, P, P, SZ, P]),
         "gn_forward_stats": (I, [P, I, P, P, I64, I64, I64, I64, F, P, P, P, SZ, P]),
-        "gn_forward_apply": (I, [P, I, I64, I64, I64, I64, P, I, P, SZ, P]),
-        "gn_backward": (I, [P, I, P, I, P, P, P, I64, I64, I64, I64, P, P, P, P, SZ, P]),
-        "gn_backward_reduce": (I, [P, I, P, I, P, P, P, I64, I64, I64, I64, P, P, P, SZ, P]),
-        "gn_backward_apply": (I, [P, I, P, I, I64, I64, I64, I64, P, P, SZ, P]),
+        "gn_forward_apply": (I, [P, I, I64, I64, I64, I64, I, P, I, P, SZ, P]),
+        "gn_backward": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, P, P, SZ, P]),
+        "gn_backward_reduce": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, P, SZ, P]),
+        "gn_backward_apply": (I, [P, I, P, I, I64, I64, I64, I64, I, P, P, SZ, P]),
         "gn_status_string": (ctypes.c_char_p, [I]),
         "gn_plan_query": (I, [I64, I64, I64, I64, ctypes.POINTER(GnPlanInfo)]),
         "gn_abi_version": (I, []),

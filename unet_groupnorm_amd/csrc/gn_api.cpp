@@ -15,6 +15,7 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool dtype_ok(int d) { return d == GN_F32 || d == GN_BF16; }
+bool act_ok(int a) { return a == GN_ACT_NONE || a == GN_ACT_RELU; }
 
 int plan_or_error(int64_t N, int64_t C, int64_t S, int64_t G, gn::Plan* p)
 {
@@ -69,7 +70,7 @@ class DeviceScope {
 };
 
 int fwd_check(const void* x, int x_dtype, const float* gamma, const float* beta, int64_t N,
-              int64_t C, int64_t S, int64_t G, float eps, const void* y, int y_dtype,
+              int64_t C, int64_t S, int64_t G, float eps, int activation, const void* y, int y_dtype,
               const float* mean, const float* rstd, const void* ws, size_t ws_bytes, gn::Plan* p)
 {
     if (!x || !y || !mean || !rstd || !ws) return GN_ERR_NULL;
@@ -77,6 +78,7 @@ int fwd_check(const void* x, int x_dtype, const float* gamma, const float* beta,
     if (rc) return rc;
     if (!dtype_ok(x_dtype) || !(y_dtype == x_dtype || y_dtype == GN_F32)) return GN_ERR_DTYPE;
     if (!std::isfinite(eps) || eps < 0.0f) return GN_ERR_EPS;
+    if (!act_ok(activation)) return GN_ERR_ACTIVATION;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mean, 4) || !aligned(rstd, 4) ||
         !aligned(gamma, 4) || !aligned(beta, 4))
         return GN_ERR_ALIGN;
@@ -84,16 +86,18 @@ int fwd_check(const void* x, int x_dtype, const float* gamma, const float* beta,
 }
 
 int bwd_check(const void* dy, int dy_dtype, const void* x, int x_dtype, const float* mean,
-              const float* rstd, const float* gamma, int64_t N, int64_t C, int64_t S, int64_t G,
-              const void* dx, const float* dgamma, const float* dbeta, const void* ws,
-              size_t ws_bytes, gn::Plan* p)
+              const float* rstd, const float* gamma, const float* beta, int activation, int64_t N,
+              int64_t C, int64_t S, int64_t G, const void* dx, const float* dgamma,
+              const float* dbeta, const void* ws, size_t ws_bytes, gn::Plan* p)
 {
     if (!dy || !x || !mean || !rstd || !ws) return GN_ERR_NULL;
     int rc = plan_or_error(N, C, S, G, p);
     if (rc) return rc;
     if (!dtype_ok(x_dtype) || !dtype_ok(dy_dtype)) return GN_ERR_DTYPE;
+    if (!act_ok(activation)) return GN_ERR_ACTIVATION;
     if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16) || !aligned(mean, 4) ||
-        !aligned(rstd, 4) || !aligned(gamma, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4))
+        !aligned(rstd, 4) || !aligned(gamma, 4) || !aligned(beta, 4) || !aligned(dgamma, 4) ||
+        !aligned(dbeta, 4))
         return GN_ERR_ALIGN;
     return workspace_check(ws, ws_bytes, *p);
 }
@@ -132,7 +136,7 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 2; }
+int gn_abi_version(void) { return 3; }
 
 const char* gn_status_string(int status)
 {
@@ -147,6 +151,7 @@ const char* gn_status_string(int status)
         case GN_ERR_ALIGN: return "misaligned pointer (tensors and workspace need 16 bytes, fp32 vectors 4)";
         case GN_ERR_DEVICE: return "x is not device memory or the stream belongs to another device";
         case GN_ERR_LAUNCH: return "kernel launch failed";
+        case GN_ERR_ACTIVATION: return "unknown activation (GN_ACT_NONE or GN_ACT_RELU)";
         default: return "unknown status";
     }
 }
@@ -174,34 +179,36 @@ int gn_forward_stats(const void* x, int x_dtype, const float* gamma, const float
 }
 
 int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
-                     void* y, int y_dtype, void* workspace, size_t workspace_bytes, void* stream)
+                     int activation, void* y, int y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!x || !y || !workspace) return GN_ERR_NULL;
     gn::Plan p;
     int rc = plan_or_error(N, C, S, G, &p);
     if (rc) return rc;
     if (!dtype_ok(x_dtype) || !(y_dtype == x_dtype || y_dtype == GN_F32)) return GN_ERR_DTYPE;
+    if (!act_ok(activation)) return GN_ERR_ACTIVATION;
     if (!aligned(x, 16) || !aligned(y, 16)) return GN_ERR_ALIGN;
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, gn::kargs_of(p),
+    return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, gn::kargs_of(p, activation),
                                               gn::workspace_of(workspace, p),
                                               static_cast<hipStream_t>(stream)));
 }
 
 int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta,
-               int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+               int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
                void* y, int y_dtype, float* mean, float* rstd,
                void* workspace, size_t workspace_bytes, void* stream)
 {
     gn::Plan p;
-    int rc = fwd_check(x, x_dtype, gamma, beta, N, C, S, G, eps, y, y_dtype, mean, rstd,
+    int rc = fwd_check(x, x_dtype, gamma, beta, N, C, S, G, eps, activation, y, y_dtype, mean, rstd,
                        workspace, workspace_bytes, &p);
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    const gn::KArgs a = gn::kargs_of(p);
+    const gn::KArgs a = gn::kargs_of(p, activation);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = launch_status(gn::launch_fwd_stats(x, x_dtype, gamma, beta, eps, mean, rstd, a, w, st))))
@@ -211,24 +218,25 @@ int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta
 
 int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
                        const float* mean, const float* rstd, const float* gamma,
+                       const float* beta, int activation,
                        int64_t N, int64_t C, int64_t S, int64_t G,
                        float* dgamma, float* dbeta,
                        void* workspace, size_t workspace_bytes, void* stream)
 {
     gn::Plan p;
-    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, N, C, S, G, nullptr, dgamma,
-                       dbeta, workspace, workspace_bytes, &p);
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, activation, N, C, S, G,
+                       nullptr, dgamma, dbeta, workspace, workspace_bytes, &p);
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    return launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, dgamma,
-                                               dbeta, gn::kargs_of(p),
+    return launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta,
+                                               dgamma, dbeta, gn::kargs_of(p, activation),
                                                gn::workspace_of(workspace, p),
                                                static_cast<hipStream_t>(stream)));
 }
 
 int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
-                      int64_t N, int64_t C, int64_t S, int64_t G, void* dx,
+                      int64_t N, int64_t C, int64_t S, int64_t G, int activation, void* dx,
                       void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!dy || !x || !dx || !workspace) return GN_ERR_NULL;
@@ -236,31 +244,33 @@ int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
     int rc = plan_or_error(N, C, S, G, &p);
     if (rc) return rc;
     if (!dtype_ok(x_dtype) || !dtype_ok(dy_dtype)) return GN_ERR_DTYPE;
+    if (!act_ok(activation)) return GN_ERR_ACTIVATION;
     if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(dx, 16)) return GN_ERR_ALIGN;
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, gn::kargs_of(p),
+    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, gn::kargs_of(p, activation),
                                               gn::workspace_of(workspace, p),
                                               static_cast<hipStream_t>(stream)));
 }
 
 int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
                 const float* mean, const float* rstd, const float* gamma,
+                const float* beta, int activation,
                 int64_t N, int64_t C, int64_t S, int64_t G,
                 void* dx, float* dgamma, float* dbeta,
                 void* workspace, size_t workspace_bytes, void* stream)
 {
     gn::Plan p;
-    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, N, C, S, G, dx, dgamma, dbeta,
-                       workspace, workspace_bytes, &p);
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, activation, N, C, S, G, dx,
+                       dgamma, dbeta, workspace, workspace_bytes, &p);
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    const gn::KArgs a = gn::kargs_of(p);
+    const gn::KArgs a = gn::kargs_of(p, activation);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if ((rc = launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma,
+    if ((rc = launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta,
                                                   dgamma, dbeta, a, w, st))))
         return rc;
     if (!dx) return GN_OK;

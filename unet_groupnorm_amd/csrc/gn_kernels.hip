@@ -87,6 +87,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// The optional activation ("Optimize GroupNorm", paragraphs on the fused ReLU and on the
+// NaN-correct ReLU): relu is 0 where v < 0 and v otherwise, so NaN, +Inf and -0.0 pass;
+// its gradient is blocked where the relu result is <= 0 and passes otherwise (NaN too).
+__device__ __forceinline__ float relu_f(float v) { return v < 0.0f ? 0.0f : v; }
+__device__ __forceinline__ float relu_gate(float pre, float g) { return relu_f(pre) <= 0.0f ? 0.0f : g; }
+
 // Loads of the streamed tensors are marked nontemporal: each element is read once per
 // kernel, and on MI355X this lifts a streaming read from about 6.2 to about 7 TB/s.
 template <typename T> struct Io;
@@ -557,7 +563,7 @@ fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
         const int64_t c = g * a.Cg + i;
         const float gm = gamma ? gamma[c] : 1.0f;
         const float bt = beta ? beta[c] : 0.0f;
-        coef[n * a.C + c] = make_float4(hi, lo, gm * rstd, bt);
+        coef[2 * (n * a.C + c)] = make_float4(hi, lo, gm * rstd, bt);
     }
 }
 
@@ -571,8 +577,9 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
         const int64_t j = kReverseApply ? a.jobs_a - 1 - jj : jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
-        const float4 cf = coef[jb.row];
+        const float4 cf = coef[2 * jb.row];
         const float hi = cf.x, lo = cf.y, scale = cf.z, shift = cf.w;
+        const bool act = a.act != 0;
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
             for (int u = 0; u < kApplyVecs; ++u) {
@@ -581,13 +588,18 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
                     float e[kVec], o[kVec];
                     Io<TX>::template load8<kNtApply>(x + vi * kVec, e);
 #pragma unroll
-                    for (int i = 0; i < kVec; ++i) o[i] = fmaf((e[i] - hi) - lo, scale, shift);
+                    for (int i = 0; i < kVec; ++i) {
+                        const float v = fmaf((e[i] - hi) - lo, scale, shift);
+                        o[i] = act ? relu_f(v) : v;
+                    }
                     Io<TY>::store8(y + vi * kVec, o);
                 } else {
                     for (int i = 0; i < kVec; ++i) {
                         const int64_t gi = vi * kVec + i;
-                        if (gi >= jb.lo && gi < jb.hi)
-                            Io<TY>::store1(y + gi, fmaf((Io<TX>::load1(x + gi) - hi) - lo, scale, shift));
+                        if (gi >= jb.lo && gi < jb.hi) {
+                            const float v = fmaf((Io<TX>::load1(x + gi) - hi) - lo, scale, shift);
+                            Io<TY>::store1(y + gi, act ? relu_f(v) : v);
+                        }
                     }
                 }
             }
@@ -597,10 +609,12 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
 
 // ------------------------------------------------------------------ backward
 
+// One full step of the backward sums. With the relu, dy is gated on the recomputed
+// pre-activation pre = (x - mean) * gamma*rstd + beta.
 template <typename TX, typename TD>
 __device__ __forceinline__ void bwd_full_step(const typename Io<TX>::Raw (&rx)[kStepVecs],
                                               const typename Io<TD>::Raw (&rd)[kStepVecs], float mu,
-                                              float& s1, float& s2)
+                                              bool act, float scale, float shift, float& s1, float& s2)
 {
     float d[kTile], gv[kTile];
 #pragma unroll
@@ -611,7 +625,7 @@ __device__ __forceinline__ void bwd_full_step(const typename Io<TX>::Raw (&rx)[k
 #pragma unroll
         for (int i = 0; i < kVec; ++i) {
             d[u * kVec + i] = e[i] - mu;
-            gv[u * kVec + i] = f[i];
+            gv[u * kVec + i] = act ? relu_gate(fmaf(d[u * kVec + i], scale, shift), f[i]) : f[i];
         }
     }
     s1 = s1 + tree_sum(gv);
@@ -621,13 +635,16 @@ __device__ __forceinline__ void bwd_full_step(const typename Io<TX>::Raw (&rx)[k
 template <typename TX, typename TD>
 __device__ __forceinline__ void bwd_masked_step(const TD* __restrict__ dy, const TX* __restrict__ x,
                                                 const Job& jb, int64_t sv0, int blk, int tid, float mu,
-                                                float& s1, float& s2)
+                                                bool act, float scale, float shift, float& s1, float& s2)
 {
     float xv[kTile], gv[kTile];
     const uint32_t valid = load_step_masked<kNtBwdReduce>(x, jb, sv0, blk, tid, xv);
     load_step_masked<kNtBwdReduce>(dy, jb, sv0, blk, tid, gv);  // same mask: zeros outside
 #pragma unroll
-    for (int i = 0; i < kTile; ++i) xv[i] = ((valid >> i) & 1u) ? xv[i] - mu : 0.0f;
+    for (int i = 0; i < kTile; ++i) {
+        xv[i] = ((valid >> i) & 1u) ? xv[i] - mu : 0.0f;
+        if (act) gv[i] = relu_gate(fmaf(xv[i], scale, shift), gv[i]);
+    }
     s1 = s1 + tree_sum(gv);
     s2 = s2 + tree_sumprod(gv, xv);
 }
@@ -639,6 +656,7 @@ template <typename TX, typename TD>
 __global__ void __launch_bounds__(256)
 bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
                   const float* __restrict__ mean, const float* __restrict__ rstd,
+                  const float* __restrict__ gamma, const float* __restrict__ beta,
                   KArgs a, float2* __restrict__ part)
 {
     using RawX = typename Io<TX>::Raw;
@@ -651,10 +669,13 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
         const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, ng = n * a.G + c / a.Cg;
         const float mu = mean[ng];
+        const bool act = a.act != 0;
+        const float scale = act ? rstd[ng] * (gamma ? gamma[c] : 1.0f) : 0.0f;
+        const float shift = act ? (beta ? beta[c] : 0.0f) : 0.0f;
         float s1 = 0.0f, s2 = 0.0f;  // sum dy, sum dy * (x - mu)
         int64_t fs, fe, nsteps;
         full_step_range(jb, stepv, fs, fe, nsteps);
-        if (fs > 0) bwd_masked_step(dy, x, jb, jb.v0, blk, tid, mu, s1, s2);
+        if (fs > 0) bwd_masked_step(dy, x, jb, jb.v0, blk, tid, mu, act, scale, shift, s1, s2);
         if (fe > fs) {
             RawX AX[kStepVecs], BX[kStepVecs];
             RawD AD[kStepVecs], BD[kStepVecs];
@@ -664,21 +685,21 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
             for (; s + 2 < fe; s += 2) {
                 load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
                 load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
-                bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
+                bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
                 load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
                 load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
-                bwd_full_step<TX, TD>(BX, BD, mu, s1, s2);
+                bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
             }
             if (s + 1 < fe) {
                 load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
                 load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
-                bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
-                bwd_full_step<TX, TD>(BX, BD, mu, s1, s2);
+                bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
+                bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
             } else {
-                bwd_full_step<TX, TD>(AX, AD, mu, s1, s2);
+                bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
             }
         }
-        if (fe < nsteps) bwd_masked_step(dy, x, jb, jb.v0 + fe * stepv, blk, tid, mu, s1, s2);
+        if (fe < nsteps) bwd_masked_step(dy, x, jb, jb.v0 + fe * stepv, blk, tid, mu, act, scale, shift, s1, s2);
         const float2 r = block_sum2(s1, s2, s_a, s_b);
         if (tid == 0) part[j] = make_float2(r.x, r.y * rstd[ng]);
     }
@@ -686,13 +707,15 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
 
 // Workgroups [0, ngroups) each take one group (n, g): c1 = (1/M) sum gamma_c s1,
 // c2 = (1/M) sum gamma_c s2 over the group's P partials in a fixed order, then each row's
-// dx coefficients (mean, A = rstd*gamma_c, B = -rstd*c1, E = -rstd^2*c2), so that
-// dx = rstd*(gamma_c*dy - c1 - xhat*c2) = A*dy + (B + E*(x - mean)).
+// dx coefficients (mean, A = rstd*gamma_c, B = -rstd*c1, E = -rstd^2*c2) and beta_c, so that
+// dx = rstd*(gamma_c*g - c1 - xhat*c2) = A*g + (B + E*(x - mean)), where g is dy, or with the
+// relu dy gated on pre = (x - mean)*A + beta_c.
 // Workgroups [ngroups, ngroups + nchan) each take one channel c: dgamma_c and dbeta_c as
 // the sums of the channel's N*K partials, n-major then k, in a fixed order.
 __global__ void __launch_bounds__(256)
 fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
-               const float* __restrict__ gamma, const float2* __restrict__ part, KArgs a,
+               const float* __restrict__ gamma, const float* __restrict__ beta,
+               const float2* __restrict__ part, KArgs a,
                int64_t ngroups, int64_t nchan, float4* __restrict__ coef,
                float* __restrict__ dgamma, float* __restrict__ dbeta)
 {
@@ -722,7 +745,8 @@ fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
         for (int64_t i = tid; i < a.Cg; i += blk) {
             const int64_t c = g * a.Cg + i;
             const float gm = gamma ? gamma[c] : 1.0f;
-            coef[n * a.C + c] = make_float4(mu, rs * gm, B, E);
+            coef[2 * (n * a.C + c)] = make_float4(mu, rs * gm, B, E);
+            coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, 0.0f, 0.0f, 0.0f);
         }
     } else if (w < ngroups + nchan) {
         const int64_t c = w - ngroups;
@@ -753,8 +777,10 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
         const int64_t j = kReverseApply ? a.jobs_a - 1 - jj : jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
-        const float4 cf = coef[jb.row];
+        const float4 cf = coef[2 * jb.row];
         const float mu = cf.x, A = cf.y, B = cf.z, E = cf.w;
+        const bool act = a.act != 0;
+        const float bt = act ? coef[2 * jb.row + 1].x : 0.0f;
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
             for (int u = 0; u < kApplyVecs; ++u) {
@@ -765,7 +791,9 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
                     Io<TD>::template load8<kNtBwdApply>(dy + vi * kVec, gv);
 #pragma unroll
                     for (int i = 0; i < kVec; ++i) {
-                        float t = fmaf(A, gv[i], fmaf(E, xv[i] - mu, B));
+                        const float d = xv[i] - mu;
+                        const float g = act ? relu_gate(fmaf(d, A, bt), gv[i]) : gv[i];
+                        float t = fmaf(A, g, fmaf(E, d, B));
                         if (single) t = t - t;
                         o[i] = t;
                     }
@@ -774,8 +802,10 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
                     for (int i = 0; i < kVec; ++i) {
                         const int64_t gi = vi * kVec + i;
                         if (gi >= jb.lo && gi < jb.hi) {
-                            float t = fmaf(A, Io<TD>::load1(dy + gi),
-                                           fmaf(E, Io<TX>::load1(x + gi) - mu, B));
+                            const float d = Io<TX>::load1(x + gi) - mu;
+                            const float g0 = Io<TD>::load1(dy + gi);
+                            const float g = act ? relu_gate(fmaf(d, A, bt), g0) : g0;
+                            float t = fmaf(A, g, fmaf(E, d, B));
                             if (single) t = t - t;
                             Io<TX>::store1(dx + gi, t);
                         }
@@ -843,28 +873,28 @@ hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArg
 }
 
 hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, const float* mean,
-                             const float* rstd, const float* gamma, float* dgamma, float* dbeta,
-                             const KArgs& a, Workspace ws, hipStream_t st)
+                             const float* rstd, const float* gamma, const float* beta, float* dgamma,
+                             float* dbeta, const KArgs& a, Workspace ws, hipStream_t st)
 {
     const dim3 g1 = grid_of(a.jobs), b1(unsigned(a.block));
     hipError_t e;
     if (xdt == kBF16 && dydt == kBF16)
         e = launch(bwd_reduce_kernel<uint16_t, uint16_t>, g1, b1, st, cp<uint16_t>(dy),
-                   cp<uint16_t>(x), mean, rstd, a, ws.part);
+                   cp<uint16_t>(x), mean, rstd, gamma, beta, a, ws.part);
     else if (xdt == kBF16)
         e = launch(bwd_reduce_kernel<uint16_t, float>, g1, b1, st, cp<float>(dy), cp<uint16_t>(x),
-                   mean, rstd, a, ws.part);
+                   mean, rstd, gamma, beta, a, ws.part);
     else if (dydt == kBF16)
         e = launch(bwd_reduce_kernel<float, uint16_t>, g1, b1, st, cp<uint16_t>(dy), cp<float>(x),
-                   mean, rstd, a, ws.part);
+                   mean, rstd, gamma, beta, a, ws.part);
     else
         e = launch(bwd_reduce_kernel<float, float>, g1, b1, st, cp<float>(dy), cp<float>(x), mean,
-                   rstd, a, ws.part);
+                   rstd, gamma, beta, a, ws.part);
     if (e != hipSuccess) return e;
     const int64_t ngroups = a.N * a.G;
     const int64_t nchan = (dgamma || dbeta) ? a.C : 0;
     return launch(fin_bwd_kernel, dim3(unsigned(ngroups + nchan)), dim3(256), st, mean, rstd, gamma,
-                  static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coef, dgamma, dbeta);
+                  beta, static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coef, dgamma, dbeta);
 }
 
 hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,

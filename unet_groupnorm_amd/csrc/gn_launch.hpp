@@ -20,11 +20,13 @@ struct KArgs {
     int64_t chunk, K, jobs, P;        // reduction jobs
     int64_t chunk_a, K_a, jobs_a;     // streaming jobs
     int32_t block, block_a;
+    int32_t act;                      // 0: none, 1: relu after the affine
 };
 
-inline KArgs kargs_of(const Plan& p)
+inline KArgs kargs_of(const Plan& p, int act = 0)
 {
     KArgs a;
+    a.act = act;
     a.N = p.N; a.C = p.C; a.S = p.S; a.G = p.G;
     a.Cg = p.Cg; a.M = p.M;
     a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs; a.P = p.P;
@@ -34,7 +36,7 @@ inline KArgs kargs_of(const Plan& p)
 }
 
 // Workspace views. The partials area holds one float2 per reduction job; the coefficient
-// area one float4 per row, written by a finalize kernel and read by the streaming kernel.
+// area two float4 per row, written by a finalize kernel and read by the streaming kernel.
 struct Workspace {
     float2* part;
     float4* coef;
@@ -57,8 +59,8 @@ hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArg
 // Backward, first half: per-job sums of dy and dy*xhat, then their fixed-order merge into
 // dgamma/dbeta and the per-row dx coefficients.
 hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, const float* mean,
-                             const float* rstd, const float* gamma, float* dgamma, float* dbeta,
-                             const KArgs& a, Workspace ws, hipStream_t st);
+                             const float* rstd, const float* gamma, const float* beta, float* dgamma,
+                             float* dbeta, const KArgs& a, Workspace ws, hipStream_t st);
 // Backward, second half: dx from x, dy and the per-row coefficients.
 hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,
                             const KArgs& a, Workspace ws, hipStream_t st);

@@ -66,7 +66,7 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     q.jobs_a = q.rows * q.K_a;
 
     q.ws_coef_offset = size_t(round_up(q.jobs * 8, 256));
-    q.ws_bytes = q.ws_coef_offset + size_t(round_up(q.rows * 16, 256));
+    q.ws_bytes = q.ws_coef_offset + size_t(round_up(q.rows * 32, 256));
     *p = q;
     return 0;
 }

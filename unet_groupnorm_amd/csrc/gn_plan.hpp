@@ -61,7 +61,7 @@ struct Plan {
     int64_t K_a = 0;
     int64_t jobs_a = 0;
     int block_a = 0;
-    // workspace: [partials: float2 * jobs][row coefficients: float4 * rows], 256-byte aligned
+    // workspace: [partials: float2 * jobs][row coefficients: 2 float4 * rows], 256-byte aligned
     size_t ws_coef_offset = 0;
     size_t ws_bytes = 0;
 };

@@ -11,9 +11,10 @@ import ctypes
 
 import torch
 
-from ._lib import GN_BF16, GN_F32, GN_OK, STATUS_NAMES, GnPlanInfo, lib
+from ._lib import GN_ACT_NONE, GN_ACT_RELU, GN_BF16, GN_F32, GN_OK, STATUS_NAMES, GnPlanInfo, lib
 
 _DT = {torch.float32: GN_F32, torch.bfloat16: GN_BF16}
+_ACT = {None: GN_ACT_NONE, "none": GN_ACT_NONE, "relu": GN_ACT_RELU}
 
 
 class GnError(RuntimeError):
@@ -36,6 +37,13 @@ def _dims(x, G):
     for d in x.shape[2:]:
         S *= int(d)
     return N, C, S, int(G)
+
+
+def _act(activation):
+    try:
+        return _ACT[activation]
+    except KeyError:
+        raise ValueError(f"unsupported activation {activation!r} (None or 'relu')") from None
 
 
 def _dtype(t):
@@ -88,9 +96,10 @@ def workspace_for(x, G):
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
-def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, workspace=None, out=None,
-               mean=None, rstd=None):
-    """Returns (y, mean, rstd). y has out_dtype (default: x.dtype); mean/rstd are [N, G] fp32."""
+def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, activation=None, workspace=None,
+               out=None, mean=None, rstd=None):
+    """Returns (y, mean, rstd). y has out_dtype (default: x.dtype); mean/rstd are [N, G] fp32.
+    activation: None or "relu" (applied in fp32 before the single narrowing store)."""
     _contig("x", x)
     N, C, S, G = _dims(x, G)
     dev = x.device
@@ -101,8 +110,8 @@ def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, workspace=None, o
     ws = workspace if workspace is not None else workspace_for(x, G)
     _check("gn_forward", lib.gn_forward(
         _ptr(x), _dtype(x), _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
-        N, C, S, G, float(eps), _ptr(_contig("y", y)), _dtype(y), _ptr(mean), _ptr(rstd),
-        _ptr(ws), ws.numel(), _stream(dev)))
+        N, C, S, G, float(eps), _act(activation), _ptr(_contig("y", y)), _dtype(y), _ptr(mean),
+        _ptr(rstd), _ptr(ws), ws.numel(), _stream(dev)))
     return y, mean, rstd
 
 
@@ -117,18 +126,19 @@ def gn_forward_stats(x, gamma, beta, G, eps, mean, rstd, workspace):
         _stream(dev)))
 
 
-def gn_forward_apply(x, G, y, workspace):
+def gn_forward_apply(x, G, y, workspace, activation=None):
     """Second half of gn_forward: y from x and the workspace coefficients."""
     _contig("x", x)
     N, C, S, G = _dims(x, G)
     _check("gn_forward_apply", lib.gn_forward_apply(
-        _ptr(x), _dtype(x), N, C, S, G, _ptr(_contig("y", y)), _dtype(y), _ptr(workspace),
-        workspace.numel(), _stream(x.device)))
+        _ptr(x), _dtype(x), N, C, S, G, _act(activation), _ptr(_contig("y", y)), _dtype(y),
+        _ptr(workspace), workspace.numel(), _stream(x.device)))
 
 
-def gn_backward(dy, x, mean, rstd, gamma, G, *, need_dx=True, need_dgamma=True, need_dbeta=True,
-                workspace=None, dx=None, dgamma=None, dbeta=None):
-    """Returns (dx or None, dgamma or None, dbeta or None); dx has x's dtype."""
+def gn_backward(dy, x, mean, rstd, gamma, G, *, beta=None, activation=None, need_dx=True,
+                need_dgamma=True, need_dbeta=True, workspace=None, dx=None, dgamma=None, dbeta=None):
+    """Returns (dx or None, dgamma or None, dbeta or None); dx has x's dtype. With
+    activation="relu", dy is the gradient of relu(GroupNorm(x)) and beta is needed."""
     _contig("x", x); _contig("dy", dy)
     if dy.shape != x.shape:
         raise ValueError("dy must have x's shape")
@@ -143,13 +153,15 @@ def gn_backward(dy, x, mean, rstd, gamma, G, *, need_dx=True, need_dgamma=True, 
     ws = workspace if workspace is not None else workspace_for(x, G)
     _check("gn_backward", lib.gn_backward(
         _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), N, C, S, G,
+        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
+        N, C, S, G,
         _ptr(dx if need_dx else None), _ptr(dgamma if need_dgamma else None),
         _ptr(dbeta if need_dbeta else None), _ptr(ws), ws.numel(), _stream(dev)))
     return (dx if need_dx else None, dgamma if need_dgamma else None, dbeta if need_dbeta else None)
 
 
-def gn_backward_reduce(dy, x, mean, rstd, gamma, G, dgamma, dbeta, workspace):
+def gn_backward_reduce(dy, x, mean, rstd, gamma, G, dgamma, dbeta, workspace, beta=None,
+                       activation=None):
     """First half of gn_backward: dgamma/dbeta (either may be None), coefficients left in
     the workspace."""
     _contig("x", x); _contig("dy", dy)
@@ -157,17 +169,17 @@ def gn_backward_reduce(dy, x, mean, rstd, gamma, G, dgamma, dbeta, workspace):
     dev = x.device
     _check("gn_backward_reduce", lib.gn_backward_reduce(
         _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), N, C, S, G, _ptr(dgamma), _ptr(dbeta),
-        _ptr(workspace), workspace.numel(), _stream(dev)))
+        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
+        N, C, S, G, _ptr(dgamma), _ptr(dbeta), _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
-def gn_backward_apply(dy, x, G, dx, workspace):
+def gn_backward_apply(dy, x, G, dx, workspace, activation=None):
     """Second half of gn_backward: dx from x, dy and the workspace coefficients."""
     _contig("x", x); _contig("dy", dy)
     N, C, S, G = _dims(x, G)
     _check("gn_backward_apply", lib.gn_backward_apply(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), N, C, S, G, _ptr(dx), _ptr(workspace),
-        workspace.numel(), _stream(x.device)))
+        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), N, C, S, G, _act(activation), _ptr(dx),
+        _ptr(workspace), workspace.numel(), _stream(x.device)))
 
 
 class GroupNormFn(torch.autograd.Function):
@@ -179,25 +191,27 @@ class GroupNormFn(torch.autograd.Function):
     """
 
     @staticmethod
-    def forward(ctx, x, gamma, beta, G, eps, out_dtype):
+    def forward(ctx, x, gamma, beta, G, eps, out_dtype, activation=None):
         x = x.contiguous()
-        y, mean, rstd = gn_forward(x, gamma, beta, G, eps, out_dtype)
-        ctx.save_for_backward(x, mean, rstd, gamma)
+        y, mean, rstd = gn_forward(x, gamma, beta, G, eps, out_dtype, activation=activation)
+        ctx.save_for_backward(x, mean, rstd, gamma, beta)
         ctx.G = G
+        ctx.activation = activation
         ctx.mark_non_differentiable(mean, rstd)
         return y, mean, rstd
 
     @staticmethod
     def backward(ctx, dy, _dmean, _drstd):
-        x, mean, rstd, gamma = ctx.saved_tensors
+        x, mean, rstd, gamma, beta = ctx.saved_tensors
         need = ctx.needs_input_grad
         dx, dgamma, dbeta = gn_backward(
-            dy.contiguous(), x, mean, rstd, gamma, ctx.G,
+            dy.contiguous(), x, mean, rstd, gamma, ctx.G, beta=beta, activation=ctx.activation,
             need_dx=need[0], need_dgamma=gamma is not None and need[1], need_dbeta=need[2])
-        return dx, dgamma, dbeta, None, None, None
+        return dx, dgamma, dbeta, None, None, None, None
 
 
-def group_norm(x, num_groups, weight=None, bias=None, eps=1e-5, out_dtype=None):
-    """GroupNorm over NC* input; returns y only (out_dtype defaults to x.dtype)."""
-    y, _, _ = GroupNormFn.apply(x, weight, bias, num_groups, eps, out_dtype)
+def group_norm(x, num_groups, weight=None, bias=None, eps=1e-5, out_dtype=None, activation=None):
+    """GroupNorm over NC* input, optionally followed by a fused relu; returns y only
+    (out_dtype defaults to x.dtype)."""
+    y, _, _ = GroupNormFn.apply(x, weight, bias, num_groups, eps, out_dtype, activation)
     return y
