@@ -194,10 +194,33 @@ def census(steps=10, warmup=3):
             for a, b in zip(ref, (r.y, r.mean, r.rstd, r.dx, r.dgamma, r.dbeta)):
                 identical &= bool(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)))
+    # one site of each distinct shape on its own: fwd+bwd microseconds and method-byte rate
+    per_shape = {}
+    for r in runs:
+        key = f"c{r.case.C}_g{r.case.G}_{r.case.spatial[0]}cube"
+        if key in per_shape:
+            continue
+        sms, _ = r.timed_steps(max(steps, 20), warmup)
+        per_shape[key] = {"us_per_step": round(sms * 1e3, 2),
+                          "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1)}
     return {"sites": len(runs), "elements": sum(r.case.numel for r in runs), "ms_per_pass": round(ms, 4),
             "value": round(total / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "pct_of_peak": round(100 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
-            "bitwise_identical_10_repeats": identical}
+            "bitwise_identical_10_repeats": identical, "per_shape": per_shape}
+
+
+def small_configs(steps=50, warmup=10):
+    """The launch-bound configurations, timed as fwd+bwd microseconds per step."""
+    import workloads
+    out = {}
+    for case in (workloads.TINY, workloads.DEEP, workloads.DEEP_F32OUT):
+        r = Runner(case)
+        sms, _ = r.timed_steps(steps, warmup)
+        out[case.name] = {"us_per_step": round(sms * 1e3, 2),
+                          "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1),
+                          "bytes_per_step": r.step_bytes}
+        del r
+    return out
 
 
 def copy_ceiling_gbps(nbytes=1 << 30, reps=20):
@@ -374,6 +397,8 @@ def main():
         torch.cuda.empty_cache()
         log("census: 18 GroupNorm sites of a scale-7 UNet")
         out["census"] = census()
+        log("small configurations (tiny, deep)")
+        out["small_configs"] = small_configs()
     print(json.dumps(out), flush=True)
 
 

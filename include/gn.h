@@ -197,6 +197,13 @@ typedef struct gn_plan_info {
     int32_t apply_block;          /* threads per streaming workgroup */
     int32_t apply_vectors;        /* 8-element vectors each streaming thread moves */
     size_t workspace_bytes;       /* == gn_workspace_bytes */
+    /* Resident path (S a multiple of 8 and a small enough group): the forward runs one
+     * workgroup per group (n, g), the backward one per g covering all N samples; each
+     * holds its elements in registers from the single read to the write. */
+    int32_t resident_forward;     /* 1 if the forward takes the resident path */
+    int32_t resident_backward;    /* 1 if the backward takes the resident path */
+    int32_t resident_block_forward, resident_vectors_forward;    /* threads, vectors per thread */
+    int32_t resident_block_backward, resident_vectors_backward;
 } gn_plan_info;
 
 /* Fills *out for a valid shape and returns GN_OK; otherwise returns the shape error. */

@@ -35,7 +35,7 @@ def test_status_enum_matches_header():
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == 3
+    assert lib.gn_abi_version() == 4
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every
@@ -103,3 +103,25 @@ def test_split_phase_validation():
                                  1 << 20, None) == 7
     assert lib.gn_backward_apply(A, GN_BF16, B, GN_BF16, 1, 8, 64, 4, 2, ctypes.c_void_p(0x30000), A,
                                  1 << 20, None) == 10
+
+
+def test_plan_info_struct_matches_header():
+    """The ctypes mirror of gn_plan_info has the header's fields, in order, with the same
+    widths (a drift here would make gn_plan_query write past the Python structure)."""
+    import pathlib
+
+    from unet_groupnorm_amd._lib import GnPlanInfo
+    text = (pathlib.Path(__file__).resolve().parents[1] / "include" / "gn.h").read_text()
+    body = re.search(r"typedef struct gn_plan_info \{(.*?)\} gn_plan_info;", text, re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        ctype, names = decl.split(None, 1)
+        for nm in names.split(","):
+            fields.append((nm.strip(), ctype))
+    width = {"int64_t": 8, "int32_t": 4, "size_t": 8}
+    ours = [(nm, ctypes.sizeof(t)) for nm, t in GnPlanInfo._fields_]
+    assert ours == [(nm, width[t]) for nm, t in fields]

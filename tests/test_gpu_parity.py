@@ -170,7 +170,8 @@ def test_unet_top_sites_sampled(case):
 # ----------------------------------------------------------------------------- closed forms on the GPU
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("shape,G", [((2, 6, 9, 10, 11), 3), ((1, 32, 128, 128, 128), 8)])
+@pytest.mark.parametrize("shape,G", [((2, 6, 9, 10, 11), 3), ((1, 32, 128, 128, 128), 8),
+                                     ((2, 8, 8, 8, 8), 4)])
 def test_constant_input_gives_beta_bitwise(dtype, shape, G):
     say(f"constant input {shape} {dtype}")
     N, C = shape[:2]
@@ -216,11 +217,13 @@ def test_nan_and_inf_confined_to_their_group():
     full_check(inp, "nan_inf")
 
 
-def test_large_mean_offset_keeps_variance():
-    """fp32 input at mu/sigma = 1e5, where E[x^2] - E[x]^2 loses the variance."""
-    say("mu/sigma = 1e5, fp32, (1, 4, 32, 32, 32), G=2")
+@pytest.mark.parametrize("spatial", [(32, 32, 32), (16, 16, 16)])
+def test_large_mean_offset_keeps_variance(spatial):
+    """fp32 input at mu/sigma = 1e5, where E[x^2] - E[x]^2 loses the variance (two-pass
+    kernels at 32^3, the resident path at 16^3)."""
+    say(f"mu/sigma = 1e5, fp32, (1, 4, {spatial}), G=2")
     rng = np.random.default_rng(7)
-    x = (1e5 + rng.normal(size=(1, 4, 32, 32, 32))).astype(np.float32)
+    x = (1e5 + rng.normal(size=(1, 4) + spatial)).astype(np.float32)
     xt = torch.from_numpy(x).to(DEV)
     y, mean, rstd = gn.gn_forward(xt, None, None, 2, 1e-5)
     torch.cuda.synchronize()
@@ -283,8 +286,8 @@ def test_repeats_are_bitwise_identical_with_poisoned_workspace(case):
                 assert torch.equal(u, v), f"repeat {i} differs"
 
 
-def test_split_phase_entry_points_match_fused():
-    case = workloads.SCALE7
+@pytest.mark.parametrize("case", [workloads.SCALE7, workloads.DEEP], ids=lambda c: c.name)
+def test_split_phase_entry_points_match_fused(case):
     say(f"{case.name}: split-phase entry points vs gn_forward/gn_backward")
     inp = workloads.make(case, DEV)
     x, G, gamma, beta = inp["x"], inp["G"], inp["gamma"], inp["beta"]
@@ -382,6 +385,33 @@ def test_binding_rejects_bad_arguments():
         gn.gn_forward(x.cpu().pin_memory(), None, None, 2, out=torch.empty_like(x),
                       mean=torch.empty(1, 2, device=DEV), rstd=torch.empty(1, 2, device=DEV),
                       workspace=gn.workspace_for(x, 2))
+
+
+# ----------------------------------------------------------------------------- resident path
+
+RESIDENT = [
+    # (case, forward resident, backward resident)
+    (workloads.custom(1, 16, 2, (16, 16, 16), torch.bfloat16, dist="unet", seed=41), True, True),   # M = 32768, the limit
+    (workloads.custom(1, 16, 2, (8, 9, 57), torch.bfloat16, dist="unet", seed=42), False, False),   # M = 32832, just past it
+    (workloads.custom(8, 8, 2, (8, 8, 16), torch.bfloat16, dist="normal", seed=43), True, True),    # N*M = 32768
+    (workloads.custom(9, 8, 2, (8, 8, 16), torch.float32, dist="normal", seed=44), True, False),    # N*M past the limit
+    (workloads.custom(3, 10, 2, (2, 3, 4), torch.bfloat16, dist="unet", seed=45), True, True),      # 15 vectors a group
+    (workloads.custom(2, 64, 1, (2, 2, 2), torch.float32, dist="tiny", seed=46), True, True),       # one vector per row
+    (workloads.custom(2, 16, 16, (2, 2, 2), torch.bfloat16, dist="deep", seed=47, out_dtype=torch.float32), True, True),
+    (workloads.custom(3, 12, 4, (4, 4, 6), torch.bfloat16, torch.float32, dist="deep", seed=48), True, True),
+]
+
+
+@pytest.mark.parametrize("case,rf,rb", RESIDENT, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_resident_shapes_elementwise(case, rf, rb):
+    p = gn.gn_plan_query(case.N, case.C, case.numel // (case.N * case.C), case.G)
+    assert (bool(p["resident_forward"]), bool(p["resident_backward"])) == (rf, rb)
+    full_check(workloads.make(case, "cpu"), case.name)
+
+
+@pytest.mark.parametrize("case,rf,rb", RESIDENT[:5], ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_resident_shapes_relu(case, rf, rb):
+    full_check(workloads.make(case, "cpu"), case.name + "_relu", relu=True)
 
 
 # ----------------------------------------------------------------------------- fused relu

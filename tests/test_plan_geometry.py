@@ -150,3 +150,89 @@ def test_plan_is_a_pure_function_of_shape():
     first = {s: g.gn_plan_query(*s) for s in shapes if s[1] % s[3] == 0 and s[0] * (s[1] // s[3]) * s[2] > 1}
     for s in reversed(list(first)):
         assert g.gn_plan_query(*s) == first[s]
+
+
+# ----------------------------------------------------------------------------- resident path
+
+RES_MAX_VECS = 4096  # 1024 threads x 4 vectors: the register capacity of one workgroup
+
+RES_SHAPES = [
+    (1, 8, 4096, 4), (4, 512, 512, 32), (1, 256, 16 ** 3, 32), (1, 512, 8 ** 3, 32),
+    (1, 16, 4096, 2), (1, 16, 4104, 2), (8, 8, 1024, 2), (9, 8, 1024, 2), (3, 10, 24, 2),
+    (2, 64, 8, 1), (2, 16, 8, 16), (2, 8, 216, 4), (1, 32, 128 ** 3, 8), (2, 6, 105, 2),
+    (4096, 2, 8, 2), (4097, 2, 8, 2), (1, 4096, 8, 1), (2, 4, 1, 4), (70000, 1, 8, 1),
+]
+
+
+def test_fastdiv_is_exact_where_used():
+    """The resident kernels divide in-workgroup indices (< 4096) by S/8, M/8 or C/G
+    (<= 4096) as (x * m) >> 32 with m = floor(2^32 / d) + 1; exact for every x < 2^16
+    and d <= 4096, and for sampled divisors up to 2^16."""
+    x = np.arange(1 << 16, dtype=np.uint64)
+    divisors = list(range(1, 4097)) + list(np.random.default_rng(5).integers(4097, 65537, 200))
+    for d in divisors:
+        m = np.uint64((1 << 32) // int(d) + 1)
+        assert np.array_equal((x * m) >> np.uint64(32), x // np.uint64(d)), d
+
+
+def _res_expect(N, C, S, G):
+    M = C // G * S
+    ok = S % VEC == 0 and G <= 2 ** 30
+    f = ok and M // VEC <= RES_MAX_VECS and N <= 65535   # forward grid (G, N)
+    b = ok and N * (M // VEC) <= RES_MAX_VECS
+    return f, b
+
+
+def _check_res_shape(nv, block, vecs):
+    assert vecs in (1, 2, 4) and block % 64 == 0 and 64 <= block <= 1024
+    assert block * vecs >= nv, "every vector has a lane"
+    if vecs > 1:
+        assert nv > 1024 * (vecs // 2), "no more vectors per lane than needed"
+
+
+@pytest.mark.parametrize("N,C,S,G", RES_SHAPES)
+def test_resident_choice_and_shape(N, C, S, G):
+    p = g.gn_plan_query(N, C, S, G)
+    ef, eb = _res_expect(N, C, S, G)
+    assert bool(p["resident_forward"]) == ef and bool(p["resident_backward"]) == eb
+    M = C // G * S
+    if ef:
+        _check_res_shape(M // VEC, p["resident_block_forward"], p["resident_vectors_forward"])
+    if eb:
+        _check_res_shape(N * M // VEC, p["resident_block_backward"], p["resident_vectors_backward"])
+
+
+@pytest.mark.parametrize("N,C,S,G", [s for s in RES_SHAPES if s[0] * s[1] * s[2] <= 2 ** 22])
+def test_resident_workgroups_cover_every_element_once_and_stay_in_bounds(N, C, S, G):
+    """Restates the lane -> vector -> (sample, row, address) arithmetic of res_fwd_kernel
+    and res_bwd_kernel and checks it against the volume and the LDS arrays."""
+    p = g.gn_plan_query(N, C, S, G)
+    Cg, M = C // G, C // G * S
+    total = N * C * S
+    if p["resident_forward"]:
+        B, V = p["resident_block_forward"], p["resident_vectors_forward"]
+        vg, W = M // VEC, S // VEC
+        seen = np.zeros(total // VEC, dtype=np.int32)
+        w = (np.arange(V)[:, None] * B + np.arange(B)[None, :]).reshape(-1)
+        w = w[w < vg]
+        for ng in range(N * G):
+            n, gg = divmod(ng, G)
+            vb = (n * C + gg * Cg) * W
+            assert 0 <= (w // W).max() < Cg
+            np.add.at(seen, vb + w, 1)
+        assert (seen == 1).all()
+    if p["resident_backward"]:
+        B, V = p["resident_block_backward"], p["resident_vectors_backward"]
+        vg, W = M // VEC, S // VEC
+        nvt, nrows = N * vg, N * Cg
+        assert nvt <= RES_MAX_VECS and nrows <= RES_MAX_VECS and N <= RES_MAX_VECS
+        seen = np.zeros(total // VEC, dtype=np.int32)
+        w = (np.arange(V)[:, None] * B + np.arange(B)[None, :]).reshape(-1)
+        w = w[w < nvt]
+        n, r = w // vg, w % vg
+        # per-vector sums sit at s_v[w]; row rho = n*Cg + r//W covers s_v[rho*W, (rho+1)*W)
+        assert ((n * Cg + r // W) * W + r % W == w).all()
+        for gg in range(G):
+            gv = (n * C + gg * Cg) * W + r
+            np.add.at(seen, gv, 1)
+        assert (seen == 1).all()

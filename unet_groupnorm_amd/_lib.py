@@ -35,6 +35,12 @@ class GnPlanInfo(ctypes.Structure):
         ("apply_block", ctypes.c_int32),
         ("apply_vectors", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("resident_forward", ctypes.c_int32),
+        ("resident_backward", ctypes.c_int32),
+        ("resident_block_forward", ctypes.c_int32),
+        ("resident_vectors_forward", ctypes.c_int32),
+        ("resident_block_backward", ctypes.c_int32),
+        ("resident_vectors_backward", ctypes.c_int32),
     ]
 
 

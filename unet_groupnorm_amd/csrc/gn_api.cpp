@@ -133,10 +133,16 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     out->apply_block = p.block_a;
     out->apply_vectors = gn::kApplyVecs;
     out->workspace_bytes = p.ws_bytes;
+    out->resident_forward = p.res_fwd ? 1 : 0;
+    out->resident_backward = p.res_bwd ? 1 : 0;
+    out->resident_block_forward = p.res_block_f;
+    out->resident_vectors_forward = p.res_vecs_f;
+    out->resident_block_backward = p.res_block_b;
+    out->resident_vectors_backward = p.res_vecs_b;
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 3; }
+int gn_abi_version(void) { return 4; }
 
 const char* gn_status_string(int status)
 {
@@ -173,9 +179,13 @@ int gn_forward_stats(const void* x, int x_dtype, const float* gamma, const float
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
-    return launch_status(gn::launch_fwd_stats(x, x_dtype, gamma, beta, eps, mean, rstd,
-                                              gn::kargs_of(p), gn::workspace_of(workspace, p),
-                                              static_cast<hipStream_t>(stream)));
+    const gn::KArgs a = gn::kargs_of(p);
+    const gn::Workspace w = gn::workspace_of(workspace, p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.res_fwd)
+        return launch_status(gn::launch_res_fwd(x, x_dtype, gamma, beta, eps, mean, rstd, nullptr, x_dtype,
+                                                a, w, st, p.res_block_f, p.res_vecs_f));
+    return launch_status(gn::launch_fwd_stats(x, x_dtype, gamma, beta, eps, mean, rstd, a, w, st));
 }
 
 int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
@@ -211,6 +221,9 @@ int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta
     const gn::KArgs a = gn::kargs_of(p, activation);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.res_fwd)
+        return launch_status(gn::launch_res_fwd(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype, a, w,
+                                                st, p.res_block_f, p.res_vecs_f));
     if ((rc = launch_status(gn::launch_fwd_stats(x, x_dtype, gamma, beta, eps, mean, rstd, a, w, st))))
         return rc;
     return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, a, w, st));
@@ -229,10 +242,14 @@ int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p, activation);
+    const gn::Workspace w = gn::workspace_of(workspace, p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.res_bwd)
+        return launch_status(gn::launch_res_bwd(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
+                                                dbeta, nullptr, a, w, st, p.res_block_b, p.res_vecs_b));
     return launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta,
-                                               dgamma, dbeta, gn::kargs_of(p, activation),
-                                               gn::workspace_of(workspace, p),
-                                               static_cast<hipStream_t>(stream)));
+                                               dgamma, dbeta, a, w, st));
 }
 
 int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
@@ -270,6 +287,9 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
     const gn::KArgs a = gn::kargs_of(p, activation);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.res_bwd)
+        return launch_status(gn::launch_res_bwd(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
+                                                dbeta, dx, a, w, st, p.res_block_b, p.res_vecs_b));
     if ((rc = launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta,
                                                   dgamma, dbeta, a, w, st))))
         return rc;

@@ -1,6 +1,6 @@
 // gn_kernels.hip -- GroupNorm forward/backward kernels for gfx950 (MI355X, CDNA4).
 //
-// Six kernels, three per direction:
+// Two kernel sets. The two-pass set, three kernels per direction:
 //   stats_kernel       per reduction job: (mean, M2) of x                   [read x]
 //   fin_fwd_kernel     per group: fixed-order merge -> mean, rstd, and per-row
 //                      normalize coefficients                               [tiny]
@@ -9,6 +9,9 @@
 //   fin_bwd_kernel     per group: c1, c2 -> per-row dx coefficients; per
 //                      channel: dgamma, dbeta                                [tiny]
 //   bwd_apply_kernel   per streaming job: dx                                [read x, dy, write dx]
+// and the resident set for small groups, one kernel per direction (see "resident path"):
+//   res_fwd_kernel     per group: statistics and y from registers           [read x, write y]
+//   res_bwd_kernel     per g over all samples: sums, dgamma/dbeta, dx       [read x, dy, write dx]
 //
 // The pages fold the finalize into the elementwise kernels ("Optimize GroupNorm",
 // LBANN/ScaFFold pull 93, paragraph folding seven launches into four) and cap the
@@ -816,6 +819,266 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
     }
 }
 
+// ------------------------------------------------------------------ resident path
+//
+// Groups whose rows are whole 8-element vectors and that fit in one workgroup (at most
+// kResMaxVecs vectors) are held in registers by one workgroup from the single read to the
+// write. The forward reads x once instead of twice, and each direction is one launch
+// instead of three; at the 8^3-16^3 sites of a UNet's deep levels the launches, about 5 us
+// each on MI355X, and not the bytes, are the cost. Lane t owns vectors t, t + B, t + 2B, ...
+// of the workgroup's range (B threads, V vectors each), counted in elements as above, so
+// fp32 and bf16 data reduce in the same order. The statistics are an exact two-pass over
+// the registers (mean of x - K, then the corrected sum of squared deviations), relative
+// to the group's shift K as in the two-pass kernels.
+
+constexpr int kResMaxWaves = kResMaxBlock / 64;
+
+// floor(x / d) for x < 2^16 with the launch's precomputed multiplier for d.
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f)
+{
+    return uint32_t((uint64_t(x) * f.m) >> 32);
+}
+
+// Butterfly sum over the wave; every lane returns the same value (a + b == b + a).
+__device__ __forceinline__ float wave_allsum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off);
+    return v;
+}
+
+// Block-wide sums of a and b; waves are added in wave order and every thread returns
+// the result. s holds 2 * kResMaxWaves floats and may be reused on return.
+__device__ __forceinline__ float2 block_allsum2(float a, float b, float* s)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    a = wave_allsum(a);
+    b = wave_allsum(b);
+    if (lane == 0) { s[wave] = a; s[kResMaxWaves + wave] = b; }
+    __syncthreads();
+    float ra = s[0], rb = s[kResMaxWaves];
+    for (int w = 1; w < nw; ++w) { ra = ra + s[w]; rb = rb + s[kResMaxWaves + w]; }
+    __syncthreads();
+    return make_float2(ra, rb);
+}
+
+// Forward, one workgroup per group: blockIdx.x = g, blockIdx.y = n. Writes mean, rstd, the
+// per-row normalize coefficients (the record fin_fwd_kernel writes, so that
+// gn_forward_apply can follow) and y unless y is null, computed exactly as apply_kernel
+// computes it from those coefficients.
+template <int V, typename TX, typename TY>
+__global__ void __launch_bounds__(kResMaxBlock)
+res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
+               const float* __restrict__ beta, float eps, float* __restrict__ mean_out,
+               float* __restrict__ rstd_out, KArgs a, float4* __restrict__ coef, TY* __restrict__ y)
+{
+    __shared__ float s_red[2 * kResMaxWaves];
+    const int tid = threadIdx.x, blk = blockDim.x;
+    const int vg = int(a.M / kVec);    // vectors per group (<= kResMaxVecs)
+    const float fM = float(a.M);       // exact: M <= 8 * kResMaxVecs
+    const bool act = a.act != 0;
+    const int64_t g = blockIdx.x, n = blockIdx.y, ng = n * a.G + g;
+    const int64_t row0 = n * a.C + g * a.Cg;
+    const int64_t vb = row0 * (a.S / kVec);  // the group's first vector
+    const float K = group_shift(x, a, n, g);
+    float e[V * kVec];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int w = u * blk + tid;
+        float v[kVec];
+        if (w < vg) {
+            Io<TX>::template load8<kNtApply>(x + (vb + w) * kVec, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) v[i] = K;  // contributes exact zeros below
+        }
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) e[u * kVec + i] = v[i];
+    }
+    float t[V * kVec];
+#pragma unroll
+    for (int i = 0; i < V * kVec; ++i) t[i] = e[i] - K;
+    const float m = block_allsum2(tree_sum(t), 0.0f, s_red).x / fM;
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const bool ok = u * blk + tid < vg;
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) t[u * kVec + i] = ok ? (e[u * kVec + i] - K) - m : 0.0f;
+    }
+    const float2 r = block_allsum2(tree_sum(t), tree_sumsq(t), s_red);
+    float var = (r.y - (r.x * r.x) / fM) / fM;
+    var = (var < 0.0f) ? 0.0f : var;  // NaN passes through
+    const float rstd = 1.0f / __fsqrt_rn(var + eps);
+    const float hi = K + m;
+    const float lo = (K - hi) + m;
+    if (tid == 0) {
+        mean_out[ng] = hi;
+        rstd_out[ng] = rstd;
+    }
+    for (int i = tid; i < int(a.Cg); i += blk) {
+        const int64_t c = g * a.Cg + i;
+        coef[2 * (row0 + i)] = make_float4(hi, lo, (gamma ? gamma[c] : 1.0f) * rstd, beta ? beta[c] : 0.0f);
+    }
+    if (y) {
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int w = u * blk + tid;
+            if (w < vg) {
+                const int64_t c = g * a.Cg + fdiv(uint32_t(w), a.div_W);
+                const float scale = (gamma ? gamma[c] : 1.0f) * rstd;
+                const float shift = beta ? beta[c] : 0.0f;
+                float o[kVec];
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) {
+                    const float v = fmaf((e[u * kVec + i] - hi) - lo, scale, shift);
+                    o[i] = act ? relu_f(v) : v;
+                }
+                Io<TY>::store8(y + (vb + w) * kVec, o);
+            }
+        }
+    }
+}
+
+// Backward, one workgroup per g covering the groups (n, g) of all N samples, vector w of
+// the workgroup being vector w mod (M/8) of sample w / (M/8), so that row rho = w / (S/8)
+// of the workgroup is row (n, c) = (rho / (C/G), g*C/G + rho mod (C/G)). Per vector: sum g
+// and sum g*(x - mean) (g = dy, or dy gated by the relu) into LDS; per row, in a fixed
+// order: s1 and s2 = rstd * sum g*(x - mean); per sample: c1, c2 and the dx coefficients
+// (the record fin_bwd_kernel writes, for gn_backward_apply); per channel: dgamma and dbeta
+// over the samples in order; then dx unless dx is null, computed exactly as
+// bwd_apply_kernel computes it from those coefficients.
+template <int V, typename TX, typename TD>
+__global__ void __launch_bounds__(kResMaxBlock)
+res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
+               const float* __restrict__ rstd, const float* __restrict__ gamma,
+               const float* __restrict__ beta, KArgs a, float4* __restrict__ coef,
+               float* __restrict__ dgamma, float* __restrict__ dbeta, TX* __restrict__ dx)
+{
+    __shared__ float s_v1[kResMaxVecs], s_v2[kResMaxVecs];  // per vector; later B, E per sample
+    __shared__ float s_r1[kResMaxVecs], s_r2[kResMaxVecs];  // per row, sample-major
+    const int tid = threadIdx.x, blk = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nw = blk >> 6;
+    const int W = int(a.S / kVec), Cg = int(a.Cg), N = int(a.N);
+    const int nvt = N * int(a.M / kVec);  // vectors of the workgroup (<= kResMaxVecs)
+    const int nrows = N * Cg;             // rows of the workgroup
+    const bool act = a.act != 0;
+    const int64_t g = blockIdx.x;
+    // The global vector index of workgroup row rho, and its sample and channel.
+    auto row_base = [&](int rho, int& n, int& c) {
+        n = int(fdiv(uint32_t(rho), a.div_Cg));
+        c = int(g * Cg) + (rho - n * Cg);
+        return (int64_t(n) * a.C + c) * W;
+    };
+    float xs[V * kVec], gs[V * kVec];
+    int rows[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int w = u * blk + tid;
+        rows[u] = -1;
+        if (w < nvt) {
+            const int rho = int(fdiv(uint32_t(w), a.div_W));
+            int n, c;
+            const int64_t gv = row_base(rho, n, c) + (w - rho * W);
+            const int64_t ng = int64_t(n) * a.G + g;
+            float e[kVec], f[kVec], d[kVec], q[kVec];
+            Io<TX>::template load8<kNtBwdApply>(x + gv * kVec, e);
+            Io<TD>::template load8<kNtBwdApply>(dy + gv * kVec, f);
+            const float mu = mean[ng];
+            const float A = rstd[ng] * (gamma ? gamma[c] : 1.0f);
+            const float bt = beta ? beta[c] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                d[i] = e[i] - mu;
+                q[i] = act ? relu_gate(fmaf(d[i], A, bt), f[i]) : f[i];
+                xs[u * kVec + i] = e[i];
+                gs[u * kVec + i] = q[i];
+            }
+            s_v1[w] = tree_sum(q);
+            s_v2[w] = tree_sumprod(q, d);
+            rows[u] = rho;
+        }
+    }
+    __syncthreads();
+    for (int rho = wave; rho < nrows; rho += nw) {
+        float p1 = 0.0f, p2 = 0.0f;
+        for (int k = lane; k < W; k += 64) {
+            p1 = p1 + s_v1[rho * W + k];
+            p2 = p2 + s_v2[rho * W + k];
+        }
+        p1 = wave_allsum(p1);
+        p2 = wave_allsum(p2);
+        if (lane == 0) {
+            const int n = int(fdiv(uint32_t(rho), a.div_Cg));
+            s_r1[rho] = p1;
+            s_r2[rho] = p2 * rstd[int64_t(n) * a.G + g];
+        }
+    }
+    __syncthreads();
+    for (int n = wave; n < N; n += nw) {
+        float t1 = 0.0f, t2 = 0.0f;
+        for (int i = lane; i < Cg; i += 64) {
+            const float gm = gamma ? gamma[g * Cg + i] : 1.0f;
+            t1 = t1 + gm * s_r1[n * Cg + i];
+            t2 = t2 + gm * s_r2[n * Cg + i];
+        }
+        t1 = wave_allsum(t1);
+        t2 = wave_allsum(t2);
+        if (lane == 0) {
+            const float rs = rstd[int64_t(n) * a.G + g];
+            const float c1 = float(double(t1) / double(a.M));
+            const float c2 = float(double(t2) / double(a.M));
+            s_v1[n] = -(rs * c1);
+            s_v2[n] = -((rs * rs) * c2);
+        }
+    }
+    __syncthreads();
+    for (int rho = tid; rho < nrows; rho += blk) {
+        int n, c;
+        (void)row_base(rho, n, c);
+        const int64_t ng = int64_t(n) * a.G + g, row = int64_t(n) * a.C + c;
+        const float gm = gamma ? gamma[c] : 1.0f;
+        coef[2 * row] = make_float4(mean[ng], rstd[ng] * gm, s_v1[n], s_v2[n]);
+        coef[2 * row + 1] = make_float4(beta ? beta[c] : 0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    if (dgamma || dbeta) {
+        for (int i = wave; i < Cg; i += nw) {
+            float q1 = 0.0f, q2 = 0.0f;
+            for (int n = lane; n < N; n += 64) {
+                q1 = q1 + s_r2[n * Cg + i];
+                q2 = q2 + s_r1[n * Cg + i];
+            }
+            q1 = wave_allsum(q1);
+            q2 = wave_allsum(q2);
+            if (lane == 0) {
+                if (dgamma) dgamma[g * Cg + i] = q1;
+                if (dbeta) dbeta[g * Cg + i] = q2;
+            }
+        }
+    }
+    if (dx) {
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int rho = rows[u];
+            if (rho >= 0) {
+                const int w = u * blk + tid;
+                int n, c;
+                const int64_t gv = row_base(rho, n, c) + (w - rho * W);
+                const int64_t ng = int64_t(n) * a.G + g;
+                const float mu = mean[ng];
+                const float A = rstd[ng] * (gamma ? gamma[c] : 1.0f);
+                const float B = s_v1[n], E = s_v2[n];
+                float o[kVec];
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) {
+                    const float d = xs[u * kVec + i] - mu;
+                    o[i] = fmaf(A, gs[u * kVec + i], fmaf(E, d, B));
+                }
+                Io<TX>::store8(dx + gv * kVec, o);
+            }
+        }
+    }
+}
+
 // Launches kernel k and returns the runtime's status for this launch alone.
 template <typename... P, typename... A>
 hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... args)
@@ -913,6 +1176,76 @@ hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, vo
                       cp<float>(x), a, coef, mp<float>(dx));
     return launch(bwd_apply_kernel<float, float>, grid, block, st, cp<float>(dy), cp<float>(x), a,
                   coef, mp<float>(dx));
+}
+
+template <int V, typename TX>
+hipError_t res_fwd_v(const void* x, const float* gamma, const float* beta, float eps, float* mean,
+                     float* rstd, void* y, int ydt, const KArgs& a, Workspace ws, hipStream_t st, int block)
+{
+    const dim3 grid(unsigned(a.G), unsigned(a.N)), blk{unsigned(block)};
+    if (y && ydt == kF32)
+        return launch(res_fwd_kernel<V, TX, float>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd,
+                      a, ws.coef, mp<float>(y));
+    return launch(res_fwd_kernel<V, TX, TX>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd, a,
+                  ws.coef, mp<TX>(y));
+}
+
+template <typename TX>
+hipError_t res_fwd_t(const void* x, const float* gamma, const float* beta, float eps, float* mean,
+                     float* rstd, void* y, int ydt, const KArgs& a, Workspace ws, hipStream_t st,
+                     int block, int vecs)
+{
+    if (vecs == 1) return res_fwd_v<1, TX>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block);
+    if (vecs == 2) return res_fwd_v<2, TX>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block);
+    return res_fwd_v<4, TX>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block);
+}
+
+template <int V, typename TX, typename TD>
+hipError_t res_bwd_v(const void* dy, const void* x, const float* mean, const float* rstd,
+                     const float* gamma, const float* beta, float* dgamma, float* dbeta, void* dx,
+                     const KArgs& a, Workspace ws, hipStream_t st, int block)
+{
+    return launch(res_bwd_kernel<V, TX, TD>, dim3(unsigned(a.G)), dim3(unsigned(block)), st, cp<TD>(dy),
+                  cp<TX>(x), mean, rstd, gamma, beta, a, ws.coef, dgamma, dbeta, mp<TX>(dx));
+}
+
+template <typename TX, typename TD>
+hipError_t res_bwd_t(const void* dy, const void* x, const float* mean, const float* rstd,
+                     const float* gamma, const float* beta, float* dgamma, float* dbeta, void* dx,
+                     const KArgs& a, Workspace ws, hipStream_t st, int block, int vecs)
+{
+    if (vecs == 1)
+        return res_bwd_v<1, TX, TD>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block);
+    if (vecs == 2)
+        return res_bwd_v<2, TX, TD>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block);
+    return res_bwd_v<4, TX, TD>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block);
+}
+
+hipError_t launch_res_fwd(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                          float* mean, float* rstd, void* y, int ydt, const KArgs& a, Workspace ws,
+                          hipStream_t st, int block, int vecs)
+{
+    if (xdt == kBF16)
+        return res_fwd_t<uint16_t>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block, vecs);
+    return res_fwd_t<float>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block, vecs);
+}
+
+hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                          const float* rstd, const float* gamma, const float* beta, float* dgamma,
+                          float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st,
+                          int block, int vecs)
+{
+    if (xdt == kBF16 && dydt == kBF16)
+        return res_bwd_t<uint16_t, uint16_t>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st,
+                                             block, vecs);
+    if (xdt == kBF16)
+        return res_bwd_t<uint16_t, float>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st,
+                                          block, vecs);
+    if (dydt == kBF16)
+        return res_bwd_t<float, uint16_t>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st,
+                                          block, vecs);
+    return res_bwd_t<float, float>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block,
+                                   vecs);
 }
 
 }  // namespace gn

@@ -13,6 +13,19 @@ constexpr int kBF16 = 1;
 // Largest grid launched; kernels stride over any further jobs.
 constexpr int64_t kMaxGrid = int64_t(1) << 30;
 
+// Division by a divisor d fixed for a launch: floor(x / d) = (x * m) >> 32 with
+// m = floor(2^32 / d) + 1, exact for x < 2^16 and d <= 2^16, because the product exceeds
+// x / d by x * (m - 2^32 / d) / 2^32 < 2^-16 <= 1 / d, less than the distance from x / d
+// to the next integer. The resident path's in-workgroup indices stay below 4096.
+struct FastDiv {
+    uint64_t m;
+};
+
+inline FastDiv fastdiv_of(int64_t d)
+{
+    return FastDiv{(d >= 1 && d <= 65536) ? (uint64_t(1) << 32) / uint64_t(d) + 1 : 0};
+}
+
 // Plain-old-data view of a Plan, passed by value to every kernel.
 struct KArgs {
     int64_t N, C, S, G;
@@ -21,6 +34,7 @@ struct KArgs {
     int64_t chunk_a, K_a, jobs_a;     // streaming jobs
     int32_t block, block_a;
     int32_t act;                      // 0: none, 1: relu after the affine
+    FastDiv div_W, div_vg, div_Cg;    // resident path: S/8, M/8 and C/G as divisors
 };
 
 inline KArgs kargs_of(const Plan& p, int act = 0)
@@ -32,6 +46,9 @@ inline KArgs kargs_of(const Plan& p, int act = 0)
     a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs; a.P = p.P;
     a.chunk_a = p.chunk_a; a.K_a = p.K_a; a.jobs_a = p.jobs_a;
     a.block = p.block; a.block_a = p.block_a;
+    a.div_W = fastdiv_of(p.S % kVec == 0 ? p.S / kVec : 0);
+    a.div_vg = fastdiv_of(p.S % kVec == 0 ? p.M / kVec : 0);
+    a.div_Cg = fastdiv_of(p.Cg);
     return a;
 }
 
@@ -64,5 +81,16 @@ hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, c
 // Backward, second half: dx from x, dy and the per-row coefficients.
 hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,
                             const KArgs& a, Workspace ws, hipStream_t st);
+
+// Resident path, forward: statistics, the per-row coefficients, and y unless y is null.
+hipError_t launch_res_fwd(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                          float* mean, float* rstd, void* y, int ydt, const KArgs& a, Workspace ws,
+                          hipStream_t st, int block, int vecs);
+// Resident path, backward: dgamma/dbeta (either may be null), the per-row dx coefficients,
+// and dx unless dx is null.
+hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                          const float* rstd, const float* gamma, const float* beta, float* dgamma,
+                          float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st,
+                          int block, int vecs);
 
 }  // namespace gn

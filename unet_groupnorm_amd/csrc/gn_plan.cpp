@@ -8,6 +8,17 @@ namespace {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// Lane vectors (1, 2 or 4) and threads (a multiple of 64, at most kResMaxBlock) of a
+// resident workgroup covering nv vectors.
+void resident_shape(int64_t nv, int* block, int* vecs)
+{
+    int v = 1;
+    while (v < kResMaxLaneVecs && nv > int64_t(kResMaxBlock) * v) v *= 2;
+    const int64_t b = round_up(ceil_div(nv, v), 64);
+    *vecs = v;
+    *block = int(b < 64 ? 64 : b);
+}
+
 }  // namespace
 
 int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
@@ -64,6 +75,21 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     q.chunk_a = S <= step_a ? S : step_a;
     q.K_a = ceil_div(S, q.chunk_a);
     q.jobs_a = q.rows * q.K_a;
+
+    // Resident path: rows of whole vectors (so every vector lies in one row and every row
+    // starts on a vector) and a workgroup's share within kResMaxVecs.
+    // The forward's grid is (G, N), so N stays within the y extent every device accepts.
+    if (GN_RESIDENT && S % kVec == 0 && G <= (int64_t(1) << 30)) {
+        const int64_t vg = q.M / kVec;
+        if (vg <= kResMaxVecs && N <= 65535) {
+            q.res_fwd = true;
+            resident_shape(vg, &q.res_block_f, &q.res_vecs_f);
+        }
+        if (N <= kResMaxVecs / vg) {
+            q.res_bwd = true;
+            resident_shape(N * vg, &q.res_block_b, &q.res_vecs_b);
+        }
+    }
 
     q.ws_coef_offset = size_t(round_up(q.jobs * 8, 256));
     q.ws_bytes = q.ws_coef_offset + size_t(round_up(q.rows * 32, 256));

@@ -12,6 +12,9 @@
 //   - streaming jobs (normalize, dx): one short step each, so that the grid is large
 //     and every workgroup moves a few KiB and retires. They reduce nothing, so their
 //     shape can change without moving a bit.
+// Small groups whose rows are whole 8-element vectors take the resident path instead: one
+// workgroup holds a group (forward) or a group across all samples (backward) in registers
+// from the single read to the write, one launch per direction.
 //
 // This unit is plain C++ (no HIP), so it is exercised on a host without a GPU.
 #pragma once
@@ -40,6 +43,14 @@ constexpr int kStepVecs = GN_STEP_VECS;
 constexpr int64_t kTargetJobs = GN_TARGET_JOBS;
 // Vectors each lane moves in a streaming job.
 constexpr int kApplyVecs = GN_APPLY_VECS;
+// Resident path: one workgroup holds a whole group in registers (at most kResMaxBlock
+// threads with kResMaxLaneVecs vectors each). GN_RESIDENT=0 turns it off (measurement).
+#ifndef GN_RESIDENT
+#define GN_RESIDENT 1
+#endif
+constexpr int kResMaxBlock = 1024;
+constexpr int kResMaxLaneVecs = 4;
+constexpr int64_t kResMaxVecs = int64_t(kResMaxBlock) * kResMaxLaneVecs;  // 32768 elements
 // Upper bound on a reduction job's element count (in-job counts stay within 32 bits).
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
 // Upper bound on N*C*S accepted (indices stay far from int64 overflow).
@@ -61,6 +72,11 @@ struct Plan {
     int64_t K_a = 0;
     int64_t jobs_a = 0;
     int block_a = 0;
+    // resident path (one workgroup per group; every row a whole number of vectors):
+    // forward per group (n, g), backward per g across all samples
+    bool res_fwd = false, res_bwd = false;
+    int res_block_f = 0, res_vecs_f = 0;   // threads, vectors per lane (1, 2 or 4)
+    int res_block_b = 0, res_vecs_b = 0;
     // workspace: [partials: float2 * jobs][row coefficients: 2 float4 * rows], 256-byte aligned
     size_t ws_coef_offset = 0;
     size_t ws_bytes = 0;

@@ -54,7 +54,8 @@ def _dtype(t):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # ctypes takes a plain int for a c_void_p argument
+    return None if t is None else t.data_ptr()
 
 
 def _contig(name, t):
@@ -63,11 +64,16 @@ def _contig(name, t):
     return t
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(dev):
     # A tensor that is not on a GPU gets the null stream; the library then rejects it.
     if dev.type != "cuda":
         return None
-    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _vec(name, t, C, dev):
