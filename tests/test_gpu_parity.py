@@ -286,6 +286,38 @@ def test_repeats_are_bitwise_identical_with_poisoned_workspace(case):
                 assert torch.equal(u, v), f"repeat {i} differs"
 
 
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_one_workspace_across_shapes():
+    """One workspace, sized for the largest shape and poisoned with NaN before every call,
+    serves fwd/bwd, relu and dx-only calls of several shapes (two-pass and resident);
+    every output equals the one computed with a workspace of its own."""
+    cases = [workloads.SCALE7, workloads.DEEP, RAGGED[3], RAGGED[1], workloads.TINY]
+    big = max(gn.gn_workspace_bytes(c.N, c.C, c.numel // (c.N * c.C), c.G) for c in cases)
+    shared = torch.empty(big, dtype=torch.uint8, device=DEV)
+    for case in cases:
+        say(f"shared workspace: {case.name}")
+        inp = workloads.make(case, DEV)
+        x, G, gamma, beta, dy = inp["x"], inp["G"], inp["gamma"], inp["beta"], inp["dy"]
+        for act in (None, "relu"):
+            ref_f = gn.gn_forward(x, gamma, beta, G, inp["eps"], activation=act)
+            ref_b = gn.gn_backward(dy, x, ref_f[1], ref_f[2], gamma, G, beta=beta, activation=act)
+            shared.fill_(0xFF)
+            got_f = gn.gn_forward(x, gamma, beta, G, inp["eps"], activation=act, workspace=shared)
+            shared.fill_(0xFF)
+            got_b = gn.gn_backward(dy, x, got_f[1], got_f[2], gamma, G, beta=beta, activation=act,
+                                   workspace=shared)
+            shared.fill_(0xFF)
+            dx_only = gn.gn_backward(dy, x, got_f[1], got_f[2], gamma, G, beta=beta, activation=act,
+                                     need_dgamma=False, need_dbeta=False, workspace=shared)[0]
+            torch.cuda.synchronize()
+            for u, v in zip(ref_f + ref_b, got_f + got_b):
+                assert torch.equal(_bits(u), _bits(v))
+            assert torch.equal(_bits(dx_only), _bits(ref_b[0]))
+
+
 @pytest.mark.parametrize("case", [workloads.SCALE7, workloads.DEEP], ids=lambda c: c.name)
 def test_split_phase_entry_points_match_fused(case):
     say(f"{case.name}: split-phase entry points vs gn_forward/gn_backward")
