@@ -34,8 +34,9 @@
  * Layout: NCDHW contiguous; S = D*H*W; group (n, g) is the contiguous run of
  * M = (C/G)*S elements that starts at (n*C + g*C/G)*S.
  *
- * Inputs are decoded exactly to fp64: fp32 and bf16 (the upper half of an fp32)
- * widen exactly; fp64 input is taken as is (used by the finite-difference pins).
+ * Inputs are decoded exactly to fp64: fp32, bf16 (the upper half of an fp32) and fp16
+ * (IEEE binary16) widen exactly; fp64 input is taken as is (used by the
+ * finite-difference pins).
  * gamma/beta are fp32 as the GPU receives them; eps is the fp32 value widened.
  *
  * Parity pins live in tests/test_oracle.py (closed forms, an independent library,
@@ -49,10 +50,32 @@
 #define GNO_F32 0
 #define GNO_BF16 1
 #define GNO_F64 2
+#define GNO_F16 3
+
+/*
+ * IEEE binary16: sign bit, 5 exponent bits with bias 15, 10 fraction bits. Exponent 0
+ * holds zero and the subnormals fraction * 2^-24; exponent 31 holds the infinities
+ * (fraction 0) and NaN; otherwise the value is (1024 + fraction) * 2^(exponent - 25).
+ */
+static double gno_f16_value(uint16_t h)
+{
+    const int e = (h >> 10) & 0x1f, f = h & 0x3ff;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(f + 1024), e - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+void gno_f16_decode_array(const uint16_t* h, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = gno_f16_value(h[i]);
+}
 
 static double gno_load(const void* p, int dt, int64_t i)
 {
     if (dt == GNO_F32) return (double)((const float*)p)[i];
+    if (dt == GNO_F16) return gno_f16_value(((const uint16_t*)p)[i]);
     if (dt == GNO_BF16) {
         uint32_t u = ((uint32_t)((const uint16_t*)p)[i]) << 16;
         float f;
@@ -319,6 +342,40 @@ uint16_t gno_round_bf16(double v)
 void gno_round_bf16_array(const double* v, int64_t n, uint16_t* out)
 {
     for (int64_t i = 0; i < n; ++i) out[i] = gno_round_bf16(v[i]);
+}
+
+/*
+ * Rounding once from fp64 to fp16 (round to nearest, ties to even), straight from the
+ * fp64 value: 11 significant bits, so normal results are multiples of 2^(e-10) for
+ * 2^e <= |v| < 2^(e+1); results below 2^-14 are multiples of 2^-24 (subnormals);
+ * magnitudes that round to 2^16 or more overflow to infinity (the largest finite value
+ * is 65504). NaN becomes the quiet NaN with its sign. Returns the fp16 bit pattern.
+ */
+uint16_t gno_round_f16(double v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00);
+    const double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);            /* 2^(e-1) <= a < 2^e */
+    int q = (e - 1) - 10;    /* quantum exponent for 11 significant bits */
+    if (q < -24) q = -24;    /* subnormal range: fixed quantum 2^-24 */
+    const double k = nearbyint(ldexp(a, -q)); /* exact scaling; default mode rounds ties to even */
+    const double r = ldexp(k, q);
+    if (r >= 65536.0) return (uint16_t)(sign | 0x7C00);
+    if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)ldexp(r, 24)); /* subnormal */
+    int er;
+    const double m = frexp(r, &er);          /* r = m * 2^er, 0.5 <= m < 1 */
+    const int expo = er - 1 + 15;            /* biased exponent of 2^(er-1) */
+    const int frac = (int)ldexp(m, 11) - 1024;
+    return (uint16_t)(sign | (uint16_t)(expo << 10) | (uint16_t)frac);
+}
+
+void gno_round_f16_array(const double* v, int64_t n, uint16_t* out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = gno_round_f16(v[i]);
 }
 
 /* Rounding once from fp64 to fp32: the C conversion rounds to nearest-even. */

@@ -20,7 +20,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libgn_oracle.so")
 
-_TAGS = {"f32": (0, np.float32), "bf16": (1, np.uint16), "f64": (2, np.float64)}
+_TAGS = {"f32": (0, np.float32), "bf16": (1, np.uint16), "f64": (2, np.float64), "f16": (3, np.float16)}
 
 _lib = None
 
@@ -52,6 +52,10 @@ def _load():
     lib.gno_round_bf16.restype = ctypes.c_uint16
     lib.gno_round_bf16_array.argtypes = [P, I64, P]
     lib.gno_round_f32_array.argtypes = [P, I64, P]
+    lib.gno_round_f16.argtypes = [ctypes.c_double]
+    lib.gno_round_f16.restype = ctypes.c_uint16
+    lib.gno_round_f16_array.argtypes = [P, I64, P]
+    lib.gno_f16_decode_array.argtypes = [P, I64, P]
     for fn in ("gno_group_stats", "gno_forward", "gno_forward_at", "gno_backward", "gno_backward_at"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -70,13 +74,15 @@ def _typed(a, tag=None):
                 return a.numpy(), 0
             if a.dtype == torch.float64:
                 return a.numpy(), 2
+            if a.dtype == torch.float16:
+                return a.numpy(), 3
             raise TypeError(f"oracle: unsupported torch dtype {a.dtype}")
     except ImportError:
         pass
     a = np.ascontiguousarray(a)
     if tag is None:
         tag = {np.dtype(np.float32): "f32", np.dtype(np.uint16): "bf16",
-               np.dtype(np.float64): "f64"}[a.dtype]
+               np.dtype(np.float64): "f64", np.dtype(np.float16): "f16"}[a.dtype]
     code, dt = _TAGS[tag]
     if a.dtype != dt:
         raise TypeError(f"oracle: tag {tag} needs {dt}, got {a.dtype}")
@@ -202,6 +208,22 @@ def round_bf16(v):
     v = np.ascontiguousarray(v, dtype=np.float64)
     out = np.empty(v.shape, dtype=np.uint16)
     _load().gno_round_bf16_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def round_f16(v):
+    """fp64 -> fp16 bit patterns (uint16), rounded once to nearest-even."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().gno_round_f16_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def f16_bits_to_f64(bits):
+    """Exact decode of fp16 bit patterns to fp64 (the oracle's own binary16 decoder)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _load().gno_f16_decode_array(_ptr(bits), bits.size, _ptr(out))
     return out
 
 

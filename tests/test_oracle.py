@@ -121,12 +121,14 @@ def _torch_ref(x64, G, gamma, beta, eps, dy64=None):
     return y.detach(), (x64.grad, g.grad, b.grad)
 
 
-@pytest.mark.parametrize("case", ["tiny", "deep", "ragged"])
+@pytest.mark.parametrize("case", ["tiny", "deep", "ragged", "f16"])
 def test_against_torch_float64_group_norm(case):
     if case == "tiny":
         inp = _tiny()
     elif case == "deep":
         inp = workloads.make(workloads.DEEP, "cpu")
+    elif case == "f16":
+        inp = workloads.make(workloads.custom(2, 8, 4, (6, 7, 5), torch.float16, dist="unet", seed=6), "cpu")
     else:
         inp = workloads.make(workloads.custom(3, 6, 2, (5, 7, 3), torch.bfloat16, dist="unet", seed=3), "cpu")
     x, dy, G, eps = inp["x"], inp["dy"], inp["G"], inp["eps"]
@@ -306,6 +308,41 @@ def test_round_bf16_ties_double_rounding_and_specials():
     assert r(-0.0) == 0x8000
     assert np.array_equal(O.round_f32(np.array([1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24])),
                           np.array([1.0, 1.0 + 2.0 ** -22], dtype=np.float32))
+
+
+def test_f16_decode_exhaustive_against_numpy():
+    """The oracle's binary16 decoder, written from the format's definition, on all 65536
+    bit patterns against numpy's float16."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ours = O.f16_bits_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(ours, ref, equal_nan=True)
+    assert np.array_equal(np.signbit(ours), np.signbit(ref))
+
+
+def test_round_f16_against_numpy_ties_and_specials():
+    """Rounding fp64 -> fp16 once, nearest-even: random values across the whole range
+    (subnormals and the overflow edge included) against numpy's direct conversion, every
+    exact midpoint between consecutive finite fp16 values, and hand-built cases."""
+    rng = np.random.default_rng(8)
+    v = np.concatenate([rng.normal(size=50000) * 10.0 ** rng.integers(-9, 5, 50000),
+                        rng.uniform(65000, 66000, 5000), -rng.uniform(0, 2.0 ** -14, 5000)])
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.round_f16(v), ref)
+    # exact midpoints: ties go to the even neighbour (even fraction bit)
+    lo = np.arange(0, 0x7BFF, dtype=np.uint16)            # finite positives with a finite successor
+    a, b = lo.view(np.float16).astype(np.float64), (lo + 1).view(np.float16).astype(np.float64)
+    mid = (a + b) / 2                                     # exact in fp64
+    want = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint16)
+    assert np.array_equal(O.round_f16(mid), want)
+    assert np.array_equal(O.round_f16(-mid), want | np.uint16(0x8000))
+    r = O._load().gno_round_f16
+    assert r(65504.0) == 0x7BFF and r(65519.99) == 0x7BFF and r(65520.0) == 0x7C00  # tie past the max -> inf
+    assert r(2.0 ** -24) == 0x0001 and r(2.0 ** -25) == 0x0000 and r(1.5 * 2.0 ** -25) == 0x0001
+    assert r(1.0 + 2.0 ** -11 + 2.0 ** -40) == 0x3C01   # just above a tie: up
+    assert r(float("inf")) == 0x7C00 and r(float("-inf")) == 0xFC00 and r(-0.0) == 0x8000
+    assert (r(float("nan")) & 0x7C00) == 0x7C00 and (r(float("nan")) & 0x3FF) != 0
 
 
 # ----------------------------------------------------------------------------- negative control

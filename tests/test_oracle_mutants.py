@@ -39,9 +39,14 @@ MUTANTS = {
     "c2_from_s1": ("b += gno_gamma(gamma, c) * s2[n * C + c];", "b += gno_gamma(gamma, c) * s1[n * C + c];"),
     "c1_no_mean": ("c1[n * G + g] = a / (double)M;", "c1[n * G + g] = a;"),
     "s2_without_xhat": ("b += g_ * xhat;", "b += g_;"),
-    "bf16_truncate": ("double k = nearbyint(ldexp(a, -q));", "double k = floor(ldexp(a, -q));"),
+    "bf16_truncate": ("\n    double k = nearbyint(ldexp(a, -q));", "\n    double k = floor(ldexp(a, -q));"),
+    "f16_truncate": ("const double k = nearbyint(ldexp(a, -q));", "const double k = floor(ldexp(a, -q));"),
     "bf16_precision": ("int q = (e - 1) - 7;", "int q = (e - 1) - 8;"),
     "bf16_nan_payload": ("return signbit(v) ? 0xFFC0 : 0x7FC0;", "return 0x7F80;"),
+    "f16_exponent_bias": ("else v = ldexp((double)(f + 1024), e - 25);", "else v = ldexp((double)(f + 1024), e - 24);"),
+    "f16_no_subnormals": ("if (e == 0) v = ldexp((double)f, -24);", "if (e == 0) v = 0.0;"),
+    "f16_precision": ("int q = (e - 1) - 10;    /* quantum", "int q = (e - 1) - 9;    /* quantum"),
+    "f16_overflow_edge": ("if (r >= 65536.0) return", "if (r >= 65504.0) return"),
 }
 
 PINS = [
@@ -57,6 +62,9 @@ PINS = [
     pins.test_backward_closed_forms,
     pins.test_round_bf16_matches_torch_on_fp32_values,
     pins.test_round_bf16_ties_double_rounding_and_specials,
+    pins.test_f16_decode_exhaustive_against_numpy,
+    pins.test_round_f16_against_numpy_ties_and_specials,
+    lambda: pins.test_against_torch_float64_group_norm("f16"),
     pins.test_relu_option_against_torch_autograd,
     pins.test_relu_keeps_negative_zero_and_nan_group_gradient,
 ]
@@ -81,7 +89,8 @@ def test_pins_kill_mutant(name, tmp_path, monkeypatch):
     mutant = ctypes.CDLL(lib_path)
     for fn in ("gno_group_stats", "gno_forward", "gno_forward_at", "gno_backward", "gno_backward_at",
                "gno_round_bf16", "gno_round_bf16_array", "gno_round_f32_array", "gno_channel_abs_sums",
-               "gno_relu_value", "gno_gate_value"):
+               "gno_relu_value", "gno_gate_value", "gno_round_f16", "gno_round_f16_array",
+               "gno_f16_decode_array"):
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(O, "_lib", mutant)

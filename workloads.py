@@ -16,8 +16,8 @@ requested device so that 256^3 volumes are generated in place):
 - ``normal``: z ~ N(0, 1) for both x and dy (the whole-UNet census sites).
 
 In every recipe gamma ~ N(1, 0.1), beta ~ N(0, 0.1) in fp32 and eps = 1e-5.
-Values are drawn in fp32 and rounded once (nearest-even) to bf16 where the recipe
-asks for bf16. The pages' real activations come from a trained UNet on a fractal
+Values are drawn in fp32 and rounded once (nearest-even) to bf16 or fp16 where the
+case asks for a 16-bit dtype. The pages' real activations come from a trained UNet on a fractal
 dataset that is not available here; these draws stand in for them.
 """
 from dataclasses import dataclass, field
@@ -55,7 +55,7 @@ class Case:
         return (self.N, self.C) + tuple(self.spatial)
 
 
-BF16, F32 = torch.bfloat16, torch.float32
+BF16, F16, F32 = torch.bfloat16, torch.float16, torch.float32
 
 # The workloads named by the pages' UNet (sizes and distributions as listed above).
 TINY = Case("tiny_fp32_16cube", 1, 8, 4, (16, 16, 16), F32, F32, "tiny", 1001)
@@ -127,9 +127,9 @@ def make(case: Case, device="cpu", with_dy=True):
     if with_dy:
         dy = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
         dy.mul_(_dy_sigma(case))
-        # dy carries the output's values; in the fp32-output mode it holds bf16 values
-        # stored as fp32 so that both dy dtypes describe the same numbers.
-        dy = dy.to(BF16 if case.x_dtype == BF16 else F32).to(case.dy_dtype)
+        # dy carries the output's values; in the fp32-output mode it holds values of x's
+        # 16-bit dtype stored as fp32, so that both dy dtypes describe the same numbers.
+        dy = dy.to(case.x_dtype if case.x_dtype in (BF16, F16) else F32).to(case.dy_dtype)
     return {
         "x": x,
         "gamma": torch.from_numpy(gamma).to(dev),
