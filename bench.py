@@ -57,7 +57,7 @@ def kernel_source_hash():
 
 def bytes_per_elem(x_dtype, y_dtype, dy_dtype):
     import torch
-    sz = {torch.bfloat16: 2, torch.float32: 4}
+    sz = {torch.bfloat16: 2, torch.float16: 2, torch.float32: 4}
     bx, by, bdy = sz[x_dtype], sz[y_dtype], sz[dy_dtype]
     phases = {"stats": bx, "apply": bx + by, "bwd_reduce": bx + bdy, "bwd_apply": bx + bdy + bx}
     return phases, sum(phases.values())
@@ -370,6 +370,12 @@ def main():
         out["relu_fused"] = {"ms_per_step": round(rms, 5),
                              "value": round(run.step_bytes / (rms * 1e-3) / 1e9, 1)}
         run.act = None
+        log("the same site with fp16 activations")
+        r16 = Runner(workloads.SCALE7_F16)
+        fms16, _ = r16.timed_steps(max(10, args.steps // 2), 3)
+        out["fp16"] = {"workload": workloads.SCALE7_F16.name, "ms_per_step": round(fms16, 5),
+                       "value": round(r16.step_bytes / (fms16 * 1e-3) / 1e9, 1)}
+        del r16
     if not args.no_cpu_baseline:
         log("timing the fp64 CPU oracle on this host")
         out["cpu_baseline"] = cpu_baseline(run)

@@ -61,7 +61,9 @@ extern "C" {
 /* Element types of x, y, dy, dx. gamma, beta, mean, rstd, dgamma, dbeta are always fp32. */
 typedef enum gn_dtype {
     GN_F32 = 0,  /* IEEE binary32 */
-    GN_BF16 = 1  /* bfloat16: the upper 16 bits of a binary32 */
+    GN_BF16 = 1, /* bfloat16: the upper 16 bits of a binary32 */
+    GN_F16 = 2   /* IEEE binary16 ("Optimize GroupNorm", NDHWC-kernel paragraph: fp32, bf16
+                    and fp16 inputs with fp32 statistics) */
 } gn_dtype;
 
 typedef enum gn_status {
@@ -101,7 +103,7 @@ size_t gn_workspace_bytes(int64_t N, int64_t C, int64_t S, int64_t G);
 /*
  * Forward. Statistics per (n, g) in fp32 (written to mean and rstd), then
  * y = act(gamma_c * (x - mean) * rstd + beta_c) computed in fp32 and stored once in
- * y_dtype. x_dtype is GN_F32 or GN_BF16; y_dtype is x_dtype or GN_F32 (the fp32-output
+ * y_dtype. x_dtype is GN_F32, GN_BF16 or GN_F16; y_dtype is x_dtype or GN_F32 (the fp32-output
  * mode). gamma == NULL means all ones, beta == NULL all zeros. eps must be finite and
  * >= 0. activation is a gn_activation. Enqueues gn_forward_stats then gn_forward_apply
  * (three kernels).
@@ -135,7 +137,7 @@ int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S
  *   dx = rstd * (gamma_c * dy - c1 - xhat * c2),  c1 = (1/M) sum_{c in g} gamma_c sum(dy),
  *                                                 c2 = (1/M) sum_{c in g} gamma_c sum(dy*xhat)
  * in x_dtype, and dgamma_c = sum_n sum(dy * xhat), dbeta_c = sum_n sum(dy).
- * dy_dtype is GN_F32 or GN_BF16 independently of x_dtype; the same dy values in either
+ * dy_dtype is GN_F32, GN_BF16 or GN_F16 independently of x_dtype; the same dy values in any
  * dtype give bitwise identical results. gamma == NULL means all ones. dx, dgamma and
  * dbeta may each be NULL (not computed). A group with M == 1 has dx == +0 exactly for
  * finite inputs (NaN/Inf still propagate). With activation GN_ACT_RELU, dy is the gradient

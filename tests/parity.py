@@ -7,10 +7,10 @@ reference value is near zero):
   y (fp32)   |d| <= 1e-5 * max(|y64|, |gamma_c| + |beta_c|): relative to |y| where |y| is
              at least the channel's output scale (xhat has unit variance); near y = 0 a
              relative bar is ill-posed, since any fp32 mean is off by O(u * sigma)
-  y (bf16)   within 1 bf16 ulp of the fp64 answer rounded once; elements whose fp32 terms
-             cancel may instead meet the fp32 bar (counted and reported)
+  y (bf16, fp16)  within 1 ulp of the fp64 answer rounded once to that format; elements
+             whose fp32 terms cancel may instead meet the fp32 bar (counted and reported)
   dx (fp32)  |d| <= 1e-4 * max|dx64|
-  dx (bf16)  |d| <= ulp_bf16(dx64) + 1e-4 * max|dx64|
+  dx (bf16, fp16)  |d| <= ulp(dx64) + 1e-4 * max|dx64|, ulp in dx's format
   dgamma/dbeta  |d_c| <= max(1e-4 * |ref_c|, 2 * D * 2^-24 * sum|terms_c|), D the depth of
              the kernel's fp32 summation tree for the shape (the a-priori bound of fp32
              summation in that order)
@@ -42,6 +42,8 @@ def to_np(t):
 def as_f64(a):
     if a.dtype == np.uint16:
         return O.bf16_bits_to_f64(a)
+    if a.dtype == np.float16:
+        return O.f16_bits_to_f64(a.view(np.uint16))
     return a.astype(np.float64)
 
 
@@ -91,17 +93,19 @@ def check_y(y_gpu, y64, beta_at, gamma_at):
     """y_gpu: fp32 array or uint16 bf16 bits, flat; y64 fp64 flat; beta_at/gamma_at: the
     channel's beta and gamma per element."""
     fp32_floor = 1e-5 * np.maximum(np.abs(y64), np.abs(gamma_at) + np.abs(beta_at))
-    if y_gpu.dtype == np.uint16:
+    if y_gpu.dtype in (np.uint16, np.float16):
+        fmt = "bf16" if y_gpu.dtype == np.uint16 else "fp16"
         got = as_f64(y_gpu)
         ok, why = _nan_inf_match(got, y64)
         assert ok, f"y: {why}"
         fin = np.isfinite(y64)
-        ref_bits = O.round_bf16(y64)
-        dist = np.abs(_ordered(y_gpu) - _ordered(ref_bits))
+        bits = y_gpu if fmt == "bf16" else y_gpu.view(np.uint16)
+        ref_bits = O.round_bf16(y64) if fmt == "bf16" else O.round_f16(y64)
+        dist = np.abs(_ordered(bits) - _ordered(ref_bits))
         bad = fin & (dist > 1)
         fallback = bad & (np.abs(got - y64) <= fp32_floor)
         hard = bad & ~fallback
-        assert not hard.any(), (f"y(bf16): {hard.sum()} elements beyond 1 ulp, e.g. gpu "
+        assert not hard.any(), (f"y({fmt}): {hard.sum()} elements beyond 1 ulp, e.g. gpu "
                                 f"{got[hard][:4]} vs {y64[hard][:4]}")
         return {"max_ulp": int(dist[fin].max()) if fin.any() else 0, "fallback": int(fallback.sum())}
     got = y_gpu.astype(np.float64)
@@ -120,6 +124,20 @@ def bf16_ulp(v):
     return 2.0 ** (e - 7)
 
 
+def f16_ulp(v):
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def _ulp_of(dtype, v):
+    if dtype == np.uint16:
+        return bf16_ulp(v)
+    if dtype == np.float16:
+        return f16_ulp(v)
+    return 0.0
+
+
 def check_dx(dx_gpu, dx64, scale=None, band=None):
     """band: optional (mask, alt64, slack) from ReluBand.dx_terms: elements under mask may
     instead match alt64 (the other gate decision); slack widens every element's bar."""
@@ -129,16 +147,15 @@ def check_dx(dx_gpu, dx64, scale=None, band=None):
     ok, why = _nan_inf_match(got, dx64)
     assert ok, f"dx: {why}"
     fin = np.isfinite(dx64)
-    is16 = dx_gpu.dtype == np.uint16
     slack = 0.0 if band is None else band[2]
-    bar = 1e-4 * scale + (bf16_ulp(dx64) if is16 else 0.0) + slack
+    bar = 1e-4 * scale + _ulp_of(dx_gpu.dtype, dx64) + slack
     bar = np.maximum(bar, 1e-300)
     d = np.abs(got - dx64)
     over = fin & (d > bar)
     alt_used = 0
     if band is not None:
         mask, alt64, _ = band
-        bar_alt = 1e-4 * scale + (bf16_ulp(alt64) if is16 else 0.0) + slack
+        bar_alt = 1e-4 * scale + _ulp_of(dx_gpu.dtype, alt64) + slack
         alt_ok = mask & (np.abs(got - alt64) <= bar_alt)
         alt_used = int((over & alt_ok).sum())
         over &= ~alt_ok

@@ -30,12 +30,13 @@ def test_status_enum_matches_header():
     for code, name in STATUS_NAMES.items():
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
     assert re.search(r"GN_F32\s*=\s*0", text) and re.search(r"GN_BF16\s*=\s*1", text)
+    assert re.search(r"GN_F16\s*=\s*2", text)
     assert re.search(r"GN_ACT_NONE\s*=\s*0", text) and re.search(r"GN_ACT_RELU\s*=\s*1", text)
     assert GN_F32 == 0 and GN_BF16 == 1
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == 4
+    assert lib.gn_abi_version() == 5
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every

@@ -287,7 +287,7 @@ def test_repeats_are_bitwise_identical_with_poisoned_workspace(case):
 
 
 def _bits(t):
-    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    return t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t.view(torch.int32)
 
 
 def test_one_workspace_across_shapes():
@@ -417,6 +417,63 @@ def test_binding_rejects_bad_arguments():
         gn.gn_forward(x.cpu().pin_memory(), None, None, 2, out=torch.empty_like(x),
                       mean=torch.empty(1, 2, device=DEV), rstd=torch.empty(1, 2, device=DEV),
                       workspace=gn.workspace_for(x, 2))
+
+
+# ----------------------------------------------------------------------------- fp16 input
+
+F16 = torch.float16
+FP16_CASES = [
+    workloads.custom(2, 8, 4, (6, 7, 5), F16, dist="unet", seed=51),                      # two-pass, ragged
+    workloads.custom(1, 16, 4, (16, 16, 16), F16, dist="unet", seed=52),                  # resident
+    workloads.custom(2, 6, 2, (33, 17, 9), F16, dist="deep", seed=53, out_dtype=torch.float32),
+    workloads.custom(3, 12, 4, (4, 4, 6), F16, torch.bfloat16, dist="normal", seed=54),   # bf16 dy
+    workloads.custom(1, 4, 2, (64, 64, 65), F16, torch.float32, dist="tiny", seed=56),    # fp32 dy, multi-job rows
+]
+
+
+@pytest.mark.parametrize("case", FP16_CASES, ids=lambda c: c.name + "_" + str(c.dy_dtype).split(".")[-1])
+def test_fp16_elementwise(case):
+    full_check(workloads.make(case, "cpu"), case.name + "_fp16")
+
+
+@pytest.mark.parametrize("case", FP16_CASES[:2], ids=lambda c: c.name)
+def test_fp16_relu_elementwise(case):
+    full_check(workloads.make(case, "cpu"), case.name + "_fp16_relu", relu=True)
+
+
+FP16_SCALE7 = workloads.custom(1, 32, 8, (128, 128, 128), F16, dist="unet", seed=55)
+
+
+def test_fp16_top_site_sampled():
+    sampled_check(workloads.make(FP16_SCALE7, DEV), "fp16_128cube", n_random=1 << 18, seed=55)
+
+
+@pytest.mark.parametrize("case", [FP16_CASES[0], FP16_CASES[1], FP16_SCALE7], ids=lambda c: c.name)
+def test_fp16_output_is_fp32_output_rounded_once(case):
+    say(f"{case.name}: fp16 output vs fp32 output rounded once")
+    inp = workloads.make(case, DEV, with_dy=False)
+    x, G = inp["x"], inp["G"]
+    y16, m16, r16 = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], torch.float16)
+    y32, m32, r32 = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(m16, m32) and torch.equal(r16, r32)
+    ref = O.round_f16(y32.cpu().numpy().astype(np.float64).reshape(-1))
+    got = y16.cpu().numpy().reshape(-1).view(np.uint16)
+    nan = np.isnan(y32.cpu().numpy().reshape(-1))
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("case", [FP16_CASES[0], FP16_CASES[1]], ids=lambda c: c.name)
+def test_fp16_dy_and_fp32_dy_give_the_same_bits(case):
+    say(f"{case.name}: dy fp16 vs the same values in fp32")
+    inp = workloads.make(case, DEV)
+    x, G = inp["x"], inp["G"]
+    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"])
+    a = gn.gn_backward(inp["dy"], x, mean, rstd, inp["gamma"], G)
+    b = gn.gn_backward(inp["dy"].float(), x, mean, rstd, inp["gamma"], G)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(_bits(u), _bits(v))
 
 
 # ----------------------------------------------------------------------------- resident path

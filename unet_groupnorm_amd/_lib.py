@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(HERE, "libgn.so")
 
 # Status codes and dtype codes of include/gn.h.
 GN_OK = 0
-GN_F32, GN_BF16 = 0, 1
+GN_F32, GN_BF16, GN_F16 = 0, 1, 2
 GN_ACT_NONE, GN_ACT_RELU = 0, 1
 STATUS_NAMES = {
     0: "GN_OK", 1: "GN_ERR_NULL", 2: "GN_ERR_SHAPE", 3: "GN_ERR_GROUPS", 4: "GN_ERR_DTYPE",

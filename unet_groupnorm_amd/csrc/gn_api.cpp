@@ -14,7 +14,7 @@
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-bool dtype_ok(int d) { return d == GN_F32 || d == GN_BF16; }
+bool dtype_ok(int d) { return d == GN_F32 || d == GN_BF16 || d == GN_F16; }
 bool act_ok(int a) { return a == GN_ACT_NONE || a == GN_ACT_RELU; }
 
 int plan_or_error(int64_t N, int64_t C, int64_t S, int64_t G, gn::Plan* p)
@@ -142,7 +142,7 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 4; }
+int gn_abi_version(void) { return 5; }
 
 const char* gn_status_string(int status)
 {

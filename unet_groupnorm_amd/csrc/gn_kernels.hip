@@ -38,6 +38,7 @@
 #include <stdint.h>
 
 #include <tuple>
+#include <type_traits>
 
 #include "gn_launch.hpp"
 
@@ -178,6 +179,60 @@ template <> struct Io<float> {
         }
     }
     static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+};
+
+// fp16 storage (IEEE binary16): widening is exact; narrowing converts one value at a time
+// with round-to-nearest-even (the default rounding mode), keeping fp16 subnormals and
+// overflowing to infinity.
+template <> struct Io<_Float16> {
+    struct Raw {
+        u32x4 u;
+    };
+    static __device__ __forceinline__ float lo(uint32_t w)
+    {
+        return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xffffu)));
+    }
+    static __device__ __forceinline__ float hi(uint32_t w)
+    {
+        return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16)));
+    }
+    static __device__ __forceinline__ uint32_t pack(float a, float b)
+    {
+        return uint32_t(__builtin_bit_cast(uint16_t, _Float16(a))) |
+               (uint32_t(__builtin_bit_cast(uint16_t, _Float16(b))) << 16);
+    }
+    template <bool NT>
+    static __device__ __forceinline__ Raw load_raw(const _Float16* p)
+    {
+        const u32x4* q = reinterpret_cast<const u32x4*>(p);
+        return Raw{NT ? __builtin_nontemporal_load(q) : *q};
+    }
+    static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
+    {
+        v[0] = lo(r.u.x); v[1] = hi(r.u.x);
+        v[2] = lo(r.u.y); v[3] = hi(r.u.y);
+        v[4] = lo(r.u.z); v[5] = hi(r.u.z);
+        v[6] = lo(r.u.w); v[7] = hi(r.u.w);
+    }
+    template <bool NT>
+    static __device__ __forceinline__ void load8(const _Float16* p, float (&v)[8])
+    {
+        widen(load_raw<NT>(p), v);
+    }
+    static __device__ __forceinline__ float load1(const _Float16* p) { return float(*p); }
+    static __device__ __forceinline__ void store8(_Float16* p, const float (&v)[8])
+    {
+        u32x4 u;
+        u.x = pack(v[0], v[1]);
+        u.y = pack(v[2], v[3]);
+        u.z = pack(v[4], v[5]);
+        u.w = pack(v[6], v[7]);
+        if (kNtStore)
+            __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
+        else
+            *reinterpret_cast<u32x4*>(p) = u;
+    }
+    static __device__ __forceinline__ void store1(_Float16* p, float v) { *p = _Float16(v); }
 };
 
 // ------------------------------------------------------------------ job geometry
@@ -1102,23 +1157,27 @@ dim3 grid_of(int64_t jobs) { return dim3(unsigned(jobs < kMaxGrid ? jobs : kMaxG
 
 // ------------------------------------------------------------------ launchers
 
+// Calls f with a value of the storage type of dtype dt: float, bf16 (as uint16_t) or fp16.
+template <typename F>
+hipError_t with_type(int dt, F&& f)
+{
+    if (dt == kBF16) return f(uint16_t{});
+    if (dt == kF16) return f(_Float16{});
+    return f(float{});
+}
+
 hipError_t launch_fwd_stats(const void* x, int xdt, const float* gamma, const float* beta,
                             float eps, float* mean, float* rstd, const KArgs& a, Workspace ws,
                             hipStream_t st)
 {
-    const dim3 g1 = grid_of(a.jobs), b1(unsigned(a.block));
-    const dim3 g2(unsigned(a.N * a.G)), b2(256);
-    hipError_t e;
-    if (xdt == kBF16) {
-        e = launch(stats_kernel<uint16_t>, g1, b1, st, cp<uint16_t>(x), a, ws.part);
+    return with_type(xdt, [&](auto tx) {
+        using TX = decltype(tx);
+        const hipError_t e = launch(stats_kernel<TX>, grid_of(a.jobs), dim3(unsigned(a.block)), st,
+                                    cp<TX>(x), a, ws.part);
         if (e != hipSuccess) return e;
-        return launch(fin_fwd_kernel<uint16_t>, g2, b2, st, cp<uint16_t>(x), gamma, beta, eps,
-                      static_cast<const float2*>(ws.part), mean, rstd, a, ws.coef);
-    }
-    e = launch(stats_kernel<float>, g1, b1, st, cp<float>(x), a, ws.part);
-    if (e != hipSuccess) return e;
-    return launch(fin_fwd_kernel<float>, g2, b2, st, cp<float>(x), gamma, beta, eps,
-                  static_cast<const float2*>(ws.part), mean, rstd, a, ws.coef);
+        return launch(fin_fwd_kernel<TX>, dim3(unsigned(a.N * a.G)), dim3(256), st, cp<TX>(x), gamma, beta,
+                      eps, static_cast<const float2*>(ws.part), mean, rstd, a, ws.coef);
+    });
 }
 
 hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArgs& a,
@@ -1126,38 +1185,32 @@ hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArg
 {
     const dim3 grid = grid_of(a.jobs_a), block(unsigned(a.block_a));
     const float4* coef = ws.coef;
-    if (xdt == kBF16 && ydt == kBF16)
-        return launch(apply_kernel<uint16_t, uint16_t>, grid, block, st, cp<uint16_t>(x),
-                      mp<uint16_t>(y), a, coef);
-    if (xdt == kBF16)
-        return launch(apply_kernel<uint16_t, float>, grid, block, st, cp<uint16_t>(x), mp<float>(y),
-                      a, coef);
-    return launch(apply_kernel<float, float>, grid, block, st, cp<float>(x), mp<float>(y), a, coef);
+    return with_type(xdt, [&](auto tx) {
+        using TX = decltype(tx);
+        if (ydt == kF32)
+            return launch(apply_kernel<TX, float>, grid, block, st, cp<TX>(x), mp<float>(y), a, coef);
+        return launch(apply_kernel<TX, TX>, grid, block, st, cp<TX>(x), mp<TX>(y), a, coef);
+    });
 }
 
 hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, const float* mean,
                              const float* rstd, const float* gamma, const float* beta, float* dgamma,
                              float* dbeta, const KArgs& a, Workspace ws, hipStream_t st)
 {
-    const dim3 g1 = grid_of(a.jobs), b1(unsigned(a.block));
-    hipError_t e;
-    if (xdt == kBF16 && dydt == kBF16)
-        e = launch(bwd_reduce_kernel<uint16_t, uint16_t>, g1, b1, st, cp<uint16_t>(dy),
-                   cp<uint16_t>(x), mean, rstd, gamma, beta, a, ws.part);
-    else if (xdt == kBF16)
-        e = launch(bwd_reduce_kernel<uint16_t, float>, g1, b1, st, cp<float>(dy), cp<uint16_t>(x),
-                   mean, rstd, gamma, beta, a, ws.part);
-    else if (dydt == kBF16)
-        e = launch(bwd_reduce_kernel<float, uint16_t>, g1, b1, st, cp<uint16_t>(dy), cp<float>(x),
-                   mean, rstd, gamma, beta, a, ws.part);
-    else
-        e = launch(bwd_reduce_kernel<float, float>, g1, b1, st, cp<float>(dy), cp<float>(x), mean,
-                   rstd, gamma, beta, a, ws.part);
-    if (e != hipSuccess) return e;
-    const int64_t ngroups = a.N * a.G;
-    const int64_t nchan = (dgamma || dbeta) ? a.C : 0;
-    return launch(fin_bwd_kernel, dim3(unsigned(ngroups + nchan)), dim3(256), st, mean, rstd, gamma,
-                  beta, static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coef, dgamma, dbeta);
+    return with_type(xdt, [&](auto tx) {
+        return with_type(dydt, [&](auto td) {
+            using TX = decltype(tx);
+            using TD = decltype(td);
+            const hipError_t e = launch(bwd_reduce_kernel<TX, TD>, grid_of(a.jobs), dim3(unsigned(a.block)),
+                                        st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part);
+            if (e != hipSuccess) return e;
+            const int64_t ngroups = a.N * a.G;
+            const int64_t nchan = (dgamma || dbeta) ? a.C : 0;
+            return launch(fin_bwd_kernel, dim3(unsigned(ngroups + nchan)), dim3(256), st, mean, rstd, gamma,
+                          beta, static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coef, dgamma,
+                          dbeta);
+        });
+    });
 }
 
 hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,
@@ -1165,69 +1218,41 @@ hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, vo
 {
     const dim3 grid = grid_of(a.jobs_a), block(unsigned(a.block_a));
     const float4* coef = ws.coef;
-    if (xdt == kBF16 && dydt == kBF16)
-        return launch(bwd_apply_kernel<uint16_t, uint16_t>, grid, block, st, cp<uint16_t>(dy),
-                      cp<uint16_t>(x), a, coef, mp<uint16_t>(dx));
-    if (xdt == kBF16)
-        return launch(bwd_apply_kernel<uint16_t, float>, grid, block, st, cp<float>(dy),
-                      cp<uint16_t>(x), a, coef, mp<uint16_t>(dx));
-    if (dydt == kBF16)
-        return launch(bwd_apply_kernel<float, uint16_t>, grid, block, st, cp<uint16_t>(dy),
-                      cp<float>(x), a, coef, mp<float>(dx));
-    return launch(bwd_apply_kernel<float, float>, grid, block, st, cp<float>(dy), cp<float>(x), a,
-                  coef, mp<float>(dx));
+    return with_type(xdt, [&](auto tx) {
+        return with_type(dydt, [&](auto td) {
+            using TX = decltype(tx);
+            using TD = decltype(td);
+            return launch(bwd_apply_kernel<TX, TD>, grid, block, st, cp<TD>(dy), cp<TX>(x), a, coef,
+                          mp<TX>(dx));
+        });
+    });
 }
 
-template <int V, typename TX>
-hipError_t res_fwd_v(const void* x, const float* gamma, const float* beta, float eps, float* mean,
-                     float* rstd, void* y, int ydt, const KArgs& a, Workspace ws, hipStream_t st, int block)
+// Calls f with std::integral_constant<int, V> for the resident lane-vector count.
+template <typename F>
+hipError_t with_vecs(int vecs, F&& f)
 {
-    const dim3 grid(unsigned(a.G), unsigned(a.N)), blk{unsigned(block)};
-    if (y && ydt == kF32)
-        return launch(res_fwd_kernel<V, TX, float>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd,
-                      a, ws.coef, mp<float>(y));
-    return launch(res_fwd_kernel<V, TX, TX>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd, a,
-                  ws.coef, mp<TX>(y));
-}
-
-template <typename TX>
-hipError_t res_fwd_t(const void* x, const float* gamma, const float* beta, float eps, float* mean,
-                     float* rstd, void* y, int ydt, const KArgs& a, Workspace ws, hipStream_t st,
-                     int block, int vecs)
-{
-    if (vecs == 1) return res_fwd_v<1, TX>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block);
-    if (vecs == 2) return res_fwd_v<2, TX>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block);
-    return res_fwd_v<4, TX>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block);
-}
-
-template <int V, typename TX, typename TD>
-hipError_t res_bwd_v(const void* dy, const void* x, const float* mean, const float* rstd,
-                     const float* gamma, const float* beta, float* dgamma, float* dbeta, void* dx,
-                     const KArgs& a, Workspace ws, hipStream_t st, int block)
-{
-    return launch(res_bwd_kernel<V, TX, TD>, dim3(unsigned(a.G)), dim3(unsigned(block)), st, cp<TD>(dy),
-                  cp<TX>(x), mean, rstd, gamma, beta, a, ws.coef, dgamma, dbeta, mp<TX>(dx));
-}
-
-template <typename TX, typename TD>
-hipError_t res_bwd_t(const void* dy, const void* x, const float* mean, const float* rstd,
-                     const float* gamma, const float* beta, float* dgamma, float* dbeta, void* dx,
-                     const KArgs& a, Workspace ws, hipStream_t st, int block, int vecs)
-{
-    if (vecs == 1)
-        return res_bwd_v<1, TX, TD>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block);
-    if (vecs == 2)
-        return res_bwd_v<2, TX, TD>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block);
-    return res_bwd_v<4, TX, TD>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block);
+    if (vecs == 1) return f(std::integral_constant<int, 1>{});
+    if (vecs == 2) return f(std::integral_constant<int, 2>{});
+    return f(std::integral_constant<int, 4>{});
 }
 
 hipError_t launch_res_fwd(const void* x, int xdt, const float* gamma, const float* beta, float eps,
                           float* mean, float* rstd, void* y, int ydt, const KArgs& a, Workspace ws,
                           hipStream_t st, int block, int vecs)
 {
-    if (xdt == kBF16)
-        return res_fwd_t<uint16_t>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block, vecs);
-    return res_fwd_t<float>(x, gamma, beta, eps, mean, rstd, y, ydt, a, ws, st, block, vecs);
+    const dim3 grid(unsigned(a.G), unsigned(a.N)), blk{unsigned(block)};
+    return with_type(xdt, [&](auto tx) {
+        return with_vecs(vecs, [&](auto v) {
+            using TX = decltype(tx);
+            constexpr int V = decltype(v)::value;
+            if (y && ydt == kF32)
+                return launch(res_fwd_kernel<V, TX, float>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean,
+                              rstd, a, ws.coef, mp<float>(y));
+            return launch(res_fwd_kernel<V, TX, TX>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd,
+                          a, ws.coef, mp<TX>(y));
+        });
+    });
 }
 
 hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, const float* mean,
@@ -1235,17 +1260,18 @@ hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, cons
                           float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st,
                           int block, int vecs)
 {
-    if (xdt == kBF16 && dydt == kBF16)
-        return res_bwd_t<uint16_t, uint16_t>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st,
-                                             block, vecs);
-    if (xdt == kBF16)
-        return res_bwd_t<uint16_t, float>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st,
-                                          block, vecs);
-    if (dydt == kBF16)
-        return res_bwd_t<float, uint16_t>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st,
-                                          block, vecs);
-    return res_bwd_t<float, float>(dy, x, mean, rstd, gamma, beta, dgamma, dbeta, dx, a, ws, st, block,
-                                   vecs);
+    return with_type(xdt, [&](auto tx) {
+        return with_type(dydt, [&](auto td) {
+            return with_vecs(vecs, [&](auto v) {
+                using TX = decltype(tx);
+                using TD = decltype(td);
+                constexpr int V = decltype(v)::value;
+                return launch(res_bwd_kernel<V, TX, TD>, dim3(unsigned(a.G)), dim3(unsigned(block)), st,
+                              cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.coef, dgamma, dbeta,
+                              mp<TX>(dx));
+            });
+        });
+    });
 }
 
 }  // namespace gn

@@ -10,6 +10,7 @@ namespace gn {
 
 constexpr int kF32 = 0;
 constexpr int kBF16 = 1;
+constexpr int kF16 = 2;
 // Largest grid launched; kernels stride over any further jobs.
 constexpr int64_t kMaxGrid = int64_t(1) << 30;
 

@@ -11,9 +11,9 @@ import ctypes
 
 import torch
 
-from ._lib import GN_ACT_NONE, GN_ACT_RELU, GN_BF16, GN_F32, GN_OK, STATUS_NAMES, GnPlanInfo, lib
+from ._lib import GN_ACT_NONE, GN_ACT_RELU, GN_BF16, GN_F16, GN_F32, GN_OK, STATUS_NAMES, GnPlanInfo, lib
 
-_DT = {torch.float32: GN_F32, torch.bfloat16: GN_BF16}
+_DT = {torch.float32: GN_F32, torch.bfloat16: GN_BF16, torch.float16: GN_F16}
 _ACT = {None: GN_ACT_NONE, "none": GN_ACT_NONE, "relu": GN_ACT_RELU}
 
 
@@ -50,7 +50,7 @@ def _dtype(t):
     try:
         return _DT[t.dtype]
     except KeyError:
-        raise TypeError(f"unsupported dtype {t.dtype} (float32 and bfloat16 only)") from None
+        raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)") from None
 
 
 def _ptr(t):

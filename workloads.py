@@ -62,6 +62,8 @@ TINY = Case("tiny_fp32_16cube", 1, 8, 4, (16, 16, 16), F32, F32, "tiny", 1001)
 SCALE7 = Case("scale7_128cube_c32_g8", 1, 32, 8, (128, 128, 128), BF16, BF16, "unet", 1007)
 SCALE8 = Case("scale8_256cube_c32_g8", 1, 32, 8, (256, 256, 256), BF16, BF16, "unet", 1008)
 DEEP = Case("deep_n4_c512_g32_8cube", 4, 512, 32, (8, 8, 8), BF16, BF16, "deep", 1004)
+# The 128^3 site with fp16 activations (the pages list fp16 among the input dtypes).
+SCALE7_F16 = Case("scale7_128cube_c32_g8_fp16", 1, 32, 8, (128, 128, 128), F16, F16, "unet", 1017)
 # fp32-output mode: y in fp32, dy arrives in fp32 (holding bf16-representable values).
 DEEP_F32OUT = Case("deep_n4_c512_g32_8cube_f32out", 4, 512, 32, (8, 8, 8), BF16, F32, "deep", 1004,
                    out_dtype=F32)
