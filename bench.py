@@ -24,8 +24,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
 METRIC = "GroupNorm fwd+bwd achieved HBM GB/s (% of MI355X peak), bf16 128³/256³ C=32 G=8"
-KERNEL_SOURCES = ["unet_groupnorm_amd/csrc/gn_kernels.hip", "unet_groupnorm_amd/csrc/gn_plan.cpp",
-                  "unet_groupnorm_amd/csrc/gn_plan.hpp", "unet_groupnorm_amd/csrc/gn_launch.hpp"]
+KERNEL_SOURCES = ["unet_groupnorm_amd/csrc/gn_kernels.hip", "unet_groupnorm_amd/csrc/gn_device.hpp",
+                  "unet_groupnorm_amd/csrc/gn_plan.cpp", "unet_groupnorm_amd/csrc/gn_plan.hpp",
+                  "unet_groupnorm_amd/csrc/gn_launch.hpp"]
 
 
 def parse():
@@ -66,7 +67,7 @@ def bytes_per_elem(x_dtype, y_dtype, dy_dtype):
 class Runner:
     """Holds one workload resident on the GPU with preallocated outputs."""
 
-    def __init__(self, case, activation=None):
+    def __init__(self, case, activation=None, layout="ncdhw"):
         import torch
 
         import unet_groupnorm_amd as gn
@@ -75,6 +76,8 @@ class Runner:
         inp = workloads.make(case, "cuda")
         self.inp = inp
         self.x, self.dy, self.G, self.eps = inp["x"], inp["dy"], inp["G"], inp["eps"]
+        if layout == "ndhwc":
+            self.x, self.dy = gn.as_layout(self.x, layout), gn.as_layout(self.dy, layout)
         self.gamma, self.beta = inp["gamma"], inp["beta"]
         self.y = torch.empty_like(self.x, dtype=inp["out_dtype"])
         N = case.N
@@ -370,6 +373,12 @@ def main():
         out["relu_fused"] = {"ms_per_step": round(rms, 5),
                              "value": round(run.step_bytes / (rms * 1e-3) / 1e9, 1)}
         run.act = None
+        log("the same site in channels-last (NDHWC) memory")
+        rcl = Runner(case, layout="ndhwc")
+        cms, _ = rcl.timed_steps(max(10, args.steps // 2), 3)
+        out["channels_last"] = {"ms_per_step": round(cms, 5),
+                                "value": round(rcl.step_bytes / (cms * 1e-3) / 1e9, 1)}
+        del rcl
         log("the same site with fp16 activations")
         r16 = Runner(workloads.SCALE7_F16)
         fms16, _ = r16.timed_steps(max(10, args.steps // 2), 3)

@@ -77,7 +77,9 @@ typedef enum gn_status {
     GN_ERR_ALIGN = 7,     /* a pointer is not aligned as stated above */
     GN_ERR_DEVICE = 8,    /* x is not device memory, or the stream belongs to another device */
     GN_ERR_LAUNCH = 9,    /* the HIP runtime refused a launch; outputs are undefined */
-    GN_ERR_ACTIVATION = 10 /* unknown activation code */
+    GN_ERR_ACTIVATION = 10, /* unknown activation code */
+    GN_ERR_LAYOUT = 11      /* channels-last: C not a multiple of 8, C/8 not dividing 256, or
+                               C/G neither dividing 8 nor a multiple of 8 */
 } gn_status;
 
 /*
@@ -210,6 +212,52 @@ typedef struct gn_plan_info {
 
 /* Fills *out for a valid shape and returns GN_OK; otherwise returns the shape error. */
 int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out);
+
+/*
+ * Channels-last (NDHWC) activations ("Optimize GroupNorm", paragraph introducing the NDHWC
+ * kernel): x, y, dy and dx hold element (n, s, c) at flat index (n*S + s)*C + c; mean,
+ * rstd, gamma, beta, dgamma and dbeta are laid out as above. Same arguments, dtypes,
+ * semantics, ownership and errors as gn_forward / gn_backward, with the workspace of
+ * gn_workspace_bytes_cl. Supported when C is a multiple of 8, C/8 divides 256 (C <= 2048)
+ * and C/G divides 8 or is a multiple of 8 (every UNet shape); other shapes return
+ * GN_ERR_LAYOUT before anything is enqueued. Three kernels per direction.
+ */
+size_t gn_workspace_bytes_cl(int64_t N, int64_t C, int64_t S, int64_t G);
+
+int gn_forward_cl(const void* x, int x_dtype, const float* gamma, const float* beta,
+                  int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
+                  void* y, int y_dtype, float* mean, float* rstd,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+int gn_backward_cl(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                   const float* mean, const float* rstd, const float* gamma,
+                   const float* beta, int activation,
+                   int64_t N, int64_t C, int64_t S, int64_t G,
+                   void* dx, float* dgamma, float* dbeta,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The channels-last plan. A reduction job is chunk voxels of one sample (jobs_per_sample
+ * per sample; the last may be shorter); lane t of a workgroup of `block` threads owns the
+ * channel vector t mod (C/8) and voxel t / (C/8) + r * voxels_per_round of round r
+ * (rounds_per_step rounds per reduction step, apply_rounds per streaming job).
+ */
+typedef struct gn_plan_info_cl {
+    int64_t chunk;                /* voxels per reduction job */
+    int64_t jobs_per_sample;
+    int64_t jobs;                 /* N * jobs_per_sample */
+    int64_t voxels_per_round;     /* block / (C/8) */
+    int64_t apply_chunk;          /* voxels per streaming job */
+    int64_t apply_jobs_per_sample;
+    int64_t apply_jobs;
+    int32_t block;                /* threads per workgroup */
+    int32_t rounds_per_step;
+    int32_t apply_rounds;
+    int32_t groups_per_vector;    /* max(1, 8 / (C/G)) */
+    size_t workspace_bytes;       /* == gn_workspace_bytes_cl */
+} gn_plan_info_cl;
+
+int gn_plan_query_cl(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info_cl* out);
 
 /* ABI version of this header (incremented on any incompatible change). */
 int gn_abi_version(void);

@@ -6,6 +6,7 @@ import re
 
 import pytest
 
+import unet_groupnorm_amd as g
 from unet_groupnorm_amd._lib import GN_BF16, GN_F32, STATUS_NAMES, lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -20,7 +21,7 @@ def _declared_functions():
 
 def test_every_declared_function_is_exported():
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -36,7 +37,7 @@ def test_status_enum_matches_header():
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == 5
+    assert lib.gn_abi_version() == 6
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every
@@ -106,14 +107,8 @@ def test_split_phase_validation():
                                  1 << 20, None) == 10
 
 
-def test_plan_info_struct_matches_header():
-    """The ctypes mirror of gn_plan_info has the header's fields, in order, with the same
-    widths (a drift here would make gn_plan_query write past the Python structure)."""
-    import pathlib
-
-    from unet_groupnorm_amd._lib import GnPlanInfo
-    text = (pathlib.Path(__file__).resolve().parents[1] / "include" / "gn.h").read_text()
-    body = re.search(r"typedef struct gn_plan_info \{(.*?)\} gn_plan_info;", text, re.S).group(1)
+def _struct_fields(text, name):
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, re.S).group(1)
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
     fields = []
     for decl in body.split(";"):
@@ -123,6 +118,53 @@ def test_plan_info_struct_matches_header():
         ctype, names = decl.split(None, 1)
         for nm in names.split(","):
             fields.append((nm.strip(), ctype))
+    return fields
+
+
+@pytest.mark.parametrize("cname,pyname", [("gn_plan_info", "GnPlanInfo"), ("gn_plan_info_cl", "GnPlanInfoCL")])
+def test_plan_info_struct_matches_header(cname, pyname):
+    """The ctypes mirrors of the plan structs have the header's fields, in order, with the
+    same widths (a drift here would make the query write past the Python structure)."""
+    import pathlib
+
+    from unet_groupnorm_amd import _lib as L
+    text = (pathlib.Path(__file__).resolve().parents[1] / "include" / "gn.h").read_text()
     width = {"int64_t": 8, "int32_t": 4, "size_t": 8}
-    ours = [(nm, ctypes.sizeof(t)) for nm, t in GnPlanInfo._fields_]
-    assert ours == [(nm, width[t]) for nm, t in fields]
+    ours = [(nm, ctypes.sizeof(t)) for nm, t in getattr(L, pyname)._fields_]
+    assert ours == [(nm, width[t]) for nm, t in _struct_fields(text, cname)]
+
+
+
+def cl_fwd(**kw):
+    args = dict(x=A, xdt=GN_BF16, gamma=None, beta=None, N=1, C=32, S=64, G=8, eps=1e-5, act=0, y=B,
+                ydt=GN_BF16, mean=A, rstd=B, ws=A, wsb=1 << 24, stream=None)
+    args.update(kw)
+    return lib.gn_forward_cl(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=12, G=4), 11),            # C not a multiple of 8
+    (dict(C=24, G=8), 11),            # C/8 = 3 does not divide 256
+    (dict(C=48, G=4), 11),            # C/G = 12: neither divides 8 nor a multiple of 8
+    (dict(C=4096, G=8), 11),          # C/8 = 512 > 256
+    (dict(C=32, G=5), 3),             # C % G
+    (dict(N=0), 2),
+    (dict(x=None), 1),
+    (dict(wsb=16), 6),
+    (dict(xdt=7), 4),
+    (dict(act=3), 10),
+    (dict(y=ctypes.c_void_p(0x20004)), 7),
+])
+def test_channels_last_validation(kw, status):
+    assert cl_fwd(**kw) == status
+
+
+@pytest.mark.parametrize("C,G", [(8, 8), (16, 2), (32, 8), (64, 8), (128, 16), (512, 32), (2048, 1), (8, 1)])
+def test_channels_last_supported_shapes_have_a_plan(C, G):
+    p = g.gn_plan_query_cl(2, C, 1000, G)
+    Cg = C // G
+    assert p["groups_per_vector"] == max(1, 8 // Cg)
+    assert p["voxels_per_round"] * (C // 8) == p["block"]
+    assert lib.gn_workspace_bytes_cl(2, C, 1000, G) == p["workspace_bytes"] > 0
+    assert lib.gn_backward_cl(A, GN_BF16, B, GN_BF16, A, B, None, None, 0, 2, C, 1000, G, None, None, None,
+                              A, 16, None) == 6

@@ -32,27 +32,41 @@ def _on_gpu(inp):
     return out
 
 
-def _run(inp, out_dtype=None, dy=None, relu=False):
+def _run(inp, out_dtype=None, dy=None, relu=False, layout=None):
     x, G, eps = inp["x"], inp["G"], inp["eps"]
     act = "relu" if relu else None
     y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, eps, out_dtype or inp["out_dtype"],
-                                  activation=act)
+                                  activation=act, layout=layout)
     dy = inp["dy"] if dy is None else dy
-    dx, dg, db = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G, beta=inp["beta"], activation=act)
+    dx, dg, db = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G, beta=inp["beta"], activation=act,
+                                layout=layout)
     torch.cuda.synchronize()
     return {"y": y, "mean": mean, "rstd": rstd, "dx": dx, "dgamma": dg, "dbeta": db}
+
+
+def _run_layout(inp, relu, layout):
+    """Runs the GPU path with x and dy in `layout`; returns outputs as contiguous NCDHW."""
+    if layout == "ndhwc":
+        inp = dict(inp)
+        inp["x"] = gn.as_layout(inp["x"], "ndhwc")
+        inp["dy"] = gn.as_layout(inp["dy"], "ndhwc")
+    r = _run(inp, relu=relu, layout=layout)
+    if layout == "ndhwc":
+        assert r["y"].stride() == inp["x"].stride() and r["dx"].stride() == inp["x"].stride()
+        r["y"], r["dx"] = r["y"].contiguous(), r["dx"].contiguous()
+    return r
 
 
 def _chan_at(idx, x, gamma, beta):
     return P.channel_params_at(idx, tuple(x.shape), gamma.cpu().numpy(), beta.cpu().numpy())
 
 
-def full_check(inp, tag, relu=False):
+def full_check(inp, tag, relu=False, layout="ncdhw"):
     """Element-by-element comparison of every output."""
     say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} dy {inp['dy'].dtype} "
-        f"out {inp['out_dtype']} G={inp['G']} relu={relu} -> gn_forward + gn_backward")
+        f"out {inp['out_dtype']} G={inp['G']} relu={relu} {layout} -> gn_forward + gn_backward")
     g = _on_gpu(inp)
-    r = _run(g, relu=relu)
+    r = _run_layout(g, relu, layout)
     x, dy, G, eps = inp["x"].cpu(), inp["dy"].cpu(), inp["G"], inp["eps"]
     gamma, beta = inp["gamma"].cpu(), inp["beta"].cpu()
     f = O.forward(x, G, gamma, beta, eps=eps, relu=relu)
@@ -93,11 +107,11 @@ def _sample_indices(x, G, n_random, seed):
     return np.unique(np.concatenate(parts)).astype(np.int64)
 
 
-def sampled_check(inp, tag, n_random=1 << 20, seed=0, relu=False):
+def sampled_check(inp, tag, n_random=1 << 20, seed=0, relu=False, layout="ncdhw"):
     """Full statistics and parameter gradients; y and dx on sampled elements."""
-    say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} G={inp['G']} relu={relu} "
+    say(f"{tag}: shape {tuple(inp['x'].shape)} x {inp['x'].dtype} G={inp['G']} relu={relu} {layout} "
         f"(sampled) -> gn_forward + gn_backward")
-    r = _run(inp, relu=relu)
+    r = _run_layout(inp, relu, layout)
     x, dy, G, eps = inp["x"].cpu(), inp["dy"].cpu(), inp["G"], inp["eps"]
     gamma, beta = inp["gamma"].cpu(), inp["beta"].cpu()
     say(f"{tag}: oracle statistics")
@@ -474,6 +488,103 @@ def test_fp16_dy_and_fp32_dy_give_the_same_bits(case):
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(_bits(u), _bits(v))
+
+
+# ----------------------------------------------------------------------------- channels-last
+
+CL_CASES = [
+    workloads.custom(2, 32, 8, (6, 7, 5), torch.bfloat16, dist="unet", seed=61),           # C/G 4: 2 groups a vector
+    workloads.custom(1, 64, 8, (16, 16, 17), torch.bfloat16, dist="normal", seed=62),      # C/G 8
+    workloads.custom(3, 8, 8, (5, 5, 5), torch.float32, dist="tiny", seed=63),             # C/G 1: 8 groups a vector
+    workloads.custom(2, 16, 1, (9, 9, 9), torch.bfloat16, dist="deep", seed=64, out_dtype=torch.float32),
+    workloads.custom(1, 512, 32, (8, 8, 8), torch.bfloat16, dist="deep", seed=65),         # C/8 = 64
+    workloads.custom(2, 1024, 16, (3, 4, 5), torch.float16, dist="normal", seed=66),       # C/8 = 128 > 64 lanes
+    workloads.custom(1, 2048, 2048, (2, 2, 3), torch.bfloat16, dist="unet", seed=67),      # C/8 = 256, C/G 1
+    workloads.custom(2, 32, 8, (4, 4, 4), torch.float16, torch.float32, dist="unet", seed=68),
+    workloads.custom(2, 8, 8, (1, 1, 1), torch.float32, dist="normal", seed=69),           # M = 1
+    workloads.custom(1, 16, 4, (40, 41, 42), torch.bfloat16, dist="unet", seed=70),        # many jobs, ragged
+]
+
+
+@pytest.mark.parametrize("case", CL_CASES, ids=lambda c: c.name + "_" + str(c.x_dtype).split(".")[-1])
+def test_channels_last_elementwise(case):
+    full_check(workloads.make(case, "cpu"), case.name + "_cl", layout="ndhwc")
+
+
+@pytest.mark.parametrize("case", CL_CASES[:3], ids=lambda c: c.name)
+def test_channels_last_relu_elementwise(case):
+    full_check(workloads.make(case, "cpu"), case.name + "_cl_relu", relu=True, layout="ndhwc")
+
+
+def test_channels_last_nan_and_inf_confined_to_their_group():
+    say("channels-last: NaN/Inf in two groups of (2, 32, 6, 6, 6), G=8")
+    inp = workloads.make(workloads.custom(2, 32, 8, (6, 6, 6), torch.bfloat16, seed=71), "cpu")
+    x = inp["x"].clone()
+    x[0, 5, 1, 1, 1] = float("nan")
+    x[1, 30, 0, 2, 0] = float("inf")
+    inp["x"] = x
+    full_check(inp, "nan_inf_cl", layout="ndhwc")
+
+
+@pytest.mark.parametrize("case", [workloads.SCALE7], ids=lambda c: c.name)
+def test_channels_last_top_site_sampled(case):
+    sampled_check(workloads.make(case, DEV), case.name + "_cl", n_random=1 << 18, seed=case.seed, layout="ndhwc")
+
+
+def test_channels_last_bitwise_properties():
+    """bf16 output = fp32 output rounded once; bf16 and fp32 dy with the same values give
+    the same bits; ten repeats are identical; constant input gives beta exactly."""
+    case = workloads.custom(1, 64, 8, (32, 32, 32), torch.bfloat16, dist="unet", seed=72)
+    say(f"channels-last bitwise properties on {case.name}")
+    inp = workloads.make(case, DEV)
+    x, G = gn.as_layout(inp["x"], "ndhwc"), inp["G"]
+    dy = gn.as_layout(inp["dy"], "ndhwc")
+    y16, m16, r16 = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], torch.bfloat16)
+    y32, m32, r32 = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], torch.float32)
+    a = gn.gn_backward(dy, x, m16, r16, inp["gamma"], G)
+    b = gn.gn_backward(gn.as_layout(dy.float(), "ndhwc"), x, m16, r16, inp["gamma"], G)
+    torch.cuda.synchronize()
+    assert torch.equal(m16, m32) and torch.equal(r16, r32)
+    ref = O.round_bf16(y32.contiguous().cpu().numpy().astype(np.float64).reshape(-1))
+    assert np.array_equal(P.to_np(y16.contiguous()).reshape(-1), ref)
+    for u, v in zip(a, b):
+        assert torch.equal(_bits(u.contiguous()), _bits(v.contiguous()))
+    for _ in range(9):
+        c = gn.gn_backward(dy, x, m16, r16, inp["gamma"], G)
+        y2, _, _ = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y2), _bits(y16))
+        for u, v in zip(a, c):
+            assert torch.equal(_bits(u), _bits(v))
+    const = torch.full_like(x, 3.25)
+    yc, _, _ = gn.gn_forward(const, inp["gamma"], inp["beta"], G, inp["eps"])
+    torch.cuda.synchronize()
+    assert torch.equal(yc.contiguous(), inp["beta"].to(torch.bfloat16).view(1, -1, 1, 1, 1).expand_as(yc).contiguous())
+
+
+def test_channels_last_autograd_keeps_the_layout():
+    say("group_norm on a channels_last_3d tensor through autograd")
+    inp = workloads.make(workloads.custom(2, 32, 8, (8, 8, 8), torch.bfloat16, dist="unet", seed=73), DEV)
+    x = inp["x"].contiguous(memory_format=torch.channels_last_3d).requires_grad_(True)
+    gamma = inp["gamma"].clone().requires_grad_(True)
+    beta = inp["beta"].clone().requires_grad_(True)
+    y = gn.group_norm(x, inp["G"], gamma, beta, inp["eps"], activation="relu")
+    assert y.is_contiguous(memory_format=torch.channels_last_3d)
+    y.backward(inp["dy"])    # an NCDHW gradient is brought to x's layout
+    assert x.grad.is_contiguous(memory_format=torch.channels_last_3d)
+    y2, m2, r2 = gn.gn_forward(x.detach(), inp["gamma"], inp["beta"], inp["G"], inp["eps"], activation="relu")
+    dx2, dg2, db2 = gn.gn_backward(gn.as_layout(inp["dy"], "ndhwc"), x.detach(), m2, r2, inp["gamma"], inp["G"],
+                                   beta=inp["beta"], activation="relu")
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), y2) and torch.equal(x.grad, dx2)
+    assert torch.equal(gamma.grad, dg2) and torch.equal(beta.grad, db2)
+
+
+def test_channels_last_rejects_unsupported_shapes():
+    x = torch.zeros((1, 24, 4, 4, 4), dtype=torch.bfloat16, device=DEV).contiguous(memory_format=torch.channels_last_3d)
+    with pytest.raises(gn.GnError, match="GN_ERR_LAYOUT"):
+        gn.gn_forward(x, None, None, 8, out=torch.empty_like(x), mean=torch.empty(1, 8, device=DEV),
+                      rstd=torch.empty(1, 8, device=DEV), workspace=torch.empty(1 << 20, dtype=torch.uint8, device=DEV))
 
 
 # ----------------------------------------------------------------------------- resident path

@@ -236,3 +236,85 @@ def test_resident_workgroups_cover_every_element_once_and_stay_in_bounds(N, C, S
             gv = (n * C + gg * Cg) * W + r
             np.add.at(seen, gv, 1)
         assert (seen == 1).all()
+
+
+# ----------------------------------------------------------------------------- channels-last
+
+CL_SHAPES = [
+    (1, 32, 4096, 8), (2, 32, 1000, 8), (1, 64, 64 ** 3, 8), (3, 8, 77, 8), (1, 8, 77, 1),
+    (2, 16, 333, 2), (1, 512, 512, 32), (2, 2048, 40, 1), (1, 1024, 300, 64), (4, 128, 8, 16),
+    (1, 256, 4097, 32), (5, 64, 1, 64),
+]
+
+
+@pytest.mark.parametrize("N,C,S,G", CL_SHAPES)
+def test_channels_last_lanes_cover_every_vector_once(N, C, S, G):
+    """Restates the job -> voxel and lane -> (voxel, channel vector) arithmetic of the
+    channels-last kernels: every (voxel, channel vector) of the volume is read exactly once
+    by the reduction jobs and once by the streaming jobs, inside the volume."""
+    p = g.gn_plan_query_cl(N, C, S, G)
+    Cv, B, vps, R = C // VEC, p["block"], p["voxels_per_round"], p["rounds_per_step"]
+    assert B % Cv == 0 and vps == B // Cv
+    t = np.arange(B)
+    cv, vo = t % Cv, t // Cv
+    assert (p["chunk"] % (R * vps) == 0) or p["jobs_per_sample"] == 1
+    for chunk, K, rounds in ((p["chunk"], p["jobs_per_sample"], R), (p["apply_chunk"], p["apply_jobs_per_sample"], p["apply_rounds"])):
+        assert (K - 1) * chunk < S <= K * chunk
+        seen = np.zeros((N, S, Cv), dtype=np.int32)
+        for n in range(N):
+            for k in range(K):
+                v0, v1 = k * chunk, min((k + 1) * chunk, S)
+                step = rounds * vps
+                for s0 in range(v0, v1, step):
+                    for r in range(rounds):
+                        vox = s0 + r * vps + vo
+                        ok = vox < v1
+                        if not ok.any():
+                            continue
+                        off = (n * S + vox[ok]) * C + cv[ok] * VEC
+                        assert off.min() >= 0 and (off + VEC).max() <= N * S * C
+                        np.add.at(seen, (n, vox[ok], cv[ok]), 1)
+        assert (seen == 1).all()
+
+
+@pytest.mark.parametrize("N,C,S,G", CL_SHAPES)
+def test_channels_last_slots_and_holders(N, C, S, G):
+    """The lane's slots name the right groups, and the workgroup merge of group g (holder
+    lanes of each wave after the strided shuffle tree) takes exactly the lanes whose channel
+    vector holds g, each once."""
+    p = g.gn_plan_query_cl(N, C, S, G)
+    Cg, Cv, B, NGL = C // G, C // VEC, p["block"], p["groups_per_vector"]
+    W = VEC // NGL
+    for cvi in range(Cv):
+        g0 = cvi * VEC // Cg
+        for i in range(VEC):
+            assert (cvi * VEC + i) // Cg == g0 + i // W
+    reps = min(Cv, 64)
+    # lanes each holder represents after the strided tree (off = 32, 16, ..., Cv)
+    def represented(w, l):
+        if Cv >= 64:
+            return [w * 64 + l]
+        return [w * 64 + l + q * Cv for q in range(64 // Cv)]
+
+    def holder(c, w):
+        l = ((c - 64 * w) % Cv + Cv) % Cv
+        return l if l < 64 else -1
+
+    for grp in range(G):
+        if Cg < VEC:
+            lo, hi, slot = grp * Cg // VEC, grp * Cg // VEC + 1, (grp * Cg % VEC) // Cg
+        else:
+            lo, hi, slot = grp * Cg // VEC, (grp + 1) * Cg // VEC, 0
+        got = []
+        for w in range(B // 64):
+            for c in range(lo, hi):
+                l = holder(c, w)
+                if l >= 0:
+                    assert l < reps and (w * 64 + l) * NGL + slot < B * NGL
+                    got += represented(w, l)
+        want = [tt for tt in range(B) if lo <= tt % Cv < hi]
+        assert sorted(got) == want
+        # the slot of lane vector c that holds group grp
+        assert (lo * VEC // Cg) + slot == grp
+    # workspace areas: partials (jobs x C float2), per-channel float2, per-group float4
+    assert p["workspace_bytes"] >= p["jobs"] * C * 8 + N * C * 8 + N * G * 16

@@ -1,10 +1,12 @@
-"""MI355X-native 3D GroupNorm (NCDHW, bf16/fp32 in, fp32 statistics) behind a C ABI.
+"""MI355X-native 3D GroupNorm (NCDHW or channels-last; fp32, bf16 or fp16 in; fp32
+statistics) behind a C ABI.
 
 The kernels live in libgn.so (csrc/); this package is its torch binding.
 """
 from .gn import (  # noqa: F401
     GnError,
     GroupNormFn,
+    as_layout,
     gn_backward,
     gn_backward_apply,
     gn_backward_reduce,
@@ -12,7 +14,9 @@ from .gn import (  # noqa: F401
     gn_forward_apply,
     gn_forward_stats,
     gn_plan_query,
+    gn_plan_query_cl,
     gn_workspace_bytes,
     group_norm,
+    layout_of,
     workspace_for,
 )

@@ -16,7 +16,7 @@ GN_ACT_NONE, GN_ACT_RELU = 0, 1
 STATUS_NAMES = {
     0: "GN_OK", 1: "GN_ERR_NULL", 2: "GN_ERR_SHAPE", 3: "GN_ERR_GROUPS", 4: "GN_ERR_DTYPE",
     5: "GN_ERR_EPS", 6: "GN_ERR_WORKSPACE", 7: "GN_ERR_ALIGN", 8: "GN_ERR_DEVICE", 9: "GN_ERR_LAUNCH",
-    10: "GN_ERR_ACTIVATION",
+    10: "GN_ERR_ACTIVATION", 11: "GN_ERR_LAYOUT",
 }
 
 
@@ -44,6 +44,23 @@ class GnPlanInfo(ctypes.Structure):
     ]
 
 
+class GnPlanInfoCL(ctypes.Structure):
+    _fields_ = [
+        ("chunk", ctypes.c_int64),
+        ("jobs_per_sample", ctypes.c_int64),
+        ("jobs", ctypes.c_int64),
+        ("voxels_per_round", ctypes.c_int64),
+        ("apply_chunk", ctypes.c_int64),
+        ("apply_jobs_per_sample", ctypes.c_int64),
+        ("apply_jobs", ctypes.c_int64),
+        ("block", ctypes.c_int32),
+        ("rounds_per_step", ctypes.c_int32),
+        ("apply_rounds", ctypes.c_int32),
+        ("groups_per_vector", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 def _declare(lib):
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
@@ -57,6 +74,10 @@ def _declare(lib):
         "gn_status_string": (ctypes.c_char_p, [I]),
         "gn_plan_query": (I, [I64, I64, I64, I64, ctypes.POINTER(GnPlanInfo)]),
         "gn_abi_version": (I, []),
+        "gn_workspace_bytes_cl": (SZ, [I64, I64, I64, I64]),
+        "gn_forward_cl": (I, [P, I, P, P, I64, I64, I64, I64, F, I, P, I, P, P, P, SZ, P]),
+        "gn_backward_cl": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, P, P, SZ, P]),
+        "gn_plan_query_cl": (I, [I64, I64, I64, I64, ctypes.POINTER(GnPlanInfoCL)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

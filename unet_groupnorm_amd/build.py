@@ -1,7 +1,8 @@
 """Build step for libgn.so, the HIP GroupNorm library (gfx950 only).
 
-Compiles the C ABI (csrc/gn_api.cpp), the launch plan (csrc/gn_plan.cpp) and the
-kernels (csrc/gn_kernels.hip) with hipcc into ``unet_groupnorm_amd/libgn.so``.
+Compiles the C ABI (csrc/gn_api.cpp), the launch plans (csrc/gn_plan.cpp) and the
+kernels (csrc/gn_kernels.hip for NCDHW, csrc/gn_kernels_cl.hip for channels-last) with
+hipcc into ``unet_groupnorm_amd/libgn.so``.
 """
 import os
 import subprocess
@@ -11,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgn.so")
-SOURCES = ["gn_plan.cpp", "gn_api.cpp", "gn_kernels.hip"]
+SOURCES = ["gn_plan.cpp", "gn_api.cpp", "gn_kernels.hip", "gn_kernels_cl.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -142,7 +142,7 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 5; }
+int gn_abi_version(void) { return 6; }
 
 const char* gn_status_string(int status)
 {
@@ -158,6 +158,7 @@ const char* gn_status_string(int status)
         case GN_ERR_DEVICE: return "x is not device memory or the stream belongs to another device";
         case GN_ERR_LAUNCH: return "kernel launch failed";
         case GN_ERR_ACTIVATION: return "unknown activation (GN_ACT_NONE or GN_ACT_RELU)";
+        case GN_ERR_LAYOUT: return "shape not supported channels-last (C a multiple of 8 with C/8 dividing 256; C/G dividing 8 or a multiple of 8)";
         default: return "unknown status";
     }
 }
@@ -295,6 +296,85 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
         return rc;
     if (!dx) return GN_OK;
     return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, a, w, st));
+}
+
+// ------------------------------------------------------------------ channels-last
+
+static int plan_cl_or_error(int64_t N, int64_t C, int64_t S, int64_t G, gn::PlanCL* p)
+{
+    const int rc = gn::make_plan_cl(N, C, S, G, p);
+    if (rc == 0) return GN_OK;
+    return rc == 3 ? GN_ERR_GROUPS : (rc == 4 ? GN_ERR_LAYOUT : GN_ERR_SHAPE);
+}
+
+size_t gn_workspace_bytes_cl(int64_t N, int64_t C, int64_t S, int64_t G)
+{
+    gn::PlanCL p;
+    return gn::make_plan_cl(N, C, S, G, &p) == 0 ? p.ws_bytes : 0;
+}
+
+int gn_plan_query_cl(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info_cl* out)
+{
+    if (!out) return GN_ERR_NULL;
+    gn::PlanCL p;
+    const int rc = plan_cl_or_error(N, C, S, G, &p);
+    if (rc) return rc;
+    out->chunk = p.chunk;
+    out->jobs_per_sample = p.K;
+    out->jobs = p.jobs;
+    out->voxels_per_round = p.vps;
+    out->apply_chunk = p.chunk_a;
+    out->apply_jobs_per_sample = p.K_a;
+    out->apply_jobs = p.jobs_a;
+    out->block = gn::kClBlock;
+    out->rounds_per_step = gn::kClRounds;
+    out->apply_rounds = gn::kClApplyRounds;
+    out->groups_per_vector = p.ngl;
+    out->workspace_bytes = p.ws_bytes;
+    return GN_OK;
+}
+
+int gn_forward_cl(const void* x, int x_dtype, const float* gamma, const float* beta,
+                  int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
+                  void* y, int y_dtype, float* mean, float* rstd,
+                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    // Same checks as gn_forward (which also rejects what no layout supports), then the
+    // channels-last plan and its workspace size.
+    gn::Plan base;
+    int rc = fwd_check(x, x_dtype, gamma, beta, N, C, S, G, eps, activation, y, y_dtype, mean, rstd,
+                       workspace, 0, &base);
+    if (rc && rc != GN_ERR_WORKSPACE) return rc;
+    gn::PlanCL p;
+    if ((rc = plan_cl_or_error(N, C, S, G, &p))) return rc;
+    if (workspace_bytes < p.ws_bytes) return GN_ERR_WORKSPACE;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    return launch_status(gn::launch_cl_forward(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype,
+                                               gn::clargs_of(p, activation), gn::workspace_cl_of(workspace, p),
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int gn_backward_cl(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                   const float* mean, const float* rstd, const float* gamma,
+                   const float* beta, int activation,
+                   int64_t N, int64_t C, int64_t S, int64_t G,
+                   void* dx, float* dgamma, float* dbeta,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan base;
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, activation, N, C, S, G, dx,
+                       dgamma, dbeta, workspace, 0, &base);
+    if (rc && rc != GN_ERR_WORKSPACE) return rc;
+    gn::PlanCL p;
+    if ((rc = plan_cl_or_error(N, C, S, G, &p))) return rc;
+    if (workspace_bytes < p.ws_bytes) return GN_ERR_WORKSPACE;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    return launch_status(gn::launch_cl_backward(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx, dgamma,
+                                                dbeta, gn::clargs_of(p, activation),
+                                                gn::workspace_cl_of(workspace, p),
+                                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

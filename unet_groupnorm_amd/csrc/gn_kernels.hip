@@ -34,206 +34,11 @@
 // NDHWC kernel: corrected two-pass per tile combined by Chan's formula, register-only
 // reductions, fixed order, no float atomics). No atomics are used anywhere, so every
 // result is bitwise reproducible run to run.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include <tuple>
-#include <type_traits>
-
-#include "gn_launch.hpp"
-
-// Load cache policy per kernel (1: nontemporal) and the order of the streaming grid
-// (1: last row first); compile-time overridable for measurement builds.
-#ifndef GN_NT_STATS
-#define GN_NT_STATS 1
-#endif
-#ifndef GN_NT_BRED
-#define GN_NT_BRED 1
-#endif
-#ifndef GN_NT_APPLY
-#define GN_NT_APPLY 1
-#endif
-#ifndef GN_NT_BAPPLY
-#define GN_NT_BAPPLY 1
-#endif
-#ifndef GN_REVERSE_APPLY
-#define GN_REVERSE_APPLY 0
-#endif
-#ifndef GN_NT_STORE
-#define GN_NT_STORE 0
-#endif
+#include "gn_device.hpp"
 
 namespace gn {
 
 namespace {
-
-constexpr bool kNtStats = GN_NT_STATS, kNtBwdReduce = GN_NT_BRED;
-constexpr bool kNtApply = GN_NT_APPLY, kNtBwdApply = GN_NT_BAPPLY;
-constexpr bool kReverseApply = GN_REVERSE_APPLY;
-constexpr bool kNtStore = GN_NT_STORE;
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// ------------------------------------------------------------------ element access
-
-// bf16 is stored as the upper 16 bits of an fp32: widening is exact.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Narrowing fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
-{
-    f32x2 f = {a, b};
-    bf16x2 h = __builtin_convertvector(f, bf16x2);
-    return __builtin_bit_cast(uint32_t, h);
-}
-
-// The optional activation ("Optimize GroupNorm", paragraphs on the fused ReLU and on the
-// NaN-correct ReLU): relu is 0 where v < 0 and v otherwise, so NaN, +Inf and -0.0 pass;
-// its gradient is blocked where the relu result is <= 0 and passes otherwise (NaN too).
-__device__ __forceinline__ float relu_f(float v) { return v < 0.0f ? 0.0f : v; }
-__device__ __forceinline__ float relu_gate(float pre, float g) { return relu_f(pre) <= 0.0f ? 0.0f : g; }
-
-// Loads of the streamed tensors are marked nontemporal: each element is read once per
-// kernel, and on MI355X this lifts a streaming read from about 6.2 to about 7 TB/s.
-template <typename T> struct Io;
-
-template <> struct Io<uint16_t> {  // bf16 storage
-    // One 8-element vector as loaded (16 bytes), widened only where it is used.
-    struct Raw {
-        u32x4 u;
-    };
-    template <bool NT>
-    static __device__ __forceinline__ Raw load_raw(const uint16_t* p)
-    {
-        const u32x4* q = reinterpret_cast<const u32x4*>(p);
-        return Raw{NT ? __builtin_nontemporal_load(q) : *q};
-    }
-    static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
-    {
-        v[0] = bf16_lo(r.u.x); v[1] = bf16_hi(r.u.x);
-        v[2] = bf16_lo(r.u.y); v[3] = bf16_hi(r.u.y);
-        v[4] = bf16_lo(r.u.z); v[5] = bf16_hi(r.u.z);
-        v[6] = bf16_lo(r.u.w); v[7] = bf16_hi(r.u.w);
-    }
-    template <bool NT>
-    static __device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8])
-    {
-        widen(load_raw<NT>(p), v);
-    }
-    static __device__ __forceinline__ float load1(const uint16_t* p)
-    {
-        return __uint_as_float(uint32_t(*p) << 16);
-    }
-    static __device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8])
-    {
-        u32x4 u;
-        u.x = pack_bf16(v[0], v[1]);
-        u.y = pack_bf16(v[2], v[3]);
-        u.z = pack_bf16(v[4], v[5]);
-        u.w = pack_bf16(v[6], v[7]);
-        if (kNtStore)
-            __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
-        else
-            *reinterpret_cast<u32x4*>(p) = u;
-    }
-    static __device__ __forceinline__ void store1(uint16_t* p, float v)
-    {
-        *p = uint16_t(pack_bf16(v, 0.0f) & 0xffffu);
-    }
-};
-
-template <> struct Io<float> {
-    struct Raw {
-        f32x4 a, b;
-    };
-    template <bool NT>
-    static __device__ __forceinline__ Raw load_raw(const float* p)
-    {
-        const f32x4* q = reinterpret_cast<const f32x4*>(p);
-        return NT ? Raw{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1)} : Raw{q[0], q[1]};
-    }
-    static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
-    {
-        v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
-        v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
-    }
-    template <bool NT>
-    static __device__ __forceinline__ void load8(const float* p, float (&v)[8])
-    {
-        widen(load_raw<NT>(p), v);
-    }
-    static __device__ __forceinline__ float load1(const float* p) { return *p; }
-    static __device__ __forceinline__ void store8(float* p, const float (&v)[8])
-    {
-        const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
-        if (kNtStore) {
-            __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
-            __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
-        } else {
-            *reinterpret_cast<f32x4*>(p) = a;
-            *reinterpret_cast<f32x4*>(p + 4) = b;
-        }
-    }
-    static __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
-};
-
-// fp16 storage (IEEE binary16): widening is exact; narrowing converts one value at a time
-// with round-to-nearest-even (the default rounding mode), keeping fp16 subnormals and
-// overflowing to infinity.
-template <> struct Io<_Float16> {
-    struct Raw {
-        u32x4 u;
-    };
-    static __device__ __forceinline__ float lo(uint32_t w)
-    {
-        return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xffffu)));
-    }
-    static __device__ __forceinline__ float hi(uint32_t w)
-    {
-        return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16)));
-    }
-    static __device__ __forceinline__ uint32_t pack(float a, float b)
-    {
-        return uint32_t(__builtin_bit_cast(uint16_t, _Float16(a))) |
-               (uint32_t(__builtin_bit_cast(uint16_t, _Float16(b))) << 16);
-    }
-    template <bool NT>
-    static __device__ __forceinline__ Raw load_raw(const _Float16* p)
-    {
-        const u32x4* q = reinterpret_cast<const u32x4*>(p);
-        return Raw{NT ? __builtin_nontemporal_load(q) : *q};
-    }
-    static __device__ __forceinline__ void widen(const Raw& r, float (&v)[8])
-    {
-        v[0] = lo(r.u.x); v[1] = hi(r.u.x);
-        v[2] = lo(r.u.y); v[3] = hi(r.u.y);
-        v[4] = lo(r.u.z); v[5] = hi(r.u.z);
-        v[6] = lo(r.u.w); v[7] = hi(r.u.w);
-    }
-    template <bool NT>
-    static __device__ __forceinline__ void load8(const _Float16* p, float (&v)[8])
-    {
-        widen(load_raw<NT>(p), v);
-    }
-    static __device__ __forceinline__ float load1(const _Float16* p) { return float(*p); }
-    static __device__ __forceinline__ void store8(_Float16* p, const float (&v)[8])
-    {
-        u32x4 u;
-        u.x = pack(v[0], v[1]);
-        u.y = pack(v[2], v[3]);
-        u.z = pack(v[4], v[5]);
-        u.w = pack(v[6], v[7]);
-        if (kNtStore)
-            __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
-        else
-            *reinterpret_cast<u32x4*>(p) = u;
-    }
-    static __device__ __forceinline__ void store1(_Float16* p, float v) { *p = _Float16(v); }
-};
 
 // ------------------------------------------------------------------ job geometry
 
@@ -266,103 +71,6 @@ __device__ __forceinline__ int64_t job_count(const KArgs& a, int64_t k)
 {
     const int64_t end = (k + 1) * a.chunk;
     return (end < a.S ? end : a.S) - k * a.chunk;
-}
-
-// ------------------------------------------------------------------ Chan merge
-
-template <typename CT>
-struct Moments {
-    CT n;
-    float m, M2;
-};
-
-// a <- a (+) b with Chan's parallel formula. Empty operands are skipped, so a merge
-// never mixes a zero count into the mean. With equal means (a constant group) the mean
-// is untouched and M2 stays exactly zero. An infinite mean (a part holding +-Inf) stays
-// what the sum of the parts makes it (+-Inf, or NaN for opposite signs) instead of the
-// NaN that Inf - Inf would give; its M2 is already NaN.
-template <typename CT>
-__device__ __forceinline__ void chan_merge(Moments<CT>& a, CT nb, float mb, float M2b)
-{
-    if (nb == 0) return;
-    if (a.n == 0) {
-        a.n = nb; a.m = mb; a.M2 = M2b;
-        return;
-    }
-    const CT n = a.n + nb;
-    const float w = float(nb) / float(n);
-    const float d = mb - a.m;
-    const bool inf = __builtin_isinf(a.m) || __builtin_isinf(mb);
-    a.m = inf ? a.m + mb : fmaf(d, w, a.m);
-    a.M2 = (a.M2 + M2b) + (d * d) * (float(a.n) * w);
-    a.n = n;
-}
-
-// Lane 0 ends up with the merge of all 64 lanes, combined in a fixed tree: lane i takes
-// lane i + off for off = 32, 16, ..., 1 (left operand always the lower lane).
-template <typename CT>
-__device__ __forceinline__ void wave_merge(Moments<CT>& a)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const CT nb = __shfl_down(a.n, off);
-        const float mb = __shfl_down(a.m, off);
-        const float Mb = __shfl_down(a.M2, off);
-        chan_merge(a, nb, mb, Mb);
-    }
-}
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_down(v, off);
-    return v;
-}
-
-// Balanced pairwise sum of 2^k values (pairs i, i + half at every level), leaving the
-// input intact. A constant input is summed exactly: every addition doubles a value.
-template <int N>
-__device__ __forceinline__ float tree_sum(const float (&t)[N])
-{
-    float h[N / 2];
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) h[i] = t[i] + t[i + N / 2];
-#pragma unroll
-    for (int w = N / 4; w >= 1; w >>= 1) {
-#pragma unroll
-        for (int i = 0; i < w; ++i) h[i] = h[i] + h[i + w];
-    }
-    return h[0];
-}
-
-// Sum of squares in the same tree shape, first level fused: d_i^2 + d_{i+half}^2.
-template <int N>
-__device__ __forceinline__ float tree_sumsq(const float (&d)[N])
-{
-    float h[N / 2];
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) h[i] = fmaf(d[i], d[i], d[i + N / 2] * d[i + N / 2]);
-#pragma unroll
-    for (int w = N / 4; w >= 1; w >>= 1) {
-#pragma unroll
-        for (int i = 0; i < w; ++i) h[i] = h[i] + h[i + w];
-    }
-    return h[0];
-}
-
-// Sum of products in the same tree shape, first level fused: a_i b_i + a_{i+half} b_{i+half}.
-template <int N>
-__device__ __forceinline__ float tree_sumprod(const float (&a)[N], const float (&b)[N])
-{
-    float h[N / 2];
-#pragma unroll
-    for (int i = 0; i < N / 2; ++i) h[i] = fmaf(a[i], b[i], a[i + N / 2] * b[i + N / 2]);
-#pragma unroll
-    for (int w = N / 4; w >= 1; w >>= 1) {
-#pragma unroll
-        for (int i = 0; i < w; ++i) h[i] = h[i] + h[i + w];
-    }
-    return h[0];
 }
 
 constexpr int kTile = kVec * kStepVecs;  // elements per lane per step (32)
@@ -437,44 +145,6 @@ __device__ __forceinline__ uint32_t load_step_masked(const T* __restrict__ p, co
     return valid;
 }
 
-
-constexpr int kMaxWaves = 4;
-
-// Merges the per-wave moments (lane 0 of each wave) in wave order; result valid in thread 0.
-template <typename CT>
-__device__ __forceinline__ Moments<CT> block_merge(Moments<CT> a, CT* s_n, float* s_m, float* s_M)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
-    wave_merge(a);
-    if (lane == 0) { s_n[wave] = a.n; s_m[wave] = a.m; s_M[wave] = a.M2; }
-    __syncthreads();
-    Moments<CT> r = {0, 0.0f, 0.0f};
-    if (threadIdx.x == 0) {
-        r.n = s_n[0]; r.m = s_m[0]; r.M2 = s_M[0];
-        for (int w = 1; w < nw; ++w) chan_merge(r, s_n[w], s_m[w], s_M[w]);
-    }
-    __syncthreads();
-    return r;
-}
-
-// Sums (lane 0 of each wave) in wave order; result valid in thread 0.
-__device__ __forceinline__ float2 block_sum2(float a, float b, float* s_a, float* s_b)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
-    a = wave_sum(a);
-    b = wave_sum(b);
-    if (lane == 0) { s_a[wave] = a; s_b[wave] = b; }
-    __syncthreads();
-    float2 r = make_float2(0.0f, 0.0f);
-    if (threadIdx.x == 0) {
-        r.x = s_a[0]; r.y = s_b[0];
-        for (int w = 1; w < nw; ++w) { r.x = r.x + s_a[w]; r.y = r.y + s_b[w]; }
-    }
-    __syncthreads();
-    return r;
-}
 
 // ------------------------------------------------------------------ forward
 
@@ -1134,37 +804,9 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
     }
 }
 
-// Launches kernel k and returns the runtime's status for this launch alone.
-template <typename... P, typename... A>
-hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... args)
-{
-    static_assert(sizeof...(P) == sizeof...(A), "argument count");
-    std::tuple<P...> t(args...);
-    void* ptrs[sizeof...(P)];
-    std::apply([&](auto&... e) {
-        int i = 0;
-        ((ptrs[i++] = static_cast<void*>(&e)), ...);
-    }, t);
-    return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, ptrs, 0, st);
-}
-
-template <typename T> const T* cp(const void* p) { return static_cast<const T*>(p); }
-template <typename T> T* mp(void* p) { return static_cast<T*>(p); }
-
-dim3 grid_of(int64_t jobs) { return dim3(unsigned(jobs < kMaxGrid ? jobs : kMaxGrid)); }
-
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
-
-// Calls f with a value of the storage type of dtype dt: float, bf16 (as uint16_t) or fp16.
-template <typename F>
-hipError_t with_type(int dt, F&& f)
-{
-    if (dt == kBF16) return f(uint16_t{});
-    if (dt == kF16) return f(_Float16{});
-    return f(float{});
-}
 
 hipError_t launch_fwd_stats(const void* x, int xdt, const float* gamma, const float* beta,
                             float eps, float* mean, float* rstd, const KArgs& a, Workspace ws,

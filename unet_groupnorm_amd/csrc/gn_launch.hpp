@@ -94,4 +94,53 @@ hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, cons
                           float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st,
                           int block, int vecs);
 
+// ------------------------------------------------------------------ channels-last
+
+struct ClArgs {
+    int64_t N, C, S, G, Cg, M;
+    int64_t Cv, vps;
+    int64_t chunk, K, jobs;
+    int64_t chunk_a, K_a, jobs_a;
+    int32_t ngl, act;
+};
+
+inline ClArgs clargs_of(const PlanCL& p, int act = 0)
+{
+    ClArgs a;
+    a.N = p.N; a.C = p.C; a.S = p.S; a.G = p.G; a.Cg = p.Cg; a.M = p.M;
+    a.Cv = p.Cv; a.vps = p.vps;
+    a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs;
+    a.chunk_a = p.chunk_a; a.K_a = p.K_a; a.jobs_a = p.jobs_a;
+    a.ngl = p.ngl; a.act = act;
+    return a;
+}
+
+// Channels-last workspace: partials (forward: one float2 per job and group; backward: one
+// per job and channel), per-channel float2 coefficients (forward: gamma_c*rstd, beta_c;
+// backward: rstd*gamma_c, beta_c) and per-group float4 coefficients (forward: mean head,
+// mean tail; backward: mean, -rstd*c1, -rstd^2*c2).
+struct WorkspaceCL {
+    float2* part;
+    float2* coefc;
+    float4* coefg;
+};
+
+inline WorkspaceCL workspace_cl_of(void* ws, const PlanCL& p)
+{
+    char* b = static_cast<char*>(ws);
+    return WorkspaceCL{reinterpret_cast<float2*>(b), reinterpret_cast<float2*>(b + p.ws_coefc_offset),
+                       reinterpret_cast<float4*>(b + p.ws_coefg_offset)};
+}
+
+// Forward, channels-last: statistics, finalize, normalize (three kernels).
+hipError_t launch_cl_forward(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                             float* mean, float* rstd, void* y, int ydt, const ClArgs& a,
+                             WorkspaceCL ws, hipStream_t st);
+// Backward, channels-last: per-channel sums, finalize (dgamma/dbeta, dx coefficients), dx
+// unless dx is null.
+hipError_t launch_cl_backward(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                              const float* rstd, const float* gamma, const float* beta, void* dx,
+                              float* dgamma, float* dbeta, const ClArgs& a, WorkspaceCL ws,
+                              hipStream_t st);
+
 }  // namespace gn

@@ -31,6 +31,8 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     // A single value per normalization set (N == 1 and M == 1) is rejected, as the stock
     // operator does; M == 1 with N > 1 is legal and answered exactly.
     if (N * Cg * S == 1) return 2;
+    // Finalize launches take one workgroup per group (and per channel).
+    if (N > ((int64_t(1) << 31) - 1 - C) / G) return 2;
 
     Plan q;
     q.N = N; q.C = C; q.S = S; q.G = G;
@@ -93,6 +95,55 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
 
     q.ws_coef_offset = size_t(round_up(q.jobs * 8, 256));
     q.ws_bytes = q.ws_coef_offset + size_t(round_up(q.rows * 32, 256));
+    *p = q;
+    return 0;
+}
+
+int make_plan_cl(int64_t N, int64_t C, int64_t S, int64_t G, PlanCL* p)
+{
+    Plan base;
+    const int rc = make_plan(N, C, S, G, &base);
+    if (rc) return rc;
+    const int64_t Cg = C / G;
+    if (C % kVec != 0) return 4;
+    const int64_t Cv = C / kVec;
+    if (Cv > kClBlock || kClBlock % Cv != 0) return 4;
+    if (!(Cg % kVec == 0 || kVec % Cg == 0)) return 4;
+
+    PlanCL q;
+    q.N = N; q.C = C; q.S = S; q.G = G;
+    q.Cg = Cg;
+    q.M = Cg * S;
+    q.Cv = Cv;
+    q.vps = kClBlock / Cv;
+    q.ngl = int(Cg >= kVec ? 1 : kVec / Cg);
+    // Reduction jobs: whole samples split until the launch has kTargetJobs jobs or a job is
+    // one step. A job's count per group (chunk * C/G elements) stays within kMaxChunk, so
+    // every in-job count fits 32 bits.
+    const int64_t step = kClRounds * q.vps;
+    const int64_t max_chunk = kMaxChunk / (Cg > kVec ? Cg : kVec);
+    int64_t K = 1, chunk = round_up(S, step);
+    while (chunk > max_chunk) {
+        K *= 2;
+        chunk = round_up(ceil_div(S, K), step);
+        K = ceil_div(S, chunk);
+    }
+    while (N * K < kTargetJobs) {
+        const int64_t c2 = round_up(ceil_div(S, K * 2), step);
+        const int64_t k2 = ceil_div(S, c2);
+        if (k2 <= K) break;
+        K = k2;
+        chunk = c2;
+    }
+    q.K = K;
+    q.chunk = chunk;
+    q.jobs = N * K;
+    q.chunk_a = kClApplyRounds * q.vps;
+    q.K_a = ceil_div(S, q.chunk_a);
+    q.jobs_a = N * q.K_a;
+    q.ws_coefc_offset = size_t(round_up(q.jobs * C * 8, 256));
+    q.ws_coefg_offset = q.ws_coefc_offset + size_t(round_up(N * C * 8, 256));
+    q.ws_bytes = q.ws_coefg_offset + size_t(round_up(N * G * 16, 256));
     *p = q;
     return 0;
 }

@@ -86,4 +86,30 @@ struct Plan {
 // (2 = GN_ERR_SHAPE, 3 = GN_ERR_GROUPS).
 int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p);
 
+// Channels-last (NDHWC: x[n][s][c] at (n*S + s)*C + c). Every voxel is C/8 whole vectors
+// (C a multiple of 8). A workgroup of kClBlock threads gives lane t the channel vector
+// t mod (C/8) for a whole job and the voxels t / (C/8) + r * vps, vps = kClBlock / (C/8);
+// so C/8 must divide kClBlock. The lane's 8 channels lie in ngl = max(1, 8 / (C/G))
+// groups, which needs C/G to divide 8 or to be a multiple of 8.
+constexpr int kClBlock = 256;
+constexpr int kClRounds = 4;        // voxel rounds a reduction lane holds per step
+constexpr int kClApplyRounds = 4;   // voxel rounds of a streaming job
+
+struct PlanCL {
+    int64_t N = 0, C = 0, S = 0, G = 0;
+    int64_t Cg = 0, M = 0;
+    int64_t Cv = 0;      // vectors per voxel (C / 8)
+    int64_t vps = 0;     // voxels per round of a workgroup (kClBlock / Cv)
+    int ngl = 0;         // groups per lane vector: 1, 2, 4 or 8
+    // reduction jobs: chunk voxels of one sample, K jobs per sample
+    int64_t chunk = 0, K = 0, jobs = 0;
+    // streaming jobs
+    int64_t chunk_a = 0, K_a = 0, jobs_a = 0;
+    // workspace: [partials: float2 * jobs * C][per-channel: float2 * N*C][per-group: float4 * N*G]
+    size_t ws_coefc_offset = 0, ws_coefg_offset = 0, ws_bytes = 0;
+};
+
+// Returns 0 and fills *p, else 2 (shape), 3 (groups) or 4 (shape not supported channels-last).
+int make_plan_cl(int64_t N, int64_t C, int64_t S, int64_t G, PlanCL* p);
+
 }  // namespace gn

@@ -5,13 +5,17 @@ allocates outputs and the workspace with torch on x's device, passes raw pointer
 the current HIP stream of that device, and turns a non-zero status into an exception.
 All arithmetic happens in the HIP kernels.
 
-Tensors are contiguous NCDHW (any number of trailing spatial dims, flattened to S).
+Tensors are contiguous NCDHW (any number of trailing spatial dims, flattened to S), or
+contiguous with the channel dimension last (NDHWC, torch's channels_last_3d for 5-D):
+gn_forward and gn_backward take either and return outputs in the input's layout; the
+split-phase entry points take NCDHW only.
 """
 import ctypes
 
 import torch
 
-from ._lib import GN_ACT_NONE, GN_ACT_RELU, GN_BF16, GN_F16, GN_F32, GN_OK, STATUS_NAMES, GnPlanInfo, lib
+from ._lib import (GN_ACT_NONE, GN_ACT_RELU, GN_BF16, GN_F16, GN_F32, GN_OK, STATUS_NAMES, GnPlanInfo,
+                   GnPlanInfoCL, lib)
 
 _DT = {torch.float32: GN_F32, torch.bfloat16: GN_BF16, torch.float16: GN_F16}
 _ACT = {None: GN_ACT_NONE, "none": GN_ACT_NONE, "relu": GN_ACT_RELU}
@@ -58,6 +62,39 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def layout_of(t):
+    """"ncdhw" for a contiguous tensor, "ndhwc" for one that is contiguous with the channel
+    dimension last (and not also contiguous), else ValueError."""
+    if t.is_contiguous():
+        return "ncdhw"
+    if t.dim() >= 3 and t.permute(0, *range(2, t.dim()), 1).is_contiguous():
+        return "ndhwc"
+    raise ValueError("GroupNorm tensors must be contiguous NCDHW or contiguous channels-last")
+
+
+def _layout_arg(t, layout):
+    """The layout to run in: layout_of(t), or `layout` if given and t is contiguous in it
+    (where NCDHW and NDHWC memory coincide, S == 1 or C == 1, either may be asked for)."""
+    if layout is None:
+        return layout_of(t)
+    if layout == "ncdhw" and t.is_contiguous():
+        return layout
+    if layout == "ndhwc" and t.dim() >= 3 and t.permute(0, *range(2, t.dim()), 1).is_contiguous():
+        return layout
+    raise ValueError(f"tensor is not contiguous in layout {layout!r}")
+
+
+def as_layout(t, layout):
+    """t with the same values in the given layout (t itself if it already is)."""
+    if layout == "ncdhw":
+        return t.contiguous()
+    perm = (0, *range(2, t.dim()), 1)
+    if t.permute(perm).is_contiguous():
+        return t
+    inv = (0, t.dim() - 1, *range(1, t.dim() - 1))
+    return t.permute(perm).contiguous().permute(inv)
+
+
 def _contig(name, t):
     if t is not None and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (NCDHW)")
@@ -84,8 +121,9 @@ def _vec(name, t, C, dev):
     return _contig(name, t)
 
 
-def gn_workspace_bytes(N, C, S, G):
-    return int(lib.gn_workspace_bytes(N, C, S, G))
+def gn_workspace_bytes(N, C, S, G, layout="ncdhw"):
+    fn = lib.gn_workspace_bytes if layout == "ncdhw" else lib.gn_workspace_bytes_cl
+    return int(fn(N, C, S, G))
 
 
 def gn_plan_query(N, C, S, G):
@@ -94,29 +132,45 @@ def gn_plan_query(N, C, S, G):
     return {name: getattr(info, name) for name, _ in GnPlanInfo._fields_}
 
 
-def workspace_for(x, G):
+def gn_plan_query_cl(N, C, S, G):
+    info = GnPlanInfoCL()
+    _check("gn_plan_query_cl", lib.gn_plan_query_cl(N, C, S, G, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in GnPlanInfoCL._fields_}
+
+
+def workspace_for(x, G, layout=None):
+    """A workspace for x's shape and layout (or the layout given)."""
     N, C, S, G = _dims(x, G)
-    nbytes = gn_workspace_bytes(N, C, S, G)
-    if nbytes == 0:
-        _check("gn_workspace_bytes", lib.gn_plan_query(N, C, S, G, ctypes.byref(GnPlanInfo())))
+    if _layout_arg(x, layout) == "ncdhw":
+        nbytes = gn_workspace_bytes(N, C, S, G)
+        if nbytes == 0:
+            _check("gn_workspace_bytes", lib.gn_plan_query(N, C, S, G, ctypes.byref(GnPlanInfo())))
+    else:
+        nbytes = gn_workspace_bytes(N, C, S, G, "ndhwc")
+        if nbytes == 0:
+            _check("gn_workspace_bytes_cl", lib.gn_plan_query_cl(N, C, S, G, ctypes.byref(GnPlanInfoCL())))
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
 def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, activation=None, workspace=None,
-               out=None, mean=None, rstd=None):
-    """Returns (y, mean, rstd). y has out_dtype (default: x.dtype); mean/rstd are [N, G] fp32.
-    activation: None or "relu" (applied in fp32 before the single narrowing store)."""
-    _contig("x", x)
+               out=None, mean=None, rstd=None, layout=None):
+    """Returns (y, mean, rstd). y has out_dtype (default: x.dtype) and x's layout; mean/rstd
+    are [N, G] fp32. activation: None or "relu" (applied in fp32 before the single
+    narrowing store). layout: None (from x's strides), "ncdhw" or "ndhwc"."""
+    layout = _layout_arg(x, layout)
     N, C, S, G = _dims(x, G)
     dev = x.device
     out_dtype = out_dtype or x.dtype
-    y = out if out is not None else torch.empty(x.shape, dtype=out_dtype, device=dev)
+    y = out if out is not None else torch.empty_like(x, dtype=out_dtype)
+    if y.shape != x.shape or y.stride() != x.stride():
+        raise ValueError("out must have x's shape and layout")
     mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
     rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else workspace_for(x, G)
-    _check("gn_forward", lib.gn_forward(
+    ws = workspace if workspace is not None else workspace_for(x, G, layout)
+    fn, name = (lib.gn_forward, "gn_forward") if layout == "ncdhw" else (lib.gn_forward_cl, "gn_forward_cl")
+    _check(name, fn(
         _ptr(x), _dtype(x), _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
-        N, C, S, G, float(eps), _act(activation), _ptr(_contig("y", y)), _dtype(y), _ptr(mean),
+        N, C, S, G, float(eps), _act(activation), _ptr(y), _dtype(y), _ptr(mean),
         _ptr(rstd), _ptr(ws), ws.numel(), _stream(dev)))
     return y, mean, rstd
 
@@ -142,22 +196,26 @@ def gn_forward_apply(x, G, y, workspace, activation=None):
 
 
 def gn_backward(dy, x, mean, rstd, gamma, G, *, beta=None, activation=None, need_dx=True,
-                need_dgamma=True, need_dbeta=True, workspace=None, dx=None, dgamma=None, dbeta=None):
-    """Returns (dx or None, dgamma or None, dbeta or None); dx has x's dtype. With
+                need_dgamma=True, need_dbeta=True, workspace=None, dx=None, dgamma=None, dbeta=None,
+                layout=None):
+    """Returns (dx or None, dgamma or None, dbeta or None); dx has x's dtype and layout. With
     activation="relu", dy is the gradient of relu(GroupNorm(x)) and beta is needed."""
-    _contig("x", x); _contig("dy", dy)
-    if dy.shape != x.shape:
-        raise ValueError("dy must have x's shape")
+    layout = _layout_arg(x, layout)
+    if dy.shape != x.shape or dy.stride() != x.stride():
+        raise ValueError("dy must have x's shape and layout")
     N, C, S, G = _dims(x, G)
     dev = x.device
     if need_dx and dx is None:
-        dx = torch.empty(x.shape, dtype=x.dtype, device=dev)
+        dx = torch.empty_like(x)
+    if need_dx and dx.stride() != x.stride():
+        raise ValueError("dx must have x's layout")
     if need_dgamma and dgamma is None:
         dgamma = torch.empty(C, dtype=torch.float32, device=dev)
     if need_dbeta and dbeta is None:
         dbeta = torch.empty(C, dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else workspace_for(x, G)
-    _check("gn_backward", lib.gn_backward(
+    ws = workspace if workspace is not None else workspace_for(x, G, layout)
+    fn, name = (lib.gn_backward, "gn_backward") if layout == "ncdhw" else (lib.gn_backward_cl, "gn_backward_cl")
+    _check(name, fn(
         _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
         _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
         N, C, S, G,
@@ -198,7 +256,10 @@ class GroupNormFn(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, x, gamma, beta, G, eps, out_dtype, activation=None):
-        x = x.contiguous()
+        try:
+            layout_of(x)
+        except ValueError:
+            x = x.contiguous()
         y, mean, rstd = gn_forward(x, gamma, beta, G, eps, out_dtype, activation=activation)
         ctx.save_for_backward(x, mean, rstd, gamma, beta)
         ctx.G = G
@@ -211,13 +272,13 @@ class GroupNormFn(torch.autograd.Function):
         x, mean, rstd, gamma, beta = ctx.saved_tensors
         need = ctx.needs_input_grad
         dx, dgamma, dbeta = gn_backward(
-            dy.contiguous(), x, mean, rstd, gamma, ctx.G, beta=beta, activation=ctx.activation,
+            as_layout(dy, layout_of(x)), x, mean, rstd, gamma, ctx.G, beta=beta, activation=ctx.activation,
             need_dx=need[0], need_dgamma=gamma is not None and need[1], need_dbeta=need[2])
         return dx, dgamma, dbeta, None, None, None, None
 
 
 def group_norm(x, num_groups, weight=None, bias=None, eps=1e-5, out_dtype=None, activation=None):
-    """GroupNorm over NC* input, optionally followed by a fused relu; returns y only
-    (out_dtype defaults to x.dtype)."""
+    """GroupNorm over NC* input (contiguous, or channels-last), optionally followed by a fused
+    relu; returns y only, in x's layout (out_dtype defaults to x.dtype)."""
     y, _, _ = GroupNormFn.apply(x, weight, bias, num_groups, eps, out_dtype, activation)
     return y
