@@ -259,6 +259,57 @@ typedef struct gn_plan_info_cl {
 
 int gn_plan_query_cl(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info_cl* out);
 
+/*
+ * Spatial shards ("Optimize GroupNorm", DistConv paragraphs: activations split over GPUs
+ * along D/H/W, each shard normalized with its own statistics, global statistics left
+ * open). With these calls a rank holding a shard (a contiguous NCDHW tensor of S voxels
+ * per row, the same N, C, G on every rank) normalizes with the statistics of the whole
+ * volume:
+ *   forward:  gn_forward_shard_stats (this shard's record per group)
+ *             -> the caller gathers all P shards' records, [P][N*G], in shard order
+ *             -> gn_forward_shard_merge (mean, rstd; coefficients into the workspace)
+ *             -> gn_forward_apply on this shard;
+ *   backward: gn_backward_shard_sums (this shard's (s1, s2) per row, with the global mean
+ *             and rstd) -> the caller gathers [P][N*C] -> gn_backward_shard_merge (dgamma,
+ *             dbeta over the whole volume; dx coefficients into the workspace)
+ *             -> gn_backward_apply on this shard.
+ * The merges run the same fixed-order computation on every rank, so all ranks obtain
+ * bitwise identical mean, rstd, dgamma and dbeta. The workspace is this shard's
+ * (gn_workspace_bytes(N, C, S, G)). A record holds a group's element count in 32 bits, so
+ * (C/G) * S must be below 2^32; a shard whose groups have a single element must be the
+ * whole volume. Device pointers; moments and sums 16- and 8-byte aligned.
+ */
+typedef struct gn_moments {
+    float mean_hi;   /* the shard's group mean as mean_hi + mean_lo */
+    float mean_lo;
+    float m2;        /* sum of squared deviations from that mean */
+    uint32_t count;  /* elements of the group in the shard */
+} gn_moments;
+
+int gn_forward_shard_stats(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                           gn_moments* moments /* [N*G] */,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+int gn_forward_shard_merge(const gn_moments* moments /* [P][N*G] */, int64_t P,
+                           const float* gamma, const float* beta,
+                           int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+                           float* mean, float* rstd,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+int gn_backward_shard_sums(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                           const float* mean, const float* rstd, const float* gamma,
+                           const float* beta, int activation,
+                           int64_t N, int64_t C, int64_t S, int64_t G,
+                           float* sums /* [N*C][2] */,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+int gn_backward_shard_merge(const float* sums /* [P][N*C][2] */, int64_t P,
+                            const float* mean, const float* rstd, const float* gamma,
+                            const float* beta,
+                            int64_t N, int64_t C, int64_t S, int64_t S_total, int64_t G,
+                            float* dgamma, float* dbeta,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ABI version of this header (incremented on any incompatible change). */
 int gn_abi_version(void);
 

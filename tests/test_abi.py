@@ -21,7 +21,7 @@ def _declared_functions():
 
 def test_every_declared_function_is_exported():
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -37,7 +37,7 @@ def test_status_enum_matches_header():
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == 6
+    assert lib.gn_abi_version() == 7
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every
@@ -168,3 +168,37 @@ def test_channels_last_supported_shapes_have_a_plan(C, G):
     assert lib.gn_workspace_bytes_cl(2, C, 1000, G) == p["workspace_bytes"] > 0
     assert lib.gn_backward_cl(A, GN_BF16, B, GN_BF16, A, B, None, None, 0, 2, C, 1000, G, None, None, None,
                               A, 16, None) == 6
+
+
+def test_shard_entry_points_validate_before_launch():
+    U = ctypes.c_void_p
+    m = U(0x40000)
+    # forward shard stats
+    assert lib.gn_forward_shard_stats(None, GN_BF16, 1, 8, 64, 4, m, A, 1 << 20, None) == 1
+    assert lib.gn_forward_shard_stats(A, GN_BF16, 1, 8, 64, 4, U(0x40008), A, 1 << 20, None) == 7
+    assert lib.gn_forward_shard_stats(A, GN_BF16, 1, 8, 64, 4, m, A, 8, None) == 6
+    assert lib.gn_forward_shard_stats(A, GN_BF16, 1, 2, 1 << 32, 1, m, A, 1 << 20, None) == 2   # count past 32 bits
+    # forward merge
+    assert lib.gn_forward_shard_merge(m, 0, None, None, 1, 8, 64, 4, 1e-5, A, B, A, 1 << 20, None) == 2
+    assert lib.gn_forward_shard_merge(m, 2, None, None, 1, 8, 64, 3, 1e-5, A, B, A, 1 << 20, None) == 3
+    assert lib.gn_forward_shard_merge(m, 2, None, None, 1, 8, 64, 4, -1.0, A, B, A, 1 << 20, None) == 5
+    assert lib.gn_forward_shard_merge(None, 2, None, None, 1, 8, 64, 4, 1e-5, A, B, A, 1 << 20, None) == 1
+    # backward sums
+    assert lib.gn_backward_shard_sums(A, GN_BF16, B, GN_BF16, A, B, None, None, 0, 1, 8, 64, 4, None, A,
+                                      1 << 20, None) == 1
+    assert lib.gn_backward_shard_sums(A, GN_BF16, B, GN_BF16, A, B, None, None, 0, 1, 8, 64, 4, U(0x40004), A,
+                                      1 << 20, None) == 7
+    # backward merge
+    s = U(0x50000)
+    assert lib.gn_backward_shard_merge(s, 2, A, B, None, None, 1, 8, 64, 32, 4, None, None, A, 1 << 20, None) == 2
+    assert lib.gn_backward_shard_merge(s, 0, A, B, None, None, 1, 8, 64, 64, 4, None, None, A, 1 << 20, None) == 2
+    # a shard of single-element groups must be the whole volume
+    assert lib.gn_backward_shard_merge(s, 2, A, B, None, None, 2, 4, 1, 2, 4, None, None, A, 1 << 20, None) == 2
+    assert lib.gn_backward_shard_merge(s, 2, A, B, None, None, 1, 8, 64, 128, 4, None, None, A, 8, None) == 6
+
+
+def test_moments_record_layout():
+    import pathlib
+    text = (pathlib.Path(__file__).resolve().parents[1] / "include" / "gn.h").read_text()
+    assert [(n, t) for n, t in _struct_fields(text, "gn_moments")] == [
+        ("mean_hi", "float"), ("mean_lo", "float"), ("m2", "float"), ("count", "uint32_t")]

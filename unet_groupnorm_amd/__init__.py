@@ -10,8 +10,12 @@ from .gn import (  # noqa: F401
     gn_backward,
     gn_backward_apply,
     gn_backward_reduce,
+    gn_backward_shard_merge,
+    gn_backward_shard_sums,
     gn_forward,
     gn_forward_apply,
+    gn_forward_shard_merge,
+    gn_forward_shard_stats,
     gn_forward_stats,
     gn_plan_query,
     gn_plan_query_cl,

@@ -78,6 +78,10 @@ def _declare(lib):
         "gn_forward_cl": (I, [P, I, P, P, I64, I64, I64, I64, F, I, P, I, P, P, P, SZ, P]),
         "gn_backward_cl": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, P, P, SZ, P]),
         "gn_plan_query_cl": (I, [I64, I64, I64, I64, ctypes.POINTER(GnPlanInfoCL)]),
+        "gn_forward_shard_stats": (I, [P, I, I64, I64, I64, I64, P, P, SZ, P]),
+        "gn_forward_shard_merge": (I, [P, I64, P, P, I64, I64, I64, I64, F, P, P, P, SZ, P]),
+        "gn_backward_shard_sums": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, SZ, P]),
+        "gn_backward_shard_merge": (I, [P, I64, P, P, P, P, I64, I64, I64, I64, I64, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgn.so")
-SOURCES = ["gn_plan.cpp", "gn_api.cpp", "gn_kernels.hip", "gn_kernels_cl.hip"]
+SOURCES = ["gn_plan.cpp", "gn_api.cpp", "gn_kernels.hip", "gn_kernels_cl.hip", "gn_kernels_shard.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -142,7 +142,7 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 6; }
+int gn_abi_version(void) { return 7; }
 
 const char* gn_status_string(int status)
 {
@@ -296,6 +296,101 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
         return rc;
     if (!dx) return GN_OK;
     return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, a, w, st));
+}
+
+// ------------------------------------------------------------------ spatial shards
+
+static_assert(sizeof(gn_moments) == sizeof(gn::Moments16), "record layout");
+
+int gn_forward_shard_stats(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                           gn_moments* moments, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!x || !moments || !workspace) return GN_ERR_NULL;
+    gn::Plan p;
+    int rc = plan_or_error(N, C, S, G, &p);
+    if (rc) return rc;
+    if (p.M >= (int64_t(1) << 32)) return GN_ERR_SHAPE;
+    if (!dtype_ok(x_dtype)) return GN_ERR_DTYPE;
+    if (!aligned(x, 16) || !aligned(moments, 16)) return GN_ERR_ALIGN;
+    if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p);
+    const gn::Workspace w = gn::workspace_of(workspace, p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = launch_status(gn::launch_stats_partials(x, x_dtype, a, w, st)))) return rc;
+    return launch_status(gn::launch_shard_records(x, x_dtype, a, w, reinterpret_cast<gn::Moments16*>(moments), st));
+}
+
+int gn_forward_shard_merge(const gn_moments* moments, int64_t P, const float* gamma, const float* beta,
+                           int64_t N, int64_t C, int64_t S, int64_t G, float eps,
+                           float* mean, float* rstd, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!moments || !mean || !rstd || !workspace) return GN_ERR_NULL;
+    if (P < 1) return GN_ERR_SHAPE;
+    gn::Plan p;
+    int rc = plan_or_error(N, C, S, G, &p);
+    if (rc) return rc;
+    if (P > ((int64_t(1) << 62) / (N * G))) return GN_ERR_SHAPE;
+    if (!std::isfinite(eps) || eps < 0.0f) return GN_ERR_EPS;
+    if (!aligned(moments, 16) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(gamma, 4) ||
+        !aligned(beta, 4))
+        return GN_ERR_ALIGN;
+    if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(moments, stream))) return rc;
+    return launch_status(gn::launch_shard_merge_fwd(reinterpret_cast<const gn::Moments16*>(moments), P, gamma,
+                                                    beta, eps, mean, rstd, gn::kargs_of(p),
+                                                    gn::workspace_of(workspace, p),
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+int gn_backward_shard_sums(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                           const float* mean, const float* rstd, const float* gamma,
+                           const float* beta, int activation,
+                           int64_t N, int64_t C, int64_t S, int64_t G,
+                           float* sums, void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, activation, N, C, S, G, nullptr,
+                       nullptr, nullptr, workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    if (!sums) return GN_ERR_NULL;
+    if (!aligned(sums, 8)) return GN_ERR_ALIGN;
+    if (N > ((int64_t(1) << 31) - 1) / C) return GN_ERR_SHAPE;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    const gn::KArgs a = gn::kargs_of(p, activation);
+    const gn::Workspace w = gn::workspace_of(workspace, p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = launch_status(gn::launch_bwd_partials(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, a, w, st))))
+        return rc;
+    return launch_status(gn::launch_shard_sums(a, w, reinterpret_cast<float2*>(sums), st));
+}
+
+int gn_backward_shard_merge(const float* sums, int64_t P, const float* mean, const float* rstd,
+                            const float* gamma, const float* beta,
+                            int64_t N, int64_t C, int64_t S, int64_t S_total, int64_t G,
+                            float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!sums || !mean || !rstd || !workspace) return GN_ERR_NULL;
+    if (P < 1 || S_total < S) return GN_ERR_SHAPE;
+    gn::Plan p;
+    int rc = plan_or_error(N, C, S, G, &p);
+    if (rc) return rc;
+    if (S_total > gn::kMaxNumel / (N * C) || P > ((int64_t(1) << 62) / (N * C))) return GN_ERR_SHAPE;
+    // The dx kernel decides single-element groups from this shard's own size.
+    if (p.M == 1 && S_total != S) return GN_ERR_SHAPE;
+    if (!aligned(sums, 8) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(gamma, 4) ||
+        !aligned(beta, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4))
+        return GN_ERR_ALIGN;
+    if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(sums, stream))) return rc;
+    return launch_status(gn::launch_shard_merge_bwd(reinterpret_cast<const float2*>(sums), P, mean, rstd, gamma,
+                                                    beta, p.Cg * S_total, dgamma, dbeta, gn::kargs_of(p),
+                                                    gn::workspace_of(workspace, p),
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------ channels-last

@@ -357,7 +357,7 @@ hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... a
 template <typename T> const T* cp(const void* p) { return static_cast<const T*>(p); }
 template <typename T> T* mp(void* p) { return static_cast<T*>(p); }
 
-dim3 grid_of(int64_t jobs) { return dim3(unsigned(jobs < kMaxGrid ? jobs : kMaxGrid)); }
+inline dim3 grid_of(int64_t jobs) { return dim3(unsigned(jobs < kMaxGrid ? jobs : kMaxGrid)); }
 
 // Calls f with a value of the storage type of dtype dt: float, bf16 (as uint16_t) or fp16.
 template <typename F>

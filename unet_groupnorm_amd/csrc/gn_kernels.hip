@@ -42,6 +42,21 @@ namespace {
 
 // ------------------------------------------------------------------ job geometry
 
+// Workgroup -> job order. The dispatcher hands consecutive workgroups to the 8 XCDs in
+// turn; with GN_XCD_REMAP the workgroups of one XCD take one contiguous eighth of the jobs
+// (a bijection when the grid covers the jobs exactly and their count is a multiple of 8).
+#ifndef GN_XCD_REMAP
+#define GN_XCD_REMAP 0
+#endif
+#ifndef GN_XCD_REMAP_RED
+#define GN_XCD_REMAP_RED 0
+#endif
+__device__ __forceinline__ int64_t xcd_job(int64_t b, int64_t jobs, bool on)
+{
+    if (!on || (jobs & 7) != 0 || int64_t(gridDim.x) != jobs) return b;
+    return (b & 7) * (jobs >> 3) + (b >> 3);
+}
+
 struct Job {
     int64_t row, k;   // row = n*C + c, job index within the row
     int64_t lo, hi;   // global element range [lo, hi)
@@ -212,7 +227,8 @@ stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kStepVecs;
 
-    for (int64_t j = blockIdx.x; j < a.jobs; j += gridDim.x) {
+    for (int64_t wb = blockIdx.x; wb < a.jobs; wb += gridDim.x) {
+        const int64_t j = xcd_job(wb, a.jobs, GN_XCD_REMAP_RED);
         const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, g = (jb.row - n * a.C) / a.Cg;
         const float K = group_shift(x, a, n, g);
@@ -303,7 +319,8 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kApplyVecs;
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
-        const int64_t j = kReverseApply ? a.jobs_a - 1 - jj : jj;
+        const int64_t jx = xcd_job(jj, a.jobs_a, GN_XCD_REMAP);
+        const int64_t j = kReverseApply ? a.jobs_a - 1 - jx : jx;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row];
         const float hi = cf.x, lo = cf.y, scale = cf.z, shift = cf.w;
@@ -393,7 +410,8 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kStepVecs;
 
-    for (int64_t j = blockIdx.x; j < a.jobs; j += gridDim.x) {
+    for (int64_t wb = blockIdx.x; wb < a.jobs; wb += gridDim.x) {
+        const int64_t j = xcd_job(wb, a.jobs, GN_XCD_REMAP_RED);
         const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, ng = n * a.G + c / a.Cg;
         const float mu = mean[ng];
@@ -503,7 +521,8 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
     // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
     const bool single = (a.M == 1);
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
-        const int64_t j = kReverseApply ? a.jobs_a - 1 - jj : jj;
+        const int64_t jx = xcd_job(jj, a.jobs_a, GN_XCD_REMAP);
+        const int64_t j = kReverseApply ? a.jobs_a - 1 - jx : jx;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row];
         const float mu = cf.x, A = cf.y, B = cf.z, E = cf.w;
@@ -807,6 +826,28 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
+
+hipError_t launch_stats_partials(const void* x, int xdt, const KArgs& a, Workspace ws, hipStream_t st)
+{
+    return with_type(xdt, [&](auto tx) {
+        using TX = decltype(tx);
+        return launch(stats_kernel<TX>, grid_of(a.jobs), dim3(unsigned(a.block)), st, cp<TX>(x), a, ws.part);
+    });
+}
+
+hipError_t launch_bwd_partials(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                               const float* rstd, const float* gamma, const float* beta, const KArgs& a,
+                               Workspace ws, hipStream_t st)
+{
+    return with_type(xdt, [&](auto tx) {
+        return with_type(dydt, [&](auto td) {
+            using TX = decltype(tx);
+            using TD = decltype(td);
+            return launch(bwd_reduce_kernel<TX, TD>, grid_of(a.jobs), dim3(unsigned(a.block)), st, cp<TD>(dy),
+                          cp<TX>(x), mean, rstd, gamma, beta, a, ws.part);
+        });
+    });
+}
 
 hipError_t launch_fwd_stats(const void* x, int xdt, const float* gamma, const float* beta,
                             float eps, float* mean, float* rstd, const KArgs& a, Workspace ws,

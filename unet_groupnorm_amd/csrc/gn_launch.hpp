@@ -94,6 +94,36 @@ hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, cons
                           float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st,
                           int block, int vecs);
 
+// The partial reductions alone (one float2 per reduction job in ws.part).
+hipError_t launch_stats_partials(const void* x, int xdt, const KArgs& a, Workspace ws, hipStream_t st);
+hipError_t launch_bwd_partials(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                               const float* rstd, const float* gamma, const float* beta, const KArgs& a,
+                               Workspace ws, hipStream_t st);
+
+// ------------------------------------------------------------------ spatial shards
+//
+// One shard's statistics record per group: mean = mean_hi + mean_lo, m2 = sum of squared
+// deviations from that mean, count = elements of the group in the shard. Same layout as
+// gn_moments in gn.h.
+struct Moments16 {
+    float mean_hi, mean_lo, m2;
+    uint32_t count;
+};
+
+// Forward: the shard's partials -> one record per group (after launch_stats_partials).
+hipError_t launch_shard_records(const void* x, int xdt, const KArgs& a, Workspace ws, Moments16* rec,
+                                hipStream_t st);
+// Forward: P shards' records, merged in shard order -> mean, rstd, normalize coefficients.
+hipError_t launch_shard_merge_fwd(const Moments16* rec, int64_t P, const float* gamma, const float* beta,
+                                  float eps, float* mean, float* rstd, const KArgs& a, Workspace ws,
+                                  hipStream_t st);
+// Backward: the shard's partials -> per-row (sum g, rstd * sum g*(x - mean)).
+hipError_t launch_shard_sums(const KArgs& a, Workspace ws, float2* sums, hipStream_t st);
+// Backward: P shards' sums, merged in shard order -> dgamma, dbeta and dx coefficients.
+hipError_t launch_shard_merge_bwd(const float2* sums, int64_t P, const float* mean, const float* rstd,
+                                  const float* gamma, const float* beta, int64_t M_total, float* dgamma,
+                                  float* dbeta, const KArgs& a, Workspace ws, hipStream_t st);
+
 // ------------------------------------------------------------------ channels-last
 
 struct ClArgs {

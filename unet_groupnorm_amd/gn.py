@@ -246,6 +246,94 @@ def gn_backward_apply(dy, x, G, dx, workspace, activation=None):
         _ptr(workspace), workspace.numel(), _stream(x.device)))
 
 
+# ----------------------------------------------------------------------------- spatial shards
+#
+# A rank holding a spatial shard of the volume (contiguous NCDHW, the same N, C, G on every
+# rank) normalizes with the statistics of the whole volume: shard stats -> gather the P
+# records in shard order (e.g. one all_gather_into_tensor) -> merge -> gn_forward_apply;
+# backward: shard sums -> gather -> merge -> gn_backward_apply. The merges give every rank
+# the same bits. `workspace` is this shard's (workspace_for(x_shard, G)) and carries the
+# merge's coefficients to the apply call.
+
+def _dims_of_shape(shape, G):
+    N, C = int(shape[0]), int(shape[1])
+    S = 1
+    for d in shape[2:]:
+        S *= int(d)
+    return N, C, S, int(G)
+
+
+def gn_forward_shard_stats(x, G, *, moments=None, workspace=None):
+    """This shard's record per group, a [N*G, 4] float32 tensor of rows (mean head, mean
+    tail, M2, element count as uint32 bits) -- the gn_moments layout."""
+    _contig("x", x)
+    N, C, S, G = _dims(x, G)
+    moments = moments if moments is not None else torch.empty((N * G, 4), dtype=torch.float32, device=x.device)
+    ws = workspace if workspace is not None else workspace_for(x, G)
+    _check("gn_forward_shard_stats", lib.gn_forward_shard_stats(
+        _ptr(x), _dtype(x), N, C, S, G, _ptr(_contig("moments", moments)), _ptr(ws), ws.numel(),
+        _stream(x.device)))
+    return moments
+
+
+def gn_forward_shard_merge(moments, gamma, beta, shape, G, eps=1e-5, *, workspace, mean=None, rstd=None):
+    """moments: [P, N*G, 4], every shard's records in shard order; shape: this shard's
+    shape. Returns (mean, rstd) of the whole volume; the workspace then holds this shard's
+    normalize coefficients for gn_forward_apply."""
+    N, C, S, G = _dims_of_shape(shape, G)
+    _contig("moments", moments)
+    P = moments.numel() // (N * G * 4)
+    if moments.numel() != P * N * G * 4 or P < 1:
+        raise ValueError("moments must be [P, N*G, 4]")
+    dev = moments.device
+    mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
+    rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
+    _check("gn_forward_shard_merge", lib.gn_forward_shard_merge(
+        _ptr(moments), P, _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
+        N, C, S, G, float(eps), _ptr(mean), _ptr(rstd), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return mean, rstd
+
+
+def gn_backward_shard_sums(dy, x, mean, rstd, gamma, G, *, beta=None, activation=None, sums=None,
+                           workspace=None):
+    """This shard's (sum g, rstd * sum g*(x - mean)) per row (n, c), [N*C, 2] float32, with
+    the whole volume's mean and rstd."""
+    _contig("x", x); _contig("dy", dy)
+    N, C, S, G = _dims(x, G)
+    dev = x.device
+    sums = sums if sums is not None else torch.empty((N * C, 2), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else workspace_for(x, G)
+    _check("gn_backward_shard_sums", lib.gn_backward_shard_sums(
+        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
+        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
+        N, C, S, G, _ptr(_contig("sums", sums)), _ptr(ws), ws.numel(), _stream(dev)))
+    return sums
+
+
+def gn_backward_shard_merge(sums, mean, rstd, gamma, shape, S_total, G, *, workspace, beta=None,
+                            need_dgamma=True, need_dbeta=True, dgamma=None, dbeta=None):
+    """sums: [P, N*C, 2], every shard's sums in shard order; shape: this shard's shape;
+    S_total: voxels per row of the whole volume. Returns (dgamma, dbeta) of the whole volume
+    (None where not needed); the workspace then holds this shard's dx coefficients for
+    gn_backward_apply."""
+    N, C, S, G = _dims_of_shape(shape, G)
+    _contig("sums", sums)
+    P = sums.numel() // (N * C * 2)
+    if sums.numel() != P * N * C * 2 or P < 1:
+        raise ValueError("sums must be [P, N*C, 2]")
+    dev = sums.device
+    if need_dgamma and dgamma is None:
+        dgamma = torch.empty(C, dtype=torch.float32, device=dev)
+    if need_dbeta and dbeta is None:
+        dbeta = torch.empty(C, dtype=torch.float32, device=dev)
+    _check("gn_backward_shard_merge", lib.gn_backward_shard_merge(
+        _ptr(sums), P, _ptr(mean), _ptr(rstd), _ptr(_vec("gamma", gamma, C, dev)),
+        _ptr(_vec("beta", beta, C, dev)), N, C, S, int(S_total), G,
+        _ptr(dgamma if need_dgamma else None), _ptr(dbeta if need_dbeta else None),
+        _ptr(workspace), workspace.numel(), _stream(dev)))
+    return (dgamma if need_dgamma else None, dbeta if need_dbeta else None)
+
+
 class GroupNormFn(torch.autograd.Function):
     """y = GroupNorm(x) with the HIP kernels in both directions.
 
