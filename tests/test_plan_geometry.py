@@ -41,7 +41,7 @@ def test_plan_is_consistent(N, C, S, G):
     assert p["rows"] == N * C
     assert p["jobs"] == p["rows"] * p["chunks_per_row"]
     assert p["partials_per_group"] == (C // G) * p["chunks_per_row"]
-    assert p["block"] in (64, 128, 256)
+    assert p["block"] in (64, 128, 256, 512)
     assert (p["chunks_per_row"] - 1) * p["chunk"] < S <= p["chunks_per_row"] * p["chunk"]
     assert p["workspace_bytes"] >= 8 * p["jobs"] and p["workspace_bytes"] % 256 == 0
     assert g.gn_workspace_bytes(N, C, S, G) == p["workspace_bytes"]
@@ -317,4 +317,4 @@ def test_channels_last_slots_and_holders(N, C, S, G):
         # the slot of lane vector c that holds group grp
         assert (lo * VEC // Cg) + slot == grp
     # workspace areas: partials (jobs x C float2), per-channel float2, per-group float4
-    assert p["workspace_bytes"] >= p["jobs"] * C * 8 + N * C * 8 + N * G * 16
+    assert p["workspace_bytes"] >= p["jobs"] * (C + G) * 8 + N * C * 8 + N * G * 16

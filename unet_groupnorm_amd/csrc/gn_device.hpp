@@ -302,7 +302,8 @@ __device__ __forceinline__ float tree_sumprod(const float (&a)[N], const float (
     return h[0];
 }
 
-constexpr int kMaxWaves = 4;
+// Waves of the largest workgroup a fixed-order block reduction serves (512 threads).
+constexpr int kMaxWaves = 8;
 
 // Merges the per-wave moments (lane 0 of each wave) in wave order; result valid in thread 0.
 template <typename CT>

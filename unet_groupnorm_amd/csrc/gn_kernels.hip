@@ -218,7 +218,7 @@ __device__ __forceinline__ void stats_masked_step(const TX* __restrict__ x, cons
 // the current step is reduced, alternating between two register sets so that waiting for
 // one set leaves the other in flight.
 template <typename TX>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRedBlock)
 stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
 {
     using Raw = typename Io<TX>::Raw;
@@ -398,7 +398,7 @@ __device__ __forceinline__ void bwd_masked_step(const TD* __restrict__ dy, const
 // summing their tiles in step order, then the shuffle tree, then the waves in order. The
 // full steps are software-pipelined as in stats_kernel.
 template <typename TX, typename TD>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRedBlock)
 bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
                   const float* __restrict__ mean, const float* __restrict__ rstd,
                   const float* __restrict__ gamma, const float* __restrict__ beta,

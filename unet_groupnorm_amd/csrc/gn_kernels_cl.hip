@@ -405,12 +405,14 @@ template <int NGL, bool ACT, typename TX, typename TD>
 __global__ void __launch_bounds__(kClBlock)
 cl_bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                      const float* __restrict__ rstd, const float* __restrict__ gamma,
-                     const float* __restrict__ beta, ClArgs a, float2* __restrict__ part)
+                     const float* __restrict__ beta, ClArgs a, float2* __restrict__ part,
+                     float2* __restrict__ partg)
 {
     using RawX = typename Io<TX>::Raw;
     using RawD = typename Io<TD>::Raw;
     constexpr int W = kVec / NGL;
     __shared__ float s_1[kClBlock * kVec], s_2[kClBlock * kVec];
+    __shared__ float s_c1[kClBlock * kVec], s_c2[kClBlock * kVec];  // per channel, gamma-weighted
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Cv = int(a.Cv), cv = tid % Cv, vo = tid / Cv, vps = int(a.vps);
     const int reps = Cv < 64 ? Cv : 64;
@@ -499,21 +501,36 @@ cl_bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
                     t2 = t2 + s_2[(w * 64 + l) * kVec + i];
                 }
             }
-            part[(c * a.N + n) * a.K + k] = make_float2(t1, t2 * rstd[n * a.G + c / a.Cg]);
+            const float s2c = t2 * rstd[n * a.G + c / a.Cg];
+            part[(c * a.N + n) * a.K + k] = make_float2(t1, s2c);
+            const float gm = gamma ? gamma[c] : 1.0f;
+            s_c1[c] = gm * t1;
+            s_c2[c] = gm * s2c;
+        }
+        __syncthreads();
+        // per group: the gamma-weighted channel sums in channel order
+        for (int64_t g = tid; g < a.G; g += blockDim.x) {
+            float u1 = 0.0f, u2 = 0.0f;
+            for (int64_t i = 0; i < a.Cg; ++i) {
+                u1 = u1 + s_c1[g * a.Cg + i];
+                u2 = u2 + s_c2[g * a.Cg + i];
+            }
+            partg[(g * a.N + n) * a.K + k] = make_float2(u1, u2);
         }
         __syncthreads();
     }
 }
 
 // Workgroups [0, ngroups) each take one group (n, g): c1 = (1/M) sum gamma_c s1 and
-// c2 = (1/M) sum gamma_c s2 over the group's K * C/G partials in a fixed order (channel-major,
-// then job), then (mean, B = -rstd*c1, E = -rstd^2*c2) per group and (A = rstd*gamma_c,
+// c2 = (1/M) sum gamma_c s2 over the group's K per-job gamma-weighted partials in a fixed
+// order (lane t takes jobs t, t + B, ..., then the shuffle tree, then the waves), then (mean, B = -rstd*c1, E = -rstd^2*c2) per group and (A = rstd*gamma_c,
 // beta_c) per channel, so that dx = A*g + (B + E*(x - mean)). Workgroups [ngroups,
 // ngroups + nchan) each take one channel: dgamma_c and dbeta_c over its N*K partials.
 __global__ void __launch_bounds__(256)
 cl_fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
                   const float* __restrict__ gamma, const float* __restrict__ beta,
-                  const float2* __restrict__ part, ClArgs a, int64_t ngroups, int64_t nchan,
+                  const float2* __restrict__ part, const float2* __restrict__ partg, ClArgs a,
+                  int64_t ngroups, int64_t nchan,
                   float2* __restrict__ coefc, float4* __restrict__ coefg, float* __restrict__ dgamma,
                   float* __restrict__ dbeta)
 {
@@ -525,22 +542,19 @@ cl_fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd
         const int64_t n = w / a.G, g = w - n * a.G;
         const float mu = mean[w], rs = rstd[w];
         float t1 = 0.0f, t2 = 0.0f;
-        const int64_t cnt = a.K * a.Cg;
-        for (int64_t i0 = tid; i0 < cnt; i0 += kBatch * blk) {
+        const float2* pg = partg + (g * a.N + n) * a.K;
+        for (int64_t k0 = tid; k0 < a.K; k0 += kBatch * blk) {
             float2 pp[kBatch];
-            float gm[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int64_t i = i0 + int64_t(u) * blk;
-                const int64_t ci = i / a.K, kk = i - ci * a.K, c = g * a.Cg + ci;
-                pp[u] = i < cnt ? part[(c * a.N + n) * a.K + kk] : make_float2(0.0f, 0.0f);
-                gm[u] = (i < cnt && gamma) ? gamma[c] : 1.0f;
+                const int64_t kk = k0 + int64_t(u) * blk;
+                pp[u] = kk < a.K ? pg[kk] : make_float2(0.0f, 0.0f);
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                if (i0 + int64_t(u) * blk < cnt) {
-                    t1 = t1 + gm[u] * pp[u].x;
-                    t2 = t2 + gm[u] * pp[u].y;
+                if (k0 + int64_t(u) * blk < a.K) {
+                    t1 = t1 + pp[u].x;
+                    t2 = t2 + pp[u].y;
                 }
             }
         }
@@ -683,15 +697,15 @@ hipError_t launch_cl_backward(const void* dy, int dydt, const void* x, int xdt, 
                 constexpr int NGL = decltype(ng)::value;
                 hipError_t e = a.act
                     ? launch(cl_bwd_reduce_kernel<NGL, true, TX, TD>, grid_of(a.jobs), dim3(kClBlock), st,
-                             cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part)
+                             cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part, ws.partg)
                     : launch(cl_bwd_reduce_kernel<NGL, false, TX, TD>, grid_of(a.jobs), dim3(kClBlock), st,
-                             cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part);
+                             cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part, ws.partg);
                 if (e != hipSuccess) return e;
                 const int64_t ngroups = a.N * a.G;
                 const int64_t nchan = (dgamma || dbeta) ? a.C : 0;
                 e = launch(cl_fin_bwd_kernel, dim3(unsigned(ngroups + nchan)), dim3(256), st, mean, rstd, gamma,
-                           beta, static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coefc, ws.coefg,
-                           dgamma, dbeta);
+                           beta, static_cast<const float2*>(ws.part), static_cast<const float2*>(ws.partg), a,
+                           ngroups, nchan, ws.coefc, ws.coefg, dgamma, dbeta);
                 if (e != hipSuccess || !dx) return e;
                 return launch(cl_bwd_apply_kernel<NGL, TX, TD>, grid_of(a.jobs_a), dim3(kClBlock), st,
                               cp<TD>(dy), cp<TX>(x), a, static_cast<const float2*>(ws.coefc),

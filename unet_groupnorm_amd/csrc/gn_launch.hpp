@@ -151,6 +151,7 @@ inline ClArgs clargs_of(const PlanCL& p, int act = 0)
 // mean tail; backward: mean, -rstd*c1, -rstd^2*c2).
 struct WorkspaceCL {
     float2* part;
+    float2* partg;   // backward: per job and group, sum over the group's channels of gamma_c * partial_c
     float2* coefc;
     float4* coefg;
 };
@@ -158,7 +159,8 @@ struct WorkspaceCL {
 inline WorkspaceCL workspace_cl_of(void* ws, const PlanCL& p)
 {
     char* b = static_cast<char*>(ws);
-    return WorkspaceCL{reinterpret_cast<float2*>(b), reinterpret_cast<float2*>(b + p.ws_coefc_offset),
+    return WorkspaceCL{reinterpret_cast<float2*>(b), reinterpret_cast<float2*>(b + p.ws_partg_offset),
+                       reinterpret_cast<float2*>(b + p.ws_coefc_offset),
                        reinterpret_cast<float4*>(b + p.ws_coefg_offset)};
 }
 

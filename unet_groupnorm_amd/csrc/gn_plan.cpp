@@ -44,7 +44,7 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     // that short rows (8^3 voxels) do not leave most lanes idle.
     const int64_t row_vecs = ceil_div(S, kVec) + 1;  // +1: a row need not start on a vector
     int block = 64;
-    while (block < 256 && int64_t(block) * kStepVecs < row_vecs) block *= 2;
+    while (block < kRedBlock && int64_t(block) * kStepVecs < row_vecs) block *= 2;
     const int64_t step = int64_t(block) * kStepVecs * kVec;  // elements per workgroup step
 
     // Chunking: a whole row per job, halved while the launch has fewer than kTargetJobs
@@ -128,7 +128,7 @@ int make_plan_cl(int64_t N, int64_t C, int64_t S, int64_t G, PlanCL* p)
         chunk = round_up(ceil_div(S, K), step);
         K = ceil_div(S, chunk);
     }
-    while (N * K < kTargetJobs) {
+    while (N * K < kClTargetJobs) {
         const int64_t c2 = round_up(ceil_div(S, K * 2), step);
         const int64_t k2 = ceil_div(S, c2);
         if (k2 <= K) break;
@@ -141,7 +141,8 @@ int make_plan_cl(int64_t N, int64_t C, int64_t S, int64_t G, PlanCL* p)
     q.chunk_a = kClApplyRounds * q.vps;
     q.K_a = ceil_div(S, q.chunk_a);
     q.jobs_a = N * q.K_a;
-    q.ws_coefc_offset = size_t(round_up(q.jobs * C * 8, 256));
+    q.ws_partg_offset = size_t(round_up(q.jobs * C * 8, 256));
+    q.ws_coefc_offset = q.ws_partg_offset + size_t(round_up(q.jobs * G * 8, 256));
     q.ws_coefg_offset = q.ws_coefc_offset + size_t(round_up(N * C * 8, 256));
     q.ws_bytes = q.ws_coefg_offset + size_t(round_up(N * G * 16, 256));
     *p = q;

@@ -37,6 +37,11 @@ constexpr int kVec = 8;
 #ifndef GN_APPLY_VECS
 #define GN_APPLY_VECS 1
 #endif
+// Largest reduction workgroup (threads); the plan sizes smaller ones to short rows.
+#ifndef GN_RED_BLOCK
+#define GN_RED_BLOCK 256
+#endif
+constexpr int kRedBlock = GN_RED_BLOCK;
 // Vectors each lane holds per step of a reduction job (register tile = kVec * kStepVecs).
 constexpr int kStepVecs = GN_STEP_VECS;
 // Reduction workgroups a launch aims for (2048: 8 per CU on the 256 CUs of an MI355X).
@@ -92,6 +97,14 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p);
 // so C/8 must divide kClBlock. The lane's 8 channels lie in ngl = max(1, 8 / (C/G))
 // groups, which needs C/G to divide 8 or to be a multiple of 8.
 constexpr int kClBlock = 256;
+// Reduction workgroups a channels-last launch aims for. Fewer and longer jobs than the
+// NCDHW plan's: each job ends in per-channel shuffle trees and three workgroup barriers,
+// and its K partials per group feed the finalize (measured on MI355X, 128^3 and 256^3,
+// C=32: 256-512 jobs best, 2048 about 5% slower, 128 too few).
+#ifndef GN_CL_TARGET_JOBS
+#define GN_CL_TARGET_JOBS 512
+#endif
+constexpr int64_t kClTargetJobs = GN_CL_TARGET_JOBS;
 constexpr int kClRounds = 4;        // voxel rounds a reduction lane holds per step
 constexpr int kClApplyRounds = 4;   // voxel rounds of a streaming job
 
@@ -105,8 +118,9 @@ struct PlanCL {
     int64_t chunk = 0, K = 0, jobs = 0;
     // streaming jobs
     int64_t chunk_a = 0, K_a = 0, jobs_a = 0;
-    // workspace: [partials: float2 * jobs * C][per-channel: float2 * N*C][per-group: float4 * N*G]
-    size_t ws_coefc_offset = 0, ws_coefg_offset = 0, ws_bytes = 0;
+    // workspace: [partials: float2 * jobs * C][group partials: float2 * jobs * G]
+    // [per-channel: float2 * N*C][per-group: float4 * N*G]
+    size_t ws_partg_offset = 0, ws_coefc_offset = 0, ws_coefg_offset = 0, ws_bytes = 0;
 };
 
 // Returns 0 and fills *p, else 2 (shape), 3 (groups) or 4 (shape not supported channels-last).
