@@ -13,7 +13,10 @@ reference value is near zero):
   dx (bf16, fp16)  |d| <= ulp(dx64) + 1e-4 * max|dx64|, ulp in dx's format
   dgamma/dbeta  |d_c| <= max(1e-4 * |ref_c|, 2 * D * 2^-24 * sum|terms_c|), D the depth of
              the kernel's fp32 summation tree for the shape (the a-priori bound of fp32
-             summation in that order)
+             summation in that order); dgamma also gets the propagation of the published fp32
+             statistics' rounding, 4 * 2^-24 * (max_n |mean| * rstd * sum|g| + |ref_c|), since
+             dgamma_c = sum g * (x - mean) * rstd moves by rstd * sum g per unit of mean and
+             the backward consumes the forward's fp32 mean and rstd (stats_slack)
 NaN must match NaN (position for position) and infinities must match exactly.
 
 With the fused relu, the gate is a sign decision taken on the fp32 pre-activation. Where
@@ -190,6 +193,18 @@ def check_param(name, got, ref, abs_terms, depth, slack=0.0):
     fin = np.isfinite(ref)
     assert (d[fin] <= bar[fin]).all(), f"{name}: worst {np.max(d[fin] / bar[fin]):.3g} of the bar"
     return {f"{name}_of_bar": float(np.max(d[fin] / bar[fin])) if fin.any() else 0.0}
+
+
+def stats_slack(mean64, rstd64, abs_dy, ref, C):
+    """The part of dgamma's deviation owed to the fp32 rounding of the statistics the
+    backward consumes: 4 * 2^-24 * (max_n |mean_g| * rstd_g * sum|g|_c + |ref_c|)."""
+    mean64 = np.asarray(mean64, dtype=np.float64)
+    rstd64 = np.asarray(rstd64, dtype=np.float64)
+    G = mean64.shape[1]
+    with np.errstate(invalid="ignore"):
+        w = np.max(np.abs(mean64) * rstd64, axis=0)          # [G]
+    w = np.repeat(np.where(np.isfinite(w), w, 0.0), C // G)  # [C]
+    return 4 * U32 * (w * np.asarray(abs_dy) + np.abs(np.asarray(ref)))
 
 
 class ReluBand:

@@ -82,7 +82,8 @@ def full_check(inp, tag, relu=False, layout="ncdhw"):
     N, C = x.shape[:2]
     depth = P.reduction_depth(gn.gn_plan_query(N, C, x.numel() // (N * C), G), N)
     rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth,
-                             0.0 if band is None else band.dgamma))
+                             (0.0 if band is None else band.dgamma)
+                             + P.stats_slack(b["mean"], b["rstd"], a_dy, b["dgamma"], x.shape[1])))
     rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth,
                              0.0 if band is None else band.dbeta))
     say(f"{tag}: ok {rep}")
@@ -131,7 +132,8 @@ def sampled_check(inp, tag, n_random=1 << 20, seed=0, relu=False, layout="ncdhw"
     N, C = x.shape[:2]
     depth = P.reduction_depth(gn.gn_plan_query(N, C, x.numel() // (N * C), G), N)
     rep.update(P.check_param("dgamma", P.to_np(r["dgamma"]), b["dgamma"], a_dyx, depth,
-                             0.0 if band is None else band.dgamma))
+                             (0.0 if band is None else band.dgamma)
+                             + P.stats_slack(b["mean"], b["rstd"], a_dy, b["dgamma"], x.shape[1])))
     rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth,
                              0.0 if band is None else band.dbeta))
     if band is not None:
