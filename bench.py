@@ -26,7 +26,7 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
 METRIC = "GroupNorm fwd+bwd achieved HBM GB/s (% of MI355X peak), bf16 128³/256³ C=32 G=8"
 KERNEL_SOURCES = ["unet_groupnorm_amd/csrc/gn_kernels.hip", "unet_groupnorm_amd/csrc/gn_device.hpp",
                   "unet_groupnorm_amd/csrc/gn_plan.cpp", "unet_groupnorm_amd/csrc/gn_plan.hpp",
-                  "unet_groupnorm_amd/csrc/gn_launch.hpp"]
+                  "unet_groupnorm_amd/csrc/gn_launch.hpp", "unet_groupnorm_amd/csrc/gn_api.cpp"]
 
 
 def parse():
@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="headline, roofline and baseline only")
     ap.add_argument("--workload", choices=["scale7", "scale8"], default="scale7",
                     help="the 128^3 (default) or 256^3 C=32 G=8 bf16 site")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed steps before the warmup steps (the first timed window "
+                         "otherwise reads 2-4%% slow on a GPU that was idle a moment before)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB bf16 device copy 5 times (a kernel of known traffic "
                          "for scaling profiler byte counters)")
@@ -99,21 +102,33 @@ class Runner:
                        dbeta=self.dbeta)
 
     def phases(self):
-        """The same step through the split-phase entry points. The stats and bwd_reduce
-        phases are two kernels each (the partial reduction, then the small per-group
-        finalize); apply and bwd_apply are one kernel each."""
+        """The same step as its four kernels, one call each (gn_forward = partials + finish,
+        gn_backward likewise): stats_kernel, apply_fin_kernel, bwd_reduce_kernel and
+        bwd_apply_fin_kernel, the kernels step() launches."""
         gn = self.gn
         return [
-            ("stats", lambda: gn.gn_forward_stats(self.x, self.gamma, self.beta, self.G, self.eps,
-                                                  self.mean, self.rstd, self.ws)),
-            ("apply", lambda: gn.gn_forward_apply(self.x, self.G, self.y, self.ws, self.act)),
-            ("bwd_reduce", lambda: gn.gn_backward_reduce(self.dy, self.x, self.mean, self.rstd,
-                                                         self.gamma, self.G, self.dgamma,
-                                                         self.dbeta, self.ws, beta=self.beta,
-                                                         activation=self.act)),
-            ("bwd_apply", lambda: gn.gn_backward_apply(self.dy, self.x, self.G, self.dx, self.ws,
-                                                       self.act)),
+            ("stats", lambda: gn.gn_forward_partials(self.x, self.G, self.ws)),
+            ("apply", lambda: gn.gn_forward_finish(self.x, self.gamma, self.beta, self.G, self.eps,
+                                                   self.y, self.mean, self.rstd, self.ws, self.act)),
+            ("bwd_reduce", lambda: gn.gn_backward_partials(self.dy, self.x, self.mean, self.rstd,
+                                                           self.gamma, self.G, self.ws, beta=self.beta,
+                                                           activation=self.act)),
+            ("bwd_apply", lambda: gn.gn_backward_finish(self.dy, self.x, self.mean, self.rstd,
+                                                        self.gamma, self.G, self.dx, self.dgamma,
+                                                        self.dbeta, self.ws, beta=self.beta,
+                                                        activation=self.act)),
         ]
+
+    def settle(self, seconds):
+        """Untimed steps for `seconds` of wall time; returns how many ran."""
+        torch = self.torch
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                self.step()
+            torch.cuda.synchronize()
+            n += 20
+        return n
 
     def timed_steps(self, steps, warmup):
         torch = self.torch
@@ -203,6 +218,7 @@ def census(steps=10, warmup=3):
         key = f"c{r.case.C}_g{r.case.G}_{r.case.spatial[0]}cube"
         if key in per_shape:
             continue
+        r.settle(0.25)
         sms, _ = r.timed_steps(max(steps, 20), warmup)
         per_shape[key] = {"us_per_step": round(sms * 1e3, 2),
                           "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1)}
@@ -218,6 +234,7 @@ def small_configs(steps=50, warmup=10):
     out = {}
     for case in (workloads.TINY, workloads.DEEP, workloads.DEEP_F32OUT):
         r = Runner(case)
+        r.settle(0.25)
         sms, _ = r.timed_steps(steps, warmup)
         out[case.name] = {"us_per_step": round(sms * 1e3, 2),
                           "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1),
@@ -312,7 +329,8 @@ def main():
     case = workloads.SCALE7 if args.workload == "scale7" else workloads.SCALE8
     log(f"workload {case.name} {case.shape}; generating inputs on the GPU")
     run = Runner(case)
-    log(f"timing {args.steps} steps after {args.warmup} warmup steps")
+    settled = run.settle(args.settle) if args.settle > 0 else 0
+    log(f"timing {args.steps} steps after {settled} settling and {args.warmup} warmup steps")
     ms, wall = run.timed_steps(args.steps, args.warmup)
     value = run.step_bytes / (ms * 1e-3) / 1e9
 
@@ -324,7 +342,8 @@ def main():
     traffic, traffic_note = load_traffic(case.name)
     roofline = {
         "bound": "hbm",
-        "kernel": "bwd_apply_kernel<bf16,bf16> (dx pass: reads x and dy, writes dx)",
+        "kernel": "bwd_apply_fin_kernel<bf16,bf16> (dx pass with the backward finalize folded in: "
+                  "reads x and dy, writes dx)",
         "achieved": round(dom_gbps, 1),
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
@@ -357,6 +376,7 @@ def main():
         "roofline": roofline,
         "kernels_us": {k: round(v * 1e3, 2) for k, v in ph_ms.items()},
         "kernel_source_hash": kernel_source_hash(),
+        "settle": {"seconds": args.settle, "steps": settled},
     }
     if not args.no_extras:
         compulsory = 10 * case.numel
@@ -397,6 +417,7 @@ def main():
         c8 = workloads.SCALE8
         log(f"secondary workload {c8.name}")
         r8 = Runner(c8)
+        r8.settle(0.5)
         ms8, _ = r8.timed_steps(max(5, args.steps // 5), 3)
         ph8 = r8.timed_phases(10)
         fms8 = r8.flushed_steps(5)

@@ -107,8 +107,11 @@ size_t gn_workspace_bytes(int64_t N, int64_t C, int64_t S, int64_t G);
  * y = act(gamma_c * (x - mean) * rstd + beta_c) computed in fp32 and stored once in
  * y_dtype. x_dtype is GN_F32, GN_BF16 or GN_F16; y_dtype is x_dtype or GN_F32 (the fp32-output
  * mode). gamma == NULL means all ones, beta == NULL all zeros. eps must be finite and
- * >= 0. activation is a gn_activation. Enqueues gn_forward_stats then gn_forward_apply
- * (three kernels).
+ * >= 0. activation is a gn_activation. Two kernels: the partial statistics, then the
+ * normalize with the finalize folded into each of its workgroups ("Optimize GroupNorm",
+ * paragraph folding seven launches into four); mean, rstd and y are bitwise those of
+ * gn_forward_stats followed by gn_forward_apply (three kernels), which compute the same
+ * merge in the same order.
  */
 int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta,
                int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
@@ -145,7 +148,9 @@ int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S
  * finite inputs (NaN/Inf still propagate). With activation GN_ACT_RELU, dy is the gradient
  * of the relu's output and is gated as stated above before all of this (beta, NULL for
  * zeros, is then needed to recompute the pre-activation; it is ignored otherwise).
- * Enqueues gn_backward_reduce then, unless dx is NULL, gn_backward_apply (three kernels).
+ * With dx, two kernels: the per-job sums, then dx with the finalize (c1, c2, and dgamma,
+ * dbeta) folded in; without dx, gn_backward_reduce alone. The results are bitwise those
+ * of gn_backward_reduce followed by gn_backward_apply (three kernels).
  */
 int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
                 const float* mean, const float* rstd, const float* gamma,
@@ -175,6 +180,41 @@ int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
                       int64_t N, int64_t C, int64_t S, int64_t G, int activation, void* dx,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The two launches of gn_forward as two calls, stream-ordered on one workspace, so that
+ * each can be timed or overlapped on its own; together they are bitwise gn_forward.
+ * gn_forward_partials leaves the partial statistics of x in the workspace (one kernel);
+ * gn_forward_finish takes gn_forward's arguments, merges them and writes mean, rstd and y
+ * (one kernel). On shapes that gn_plan_query reports resident_forward for, the first call
+ * enqueues nothing and the second runs the whole forward. Errors as gn_forward.
+ */
+int gn_forward_partials(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+int gn_forward_finish(const void* x, int x_dtype, const float* gamma, const float* beta,
+                      int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
+                      void* y, int y_dtype, float* mean, float* rstd,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two launches of gn_backward, likewise: gn_backward_partials leaves the per-job sums
+ * of dy and dy*xhat in the workspace; gn_backward_finish takes gn_backward's arguments and
+ * writes dx, dgamma and dbeta (each may be NULL; with dx NULL it runs the finalize alone).
+ * Together they are bitwise gn_backward; resident_backward shapes as above.
+ */
+int gn_backward_partials(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                         const float* mean, const float* rstd, const float* gamma,
+                         const float* beta, int activation,
+                         int64_t N, int64_t C, int64_t S, int64_t G,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+int gn_backward_finish(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                       const float* mean, const float* rstd, const float* gamma,
+                       const float* beta, int activation,
+                       int64_t N, int64_t C, int64_t S, int64_t G,
+                       void* dx, float* dgamma, float* dbeta,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static English description of a status code (never NULL). */
 const char* gn_status_string(int status);
 
@@ -184,8 +224,10 @@ const char* gn_status_string(int status);
  * reductions work on jobs: reduction job j covers elements
  * [k*chunk, min((k+1)*chunk, S)) of row r = j / chunks_per_row (row r = n*C + c),
  * k = j % chunks_per_row, and leaves one fp32 partial; their number and length fix the
- * reduction order. The streaming kernels (normalize, dx) cover the rows the same way
- * with apply_chunk and apply_chunks_per_row; they reduce nothing.
+ * reduction order. The streaming kernels of the split-phase entry points (normalize, dx)
+ * cover the rows the same way with apply_chunk and apply_chunks_per_row, and those of
+ * gn_forward / gn_backward, which merge their group's partials first, with fold_chunk
+ * and fold_chunks_per_row (256 threads each); neither reduces anything that is stored.
  */
 typedef struct gn_plan_info {
     int64_t rows;                 /* N*C */
@@ -208,6 +250,9 @@ typedef struct gn_plan_info {
     int32_t resident_backward;    /* 1 if the backward takes the resident path */
     int32_t resident_block_forward, resident_vectors_forward;    /* threads, vectors per thread */
     int32_t resident_block_backward, resident_vectors_backward;
+    int64_t fold_chunk;           /* elements per streaming job with the finalize folded in */
+    int64_t fold_chunks_per_row;
+    int64_t fold_jobs;            /* rows * fold_chunks_per_row */
 } gn_plan_info;
 
 /* Fills *out for a valid shape and returns GN_OK; otherwise returns the shape error. */

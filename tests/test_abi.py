@@ -21,7 +21,7 @@ def _declared_functions():
 
 def test_every_declared_function_is_exported():
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 22, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -37,7 +37,7 @@ def test_status_enum_matches_header():
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == 7
+    assert lib.gn_abi_version() == 8
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every
@@ -46,18 +46,18 @@ A = ctypes.c_void_p(0x10000)
 B = ctypes.c_void_p(0x20000)
 
 
-def fwd(**kw):
+def fwd(fn="gn_forward", **kw):
     args = dict(x=A, xdt=GN_BF16, gamma=None, beta=None, N=1, C=8, S=64, G=4, eps=1e-5, act=0, y=B,
                 ydt=GN_BF16, mean=A, rstd=B, ws=A, wsb=1 << 20, stream=None)
     args.update(kw)
-    return lib.gn_forward(*args.values())
+    return getattr(lib, fn)(*args.values())
 
 
-def bwd(**kw):
+def bwd(fn="gn_backward", **kw):
     args = dict(dy=A, dydt=GN_BF16, x=B, xdt=GN_BF16, mean=A, rstd=B, gamma=None, beta=None, act=0,
                 N=1, C=8, S=64, G=4, dx=A, dgamma=None, dbeta=None, ws=B, wsb=1 << 20, stream=None)
     args.update(kw)
-    return lib.gn_backward(*args.values())
+    return getattr(lib, fn)(*args.values())
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -71,8 +71,9 @@ def bwd(**kw):
     (dict(ws=ctypes.c_void_p(0x10004)), 7), (dict(mean=ctypes.c_void_p(0x10001)), 7),
     (dict(act=2), 10), (dict(act=-1), 10),
 ])
-def test_forward_validation(kw, status):
-    assert fwd(**kw) == status
+@pytest.mark.parametrize("fn", ["gn_forward", "gn_forward_finish"])
+def test_forward_validation(kw, status, fn):
+    assert fwd(fn, **kw) == status
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -82,8 +83,26 @@ def test_forward_validation(kw, status):
     (dict(dgamma=ctypes.c_void_p(0x10002)), 7), (dict(beta=ctypes.c_void_p(0x10002)), 7),
     (dict(act=5), 10),
 ])
-def test_backward_validation(kw, status):
-    assert bwd(**kw) == status
+@pytest.mark.parametrize("fn", ["gn_backward", "gn_backward_finish"])
+def test_backward_validation(kw, status, fn):
+    assert bwd(fn, **kw) == status
+
+
+def test_partials_validation():
+    assert lib.gn_forward_partials(None, GN_BF16, 1, 8, 64, 4, A, 1 << 20, None) == 1
+    assert lib.gn_forward_partials(A, GN_BF16, 1, 8, 64, 4, None, 1 << 20, None) == 1
+    assert lib.gn_forward_partials(A, GN_BF16, 1, 8, 64, 3, A, 1 << 20, None) == 3
+    assert lib.gn_forward_partials(A, GN_BF16, 0, 8, 64, 4, A, 1 << 20, None) == 2
+    assert lib.gn_forward_partials(A, 9, 1, 8, 64, 4, A, 1 << 20, None) == 4
+    assert lib.gn_forward_partials(A, GN_BF16, 1, 8, 64, 4, A, 8, None) == 6
+    assert lib.gn_forward_partials(ctypes.c_void_p(0x10002), GN_BF16, 1, 8, 64, 4, A, 1 << 20, None) == 7
+    args = [A, GN_BF16, B, GN_BF16, A, B, None, None, 0, 1, 8, 64, 4, A, 1 << 20, None]
+    assert lib.gn_backward_partials(*args[:-3], None, 1 << 20, None) == 1
+    assert lib.gn_backward_partials(None, *args[1:]) == 1
+    assert lib.gn_backward_partials(*args[:8], 3, *args[9:]) == 10
+    assert lib.gn_backward_partials(*args[:12], 3, *args[13:]) == 3
+    assert lib.gn_backward_partials(*args[:-2], 16, None) == 6
+    assert lib.gn_backward_partials(*args[:4], ctypes.c_void_p(0x10001), *args[5:]) == 7
 
 
 def test_split_phase_validation():

@@ -334,7 +334,16 @@ def test_one_workspace_across_shapes():
             assert torch.equal(_bits(dx_only), _bits(ref_b[0]))
 
 
-@pytest.mark.parametrize("case", [workloads.SCALE7, workloads.DEEP], ids=lambda c: c.name)
+SPLIT_CASES = [
+    workloads.SCALE7, workloads.DEEP,
+    # ragged rows (S not a multiple of 8) split into several folded jobs with edge steps
+    workloads.custom(2, 24, 6, (33, 31, 29), torch.bfloat16, dist="unet", seed=71),
+    workloads.custom(3, 12, 3, (40, 41, 37), torch.float16, torch.float32, dist="deep", seed=72),
+    workloads.custom(1, 16, 4, (50, 60, 70), torch.float32, dist="normal", seed=73),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=lambda c: c.name)
 def test_split_phase_entry_points_match_fused(case):
     say(f"{case.name}: split-phase entry points vs gn_forward/gn_backward")
     inp = workloads.make(case, DEV)
@@ -348,6 +357,15 @@ def test_split_phase_entry_points_match_fused(case):
     dx2, dg2, db2 = torch.empty_like(dx), torch.empty_like(dg), torch.empty_like(db)
     gn.gn_backward_reduce(inp["dy"], x, mean2, rstd2, gamma, G, dg2, db2, ws)
     gn.gn_backward_apply(inp["dy"], x, G, dx2, ws)
+    torch.cuda.synchronize()
+    for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2), (dg, dg2), (db, db2)):
+        assert torch.equal(u, v)
+    say(f"{case.name}: the two-call halves of gn_forward/gn_backward vs the fused calls")
+    ws.fill_(0xFF)
+    gn.gn_forward_partials(x, G, ws)
+    gn.gn_forward_finish(x, gamma, beta, G, inp["eps"], y2, mean2, rstd2, ws)
+    gn.gn_backward_partials(inp["dy"], x, mean2, rstd2, gamma, G, ws)
+    gn.gn_backward_finish(inp["dy"], x, mean2, rstd2, gamma, G, dx2, dg2, db2, ws)
     torch.cuda.synchronize()
     for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2), (dg, dg2), (db, db2)):
         assert torch.equal(u, v)

@@ -135,6 +135,65 @@ def test_streaming_jobs_cover_every_element_once_and_stay_in_bounds(N, C, S, G):
     assert (seen == 1).all()
 
 
+def _full_step_range(v0, vf0, vf1, nvec, stepv):
+    nsteps = -(-nvec // stepv)
+    fs = 1 if v0 < vf0 else 0
+    fe = max((vf1 - v0) // stepv, fs)
+    return fs, fe, nsteps
+
+
+@pytest.mark.parametrize("V", [1, 2, 4])
+@pytest.mark.parametrize("N,C,S,G", [s for s in SHAPES if s[0] * s[1] * s[2] <= 2 ** 22])
+def test_folded_jobs_cover_every_element_once_and_stay_in_bounds(N, C, S, G, V):
+    """apply_fin_kernel / bwd_apply_fin_kernel: 256 threads, V vectors per lane per step,
+    full steps [fs, fe) from raw vector loads, at most one edge step on each side element by
+    element; every group has exactly one publishing job (its first row's first job) and
+    every channel one dgamma/dbeta job (sample 0, first job)."""
+    p = g.gn_plan_query(N, C, S, G)
+    total = N * C * S
+    seen = np.zeros(total, dtype=np.int32)
+    blk, stepv = 256, 256 * V
+    K, chunk = p["fold_chunks_per_row"], p["fold_chunk"]
+    assert p["fold_jobs"] == p["rows"] * K
+    assert chunk <= max(p["chunk"], 1) and (chunk <= 8192 or chunk == p["chunk"])
+    assert (K - 1) * chunk < S <= K * chunk
+    Cg = C // G
+    publishers = np.zeros(N * G, dtype=np.int32)
+    param_jobs = np.zeros(C, dtype=np.int32)
+    for j in range(p["fold_jobs"]):
+        row, k = divmod(j, K)
+        n, c = divmod(row, C)
+        gg = c // Cg
+        if k == 0 and c == gg * Cg:
+            publishers[n * G + gg] += 1
+        if k == 0 and n == 0:
+            param_jobs[c] += 1
+        pbase = (n * C + gg * Cg) * p["chunks_per_row"]
+        assert 0 <= pbase and pbase + p["partials_per_group"] <= p["jobs"]
+        lo, hi = row * S + k * chunk, row * S + min((k + 1) * chunk, S)
+        assert 0 <= lo < hi <= total
+        v0, vf0, vf1 = lo // VEC, (lo + VEC - 1) // VEC, hi // VEC
+        nvec = (hi + VEC - 1) // VEC - v0
+        fs, fe, nsteps = _full_step_range(v0, vf0, vf1, nvec, stepv)
+        lanes = np.arange(blk)
+        for s_ in range(fs, fe):  # raw loads: every vector must be whole and inside the job
+            vi = (v0 + s_ * stepv + np.arange(V)[:, None] * blk + lanes[None, :]).reshape(-1)
+            assert ((vi >= vf0) & (vi < vf1)).all()
+            for e in range(VEC):
+                np.add.at(seen, vi * VEC + e, 1)
+        edge = ([0] if fs > 0 else []) + ([fe] if fe < nsteps else [])
+        for s_ in edge:
+            vi = (v0 + s_ * stepv + np.arange(V)[:, None] * blk + lanes[None, :]).reshape(-1)
+            whole = (vi >= vf0) & (vi < vf1)
+            for e in range(VEC):
+                np.add.at(seen, vi[whole] * VEC + e, 1)
+            elems = vi[~whole][:, None] * VEC + np.arange(VEC)[None, :]
+            ok = (elems >= lo) & (elems < hi)
+            np.add.at(seen, elems[ok], 1)
+    assert (seen == 1).all()
+    assert (publishers == 1).all() and (param_jobs == 1).all()
+
+
 def test_invalid_shapes_are_rejected_before_any_launch():
     info = g.gn_plan_query  # noqa: F841
     assert lib.gn_workspace_bytes(0, 4, 8, 2) == 0

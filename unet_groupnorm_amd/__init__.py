@@ -9,11 +9,15 @@ from .gn import (  # noqa: F401
     as_layout,
     gn_backward,
     gn_backward_apply,
+    gn_backward_finish,
+    gn_backward_partials,
     gn_backward_reduce,
     gn_backward_shard_merge,
     gn_backward_shard_sums,
     gn_forward,
     gn_forward_apply,
+    gn_forward_finish,
+    gn_forward_partials,
     gn_forward_shard_merge,
     gn_forward_shard_stats,
     gn_forward_stats,

@@ -41,6 +41,9 @@ class GnPlanInfo(ctypes.Structure):
         ("resident_vectors_forward", ctypes.c_int32),
         ("resident_block_backward", ctypes.c_int32),
         ("resident_vectors_backward", ctypes.c_int32),
+        ("fold_chunk", ctypes.c_int64),
+        ("fold_chunks_per_row", ctypes.c_int64),
+        ("fold_jobs", ctypes.c_int64),
     ]
 
 
@@ -78,6 +81,10 @@ def _declare(lib):
         "gn_forward_cl": (I, [P, I, P, P, I64, I64, I64, I64, F, I, P, I, P, P, P, SZ, P]),
         "gn_backward_cl": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, P, P, SZ, P]),
         "gn_plan_query_cl": (I, [I64, I64, I64, I64, ctypes.POINTER(GnPlanInfoCL)]),
+        "gn_forward_partials": (I, [P, I, I64, I64, I64, I64, P, SZ, P]),
+        "gn_forward_finish": (I, [P, I, P, P, I64, I64, I64, I64, F, I, P, I, P, P, P, SZ, P]),
+        "gn_backward_partials": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, SZ, P]),
+        "gn_backward_finish": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, P, P, SZ, P]),
         "gn_forward_shard_stats": (I, [P, I, I64, I64, I64, I64, P, P, SZ, P]),
         "gn_forward_shard_merge": (I, [P, I64, P, P, I64, I64, I64, I64, F, P, P, P, SZ, P]),
         "gn_backward_shard_sums": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, SZ, P]),

@@ -11,7 +11,16 @@
 #include "gn_launch.hpp"
 #include "gn_plan.hpp"
 
+// Whether gn_forward and gn_backward (with dx) run the finalize inside the streaming pass
+// (two launches per direction) or as a kernel of its own (three); compile-time
+// overridable for measurement builds. The split-phase entry points always run it alone.
+#ifndef GN_FOLD_FINALIZE
+#define GN_FOLD_FINALIZE 1
+#endif
+
 namespace {
+
+constexpr bool kFoldFinalize = GN_FOLD_FINALIZE;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool dtype_ok(int d) { return d == GN_F32 || d == GN_BF16 || d == GN_F16; }
@@ -104,6 +113,54 @@ int bwd_check(const void* dy, int dy_dtype, const void* x, int x_dtype, const fl
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GN_OK : GN_ERR_LAUNCH; }
 
+// The two halves of gn_forward. On the resident path the first does nothing and the
+// second runs the whole forward.
+int fwd_partials(const void* x, int x_dtype, const gn::Plan& p, const gn::KArgs& a, gn::Workspace w,
+                 hipStream_t st)
+{
+    if (p.res_fwd) return GN_OK;
+    return launch_status(gn::launch_stats_partials(x, x_dtype, a, w, st));
+}
+
+int fwd_finish(const void* x, int x_dtype, const float* gamma, const float* beta, float eps, void* y,
+               int y_dtype, float* mean, float* rstd, const gn::Plan& p, const gn::KArgs& a,
+               gn::Workspace w, hipStream_t st)
+{
+    if (p.res_fwd)
+        return launch_status(gn::launch_res_fwd(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype, a, w,
+                                                st, p.res_block_f, p.res_vecs_f));
+    if (kFoldFinalize)
+        return launch_status(gn::launch_fwd_apply_fin(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype, a,
+                                                      w, st));
+    const int rc = launch_status(gn::launch_fin_fwd(x, x_dtype, gamma, beta, eps, mean, rstd, a, w, st));
+    if (rc) return rc;
+    return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, a, w, st));
+}
+
+// The two halves of gn_backward, likewise.
+int bwd_partials(const void* dy, int dy_dtype, const void* x, int x_dtype, const float* mean,
+                 const float* rstd, const float* gamma, const float* beta, const gn::Plan& p,
+                 const gn::KArgs& a, gn::Workspace w, hipStream_t st)
+{
+    if (p.res_bwd) return GN_OK;
+    return launch_status(gn::launch_bwd_partials(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, a, w, st));
+}
+
+int bwd_finish(const void* dy, int dy_dtype, const void* x, int x_dtype, const float* mean, const float* rstd,
+               const float* gamma, const float* beta, void* dx, float* dgamma, float* dbeta,
+               const gn::Plan& p, const gn::KArgs& a, gn::Workspace w, hipStream_t st)
+{
+    if (p.res_bwd)
+        return launch_status(gn::launch_res_bwd(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
+                                                dbeta, dx, a, w, st, p.res_block_b, p.res_vecs_b));
+    if (kFoldFinalize && dx)
+        return launch_status(gn::launch_bwd_apply_fin(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
+                                                      dbeta, dx, a, w, st));
+    const int rc = launch_status(gn::launch_fin_bwd(mean, rstd, gamma, beta, dgamma, dbeta, a, w, st));
+    if (rc || !dx) return rc;
+    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, a, w, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,10 +196,13 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     out->resident_vectors_forward = p.res_vecs_f;
     out->resident_block_backward = p.res_block_b;
     out->resident_vectors_backward = p.res_vecs_b;
+    out->fold_chunk = p.chunk_f;
+    out->fold_chunks_per_row = p.K_f;
+    out->fold_jobs = p.jobs_f;
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 7; }
+int gn_abi_version(void) { return 8; }
 
 const char* gn_status_string(int status)
 {
@@ -222,12 +282,39 @@ int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta
     const gn::KArgs a = gn::kargs_of(p, activation);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.res_fwd)
-        return launch_status(gn::launch_res_fwd(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype, a, w,
-                                                st, p.res_block_f, p.res_vecs_f));
-    if ((rc = launch_status(gn::launch_fwd_stats(x, x_dtype, gamma, beta, eps, mean, rstd, a, w, st))))
-        return rc;
-    return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, a, w, st));
+    if ((rc = fwd_partials(x, x_dtype, p, a, w, st))) return rc;
+    return fwd_finish(x, x_dtype, gamma, beta, eps, y, y_dtype, mean, rstd, p, a, w, st);
+}
+
+int gn_forward_partials(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S, int64_t G,
+                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!x || !workspace) return GN_ERR_NULL;
+    gn::Plan p;
+    int rc = plan_or_error(N, C, S, G, &p);
+    if (rc) return rc;
+    if (!dtype_ok(x_dtype)) return GN_ERR_DTYPE;
+    if (!aligned(x, 16)) return GN_ERR_ALIGN;
+    if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    return fwd_partials(x, x_dtype, p, gn::kargs_of(p), gn::workspace_of(workspace, p),
+                        static_cast<hipStream_t>(stream));
+}
+
+int gn_forward_finish(const void* x, int x_dtype, const float* gamma, const float* beta,
+                      int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
+                      void* y, int y_dtype, float* mean, float* rstd,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = fwd_check(x, x_dtype, gamma, beta, N, C, S, G, eps, activation, y, y_dtype, mean, rstd,
+                       workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    return fwd_finish(x, x_dtype, gamma, beta, eps, y, y_dtype, mean, rstd, p, gn::kargs_of(p, activation),
+                      gn::workspace_of(workspace, p), static_cast<hipStream_t>(stream));
 }
 
 int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
@@ -288,14 +375,42 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
     const gn::KArgs a = gn::kargs_of(p, activation);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.res_bwd)
-        return launch_status(gn::launch_res_bwd(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
-                                                dbeta, dx, a, w, st, p.res_block_b, p.res_vecs_b));
-    if ((rc = launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta,
-                                                  dgamma, dbeta, a, w, st))))
-        return rc;
-    if (!dx) return GN_OK;
-    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, a, w, st));
+    if ((rc = bwd_partials(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, p, a, w, st))) return rc;
+    return bwd_finish(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx, dgamma, dbeta, p, a, w, st);
+}
+
+int gn_backward_partials(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                         const float* mean, const float* rstd, const float* gamma,
+                         const float* beta, int activation,
+                         int64_t N, int64_t C, int64_t S, int64_t G,
+                         void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, activation, N, C, S, G, nullptr,
+                       nullptr, nullptr, workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    return bwd_partials(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, p, gn::kargs_of(p, activation),
+                        gn::workspace_of(workspace, p), static_cast<hipStream_t>(stream));
+}
+
+int gn_backward_finish(const void* dy, int dy_dtype, const void* x, int x_dtype,
+                       const float* mean, const float* rstd, const float* gamma,
+                       const float* beta, int activation,
+                       int64_t N, int64_t C, int64_t S, int64_t G,
+                       void* dx, float* dgamma, float* dbeta,
+                       void* workspace, size_t workspace_bytes, void* stream)
+{
+    gn::Plan p;
+    int rc = bwd_check(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, activation, N, C, S, G, dx,
+                       dgamma, dbeta, workspace, workspace_bytes, &p);
+    if (rc) return rc;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    return bwd_finish(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx, dgamma, dbeta, p,
+                      gn::kargs_of(p, activation), gn::workspace_of(workspace, p),
+                      static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ spatial shards

@@ -32,6 +32,13 @@
 #ifndef GN_NT_STORE
 #define GN_NT_STORE 0
 #endif
+// Store policy of the streaming kernels with the finalize folded in (1: nontemporal). Their
+// workgroups each write a run of tens of KiB, and nontemporal stores measured about 7%
+// faster for them at 256^3 on MI355X (the one-step streaming kernels: no gain; the
+// channels-last ones: mixed), so the default differs from GN_NT_STORE's.
+#ifndef GN_NT_STORE_FOLD
+#define GN_NT_STORE_FOLD 1
+#endif
 
 namespace gn {
 
@@ -40,7 +47,7 @@ namespace {
 constexpr bool kNtStats = GN_NT_STATS, kNtBwdReduce = GN_NT_BRED;
 constexpr bool kNtApply = GN_NT_APPLY, kNtBwdApply = GN_NT_BAPPLY;
 constexpr bool kReverseApply = GN_REVERSE_APPLY;
-constexpr bool kNtStore = GN_NT_STORE;
+constexpr bool kNtStore = GN_NT_STORE, kNtStoreFold = GN_NT_STORE_FOLD;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -98,6 +105,7 @@ template <> struct Io<uint16_t> {  // bf16 storage
     {
         return __uint_as_float(uint32_t(*p) << 16);
     }
+    template <bool NT = kNtStore>
     static __device__ __forceinline__ void store8(uint16_t* p, const float (&v)[8])
     {
         u32x4 u;
@@ -105,7 +113,7 @@ template <> struct Io<uint16_t> {  // bf16 storage
         u.y = pack_bf16(v[2], v[3]);
         u.z = pack_bf16(v[4], v[5]);
         u.w = pack_bf16(v[6], v[7]);
-        if (kNtStore)
+        if (NT)
             __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
         else
             *reinterpret_cast<u32x4*>(p) = u;
@@ -137,10 +145,11 @@ template <> struct Io<float> {
         widen(load_raw<NT>(p), v);
     }
     static __device__ __forceinline__ float load1(const float* p) { return *p; }
+    template <bool NT = kNtStore>
     static __device__ __forceinline__ void store8(float* p, const float (&v)[8])
     {
         const f32x4 a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
-        if (kNtStore) {
+        if (NT) {
             __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
             __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
         } else {
@@ -153,7 +162,16 @@ template <> struct Io<float> {
 
 // fp16 storage (IEEE binary16): widening is exact; narrowing converts one value at a time
 // with round-to-nearest-even (the default rounding mode), keeping fp16 subnormals and
-// overflowing to infinity.
+// overflowing to infinity. The value is first pinned as an fp32 register: otherwise the
+// compiler fuses an fma that produced it with the narrowing (v_fma_mixlo_f16), which rounds
+// the exact product-sum to fp16 once, and an fp16 output would no longer be the fp32
+// output rounded, wherever the fp32 result is an fp16 midpoint.
+__device__ __forceinline__ float pin_f32(float v)
+{
+    asm("" : "+v"(v));
+    return v;
+}
+
 template <> struct Io<_Float16> {
     struct Raw {
         u32x4 u;
@@ -168,8 +186,8 @@ template <> struct Io<_Float16> {
     }
     static __device__ __forceinline__ uint32_t pack(float a, float b)
     {
-        return uint32_t(__builtin_bit_cast(uint16_t, _Float16(a))) |
-               (uint32_t(__builtin_bit_cast(uint16_t, _Float16(b))) << 16);
+        return uint32_t(__builtin_bit_cast(uint16_t, _Float16(pin_f32(a)))) |
+               (uint32_t(__builtin_bit_cast(uint16_t, _Float16(pin_f32(b)))) << 16);
     }
     template <bool NT>
     static __device__ __forceinline__ Raw load_raw(const _Float16* p)
@@ -190,6 +208,7 @@ template <> struct Io<_Float16> {
         widen(load_raw<NT>(p), v);
     }
     static __device__ __forceinline__ float load1(const _Float16* p) { return float(*p); }
+    template <bool NT = kNtStore>
     static __device__ __forceinline__ void store8(_Float16* p, const float (&v)[8])
     {
         u32x4 u;
@@ -197,12 +216,12 @@ template <> struct Io<_Float16> {
         u.y = pack(v[2], v[3]);
         u.z = pack(v[4], v[5]);
         u.w = pack(v[6], v[7]);
-        if (kNtStore)
+        if (NT)
             __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
         else
             *reinterpret_cast<u32x4*>(p) = u;
     }
-    static __device__ __forceinline__ void store1(_Float16* p, float v) { *p = _Float16(v); }
+    static __device__ __forceinline__ void store1(_Float16* p, float v) { *p = _Float16(pin_f32(v)); }
 };
 
 // ------------------------------------------------------------------ Chan merge

@@ -1,25 +1,34 @@
 // gn_kernels.hip -- GroupNorm forward/backward kernels for gfx950 (MI355X, CDNA4).
 //
-// Two kernel sets. The two-pass set, three kernels per direction:
-//   stats_kernel       per reduction job: (mean, M2) of x                   [read x]
-//   fin_fwd_kernel     per group: fixed-order merge -> mean, rstd, and per-row
-//                      normalize coefficients                               [tiny]
-//   apply_kernel       per streaming job: y = (x - mean) * gamma*rstd + beta [read x, write y]
-//   bwd_reduce_kernel  per reduction job: sum dy, sum dy*xhat               [read x, dy]
-//   fin_bwd_kernel     per group: c1, c2 -> per-row dx coefficients; per
-//                      channel: dgamma, dbeta                                [tiny]
-//   bwd_apply_kernel   per streaming job: dx                                [read x, dy, write dx]
-// and the resident set for small groups, one kernel per direction (see "resident path"):
-//   res_fwd_kernel     per group: statistics and y from registers           [read x, write y]
-//   res_bwd_kernel     per g over all samples: sums, dgamma/dbeta, dx       [read x, dy, write dx]
+// Three kernel sets. The two-pass set, two kernels per direction, used by gn_forward and
+// gn_backward:
+//   stats_kernel          per reduction job: (mean, M2) of x                  [read x]
+//   apply_fin_kernel      per folded job: the group's finalize, then
+//                         y = (x - mean) * gamma*rstd + beta                 [read x, write y]
+//   bwd_reduce_kernel     per reduction job: sum dy, sum dy*xhat              [read x, dy]
+//   bwd_apply_fin_kernel  per folded job: the group's c1, c2, then dx; per
+//                         channel (one job each): dgamma, dbeta              [read x, dy, write dx]
+// The split-phase entry points run the finalize as a kernel of its own, so that the
+// statistics exist between the two calls, and stream with one-step jobs:
+//   fin_fwd_kernel        per group: fixed-order merge -> mean, rstd, and per-row
+//                         normalize coefficients                             [tiny]
+//   apply_kernel          per streaming job: y from the coefficients          [read x, write y]
+//   fin_bwd_kernel        per group: c1, c2 -> per-row dx coefficients; per
+//                         channel: dgamma, dbeta                             [tiny]
+//   bwd_apply_kernel      per streaming job: dx                              [read x, dy, write dx]
+// Both run the same merge code in the same order, so their results agree bitwise. The
+// resident set for small groups, one kernel per direction (see "resident path"):
+//   res_fwd_kernel        per group: statistics and y from registers          [read x, write y]
+//   res_bwd_kernel        per g over all samples: sums, dgamma/dbeta, dx      [read x, dy, write dx]
 //
 // The pages fold the finalize into the elementwise kernels ("Optimize GroupNorm",
 // LBANN/ScaFFold pull 93, paragraph folding seven launches into four) and cap the
-// elementwise grid so that the redundant partial reads stay small. On MI355X the
-// streaming kernels move data fastest as a very large grid of workgroups that each move
-// a few KiB once, which a folded finalize would multiply; so here the finalize runs once
-// per group in a small kernel of its own and the streaming kernels read 16 bytes of
-// per-row coefficients.
+// elementwise grid so that the redundant partial reads stay small. Here the folded jobs
+// are kFoldChunk elements (16 KiB of bf16 in, 16 KiB out), so a group's P partials (2 KiB
+// at 128^3, C=32, G=8) are re-read from L2 by a few hundred workgroups instead of a few
+// thousand one-step ones; on MI355X that removes the finalize launch (about 5 us each
+// way) for about 1 us of merge latency per workgroup, most of it behind the workgroup's
+// first loads.
 //
 // A reduction job is a contiguous run of one row (row = n*C + c). Lane t of a workgroup
 // owns the 8-element vectors t, t + B, t + 2B, ... of its job (B = block size, vectors
@@ -163,13 +172,13 @@ __device__ __forceinline__ uint32_t load_step_masked(const T* __restrict__ p, co
 
 // ------------------------------------------------------------------ forward
 
-// The lane's kStepVecs raw vectors of one full step.
-template <bool NT, typename T>
+// The lane's V raw vectors of one full step.
+template <bool NT, int V, typename T>
 __device__ __forceinline__ void load_raw_step(const T* __restrict__ p, int64_t sv0, int blk, int tid,
-                                              typename Io<T>::Raw (&r)[kStepVecs])
+                                              typename Io<T>::Raw (&r)[V])
 {
 #pragma unroll
-    for (int u = 0; u < kStepVecs; ++u) r[u] = Io<T>::template load_raw<NT>(p + (sv0 + int64_t(u) * blk + tid) * kVec);
+    for (int u = 0; u < V; ++u) r[u] = Io<T>::template load_raw<NT>(p + (sv0 + int64_t(u) * blk + tid) * kVec);
 }
 
 // Steps [fs, fe) of a job are full; step 0 when fs = 1 and step fe when fe < nsteps hold
@@ -263,22 +272,28 @@ stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
     }
 }
 
-// One workgroup per group (n, g): merges the group's P partials in a fixed order (lane
-// t takes partials t, t + B, ... in index order, then the shuffle tree, then the waves
-// in order), publishes mean and rstd, and writes each row's normalize coefficients
-// (mean head, mean tail, gamma_c * rstd, beta_c).
+// Shared memory of the forward finalize.
+struct FinFwdLds {
+    uint64_t n[kMaxWaves];
+    float m[kMaxWaves], M[kMaxWaves];
+    float stat[3];
+};
+
+struct GroupStat {
+    float hi, lo, rstd;
+};
+
+// The forward finalize of group (n, g), called by every thread of a 256-thread workgroup:
+// the group's P partials merged in a fixed order (lane t takes partials t, t + 256, ... in
+// index order, then the shuffle tree, then the waves in order), var = M2 / M, rstd, and
+// the mean as an unevaluated sum hi + lo: hi is the fp32 mean that is published, lo what
+// rounding it left out. The normalize takes x - mean as (x - hi) - lo, which is exact in
+// its first step whenever x is close to the mean. Every thread receives the result.
 template <typename TX>
-__global__ void __launch_bounds__(256)
-fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
-               const float* __restrict__ beta, float eps, const float2* __restrict__ part,
-               float* __restrict__ mean_out, float* __restrict__ rstd_out, KArgs a,
-               float4* __restrict__ coef)
+__device__ __forceinline__ GroupStat group_stat(const TX* __restrict__ x, const float2* __restrict__ part,
+                                                const KArgs& a, float eps, int64_t n, int64_t g,
+                                                FinFwdLds& l)
 {
-    __shared__ uint64_t s_n[kMaxWaves];
-    __shared__ float s_m[kMaxWaves], s_M[kMaxWaves];
-    __shared__ float s_stat[3];
-    const int64_t ng = blockIdx.x;
-    const int64_t n = ng / a.G, g = ng - n * a.G;
     const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
     // Requested before the merge so that its latency overlaps the partials' loads.
     const float K = group_shift(x, a, n, g);
@@ -287,27 +302,96 @@ fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
         const float2 pm = part[pbase + j];
         chan_merge(acc, uint64_t(job_count(a, j % a.K)), pm.x, pm.y);
     }
-    const Moments<uint64_t> r = block_merge(acc, s_n, s_m, s_M);
+    const Moments<uint64_t> r = block_merge(acc, l.n, l.m, l.M);
     if (threadIdx.x == 0) {
         float var = float(double(r.M2) / double(a.M));
         var = (var < 0.0f) ? 0.0f : var;  // rounding can leave a tiny negative; NaN passes through
-        const float rstd = 1.0f / __fsqrt_rn(var + eps);
-        // The mean as an unevaluated sum hi + lo: hi is the fp32 mean that is published,
-        // lo what rounding it left out. The normalize takes x - mean as (x - hi) - lo,
-        // which is exact in its first step whenever x is close to the mean.
         const float hi = K + r.m;
-        const float lo = (K - hi) + r.m;
-        mean_out[ng] = hi;
-        rstd_out[ng] = rstd;
-        s_stat[0] = hi; s_stat[1] = lo; s_stat[2] = rstd;
+        l.stat[0] = hi;
+        l.stat[1] = (K - hi) + r.m;
+        l.stat[2] = 1.0f / __fsqrt_rn(var + eps);
     }
     __syncthreads();
-    const float hi = s_stat[0], lo = s_stat[1], rstd = s_stat[2];
+    // The next writer of l.stat is thread 0 after two barriers of the next merge.
+    return GroupStat{l.stat[0], l.stat[1], l.stat[2]};
+}
+
+// Publishes group (n, g)'s mean and rstd and writes each of its rows' normalize
+// coefficients (mean head, mean tail, gamma_c * rstd, beta_c).
+__device__ __forceinline__ void publish_group_stat(const GroupStat& st, const float* __restrict__ gamma,
+                                                   const float* __restrict__ beta, const KArgs& a,
+                                                   int64_t n, int64_t g, float* __restrict__ mean_out,
+                                                   float* __restrict__ rstd_out, float4* __restrict__ coef)
+{
+    if (threadIdx.x == 0) {
+        mean_out[n * a.G + g] = st.hi;
+        rstd_out[n * a.G + g] = st.rstd;
+    }
     for (int64_t i = threadIdx.x; i < a.Cg; i += blockDim.x) {
         const int64_t c = g * a.Cg + i;
         const float gm = gamma ? gamma[c] : 1.0f;
         const float bt = beta ? beta[c] : 0.0f;
-        coef[2 * (n * a.C + c)] = make_float4(hi, lo, gm * rstd, bt);
+        coef[2 * (n * a.C + c)] = make_float4(st.hi, st.lo, gm * st.rstd, bt);
+    }
+}
+
+// One workgroup per group (n, g): the forward finalize, mean and rstd, and the rows'
+// normalize coefficients for apply_kernel.
+template <typename TX>
+__global__ void __launch_bounds__(256)
+fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
+               const float* __restrict__ beta, float eps, const float2* __restrict__ part,
+               float* __restrict__ mean_out, float* __restrict__ rstd_out, KArgs a,
+               float4* __restrict__ coef)
+{
+    __shared__ FinFwdLds l;
+    const int64_t ng = blockIdx.x;
+    const int64_t n = ng / a.G, g = ng - n * a.G;
+    const GroupStat st = group_stat(x, part, a, eps, n, g, l);
+    publish_group_stat(st, gamma, beta, a, n, g, mean_out, rstd_out, coef);
+}
+
+// Vectors per lane per step of the folded streaming kernels, and the waves per SIMD they
+// are compiled for (their register cap).
+#ifndef GN_FIN_VECS
+#define GN_FIN_VECS 2
+#endif
+constexpr int kFinVecs = GN_FIN_VECS;
+#ifndef GN_FIN_WAVES_F
+#define GN_FIN_WAVES_F 4
+#endif
+#ifndef GN_FIN_WAVES_B
+#define GN_FIN_WAVES_B 3
+#endif
+
+// The normalize of one element: ((x - hi) - lo) * gamma*rstd + beta, then the relu.
+struct Affine {
+    float hi, lo, scale, shift;
+    bool act;
+    __device__ __forceinline__ float operator()(float e) const
+    {
+        const float v = fmaf((e - hi) - lo, scale, shift);
+        return act ? relu_f(v) : v;
+    }
+};
+
+// y for vector vi of job jb: one vector load and store when the vector lies wholly inside
+// the job, element-wise at its edges.
+template <typename TX, typename TY>
+__device__ __forceinline__ void apply_vec(const TX* __restrict__ x, TY* __restrict__ y, const Job& jb,
+                                          int64_t vi, const Affine& f)
+{
+    if (vi >= jb.vf0 && vi < jb.vf1) {
+        float e[kVec], o[kVec];
+        Io<TX>::template load8<kNtApply>(x + vi * kVec, e);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) o[i] = f(e[i]);
+        Io<TY>::store8(y + vi * kVec, o);
+    } else {
+        for (int i = 0; i < kVec; ++i) {
+            const int64_t gi = vi * kVec + i;
+            if (gi >= jb.lo && gi < jb.hi) Io<TY>::store1(y + gi, f(Io<TX>::load1(x + gi)));
+        }
     }
 }
 
@@ -323,31 +407,84 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
         const int64_t j = kReverseApply ? a.jobs_a - 1 - jx : jx;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row];
-        const float hi = cf.x, lo = cf.y, scale = cf.z, shift = cf.w;
-        const bool act = a.act != 0;
+        const Affine f = {cf.x, cf.y, cf.z, cf.w, a.act != 0};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
-            for (int u = 0; u < kApplyVecs; ++u) {
-                const int64_t vi = sv0 + int64_t(u) * blk + tid;
-                if (vi >= jb.vf0 && vi < jb.vf1) {
-                    float e[kVec], o[kVec];
-                    Io<TX>::template load8<kNtApply>(x + vi * kVec, e);
+            for (int u = 0; u < kApplyVecs; ++u) apply_vec(x, y, jb, sv0 + int64_t(u) * blk + tid, f);
+        }
+    }
+}
+
+// y for the lane's V vectors of one full step, from raw loads.
+template <typename TX, typename TY, int V>
+__device__ __forceinline__ void apply_full_step(const typename Io<TX>::Raw (&r)[V], TY* __restrict__ y,
+                                                int64_t sv0, int blk, int tid, const Affine& f)
+{
 #pragma unroll
-                    for (int i = 0; i < kVec; ++i) {
-                        const float v = fmaf((e[i] - hi) - lo, scale, shift);
-                        o[i] = act ? relu_f(v) : v;
-                    }
-                    Io<TY>::store8(y + vi * kVec, o);
-                } else {
-                    for (int i = 0; i < kVec; ++i) {
-                        const int64_t gi = vi * kVec + i;
-                        if (gi >= jb.lo && gi < jb.hi) {
-                            const float v = fmaf((Io<TX>::load1(x + gi) - hi) - lo, scale, shift);
-                            Io<TY>::store1(y + gi, act ? relu_f(v) : v);
-                        }
-                    }
-                }
+    for (int u = 0; u < V; ++u) {
+        float e[kVec], o[kVec];
+        Io<TX>::widen(r[u], e);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) o[i] = f(e[i]);
+        Io<TY>::template store8<kNtStoreFold>(y + (sv0 + int64_t(u) * blk + tid) * kVec, o);
+    }
+}
+
+// The normalize with the forward finalize folded in ("Optimize GroupNorm", the paragraph
+// folding the finalize into the elementwise kernels with a capped grid), over the folded
+// streaming jobs: each 256-thread workgroup takes one job (a contiguous run of one row of
+// at most kFoldChunk elements), merges its group's P partials exactly as fin_fwd_kernel does (so the
+// statistics are bitwise those of the split-phase path), and streams the job. The
+// partials it re-reads are a few percent of the bytes it moves, and the separate
+// finalize launch is gone. The group's first job publishes mean, rstd and the rows'
+// coefficients. The job's first full step is requested before the merge so that its
+// latency overlaps it; the full steps are software-pipelined as in stats_kernel.
+template <typename TX, typename TY>
+__global__ void __launch_bounds__(256, GN_FIN_WAVES_F)
+apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
+                 float eps, const float2* __restrict__ part, float* __restrict__ mean_out,
+                 float* __restrict__ rstd_out, KArgs a, float4* __restrict__ coef, TY* __restrict__ y)
+{
+    using Raw = typename Io<TX>::Raw;
+    __shared__ FinFwdLds l;
+    const int tid = threadIdx.x, blk = blockDim.x;
+    constexpr int V = kFinVecs;
+    const int64_t stepv = int64_t(blk) * V;
+    for (int64_t j = blockIdx.x; j < a.jobs_f; j += gridDim.x) {
+        const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
+        const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg;
+        int64_t fs, fe, nsteps;
+        full_step_range(jb, stepv, fs, fe, nsteps);
+        Raw A[V], B[V];
+        if (fe > fs) load_raw_step<kNtApply>(x, jb.v0 + fs * stepv, blk, tid, A);
+        const GroupStat st = group_stat(x, part, a, eps, n, g, l);
+        if (jb.k == 0 && c == g * a.Cg) publish_group_stat(st, gamma, beta, a, n, g, mean_out, rstd_out, coef);
+        const Affine f = {st.hi, st.lo, (gamma ? gamma[c] : 1.0f) * st.rstd, beta ? beta[c] : 0.0f, a.act != 0};
+        // The edge steps stay rolled: unrolled, their element-wise loads would set the
+        // kernel's register count.
+        if (fs > 0) {
+#pragma unroll 1
+            for (int u = 0; u < V; ++u) apply_vec(x, y, jb, jb.v0 + int64_t(u) * blk + tid, f);
+        }
+        if (fe > fs) {
+            int64_t s = fs;
+            for (; s + 2 < fe; s += 2) {
+                load_raw_step<kNtApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                apply_full_step<TX, TY, V>(A, y, jb.v0 + s * stepv, blk, tid, f);
+                load_raw_step<kNtApply>(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
+                apply_full_step<TX, TY, V>(B, y, jb.v0 + (s + 1) * stepv, blk, tid, f);
             }
+            if (s + 1 < fe) {
+                load_raw_step<kNtApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                apply_full_step<TX, TY, V>(A, y, jb.v0 + s * stepv, blk, tid, f);
+                apply_full_step<TX, TY, V>(B, y, jb.v0 + (s + 1) * stepv, blk, tid, f);
+            } else {
+                apply_full_step<TX, TY, V>(A, y, jb.v0 + s * stepv, blk, tid, f);
+            }
+        }
+        if (fe < nsteps) {
+#pragma unroll 1
+            for (int u = 0; u < V; ++u) apply_vec(x, y, jb, jb.v0 + fe * stepv + int64_t(u) * blk + tid, f);
         }
     }
 }
@@ -451,13 +588,91 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
     }
 }
 
-// Workgroups [0, ngroups) each take one group (n, g): c1 = (1/M) sum gamma_c s1,
-// c2 = (1/M) sum gamma_c s2 over the group's P partials in a fixed order, then each row's
-// dx coefficients (mean, A = rstd*gamma_c, B = -rstd*c1, E = -rstd^2*c2) and beta_c, so that
-// dx = rstd*(gamma_c*g - c1 - xhat*c2) = A*g + (B + E*(x - mean)), where g is dy, or with the
-// relu dy gated on pre = (x - mean)*A + beta_c.
-// Workgroups [ngroups, ngroups + nchan) each take one channel c: dgamma_c and dbeta_c as
-// the sums of the channel's N*K partials, n-major then k, in a fixed order.
+// c1 = (1/M) sum gamma_c s1 and c2 = (1/M) sum gamma_c s2 of group (n, g), called by every
+// thread of a 256-thread workgroup: the group's P partials in a fixed order (lane t takes
+// partials t, t + 256, ... in index order, then the shuffle tree, then the waves in order).
+// Every thread receives the result.
+__device__ __forceinline__ float2 group_c12(const float2* __restrict__ part, const float* __restrict__ gamma,
+                                            const KArgs& a, int64_t n, int64_t g, float* s_a, float* s_b,
+                                            float* s_coef)
+{
+    const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
+    float t1 = 0.0f, t2 = 0.0f;
+    for (int64_t i = threadIdx.x; i < a.P; i += blockDim.x) {
+        const float2 pp = part[pbase + i];
+        const float gm = gamma ? gamma[g * a.Cg + i / a.K] : 1.0f;
+        t1 = t1 + gm * pp.x;
+        t2 = t2 + gm * pp.y;
+    }
+    const float2 r = block_sum2(t1, t2, s_a, s_b);
+    if (threadIdx.x == 0) {
+        s_coef[0] = float(double(r.x) / double(a.M));
+        s_coef[1] = float(double(r.y) / double(a.M));
+    }
+    __syncthreads();
+    // The next writer of s_coef is thread 0 after two barriers of the next sum.
+    return make_float2(s_coef[0], s_coef[1]);
+}
+
+// The dx coefficients of row (n, c): mean, A = rstd*gamma_c, B = -rstd*c1, E = -rstd^2*c2, so
+// that dx = rstd*(gamma_c*g - c1 - xhat*c2) = A*g + (B + E*(x - mean)), where g is dy, or with
+// the relu dy gated on pre = (x - mean)*A + beta_c.
+struct DxCoef {
+    float mu, A, B, E, bt;
+    bool act, single;
+    // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
+    __device__ __forceinline__ float operator()(float xv, float gv) const
+    {
+        const float d = xv - mu;
+        const float g = act ? relu_gate(fmaf(d, A, bt), gv) : gv;
+        float t = fmaf(A, g, fmaf(E, d, B));
+        if (single) t = t - t;
+        return t;
+    }
+};
+
+__device__ __forceinline__ DxCoef dx_coef(float mu, float rs, float gm, float2 c12, float bt, const KArgs& a)
+{
+    return DxCoef{mu, rs * gm, -(rs * c12.x), -((rs * rs) * c12.y), bt, a.act != 0, a.M == 1};
+}
+
+// Writes the dx coefficient records of group (n, g)'s rows for bwd_apply_kernel.
+__device__ __forceinline__ void publish_dx_coef(float mu, float rs, float2 c12, const float* __restrict__ gamma,
+                                                const float* __restrict__ beta, const KArgs& a, int64_t n,
+                                                int64_t g, float4* __restrict__ coef)
+{
+    for (int64_t i = threadIdx.x; i < a.Cg; i += blockDim.x) {
+        const int64_t c = g * a.Cg + i;
+        const DxCoef k = dx_coef(mu, rs, gamma ? gamma[c] : 1.0f, c12, 0.0f, a);
+        coef[2 * (n * a.C + c)] = make_float4(mu, k.A, k.B, k.E);
+        coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, 0.0f, 0.0f, 0.0f);
+    }
+}
+
+// dgamma_c and dbeta_c as the sums of channel c's N*K partials, n-major then k, in a fixed
+// order (lane t takes t, t + 256, ..., then the shuffle tree, then the waves in order);
+// called by every thread, written by thread 0.
+__device__ __forceinline__ void channel_param_sums(const float2* __restrict__ part, const KArgs& a, int64_t c,
+                                                   float* s_a, float* s_b, float* __restrict__ dgamma,
+                                                   float* __restrict__ dbeta)
+{
+    float sa = 0.0f, sb = 0.0f;
+    for (int64_t i = threadIdx.x; i < a.N * a.K; i += blockDim.x) {
+        const int64_t nn = i / a.K, kk = i - nn * a.K;
+        const float2 pp = part[(nn * a.C + c) * a.K + kk];
+        sa = sa + pp.y;
+        sb = sb + pp.x;
+    }
+    const float2 r = block_sum2(sa, sb, s_a, s_b);
+    if (threadIdx.x == 0) {
+        if (dgamma) dgamma[c] = r.x;
+        if (dbeta) dbeta[c] = r.y;
+    }
+}
+
+// Workgroups [0, ngroups) each take one group (n, g): c1 and c2, then each row's dx
+// coefficients and beta_c. Workgroups [ngroups, ngroups + nchan) each take one channel c:
+// dgamma_c and dbeta_c.
 __global__ void __launch_bounds__(256)
 fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
                const float* __restrict__ gamma, const float* __restrict__ beta,
@@ -467,46 +682,34 @@ fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
 {
     __shared__ float s_a[kMaxWaves], s_b[kMaxWaves];
     __shared__ float s_coef[2];
-    const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t w = blockIdx.x;
     if (w < ngroups) {
         const int64_t n = w / a.G, g = w - n * a.G;
-        const int64_t pbase = (n * a.C + g * a.Cg) * a.K;
         const float mu = mean[w], rs = rstd[w];  // requested before the merge
-        float t1 = 0.0f, t2 = 0.0f;
-        for (int64_t i = tid; i < a.P; i += blk) {
-            const float2 pp = part[pbase + i];
-            const float gm = gamma ? gamma[g * a.Cg + i / a.K] : 1.0f;
-            t1 = t1 + gm * pp.x;
-            t2 = t2 + gm * pp.y;
-        }
-        const float2 r = block_sum2(t1, t2, s_a, s_b);
-        if (tid == 0) {
-            s_coef[0] = float(double(r.x) / double(a.M));
-            s_coef[1] = float(double(r.y) / double(a.M));
-        }
-        __syncthreads();
-        const float B = -(rs * s_coef[0]);
-        const float E = -((rs * rs) * s_coef[1]);
-        for (int64_t i = tid; i < a.Cg; i += blk) {
-            const int64_t c = g * a.Cg + i;
-            const float gm = gamma ? gamma[c] : 1.0f;
-            coef[2 * (n * a.C + c)] = make_float4(mu, rs * gm, B, E);
-            coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, 0.0f, 0.0f, 0.0f);
-        }
+        const float2 c12 = group_c12(part, gamma, a, n, g, s_a, s_b, s_coef);
+        publish_dx_coef(mu, rs, c12, gamma, beta, a, n, g, coef);
     } else if (w < ngroups + nchan) {
-        const int64_t c = w - ngroups;
-        float sa = 0.0f, sb = 0.0f;
-        for (int64_t i = tid; i < a.N * a.K; i += blk) {
-            const int64_t nn = i / a.K, kk = i - nn * a.K;
-            const float2 pp = part[(nn * a.C + c) * a.K + kk];
-            sa = sa + pp.y;
-            sb = sb + pp.x;
-        }
-        const float2 r = block_sum2(sa, sb, s_a, s_b);
-        if (tid == 0) {
-            if (dgamma) dgamma[c] = r.x;
-            if (dbeta) dbeta[c] = r.y;
+        channel_param_sums(part, a, w - ngroups, s_a, s_b, dgamma, dbeta);
+    }
+}
+
+// dx for vector vi of job jb: vector loads and store when the vector lies wholly inside the
+// job, element-wise at its edges.
+template <typename TX, typename TD>
+__device__ __forceinline__ void dx_vec(const TD* __restrict__ dy, const TX* __restrict__ x, TX* __restrict__ dx,
+                                       const Job& jb, int64_t vi, const DxCoef& k)
+{
+    if (vi >= jb.vf0 && vi < jb.vf1) {
+        float xv[kVec], gv[kVec], o[kVec];
+        Io<TX>::template load8<kNtBwdApply>(x + vi * kVec, xv);
+        Io<TD>::template load8<kNtBwdApply>(dy + vi * kVec, gv);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) o[i] = k(xv[i], gv[i]);
+        Io<TX>::store8(dx + vi * kVec, o);
+    } else {
+        for (int i = 0; i < kVec; ++i) {
+            const int64_t gi = vi * kVec + i;
+            if (gi >= jb.lo && gi < jb.hi) Io<TX>::store1(dx + gi, k(Io<TX>::load1(x + gi), Io<TD>::load1(dy + gi)));
         }
     }
 }
@@ -518,47 +721,100 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
 {
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kApplyVecs;
-    // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
-    const bool single = (a.M == 1);
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
         const int64_t jx = xcd_job(jj, a.jobs_a, GN_XCD_REMAP);
         const int64_t j = kReverseApply ? a.jobs_a - 1 - jx : jx;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row];
-        const float mu = cf.x, A = cf.y, B = cf.z, E = cf.w;
         const bool act = a.act != 0;
-        const float bt = act ? coef[2 * jb.row + 1].x : 0.0f;
+        const DxCoef k = {cf.x, cf.y, cf.z, cf.w, act ? coef[2 * jb.row + 1].x : 0.0f, act, a.M == 1};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
-            for (int u = 0; u < kApplyVecs; ++u) {
-                const int64_t vi = sv0 + int64_t(u) * blk + tid;
-                if (vi >= jb.vf0 && vi < jb.vf1) {
-                    float xv[kVec], gv[kVec], o[kVec];
-                    Io<TX>::template load8<kNtBwdApply>(x + vi * kVec, xv);
-                    Io<TD>::template load8<kNtBwdApply>(dy + vi * kVec, gv);
+            for (int u = 0; u < kApplyVecs; ++u) dx_vec(dy, x, dx, jb, sv0 + int64_t(u) * blk + tid, k);
+        }
+    }
+}
+
+// dx for the lane's V vectors of one full step, from raw loads.
+template <typename TX, typename TD, int V>
+__device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V],
+                                             const typename Io<TD>::Raw (&rd)[V], TX* __restrict__ dx,
+                                             int64_t sv0, int blk, int tid, const DxCoef& k)
+{
 #pragma unroll
-                    for (int i = 0; i < kVec; ++i) {
-                        const float d = xv[i] - mu;
-                        const float g = act ? relu_gate(fmaf(d, A, bt), gv[i]) : gv[i];
-                        float t = fmaf(A, g, fmaf(E, d, B));
-                        if (single) t = t - t;
-                        o[i] = t;
-                    }
-                    Io<TX>::store8(dx + vi * kVec, o);
-                } else {
-                    for (int i = 0; i < kVec; ++i) {
-                        const int64_t gi = vi * kVec + i;
-                        if (gi >= jb.lo && gi < jb.hi) {
-                            const float d = Io<TX>::load1(x + gi) - mu;
-                            const float g0 = Io<TD>::load1(dy + gi);
-                            const float g = act ? relu_gate(fmaf(d, A, bt), g0) : g0;
-                            float t = fmaf(A, g, fmaf(E, d, B));
-                            if (single) t = t - t;
-                            Io<TX>::store1(dx + gi, t);
-                        }
-                    }
-                }
+    for (int u = 0; u < V; ++u) {
+        float xv[kVec], gv[kVec], o[kVec];
+        Io<TX>::widen(rx[u], xv);
+        Io<TD>::widen(rd[u], gv);
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) o[i] = k(xv[i], gv[i]);
+        Io<TX>::template store8<kNtStoreFold>(dx + (sv0 + int64_t(u) * blk + tid) * kVec, o);
+    }
+}
+
+// dx with the backward finalize folded in, over the folded streaming jobs, as apply_fin_kernel
+// does for the forward: each 256-thread workgroup takes one job, forms its group's c1, c2
+// exactly as fin_bwd_kernel does, and streams the job. The group's first job writes the
+// rows' coefficient records; the first job of channel c in sample 0 writes dgamma_c and
+// dbeta_c, summed exactly as fin_bwd_kernel sums them.
+template <typename TX, typename TD>
+__global__ void __launch_bounds__(256, GN_FIN_WAVES_B)
+bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
+                     const float* __restrict__ rstd, const float* __restrict__ gamma,
+                     const float* __restrict__ beta, const float2* __restrict__ part, KArgs a,
+                     float4* __restrict__ coef, float* __restrict__ dgamma, float* __restrict__ dbeta,
+                     TX* __restrict__ dx)
+{
+    using RawX = typename Io<TX>::Raw;
+    using RawD = typename Io<TD>::Raw;
+    __shared__ float s_a[kMaxWaves], s_b[kMaxWaves];
+    __shared__ float s_coef[2];
+    const int tid = threadIdx.x, blk = blockDim.x;
+    constexpr int V = kFinVecs;
+    const int64_t stepv = int64_t(blk) * V;
+    for (int64_t j = blockIdx.x; j < a.jobs_f; j += gridDim.x) {
+        const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
+        const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg, ng = n * a.G + g;
+        int64_t fs, fe, nsteps;
+        full_step_range(jb, stepv, fs, fe, nsteps);
+        RawX AX[V], BX[V];
+        RawD AD[V], BD[V];
+        if (fe > fs) {
+            load_raw_step<kNtBwdApply>(x, jb.v0 + fs * stepv, blk, tid, AX);
+            load_raw_step<kNtBwdApply>(dy, jb.v0 + fs * stepv, blk, tid, AD);
+        }
+        const float mu = mean[ng], rs = rstd[ng];
+        const float2 c12 = group_c12(part, gamma, a, n, g, s_a, s_b, s_coef);
+        if (jb.k == 0 && c == g * a.Cg) publish_dx_coef(mu, rs, c12, gamma, beta, a, n, g, coef);
+        if ((dgamma || dbeta) && jb.k == 0 && n == 0) channel_param_sums(part, a, c, s_a, s_b, dgamma, dbeta);
+        const bool act = a.act != 0;
+        const DxCoef k = dx_coef(mu, rs, gamma ? gamma[c] : 1.0f, c12, act ? (beta ? beta[c] : 0.0f) : 0.0f, a);
+        if (fs > 0) {  // rolled, as in apply_fin_kernel
+#pragma unroll 1
+            for (int u = 0; u < V; ++u) dx_vec(dy, x, dx, jb, jb.v0 + int64_t(u) * blk + tid, k);
+        }
+        if (fe > fs) {
+            int64_t s = fs;
+            for (; s + 2 < fe; s += 2) {
+                load_raw_step<kNtBwdApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<kNtBwdApply>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                dx_full_step<TX, TD, V>(AX, AD, dx, jb.v0 + s * stepv, blk, tid, k);
+                load_raw_step<kNtBwdApply>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
+                load_raw_step<kNtBwdApply>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
+                dx_full_step<TX, TD, V>(BX, BD, dx, jb.v0 + (s + 1) * stepv, blk, tid, k);
             }
+            if (s + 1 < fe) {
+                load_raw_step<kNtBwdApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<kNtBwdApply>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                dx_full_step<TX, TD, V>(AX, AD, dx, jb.v0 + s * stepv, blk, tid, k);
+                dx_full_step<TX, TD, V>(BX, BD, dx, jb.v0 + (s + 1) * stepv, blk, tid, k);
+            } else {
+                dx_full_step<TX, TD, V>(AX, AD, dx, jb.v0 + s * stepv, blk, tid, k);
+            }
+        }
+        if (fe < nsteps) {
+#pragma unroll 1
+            for (int u = 0; u < V; ++u) dx_vec(dy, x, dx, jb, jb.v0 + fe * stepv + int64_t(u) * blk + tid, k);
         }
     }
 }
@@ -863,6 +1119,25 @@ hipError_t launch_fwd_stats(const void* x, int xdt, const float* gamma, const fl
     });
 }
 
+hipError_t launch_fin_fwd(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                          float* mean, float* rstd, const KArgs& a, Workspace ws, hipStream_t st)
+{
+    return with_type(xdt, [&](auto tx) {
+        using TX = decltype(tx);
+        return launch(fin_fwd_kernel<TX>, dim3(unsigned(a.N * a.G)), dim3(256), st, cp<TX>(x), gamma, beta,
+                      eps, static_cast<const float2*>(ws.part), mean, rstd, a, ws.coef);
+    });
+}
+
+hipError_t launch_fin_bwd(const float* mean, const float* rstd, const float* gamma, const float* beta,
+                          float* dgamma, float* dbeta, const KArgs& a, Workspace ws, hipStream_t st)
+{
+    const int64_t ngroups = a.N * a.G;
+    const int64_t nchan = (dgamma || dbeta) ? a.C : 0;
+    return launch(fin_bwd_kernel, dim3(unsigned(ngroups + nchan)), dim3(256), st, mean, rstd, gamma, beta,
+                  static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coef, dgamma, dbeta);
+}
+
 hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArgs& a,
                             Workspace ws, hipStream_t st)
 {
@@ -907,6 +1182,36 @@ hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, vo
             using TD = decltype(td);
             return launch(bwd_apply_kernel<TX, TD>, grid, block, st, cp<TD>(dy), cp<TX>(x), a, coef,
                           mp<TX>(dx));
+        });
+    });
+}
+
+hipError_t launch_fwd_apply_fin(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                                float* mean, float* rstd, void* y, int ydt, const KArgs& a, Workspace ws,
+                                hipStream_t st)
+{
+    const float2* part = static_cast<const float2*>(ws.part);
+    return with_type(xdt, [&](auto tx) {
+        using TX = decltype(tx);
+        if (ydt == kF32)
+            return launch(apply_fin_kernel<TX, float>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma, beta,
+                          eps, part, mean, rstd, a, ws.coef, mp<float>(y));
+        return launch(apply_fin_kernel<TX, TX>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma, beta, eps,
+                      part, mean, rstd, a, ws.coef, mp<TX>(y));
+    });
+}
+
+hipError_t launch_bwd_apply_fin(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                                const float* rstd, const float* gamma, const float* beta, float* dgamma,
+                                float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st)
+{
+    const float2* part = static_cast<const float2*>(ws.part);
+    return with_type(xdt, [&](auto tx) {
+        return with_type(dydt, [&](auto td) {
+            using TX = decltype(tx);
+            using TD = decltype(td);
+            return launch(bwd_apply_fin_kernel<TX, TD>, grid_of(a.jobs_f), dim3(256), st, cp<TD>(dy), cp<TX>(x),
+                          mean, rstd, gamma, beta, part, a, ws.coef, dgamma, dbeta, mp<TX>(dx));
         });
     });
 }

@@ -33,6 +33,7 @@ struct KArgs {
     int64_t Cg, M;
     int64_t chunk, K, jobs, P;        // reduction jobs
     int64_t chunk_a, K_a, jobs_a;     // streaming jobs
+    int64_t chunk_f, K_f, jobs_f;     // streaming jobs with the finalize folded in
     int32_t block, block_a;
     int32_t act;                      // 0: none, 1: relu after the affine
     FastDiv div_W, div_vg, div_Cg;    // resident path: S/8, M/8 and C/G as divisors
@@ -46,6 +47,7 @@ inline KArgs kargs_of(const Plan& p, int act = 0)
     a.Cg = p.Cg; a.M = p.M;
     a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs; a.P = p.P;
     a.chunk_a = p.chunk_a; a.K_a = p.K_a; a.jobs_a = p.jobs_a;
+    a.chunk_f = p.chunk_f; a.K_f = p.K_f; a.jobs_f = p.jobs_f;
     a.block = p.block; a.block_a = p.block_a;
     a.div_W = fastdiv_of(p.S % kVec == 0 ? p.S / kVec : 0);
     a.div_vg = fastdiv_of(p.S % kVec == 0 ? p.M / kVec : 0);
@@ -82,6 +84,21 @@ hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, c
 // Backward, second half: dx from x, dy and the per-row coefficients.
 hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,
                             const KArgs& a, Workspace ws, hipStream_t st);
+
+// The finalize alone, after launch_stats_partials / launch_bwd_partials.
+hipError_t launch_fin_fwd(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                          float* mean, float* rstd, const KArgs& a, Workspace ws, hipStream_t st);
+hipError_t launch_fin_bwd(const float* mean, const float* rstd, const float* gamma, const float* beta,
+                          float* dgamma, float* dbeta, const KArgs& a, Workspace ws, hipStream_t st);
+// The finalize folded into the streaming pass (after launch_stats_partials /
+// launch_bwd_partials): the same statistics, coefficients and parameter gradients as the
+// split kernels, bitwise, with one launch fewer per direction.
+hipError_t launch_fwd_apply_fin(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                                float* mean, float* rstd, void* y, int ydt, const KArgs& a, Workspace ws,
+                                hipStream_t st);
+hipError_t launch_bwd_apply_fin(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                                const float* rstd, const float* gamma, const float* beta, float* dgamma,
+                                float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st);
 
 // Resident path, forward: statistics, the per-row coefficients, and y unless y is null.
 hipError_t launch_res_fwd(const void* x, int xdt, const float* gamma, const float* beta, float eps,

@@ -78,6 +78,11 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     q.K_a = ceil_div(S, q.chunk_a);
     q.jobs_a = q.rows * q.K_a;
 
+    // Folded streaming jobs: the reduction jobs, split further where they exceed kFoldChunk.
+    q.chunk_f = chunk <= kFoldChunk ? chunk : kFoldChunk;
+    q.K_f = ceil_div(S, q.chunk_f);
+    q.jobs_f = q.rows * q.K_f;
+
     // Resident path: rows of whole vectors (so every vector lies in one row and every row
     // starts on a vector) and a workgroup's share within kResMaxVecs.
     // The forward's grid is (G, N), so N stays within the y extent every device accepts.

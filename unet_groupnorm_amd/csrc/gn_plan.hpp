@@ -56,6 +56,15 @@ constexpr int kApplyVecs = GN_APPLY_VECS;
 constexpr int kResMaxBlock = 1024;
 constexpr int kResMaxLaneVecs = 4;
 constexpr int64_t kResMaxVecs = int64_t(kResMaxBlock) * kResMaxLaneVecs;  // 32768 elements
+// Elements per job of the streaming kernels that run the finalize themselves (gn_forward,
+// gn_backward with dx): each such workgroup first merges its group's partials, so its job
+// is long enough to amortize that and short enough that the grid stays large (measured on
+// MI355X, bf16, 128^3 and 256^3 with C=32 and the 32^3-64^3 UNet sites: 8192-12288 best;
+// 4096 about 20% slower, 32768 and more up to 9% slower at 256^3).
+#ifndef GN_FOLD_CHUNK
+#define GN_FOLD_CHUNK 8192
+#endif
+constexpr int64_t kFoldChunk = GN_FOLD_CHUNK;
 // Upper bound on a reduction job's element count (in-job counts stay within 32 bits).
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
 // Upper bound on N*C*S accepted (indices stay far from int64 overflow).
@@ -77,6 +86,10 @@ struct Plan {
     int64_t K_a = 0;
     int64_t jobs_a = 0;
     int block_a = 0;
+    // streaming jobs of the kernels with the finalize folded in (256 threads each)
+    int64_t chunk_f = 0;
+    int64_t K_f = 0;
+    int64_t jobs_f = 0;
     // resident path (one workgroup per group; every row a whole number of vectors):
     // forward per group (n, g), backward per g across all samples
     bool res_fwd = false, res_bwd = false;

@@ -246,6 +246,50 @@ def gn_backward_apply(dy, x, G, dx, workspace, activation=None):
         _ptr(workspace), workspace.numel(), _stream(x.device)))
 
 
+def gn_forward_partials(x, G, workspace):
+    """gn_forward's first launch: the partial statistics of x, left in the workspace."""
+    _contig("x", x)
+    N, C, S, G = _dims(x, G)
+    _check("gn_forward_partials", lib.gn_forward_partials(
+        _ptr(x), _dtype(x), N, C, S, G, _ptr(workspace), workspace.numel(), _stream(x.device)))
+
+
+def gn_forward_finish(x, gamma, beta, G, eps, y, mean, rstd, workspace, activation=None):
+    """gn_forward's second launch: the finalize, then y (after gn_forward_partials)."""
+    _contig("x", x)
+    N, C, S, G = _dims(x, G)
+    dev = x.device
+    _check("gn_forward_finish", lib.gn_forward_finish(
+        _ptr(x), _dtype(x), _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
+        N, C, S, G, float(eps), _act(activation), _ptr(_contig("y", y)), _dtype(y), _ptr(mean),
+        _ptr(rstd), _ptr(workspace), workspace.numel(), _stream(dev)))
+
+
+def gn_backward_partials(dy, x, mean, rstd, gamma, G, workspace, beta=None, activation=None):
+    """gn_backward's first launch: the per-job sums, left in the workspace."""
+    _contig("x", x); _contig("dy", dy)
+    N, C, S, G = _dims(x, G)
+    dev = x.device
+    _check("gn_backward_partials", lib.gn_backward_partials(
+        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
+        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
+        N, C, S, G, _ptr(workspace), workspace.numel(), _stream(dev)))
+
+
+def gn_backward_finish(dy, x, mean, rstd, gamma, G, dx, dgamma, dbeta, workspace, beta=None,
+                       activation=None):
+    """gn_backward's second launch: dx, dgamma, dbeta (each may be None) after
+    gn_backward_partials."""
+    _contig("x", x); _contig("dy", dy)
+    N, C, S, G = _dims(x, G)
+    dev = x.device
+    _check("gn_backward_finish", lib.gn_backward_finish(
+        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
+        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
+        N, C, S, G, _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(workspace), workspace.numel(),
+        _stream(dev)))
+
+
 # ----------------------------------------------------------------------------- spatial shards
 #
 # A rank holding a spatial shard of the volume (contiguous NCDHW, the same N, C, G on every
