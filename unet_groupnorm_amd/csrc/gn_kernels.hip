@@ -209,12 +209,12 @@ __device__ __forceinline__ void stats_full_step(const typename Io<TX>::Raw (&r)[
     chan_merge(acc, uint32_t(kTile), m, M2);
 }
 
-template <typename TX>
+template <bool NT, typename TX>
 __device__ __forceinline__ void stats_masked_step(const TX* __restrict__ x, const Job& jb, int64_t sv0,
                                                   int blk, int tid, float K, Moments<uint32_t>& acc)
 {
     float v[kTile];
-    const uint32_t valid = load_step_masked<kNtStats>(x, jb, sv0, blk, tid, v);
+    const uint32_t valid = load_step_masked<NT>(x, jb, sv0, blk, tid, v);
     if (valid) {
         const uint32_t cnt = __builtin_popcount(valid);
         float m, M2;
@@ -226,7 +226,7 @@ __device__ __forceinline__ void stats_masked_step(const TX* __restrict__ x, cons
 // The full steps are software-pipelined: the next step's vectors are requested before
 // the current step is reduced, alternating between two register sets so that waiting for
 // one set leaves the other in flight.
-template <typename TX>
+template <typename TX, bool NT>
 __global__ void __launch_bounds__(kRedBlock)
 stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
 {
@@ -247,26 +247,26 @@ stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
         // At most one partial step before and one after the full steps. They are written as
         // conditionals: a one-trip loop over them was merged twice when built by hipcc
         // (ROCm 7.2) for gfx950.
-        if (fs > 0) stats_masked_step(x, jb, jb.v0, blk, tid, K, acc);
+        if (fs > 0) stats_masked_step<NT>(x, jb, jb.v0, blk, tid, K, acc);
         if (fe > fs) {
             Raw A[kStepVecs], B[kStepVecs];
-            load_raw_step<kNtStats>(x, jb.v0 + fs * stepv, blk, tid, A);
+            load_raw_step<NT>(x, jb.v0 + fs * stepv, blk, tid, A);
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step<kNtStats>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
                 stats_full_step<TX>(A, K, acc);
-                load_raw_step<kNtStats>(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
+                load_raw_step<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
                 stats_full_step<TX>(B, K, acc);
             }
             if (s + 1 < fe) {
-                load_raw_step<kNtStats>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
                 stats_full_step<TX>(A, K, acc);
                 stats_full_step<TX>(B, K, acc);
             } else {
                 stats_full_step<TX>(A, K, acc);
             }
         }
-        if (fe < nsteps) stats_masked_step(x, jb, jb.v0 + fe * stepv, blk, tid, K, acc);
+        if (fe < nsteps) stats_masked_step<NT>(x, jb, jb.v0 + fe * stepv, blk, tid, K, acc);
         const Moments<uint32_t> r = block_merge(acc, s_n, s_m, s_M);
         if (tid == 0) part[j] = make_float2(r.m, r.M2);
     }
@@ -377,13 +377,13 @@ struct Affine {
 
 // y for vector vi of job jb: one vector load and store when the vector lies wholly inside
 // the job, element-wise at its edges.
-template <typename TX, typename TY>
+template <bool NT, typename TX, typename TY>
 __device__ __forceinline__ void apply_vec(const TX* __restrict__ x, TY* __restrict__ y, const Job& jb,
                                           int64_t vi, const Affine& f)
 {
     if (vi >= jb.vf0 && vi < jb.vf1) {
         float e[kVec], o[kVec];
-        Io<TX>::template load8<kNtApply>(x + vi * kVec, e);
+        Io<TX>::template load8<NT>(x + vi * kVec, e);
 #pragma unroll
         for (int i = 0; i < kVec; ++i) o[i] = f(e[i]);
         Io<TY>::store8(y + vi * kVec, o);
@@ -410,7 +410,7 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
         const Affine f = {cf.x, cf.y, cf.z, cf.w, a.act != 0};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
-            for (int u = 0; u < kApplyVecs; ++u) apply_vec(x, y, jb, sv0 + int64_t(u) * blk + tid, f);
+            for (int u = 0; u < kApplyVecs; ++u) apply_vec<kNtApply>(x, y, jb, sv0 + int64_t(u) * blk + tid, f);
         }
     }
 }
@@ -439,7 +439,7 @@ __device__ __forceinline__ void apply_full_step(const typename Io<TX>::Raw (&r)[
 // finalize launch is gone. The group's first job publishes mean, rstd and the rows'
 // coefficients. The job's first full step is requested before the merge so that its
 // latency overlaps it; the full steps are software-pipelined as in stats_kernel.
-template <typename TX, typename TY>
+template <typename TX, typename TY, bool NT>
 __global__ void __launch_bounds__(256, GN_FIN_WAVES_F)
 apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
                  float eps, const float2* __restrict__ part, float* __restrict__ mean_out,
@@ -450,13 +450,14 @@ apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, cons
     const int tid = threadIdx.x, blk = blockDim.x;
     constexpr int V = kFinVecs;
     const int64_t stepv = int64_t(blk) * V;
-    for (int64_t j = blockIdx.x; j < a.jobs_f; j += gridDim.x) {
+    for (int64_t jj = blockIdx.x; jj < a.jobs_f; jj += gridDim.x) {
+        const int64_t j = kReverseApply ? a.jobs_f - 1 - jj : jj;
         const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg;
         int64_t fs, fe, nsteps;
         full_step_range(jb, stepv, fs, fe, nsteps);
         Raw A[V], B[V];
-        if (fe > fs) load_raw_step<kNtApply>(x, jb.v0 + fs * stepv, blk, tid, A);
+        if (fe > fs) load_raw_step<NT>(x, jb.v0 + fs * stepv, blk, tid, A);
         const GroupStat st = group_stat(x, part, a, eps, n, g, l);
         if (jb.k == 0 && c == g * a.Cg) publish_group_stat(st, gamma, beta, a, n, g, mean_out, rstd_out, coef);
         const Affine f = {st.hi, st.lo, (gamma ? gamma[c] : 1.0f) * st.rstd, beta ? beta[c] : 0.0f, a.act != 0};
@@ -464,18 +465,18 @@ apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, cons
         // kernel's register count.
         if (fs > 0) {
 #pragma unroll 1
-            for (int u = 0; u < V; ++u) apply_vec(x, y, jb, jb.v0 + int64_t(u) * blk + tid, f);
+            for (int u = 0; u < V; ++u) apply_vec<NT>(x, y, jb, jb.v0 + int64_t(u) * blk + tid, f);
         }
         if (fe > fs) {
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step<kNtApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
                 apply_full_step<TX, TY, V>(A, y, jb.v0 + s * stepv, blk, tid, f);
-                load_raw_step<kNtApply>(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
+                load_raw_step<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, A);
                 apply_full_step<TX, TY, V>(B, y, jb.v0 + (s + 1) * stepv, blk, tid, f);
             }
             if (s + 1 < fe) {
-                load_raw_step<kNtApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, B);
                 apply_full_step<TX, TY, V>(A, y, jb.v0 + s * stepv, blk, tid, f);
                 apply_full_step<TX, TY, V>(B, y, jb.v0 + (s + 1) * stepv, blk, tid, f);
             } else {
@@ -484,7 +485,7 @@ apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, cons
         }
         if (fe < nsteps) {
 #pragma unroll 1
-            for (int u = 0; u < V; ++u) apply_vec(x, y, jb, jb.v0 + fe * stepv + int64_t(u) * blk + tid, f);
+            for (int u = 0; u < V; ++u) apply_vec<NT>(x, y, jb, jb.v0 + fe * stepv + int64_t(u) * blk + tid, f);
         }
     }
 }
@@ -514,14 +515,14 @@ __device__ __forceinline__ void bwd_full_step(const typename Io<TX>::Raw (&rx)[k
     s2 = s2 + tree_sumprod(gv, d);
 }
 
-template <typename TX, typename TD>
+template <bool NT, typename TX, typename TD>
 __device__ __forceinline__ void bwd_masked_step(const TD* __restrict__ dy, const TX* __restrict__ x,
                                                 const Job& jb, int64_t sv0, int blk, int tid, float mu,
                                                 bool act, float scale, float shift, float& s1, float& s2)
 {
     float xv[kTile], gv[kTile];
-    const uint32_t valid = load_step_masked<kNtBwdReduce>(x, jb, sv0, blk, tid, xv);
-    load_step_masked<kNtBwdReduce>(dy, jb, sv0, blk, tid, gv);  // same mask: zeros outside
+    const uint32_t valid = load_step_masked<NT>(x, jb, sv0, blk, tid, xv);
+    load_step_masked<NT>(dy, jb, sv0, blk, tid, gv);  // same mask: zeros outside
 #pragma unroll
     for (int i = 0; i < kTile; ++i) {
         xv[i] = ((valid >> i) & 1u) ? xv[i] - mu : 0.0f;
@@ -534,7 +535,7 @@ __device__ __forceinline__ void bwd_masked_step(const TD* __restrict__ dy, const
 // Per job: s1 = sum dy and s2 = rstd * sum dy * (x - mean) over the job's elements, lanes
 // summing their tiles in step order, then the shuffle tree, then the waves in order. The
 // full steps are software-pipelined as in stats_kernel.
-template <typename TX, typename TD>
+template <typename TX, typename TD, bool NT>
 __global__ void __launch_bounds__(kRedBlock)
 bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
                   const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -558,31 +559,31 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
         float s1 = 0.0f, s2 = 0.0f;  // sum dy, sum dy * (x - mu)
         int64_t fs, fe, nsteps;
         full_step_range(jb, stepv, fs, fe, nsteps);
-        if (fs > 0) bwd_masked_step(dy, x, jb, jb.v0, blk, tid, mu, act, scale, shift, s1, s2);
+        if (fs > 0) bwd_masked_step<NT>(dy, x, jb, jb.v0, blk, tid, mu, act, scale, shift, s1, s2);
         if (fe > fs) {
             RawX AX[kStepVecs], BX[kStepVecs];
             RawD AD[kStepVecs], BD[kStepVecs];
-            load_raw_step<kNtBwdReduce>(x, jb.v0 + fs * stepv, blk, tid, AX);
-            load_raw_step<kNtBwdReduce>(dy, jb.v0 + fs * stepv, blk, tid, AD);
+            load_raw_step<NT>(x, jb.v0 + fs * stepv, blk, tid, AX);
+            load_raw_step<NT>(dy, jb.v0 + fs * stepv, blk, tid, AD);
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
-                load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
-                load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
+                load_raw_step<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
+                load_raw_step<NT>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
                 bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
             }
             if (s + 1 < fe) {
-                load_raw_step<kNtBwdReduce>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step<kNtBwdReduce>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
                 bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
             } else {
                 bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
             }
         }
-        if (fe < nsteps) bwd_masked_step(dy, x, jb, jb.v0 + fe * stepv, blk, tid, mu, act, scale, shift, s1, s2);
+        if (fe < nsteps) bwd_masked_step<NT>(dy, x, jb, jb.v0 + fe * stepv, blk, tid, mu, act, scale, shift, s1, s2);
         const float2 r = block_sum2(s1, s2, s_a, s_b);
         if (tid == 0) part[j] = make_float2(r.x, r.y * rstd[ng]);
     }
@@ -695,14 +696,14 @@ fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
 
 // dx for vector vi of job jb: vector loads and store when the vector lies wholly inside the
 // job, element-wise at its edges.
-template <typename TX, typename TD>
+template <bool NT, typename TX, typename TD>
 __device__ __forceinline__ void dx_vec(const TD* __restrict__ dy, const TX* __restrict__ x, TX* __restrict__ dx,
                                        const Job& jb, int64_t vi, const DxCoef& k)
 {
     if (vi >= jb.vf0 && vi < jb.vf1) {
         float xv[kVec], gv[kVec], o[kVec];
-        Io<TX>::template load8<kNtBwdApply>(x + vi * kVec, xv);
-        Io<TD>::template load8<kNtBwdApply>(dy + vi * kVec, gv);
+        Io<TX>::template load8<NT>(x + vi * kVec, xv);
+        Io<TD>::template load8<NT>(dy + vi * kVec, gv);
 #pragma unroll
         for (int i = 0; i < kVec; ++i) o[i] = k(xv[i], gv[i]);
         Io<TX>::store8(dx + vi * kVec, o);
@@ -730,7 +731,7 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
         const DxCoef k = {cf.x, cf.y, cf.z, cf.w, act ? coef[2 * jb.row + 1].x : 0.0f, act, a.M == 1};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
-            for (int u = 0; u < kApplyVecs; ++u) dx_vec(dy, x, dx, jb, sv0 + int64_t(u) * blk + tid, k);
+            for (int u = 0; u < kApplyVecs; ++u) dx_vec<kNtBwdApply>(dy, x, dx, jb, sv0 + int64_t(u) * blk + tid, k);
         }
     }
 }
@@ -757,7 +758,7 @@ __device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V]
 // exactly as fin_bwd_kernel does, and streams the job. The group's first job writes the
 // rows' coefficient records; the first job of channel c in sample 0 writes dgamma_c and
 // dbeta_c, summed exactly as fin_bwd_kernel sums them.
-template <typename TX, typename TD>
+template <typename TX, typename TD, bool NT>
 __global__ void __launch_bounds__(256, GN_FIN_WAVES_B)
 bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                      const float* __restrict__ rstd, const float* __restrict__ gamma,
@@ -772,7 +773,8 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
     const int tid = threadIdx.x, blk = blockDim.x;
     constexpr int V = kFinVecs;
     const int64_t stepv = int64_t(blk) * V;
-    for (int64_t j = blockIdx.x; j < a.jobs_f; j += gridDim.x) {
+    for (int64_t jj = blockIdx.x; jj < a.jobs_f; jj += gridDim.x) {
+        const int64_t j = kReverseApply ? a.jobs_f - 1 - jj : jj;
         const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg, ng = n * a.G + g;
         int64_t fs, fe, nsteps;
@@ -780,8 +782,8 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
         RawX AX[V], BX[V];
         RawD AD[V], BD[V];
         if (fe > fs) {
-            load_raw_step<kNtBwdApply>(x, jb.v0 + fs * stepv, blk, tid, AX);
-            load_raw_step<kNtBwdApply>(dy, jb.v0 + fs * stepv, blk, tid, AD);
+            load_raw_step<NT>(x, jb.v0 + fs * stepv, blk, tid, AX);
+            load_raw_step<NT>(dy, jb.v0 + fs * stepv, blk, tid, AD);
         }
         const float mu = mean[ng], rs = rstd[ng];
         const float2 c12 = group_c12(part, gamma, a, n, g, s_a, s_b, s_coef);
@@ -791,21 +793,21 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
         const DxCoef k = dx_coef(mu, rs, gamma ? gamma[c] : 1.0f, c12, act ? (beta ? beta[c] : 0.0f) : 0.0f, a);
         if (fs > 0) {  // rolled, as in apply_fin_kernel
 #pragma unroll 1
-            for (int u = 0; u < V; ++u) dx_vec(dy, x, dx, jb, jb.v0 + int64_t(u) * blk + tid, k);
+            for (int u = 0; u < V; ++u) dx_vec<NT>(dy, x, dx, jb, jb.v0 + int64_t(u) * blk + tid, k);
         }
         if (fe > fs) {
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step<kNtBwdApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step<kNtBwdApply>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 dx_full_step<TX, TD, V>(AX, AD, dx, jb.v0 + s * stepv, blk, tid, k);
-                load_raw_step<kNtBwdApply>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
-                load_raw_step<kNtBwdApply>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
+                load_raw_step<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
+                load_raw_step<NT>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
                 dx_full_step<TX, TD, V>(BX, BD, dx, jb.v0 + (s + 1) * stepv, blk, tid, k);
             }
             if (s + 1 < fe) {
-                load_raw_step<kNtBwdApply>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step<kNtBwdApply>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 dx_full_step<TX, TD, V>(AX, AD, dx, jb.v0 + s * stepv, blk, tid, k);
                 dx_full_step<TX, TD, V>(BX, BD, dx, jb.v0 + (s + 1) * stepv, blk, tid, k);
             } else {
@@ -814,7 +816,7 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
         }
         if (fe < nsteps) {
 #pragma unroll 1
-            for (int u = 0; u < V; ++u) dx_vec(dy, x, dx, jb, jb.v0 + fe * stepv + int64_t(u) * blk + tid, k);
+            for (int u = 0; u < V; ++u) dx_vec<NT>(dy, x, dx, jb, jb.v0 + fe * stepv + int64_t(u) * blk + tid, k);
         }
     }
 }
@@ -1083,11 +1085,25 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
 
 // ------------------------------------------------------------------ launchers
 
+// Calls f with std::bool_constant<NT> for the streamed loads of a reduction or folded
+// streaming kernel: plain loads (false) when the launch was judged to fit the last-level
+// cache, so that the step's later kernels find x there, else the kernel's streaming policy
+// Stream. The policy moves no bit of any result.
+template <bool Stream, typename F>
+hipError_t with_policy(const KArgs& a, F&& f)
+{
+    if (a.cached) return f(std::bool_constant<false>{});
+    return f(std::bool_constant<Stream>{});
+}
+
 hipError_t launch_stats_partials(const void* x, int xdt, const KArgs& a, Workspace ws, hipStream_t st)
 {
     return with_type(xdt, [&](auto tx) {
-        using TX = decltype(tx);
-        return launch(stats_kernel<TX>, grid_of(a.jobs), dim3(unsigned(a.block)), st, cp<TX>(x), a, ws.part);
+        return with_policy<kNtStats>(a, [&](auto nt) {
+            using TX = decltype(tx);
+            return launch(stats_kernel<TX, decltype(nt)::value>, grid_of(a.jobs), dim3(unsigned(a.block)), st,
+                          cp<TX>(x), a, ws.part);
+        });
     });
 }
 
@@ -1097,10 +1113,13 @@ hipError_t launch_bwd_partials(const void* dy, int dydt, const void* x, int xdt,
 {
     return with_type(xdt, [&](auto tx) {
         return with_type(dydt, [&](auto td) {
-            using TX = decltype(tx);
-            using TD = decltype(td);
-            return launch(bwd_reduce_kernel<TX, TD>, grid_of(a.jobs), dim3(unsigned(a.block)), st, cp<TD>(dy),
-                          cp<TX>(x), mean, rstd, gamma, beta, a, ws.part);
+            return with_policy<kNtBwdReduce>(a, [&](auto nt) {
+                using TX = decltype(tx);
+                using TD = decltype(td);
+                return launch(bwd_reduce_kernel<TX, TD, decltype(nt)::value>, grid_of(a.jobs),
+                              dim3(unsigned(a.block)), st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a,
+                              ws.part);
+            });
         });
     });
 }
@@ -1109,14 +1128,9 @@ hipError_t launch_fwd_stats(const void* x, int xdt, const float* gamma, const fl
                             float eps, float* mean, float* rstd, const KArgs& a, Workspace ws,
                             hipStream_t st)
 {
-    return with_type(xdt, [&](auto tx) {
-        using TX = decltype(tx);
-        const hipError_t e = launch(stats_kernel<TX>, grid_of(a.jobs), dim3(unsigned(a.block)), st,
-                                    cp<TX>(x), a, ws.part);
-        if (e != hipSuccess) return e;
-        return launch(fin_fwd_kernel<TX>, dim3(unsigned(a.N * a.G)), dim3(256), st, cp<TX>(x), gamma, beta,
-                      eps, static_cast<const float2*>(ws.part), mean, rstd, a, ws.coef);
-    });
+    const hipError_t e = launch_stats_partials(x, xdt, a, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_fin_fwd(x, xdt, gamma, beta, eps, mean, rstd, a, ws, st);
 }
 
 hipError_t launch_fin_fwd(const void* x, int xdt, const float* gamma, const float* beta, float eps,
@@ -1155,20 +1169,9 @@ hipError_t launch_bwd_reduce(const void* dy, int dydt, const void* x, int xdt, c
                              const float* rstd, const float* gamma, const float* beta, float* dgamma,
                              float* dbeta, const KArgs& a, Workspace ws, hipStream_t st)
 {
-    return with_type(xdt, [&](auto tx) {
-        return with_type(dydt, [&](auto td) {
-            using TX = decltype(tx);
-            using TD = decltype(td);
-            const hipError_t e = launch(bwd_reduce_kernel<TX, TD>, grid_of(a.jobs), dim3(unsigned(a.block)),
-                                        st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part);
-            if (e != hipSuccess) return e;
-            const int64_t ngroups = a.N * a.G;
-            const int64_t nchan = (dgamma || dbeta) ? a.C : 0;
-            return launch(fin_bwd_kernel, dim3(unsigned(ngroups + nchan)), dim3(256), st, mean, rstd, gamma,
-                          beta, static_cast<const float2*>(ws.part), a, ngroups, nchan, ws.coef, dgamma,
-                          dbeta);
-        });
-    });
+    const hipError_t e = launch_bwd_partials(dy, dydt, x, xdt, mean, rstd, gamma, beta, a, ws, st);
+    if (e != hipSuccess) return e;
+    return launch_fin_bwd(mean, rstd, gamma, beta, dgamma, dbeta, a, ws, st);
 }
 
 hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, void* dx,
@@ -1192,12 +1195,15 @@ hipError_t launch_fwd_apply_fin(const void* x, int xdt, const float* gamma, cons
 {
     const float2* part = static_cast<const float2*>(ws.part);
     return with_type(xdt, [&](auto tx) {
-        using TX = decltype(tx);
-        if (ydt == kF32)
-            return launch(apply_fin_kernel<TX, float>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma, beta,
-                          eps, part, mean, rstd, a, ws.coef, mp<float>(y));
-        return launch(apply_fin_kernel<TX, TX>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma, beta, eps,
-                      part, mean, rstd, a, ws.coef, mp<TX>(y));
+        return with_policy<kNtApply>(a, [&](auto nt) {
+            using TX = decltype(tx);
+            constexpr bool NT = decltype(nt)::value;
+            if (ydt == kF32)
+                return launch(apply_fin_kernel<TX, float, NT>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma,
+                              beta, eps, part, mean, rstd, a, ws.coef, mp<float>(y));
+            return launch(apply_fin_kernel<TX, TX, NT>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma, beta,
+                          eps, part, mean, rstd, a, ws.coef, mp<TX>(y));
+        });
     });
 }
 
@@ -1208,10 +1214,13 @@ hipError_t launch_bwd_apply_fin(const void* dy, int dydt, const void* x, int xdt
     const float2* part = static_cast<const float2*>(ws.part);
     return with_type(xdt, [&](auto tx) {
         return with_type(dydt, [&](auto td) {
-            using TX = decltype(tx);
-            using TD = decltype(td);
-            return launch(bwd_apply_fin_kernel<TX, TD>, grid_of(a.jobs_f), dim3(256), st, cp<TD>(dy), cp<TX>(x),
-                          mean, rstd, gamma, beta, part, a, ws.coef, dgamma, dbeta, mp<TX>(dx));
+            return with_policy<kNtBwdApply>(a, [&](auto nt) {
+                using TX = decltype(tx);
+                using TD = decltype(td);
+                return launch(bwd_apply_fin_kernel<TX, TD, decltype(nt)::value>, grid_of(a.jobs_f), dim3(256), st,
+                              cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, part, a, ws.coef, dgamma, dbeta,
+                              mp<TX>(dx));
+            });
         });
     });
 }

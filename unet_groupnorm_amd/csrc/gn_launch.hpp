@@ -36,6 +36,7 @@ struct KArgs {
     int64_t chunk_f, K_f, jobs_f;     // streaming jobs with the finalize folded in
     int32_t block, block_a;
     int32_t act;                      // 0: none, 1: relu after the affine
+    int32_t cached;                   // host's choice: plain loads, the volume fits the LLC
     FastDiv div_W, div_vg, div_Cg;    // resident path: S/8, M/8 and C/G as divisors
 };
 
@@ -43,6 +44,7 @@ inline KArgs kargs_of(const Plan& p, int act = 0)
 {
     KArgs a;
     a.act = act;
+    a.cached = 0;
     a.N = p.N; a.C = p.C; a.S = p.S; a.G = p.G;
     a.Cg = p.Cg; a.M = p.M;
     a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs; a.P = p.P;
