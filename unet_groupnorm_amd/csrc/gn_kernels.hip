@@ -226,8 +226,19 @@ __device__ __forceinline__ void stats_masked_step(const TX* __restrict__ x, cons
 // The full steps are software-pipelined: the next step's vectors are requested before
 // the current step is reduced, alternating between two register sets so that waiting for
 // one set leaves the other in flight.
+// Waves per SIMD the statistics kernel is compiled for (0: the compiler's choice);
+// compile-time overridable for measurement builds.
+#ifndef GN_STATS_WAVES
+#define GN_STATS_WAVES 0
+#endif
+#if GN_STATS_WAVES > 0
+#define GN_STATS_BOUNDS __launch_bounds__(kRedBlock, GN_STATS_WAVES)
+#else
+#define GN_STATS_BOUNDS __launch_bounds__(kRedBlock)
+#endif
+
 template <typename TX, bool NT>
-__global__ void __launch_bounds__(kRedBlock)
+__global__ void GN_STATS_BOUNDS
 stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
 {
     using Raw = typename Io<TX>::Raw;

@@ -48,8 +48,8 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     const int64_t step = int64_t(block) * kStepVecs * kVec;  // elements per workgroup step
 
     // Chunking: a whole row per job, halved while the launch has fewer than kTargetJobs
-    // jobs and a chunk still holds at least one full step. Chunks other than the last
-    // of a row are whole steps.
+    // jobs and a chunk still holds at least one full step (then possibly one step back,
+    // below). Chunks other than the last of a row are whole steps.
     int64_t K = 1, chunk = S;
     while (chunk > kMaxChunk) {
         K *= 2;
@@ -62,6 +62,16 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
         if (k2 <= K) break;
         K = k2;
         chunk = c2;
+    }
+    // Half as many jobs when that makes them kLongChunk elements or longer and leaves at
+    // least kMinJobs of them.
+    if (K >= 2 && chunk < kLongChunk) {
+        const int64_t c2 = round_up(ceil_div(S, K / 2), step);
+        const int64_t k2 = ceil_div(S, c2);
+        if (c2 >= kLongChunk && q.rows * k2 >= kMinJobs) {
+            K = k2;
+            chunk = c2;
+        }
     }
     q.K = K;
     q.chunk = chunk;

@@ -32,7 +32,10 @@ constexpr int kVec = 8;
 #define GN_STEP_VECS 4
 #endif
 #ifndef GN_TARGET_JOBS
-#define GN_TARGET_JOBS 2048
+#define GN_TARGET_JOBS 512
+#endif
+#ifndef GN_LONG_CHUNK
+#define GN_LONG_CHUNK 262144
 #endif
 #ifndef GN_APPLY_VECS
 #define GN_APPLY_VECS 1
@@ -44,8 +47,15 @@ constexpr int kVec = 8;
 constexpr int kRedBlock = GN_RED_BLOCK;
 // Vectors each lane holds per step of a reduction job (register tile = kVec * kStepVecs).
 constexpr int kStepVecs = GN_STEP_VECS;
-// Reduction workgroups a launch aims for (2048: 8 per CU on the 256 CUs of an MI355X).
+// Reduction workgroups a launch aims for (512: 2 per CU on the 256 CUs of an MI355X), and
+// the job length (elements) for which it settles for half as many, but at least 256 (one
+// per CU). Measured on MI355X, bf16, fwd+bwd steps: against 2048 jobs, 512 is 1-2% faster
+// at 128^3-256^3 and 10% at 96^3 (C=32), and fewer, longer jobs also shorten the folded
+// kernels' partials merge; 256 jobs of 256K elements are another 1.5% at 128^3 (C=32), while
+// 256 jobs are 1-11% slower at 256^3, at 2x128^3 and at the 32^3 UNet site.
 constexpr int64_t kTargetJobs = GN_TARGET_JOBS;
+constexpr int64_t kLongChunk = GN_LONG_CHUNK;
+constexpr int64_t kMinJobs = 256;
 // Vectors each lane moves in a streaming job.
 constexpr int kApplyVecs = GN_APPLY_VECS;
 // Resident path: one workgroup holds a whole group in registers (at most kResMaxBlock
