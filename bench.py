@@ -165,6 +165,31 @@ class Runner:
             out[name] = sum(ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)) / reps
         return out  # ms
 
+    def graph_steps(self, per_graph=10, replays=20):
+        """Steps replayed from a captured HIP graph of `per_graph` steps: microseconds per
+        step without the host's per-call launch cost."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                self.step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (replays * per_graph)
+
     def flushed_steps(self, steps, flush_bytes=512 << 20):
         """Each step timed alone after overwriting a buffer twice the size of the 256 MiB
         last-level cache, so that no input starts the step in that cache."""
@@ -220,8 +245,10 @@ def census(steps=10, warmup=3):
             continue
         r.settle(0.25)
         sms, _ = r.timed_steps(max(steps, 20), warmup)
+        gms = r.graph_steps()
         per_shape[key] = {"us_per_step": round(sms * 1e3, 2),
-                          "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1)}
+                          "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1),
+                          "graph_us_per_step": round(gms * 1e3, 2)}
     return {"sites": len(runs), "elements": sum(r.case.numel for r in runs), "ms_per_pass": round(ms, 4),
             "value": round(total / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "pct_of_peak": round(100 * total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
@@ -229,16 +256,20 @@ def census(steps=10, warmup=3):
 
 
 def small_configs(steps=50, warmup=10):
-    """The launch-bound configurations, timed as fwd+bwd microseconds per step."""
+    """The launch-bound configurations, timed as fwd+bwd microseconds per step: eager (one
+    call per direction from Python) and replayed from a captured graph."""
     import workloads
     out = {}
     for case in (workloads.TINY, workloads.DEEP, workloads.DEEP_F32OUT):
         r = Runner(case)
         r.settle(0.25)
         sms, _ = r.timed_steps(steps, warmup)
+        gms = r.graph_steps()
         out[case.name] = {"us_per_step": round(sms * 1e3, 2),
                           "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1),
-                          "bytes_per_step": r.step_bytes}
+                          "bytes_per_step": r.step_bytes,
+                          "graph_us_per_step": round(gms * 1e3, 2),
+                          "graph_value": round(r.step_bytes / (gms * 1e-3) / 1e9, 1)}
         del r
     return out
 
