@@ -14,8 +14,8 @@
  *     rstd = 316, i.e. rstd = 1/sqrt(var + eps) with eps = 1e-5 inside the square
  *     root and the biased (divide by M) variance; its input gradient is exactly 0.
  *   - "Preserve GroupNorm dtype" (LBANN/ScaFFold pull 105), first paragraph: the
- *     normalized value is the full-precision answer, rounded once to the output
- *     dtype. Here "full precision" is fp64 and the rounding helpers below round
+ *     normalized value is the unrounded answer, rounded once to the output dtype.
+ *     Here that answer is computed in fp64 and the rounding helpers below round
  *     straight from fp64 (never through fp32).
  *   - Optional ReLU after the affine ("Optimize GroupNorm", paragraphs on the rung ladder
  *     with the fused ReLU and on the NaN-correct ReLU): relu(v) = 0 where v < 0, else v, so
