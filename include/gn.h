@@ -265,7 +265,8 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
  * semantics, ownership and errors as gn_forward / gn_backward, with the workspace of
  * gn_workspace_bytes_cl. Supported when C is a multiple of 8, C/8 divides 256 (C <= 2048)
  * and C/G divides 8 or is a multiple of 8 (every UNet shape); other shapes return
- * GN_ERR_LAYOUT before anything is enqueued. Three kernels per direction.
+ * GN_ERR_LAYOUT before anything is enqueued. Three kernels per direction, or one on the
+ * resident path that gn_plan_query_cl reports.
  */
 size_t gn_workspace_bytes_cl(int64_t N, int64_t C, int64_t S, int64_t G);
 
@@ -300,6 +301,12 @@ typedef struct gn_plan_info_cl {
     int32_t apply_rounds;
     int32_t groups_per_vector;    /* max(1, 8 / (C/G)) */
     size_t workspace_bytes;       /* == gn_workspace_bytes_cl */
+    /* Resident path (C/G a multiple of 8 with C/(8G) a power of two up to 8, and a small
+     * enough group): one workgroup per group (n, g) forward and per g over all N samples
+     * backward, holding its elements in registers; one kernel per direction. */
+    int32_t resident_forward, resident_backward;
+    int32_t resident_block_forward, resident_vectors_forward;
+    int32_t resident_block_backward, resident_vectors_backward;
 } gn_plan_info_cl;
 
 int gn_plan_query_cl(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info_cl* out);

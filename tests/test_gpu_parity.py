@@ -546,6 +546,40 @@ def test_channels_last_nan_and_inf_confined_to_their_group():
     full_check(inp, "nan_inf_cl", layout="ndhwc")
 
 
+CL_RES_CASES = [  # (case, relu, resident forward, resident backward)
+    (workloads.custom(1, 256, 32, (8, 8, 8), torch.bfloat16, dist="unet", seed=73), False, 1, 1),
+    (workloads.custom(1, 256, 32, (16, 16, 16), torch.bfloat16, dist="unet", seed=80), False, 0, 0),
+    (workloads.custom(1, 512, 32, (8, 8, 8), torch.bfloat16, dist="unet", seed=74), True, 1, 1),
+    (workloads.custom(4, 512, 32, (8, 8, 8), torch.bfloat16, dist="deep", seed=75), False, 1, 0),
+    (workloads.custom(2, 64, 8, (4, 4, 4), torch.float16, torch.float32, dist="normal", seed=76,
+                      out_dtype=torch.float32), True, 1, 1),
+    (workloads.custom(3, 128, 8, (2, 5, 1), torch.float32, dist="tiny", seed=77), False, 1, 0),
+    (workloads.custom(2, 64, 1, (4, 4, 4), torch.bfloat16, dist="unet", seed=78), True, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case,relu,rf,rb", CL_RES_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_channels_last_resident_elementwise(case, relu, rf, rb):
+    """Groups of whole vectors small enough for one workgroup take the channels-last resident
+    kernels (one launch a direction); every output element against the oracle."""
+    p = gn.gn_plan_query_cl(case.N, case.C, case.S, case.G)
+    assert (p["resident_forward"], p["resident_backward"]) == (rf, rb)
+    full_check(workloads.make(case, "cpu"), case.name + "_cl_res", relu=relu, layout="ndhwc")
+
+
+def test_channels_last_resident_nan_and_inf_confined_to_their_group():
+    case = workloads.custom(2, 256, 32, (4, 4, 4), torch.bfloat16, seed=79)
+    p = gn.gn_plan_query_cl(case.N, case.C, case.S, case.G)
+    assert p["resident_forward"] == 1 and p["resident_backward"] == 1
+    say("channels-last resident: NaN/Inf in two groups of (2, 256, 4, 4, 4), G=32")
+    inp = workloads.make(case, "cpu")
+    x = inp["x"].clone()
+    x[0, 17, 1, 1, 1] = float("nan")
+    x[1, 250, 0, 2, 3] = float("inf")
+    inp["x"] = x
+    full_check(inp, "nan_inf_cl_res", layout="ndhwc")
+
+
 @pytest.mark.parametrize("case", [workloads.SCALE7], ids=lambda c: c.name)
 def test_channels_last_top_site_sampled(case):
     sampled_check(workloads.make(case, DEV), case.name + "_cl", n_random=1 << 18, seed=case.seed, layout="ndhwc")

@@ -377,3 +377,75 @@ def test_channels_last_slots_and_holders(N, C, S, G):
         assert (lo * VEC // Cg) + slot == grp
     # workspace areas: partials (jobs x C float2), per-channel float2, per-group float4
     assert p["workspace_bytes"] >= p["jobs"] * (C + G) * 8 + N * C * 8 + N * G * 16
+
+
+CL_RES_SHAPES = [
+    (1, 256, 16 ** 3, 32), (1, 512, 8 ** 3, 32), (4, 512, 8 ** 3, 32), (2, 64, 4 ** 3, 8),
+    (1, 256, 64, 4), (3, 128, 10, 8), (1, 32, 2 ** 15, 4), (8, 64, 64, 1), (1, 2048, 64, 16),
+    (1, 1024, 64, 8), (2, 16, 1000, 4), (1, 64, 4097, 8), (70, 64, 64, 8), (1, 8, 1000, 1),
+]
+
+
+def _cl_res_expect(N, C, S, G):
+    Cg = C // G
+    cvg = Cg // 8
+    ok = Cg % 8 == 0 and 1 <= cvg <= 8 and (cvg & (cvg - 1)) == 0
+    vg = S * cvg
+    fwd = ok and vg <= 1024 and N <= 65535
+    bwd = ok and vg % 64 == 0 and N * vg <= 1024 and N * Cg <= 512
+    return fwd, bwd
+
+
+@pytest.mark.parametrize("N,C,S,G", CL_RES_SHAPES)
+def test_channels_last_resident_choice_and_indexing(N, C, S, G):
+    """cl_res_fwd_kernel / cl_res_bwd_kernel restated: the resident choice, every vector of
+    every group covered once and inside the volume, each lane's channel vector fixed,
+    backward waves wholly inside one sample, and every LDS index inside its array."""
+    p = g.gn_plan_query_cl(N, C, S, G)
+    fwd, bwd = _cl_res_expect(N, C, S, G)
+    assert (p["resident_forward"], p["resident_backward"]) == (int(fwd), int(bwd))
+    Cg = C // G
+    cvg = max(Cg // 8, 1)
+    l = cvg.bit_length() - 1
+    vg = S * cvg
+    total = N * S * C
+    if fwd:
+        blk, V = p["resident_block_forward"], p["resident_vectors_forward"]
+        assert blk % 64 == 0 and blk <= 1024 and blk % cvg == 0 and V in (1, 2, 4) and blk * V >= vg
+        seen = np.zeros(total, dtype=np.int32)
+        t = np.arange(blk)
+        for n in range(N):
+            for gg in range(G):
+                for u in range(V):
+                    w = u * blk + t
+                    w = w[w < vg]
+                    s, k = w >> l, w & (cvg - 1)
+                    assert (k == (w % blk) % cvg).all()
+                    off = (n * S + s) * C + gg * Cg + 8 * k
+                    assert (off + 8 <= total).all()
+                    for e in range(8):
+                        np.add.at(seen, off + e, 1)
+        assert (seen == 1).all()
+    if bwd:
+        blk, V = p["resident_block_backward"], p["resident_vectors_backward"]
+        nvt = N * vg
+        nw = blk // 64
+        assert blk % 64 == 0 and blk <= 1024 and V in (1, 2, 4) and blk * V >= nvt
+        assert nw <= 16 and cvg <= 8 and N * Cg <= 512 and N <= 64
+        seen = np.zeros(total, dtype=np.int32)
+        for gg in range(G):
+            for u in range(V):
+                for wave in range(nw):
+                    wb = u * blk + wave * 64
+                    if wb >= nvt:
+                        continue
+                    assert wb + 64 <= nvt and (wb + 63) // vg == wb // vg
+                    nn = wb // vg
+                    w = wb + np.arange(64) - nn * vg
+                    s, k = w >> l, w & (cvg - 1)
+                    assert (k == np.arange(wave * 64, wave * 64 + 64) % cvg).all()
+                    off = (nn * S + s) * C + gg * Cg + 8 * k
+                    assert (off + 8 <= total).all()
+                    for e in range(8):
+                        np.add.at(seen, off + e, 1)
+        assert (seen == 1).all()

@@ -61,6 +61,12 @@ class GnPlanInfoCL(ctypes.Structure):
         ("apply_rounds", ctypes.c_int32),
         ("groups_per_vector", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_size_t),
+        ("resident_forward", ctypes.c_int32),
+        ("resident_backward", ctypes.c_int32),
+        ("resident_block_forward", ctypes.c_int32),
+        ("resident_vectors_forward", ctypes.c_int32),
+        ("resident_block_backward", ctypes.c_int32),
+        ("resident_vectors_backward", ctypes.c_int32),
     ]
 
 

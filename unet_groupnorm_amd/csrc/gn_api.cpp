@@ -220,7 +220,7 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 8; }
+int gn_abi_version(void) { return 9; }
 
 const char* gn_status_string(int status)
 {
@@ -561,6 +561,12 @@ int gn_plan_query_cl(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info_cl
     out->apply_rounds = gn::kClApplyRounds;
     out->groups_per_vector = p.ngl;
     out->workspace_bytes = p.ws_bytes;
+    out->resident_forward = p.res_fwd ? 1 : 0;
+    out->resident_backward = p.res_bwd ? 1 : 0;
+    out->resident_block_forward = p.res_block_f;
+    out->resident_vectors_forward = p.res_vecs_f;
+    out->resident_block_backward = p.res_block_b;
+    out->resident_vectors_backward = p.res_vecs_b;
     return GN_OK;
 }
 
@@ -580,6 +586,11 @@ int gn_forward_cl(const void* x, int x_dtype, const float* gamma, const float* b
     if (workspace_bytes < p.ws_bytes) return GN_ERR_WORKSPACE;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if (p.res_fwd)
+        return launch_status(gn::launch_cl_res_forward(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype,
+                                                       gn::clargs_of(p, activation),
+                                                       static_cast<hipStream_t>(stream), p.res_block_f,
+                                                       p.res_vecs_f));
     return launch_status(gn::launch_cl_forward(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype,
                                                gn::clargs_of(p, activation), gn::workspace_cl_of(workspace, p),
                                                static_cast<hipStream_t>(stream)));
@@ -601,6 +612,11 @@ int gn_backward_cl(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if (workspace_bytes < p.ws_bytes) return GN_ERR_WORKSPACE;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if (p.res_bwd)
+        return launch_status(gn::launch_cl_res_backward(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx,
+                                                        dgamma, dbeta, gn::clargs_of(p, activation),
+                                                        static_cast<hipStream_t>(stream), p.res_block_b,
+                                                        p.res_vecs_b));
     return launch_status(gn::launch_cl_backward(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx, dgamma,
                                                 dbeta, gn::clargs_of(p, activation),
                                                 gn::workspace_cl_of(workspace, p),

@@ -360,6 +360,39 @@ __device__ __forceinline__ float2 block_sum2(float a, float b, float* s_a, float
     return r;
 }
 
+// ------------------------------------------------------------------ resident workgroups
+
+constexpr int kResMaxWaves = kResMaxBlock / 64;
+
+// floor(x / d) for x < 2^16 with the launch's precomputed multiplier for d.
+__device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f)
+{
+    return uint32_t((uint64_t(x) * f.m) >> 32);
+}
+
+// Butterfly sum over the wave; every lane returns the same value (a + b == b + a).
+__device__ __forceinline__ float wave_allsum(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off);
+    return v;
+}
+
+// Block-wide sums of a and b; waves are added in wave order and every thread returns
+// the result. s holds 2 * kResMaxWaves floats and may be reused on return.
+__device__ __forceinline__ float2 block_allsum2(float a, float b, float* s)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    a = wave_allsum(a);
+    b = wave_allsum(b);
+    if (lane == 0) { s[wave] = a; s[kResMaxWaves + wave] = b; }
+    __syncthreads();
+    float ra = s[0], rb = s[kResMaxWaves];
+    for (int w = 1; w < nw; ++w) { ra = ra + s[w]; rb = rb + s[kResMaxWaves + w]; }
+    __syncthreads();
+    return make_float2(ra, rb);
+}
+
 // Launches kernel k and returns the runtime's status for this launch alone.
 template <typename... P, typename... A>
 hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t st, A... args)

@@ -645,6 +645,213 @@ cl_bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, ClArgs 
     }
 }
 
+// ------------------------------------------------------------------ resident path
+//
+// Groups of whole vectors (C/G a multiple of 8, cvg = C/(8G) vectors per voxel, a power of
+// two up to 8) that fit one workgroup are held in registers from the single read to the
+// write, as in the NCDHW resident kernels: one launch per direction instead of three. Vector
+// w of a group is channel vector w mod cvg of voxel w / cvg; lane t holds vectors t, t + B,
+// ... (B a multiple of 64, hence of cvg), so all of a lane's vectors carry the same 8
+// channels. The statistics are an exact two-pass over the registers relative to the
+// group's first element.
+
+// Element offset of vector w (< S * cvg) of group (n, g).
+__device__ __forceinline__ int64_t cl_res_off(const ClArgs& a, int64_t n, int64_t g, int w)
+{
+    const int64_t s = w >> a.lcvg;
+    const int k = w & ((1 << a.lcvg) - 1);
+    return (n * a.S + s) * a.C + g * a.Cg + k * kVec;
+}
+
+// Forward, one workgroup per group: blockIdx.x = g, blockIdx.y = n. Writes mean, rstd and y.
+template <int V, typename TX, typename TY>
+__global__ void __launch_bounds__(kResMaxBlock)
+cl_res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
+                  float eps, float* __restrict__ mean_out, float* __restrict__ rstd_out, ClArgs a,
+                  TY* __restrict__ y)
+{
+    __shared__ float s_red[2 * kResMaxWaves];
+    const int tid = threadIdx.x, blk = blockDim.x;
+    const int vg = int(a.S << a.lcvg);  // vectors per group (<= kResMaxVecs)
+    const float fM = float(a.M);        // exact: M <= 8 * kResMaxVecs
+    const bool act = a.act != 0;
+    const int64_t g = blockIdx.x, n = blockIdx.y, ng = n * a.G + g;
+    const float K = cl_group_shift(x, a, n, g);
+    float e[V * kVec];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int w = u * blk + tid;
+        float v[kVec];
+        if (w < vg) {
+            Io<TX>::template load8<kNtApply>(x + cl_res_off(a, n, g, w), v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) v[i] = K;  // contributes exact zeros below
+        }
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) e[u * kVec + i] = v[i];
+    }
+    float t[V * kVec];
+#pragma unroll
+    for (int i = 0; i < V * kVec; ++i) t[i] = e[i] - K;
+    const float m = block_allsum2(tree_sum(t), 0.0f, s_red).x / fM;
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const bool ok = u * blk + tid < vg;
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) t[u * kVec + i] = ok ? (e[u * kVec + i] - K) - m : 0.0f;
+    }
+    const float2 r = block_allsum2(tree_sum(t), tree_sumsq(t), s_red);
+    float var = (r.y - (r.x * r.x) / fM) / fM;
+    var = (var < 0.0f) ? 0.0f : var;  // NaN passes through
+    const float rstd = 1.0f / __fsqrt_rn(var + eps);
+    const float hi = K + m;
+    const float lo = (K - hi) + m;
+    if (tid == 0) {
+        mean_out[ng] = hi;
+        rstd_out[ng] = rstd;
+    }
+    const int64_t c0 = g * a.Cg + (tid & ((1 << a.lcvg) - 1)) * kVec;  // the lane's first channel
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int w = u * blk + tid;
+        if (w < vg) {
+            float o[kVec];
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                const float scale = (gamma ? gamma[c0 + i] : 1.0f) * rstd;
+                const float v = fmaf((e[u * kVec + i] - hi) - lo, scale, beta ? beta[c0 + i] : 0.0f);
+                o[i] = act ? relu_f(v) : v;
+            }
+            Io<TY>::store8(y + cl_res_off(a, n, g, w), o);
+        }
+    }
+}
+
+// Backward, one workgroup per g covering the groups (n, g) of all N samples: vector w of
+// the workgroup is vector w mod vg of sample w / vg (vg = S * cvg, a multiple of 64, so
+// every wave lies in one sample). Per vector and channel: g (dy, or dy gated by the relu)
+// and g*(x - mean); lanes of a wave that share a channel vector add them in a butterfly
+// over the lane bits above log2(cvg); per (sample, channel) row the waves' sums in (vector
+// set, wave) order, then s2 times rstd; per sample c1, c2 over the group's channels in
+// order; per channel dgamma, dbeta over the samples in order; then dx from the registers as
+// bwd_apply computes it (dx = A*g + (B + E*(x - mean))).
+template <int V, typename TX, typename TD>
+__global__ void __launch_bounds__(kResMaxBlock)
+cl_res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
+                  const float* __restrict__ rstd, const float* __restrict__ gamma,
+                  const float* __restrict__ beta, ClArgs a, float* __restrict__ dgamma,
+                  float* __restrict__ dbeta, TX* __restrict__ dx)
+{
+    constexpr int kSlot = 2 * kVec;  // per channel vector: 8 sums of g, 8 of g*(x - mean)
+    __shared__ float s_part[kResMaxLaneVecs * kResMaxWaves * kClResMaxGroupVecs * kSlot];
+    __shared__ float s_r1[kClResMaxRows], s_r2[kClResMaxRows];
+    __shared__ float s_b[kResMaxVecs / 64], s_e[kResMaxVecs / 64];
+    const int tid = threadIdx.x, blk = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nw = blk >> 6;
+    const int cvg = 1 << a.lcvg, Cg = int(a.Cg), N = int(a.N);
+    const int vg = int(a.S << a.lcvg), nvt = N * vg;
+    const bool act = a.act != 0;
+    const int64_t g = blockIdx.x;
+    const int64_t c0 = g * Cg + (tid & (cvg - 1)) * kVec;  // the lane's first channel
+    float xs[V * kVec], gs[V * kVec];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int wb = u * blk + wave * 64;  // the wave's first vector
+        if (wb < nvt) {                      // whole waves are in or out
+            const int nn = int(fdiv(uint32_t(wb), a.div_vg));
+            const int64_t off = cl_res_off(a, nn, g, u * blk + tid - nn * vg);
+            const int64_t ng = int64_t(nn) * a.G + g;
+            float e[kVec], f[kVec], p[kSlot];
+            Io<TX>::template load8<kNtBwdApply>(x + off, e);
+            Io<TD>::template load8<kNtBwdApply>(dy + off, f);
+            const float mu = mean[ng], rs = rstd[ng];
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                const float d = e[i] - mu;
+                const float A = rs * (gamma ? gamma[c0 + i] : 1.0f);
+                const float q = act ? relu_gate(fmaf(d, A, beta ? beta[c0 + i] : 0.0f), f[i]) : f[i];
+                xs[u * kVec + i] = e[i];
+                gs[u * kVec + i] = q;
+                p[i] = q;
+                p[kVec + i] = q * d;
+            }
+            for (int o = 32; o >= cvg; o >>= 1) {
+#pragma unroll
+                for (int j = 0; j < kSlot; ++j) p[j] = p[j] + __shfl_xor(p[j], o);
+            }
+            if (lane < cvg) {
+                float* dst = s_part + ((u * kResMaxWaves + wave) * kClResMaxGroupVecs + lane) * kSlot;
+#pragma unroll
+                for (int j = 0; j < kSlot; ++j) dst[j] = p[j];
+            }
+        }
+    }
+    __syncthreads();
+    for (int r = tid; r < N * Cg; r += blk) {
+        const int nn = r / Cg, ci = r - nn * Cg;
+        const int kk = ci / kVec, j = ci - kk * kVec;
+        float t1 = 0.0f, t2 = 0.0f;
+        for (int u = 0; u < V; ++u) {
+            for (int wv = 0; wv < nw; ++wv) {
+                const int wb = u * blk + wv * 64;
+                if (wb < nvt && int(fdiv(uint32_t(wb), a.div_vg)) == nn) {
+                    const float* src = s_part + ((u * kResMaxWaves + wv) * kClResMaxGroupVecs + kk) * kSlot;
+                    t1 = t1 + src[j];
+                    t2 = t2 + src[kVec + j];
+                }
+            }
+        }
+        s_r1[r] = t1;
+        s_r2[r] = t2 * rstd[int64_t(nn) * a.G + g];
+    }
+    __syncthreads();
+    for (int nn = tid; nn < N; nn += blk) {
+        float t1 = 0.0f, t2 = 0.0f;
+        for (int ci = 0; ci < Cg; ++ci) {
+            const float gm = gamma ? gamma[g * Cg + ci] : 1.0f;
+            t1 = t1 + gm * s_r1[nn * Cg + ci];
+            t2 = t2 + gm * s_r2[nn * Cg + ci];
+        }
+        const float rs = rstd[int64_t(nn) * a.G + g];
+        s_b[nn] = -(rs * float(double(t1) / double(a.M)));
+        s_e[nn] = -((rs * rs) * float(double(t2) / double(a.M)));
+    }
+    if (dgamma || dbeta) {
+        for (int ci = tid; ci < Cg; ci += blk) {
+            float q1 = 0.0f, q2 = 0.0f;
+            for (int nn = 0; nn < N; ++nn) {
+                q1 = q1 + s_r2[nn * Cg + ci];
+                q2 = q2 + s_r1[nn * Cg + ci];
+            }
+            if (dgamma) dgamma[g * Cg + ci] = q1;
+            if (dbeta) dbeta[g * Cg + ci] = q2;
+        }
+    }
+    __syncthreads();
+    if (!dx) return;
+    const bool single = (a.M == 1);
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int wb = u * blk + wave * 64;
+        if (wb < nvt) {
+            const int nn = int(fdiv(uint32_t(wb), a.div_vg));
+            const int64_t off = cl_res_off(a, nn, g, u * blk + tid - nn * vg);
+            const int64_t ng = int64_t(nn) * a.G + g;
+            const float mu = mean[ng], rs = rstd[ng], B = s_b[nn], E = s_e[nn];
+            float o[kVec];
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                const float d = xs[u * kVec + i] - mu;
+                float t = fmaf(rs * (gamma ? gamma[c0 + i] : 1.0f), gs[u * kVec + i], fmaf(E, d, B));
+                if (single) t = t - t;
+                o[i] = t;
+            }
+            Io<TX>::store8(dx + off, o);
+        }
+    }
+}
+
 // Calls f with std::integral_constant<int, NGL> for the lane's slot count.
 template <typename F>
 hipError_t with_ngl(int ngl, F&& f)
@@ -711,6 +918,39 @@ hipError_t launch_cl_backward(const void* dy, int dydt, const void* x, int xdt, 
                               cp<TD>(dy), cp<TX>(x), a, static_cast<const float2*>(ws.coefc),
                               static_cast<const float4*>(ws.coefg), mp<TX>(dx));
             });
+        });
+    });
+}
+
+// The plan keeps a resident workgroup within 1024 vectors, one a lane (vecs == 1).
+hipError_t launch_cl_res_forward(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                                 float* mean, float* rstd, void* y, int ydt, const ClArgs& a, hipStream_t st,
+                                 int block, int vecs)
+{
+    if (vecs != 1) return hipErrorInvalidValue;
+    const dim3 grid(unsigned(a.G), unsigned(a.N)), blk{unsigned(block)};
+    return with_type(xdt, [&](auto tx) {
+        using TX = decltype(tx);
+        if (ydt == kF32)
+            return launch(cl_res_fwd_kernel<1, TX, float>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd,
+                          a, mp<float>(y));
+        return launch(cl_res_fwd_kernel<1, TX, TX>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd, a,
+                      mp<TX>(y));
+    });
+}
+
+hipError_t launch_cl_res_backward(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                                  const float* rstd, const float* gamma, const float* beta, void* dx,
+                                  float* dgamma, float* dbeta, const ClArgs& a, hipStream_t st, int block,
+                                  int vecs)
+{
+    if (vecs != 1) return hipErrorInvalidValue;
+    return with_type(xdt, [&](auto tx) {
+        return with_type(dydt, [&](auto td) {
+            using TX = decltype(tx);
+            using TD = decltype(td);
+            return launch(cl_res_bwd_kernel<1, TX, TD>, dim3(unsigned(a.G)), dim3(unsigned(block)), st,
+                          cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, dgamma, dbeta, mp<TX>(dx));
         });
     });
 }

@@ -151,6 +151,8 @@ struct ClArgs {
     int64_t chunk, K, jobs;
     int64_t chunk_a, K_a, jobs_a;
     int32_t ngl, act;
+    int32_t lcvg;                     // resident path: log2 of a group's vectors per voxel
+    FastDiv div_vg;                   // resident path: S * C/(8G), a group's vectors
 };
 
 inline ClArgs clargs_of(const PlanCL& p, int act = 0)
@@ -161,6 +163,8 @@ inline ClArgs clargs_of(const PlanCL& p, int act = 0)
     a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs;
     a.chunk_a = p.chunk_a; a.K_a = p.K_a; a.jobs_a = p.jobs_a;
     a.ngl = p.ngl; a.act = act;
+    a.lcvg = p.lcvg;
+    a.div_vg = fastdiv_of(p.res_bwd ? p.S << p.lcvg : 0);
     return a;
 }
 
@@ -193,5 +197,13 @@ hipError_t launch_cl_backward(const void* dy, int dydt, const void* x, int xdt, 
                               const float* rstd, const float* gamma, const float* beta, void* dx,
                               float* dgamma, float* dbeta, const ClArgs& a, WorkspaceCL ws,
                               hipStream_t st);
+// Channels-last resident path, one kernel per direction (block threads, vecs vectors a lane).
+hipError_t launch_cl_res_forward(const void* x, int xdt, const float* gamma, const float* beta, float eps,
+                                 float* mean, float* rstd, void* y, int ydt, const ClArgs& a, hipStream_t st,
+                                 int block, int vecs);
+hipError_t launch_cl_res_backward(const void* dy, int dydt, const void* x, int xdt, const float* mean,
+                                  const float* rstd, const float* gamma, const float* beta, void* dx,
+                                  float* dgamma, float* dbeta, const ClArgs& a, hipStream_t st, int block,
+                                  int vecs);
 
 }  // namespace gn

@@ -156,6 +156,24 @@ int make_plan_cl(int64_t N, int64_t C, int64_t S, int64_t G, PlanCL* p)
     q.chunk_a = kClApplyRounds * q.vps;
     q.K_a = ceil_div(S, q.chunk_a);
     q.jobs_a = N * q.K_a;
+    // Resident path: every group is whole vectors (C/G a multiple of 8) and fits one
+    // workgroup; the backward's workgroup also holds all samples, whose vectors start on
+    // wave boundaries (S * C/(8G) a multiple of 64), within kClResMaxRows rows.
+    const int64_t cvg = Cg / kVec;
+    if (GN_RESIDENT && Cg % kVec == 0 && cvg <= kClResMaxGroupVecs && (cvg & (cvg - 1)) == 0) {
+        const int64_t vg = S * cvg;
+        int l = 0;
+        while ((int64_t(1) << l) < cvg) ++l;
+        q.lcvg = l;
+        if (vg <= kClResMaxVecs && N <= 65535) {
+            q.res_fwd = true;
+            resident_shape(vg, &q.res_block_f, &q.res_vecs_f);
+        }
+        if (vg % 64 == 0 && N <= kClResMaxVecs / vg && N * Cg <= kClResMaxRows) {
+            q.res_bwd = true;
+            resident_shape(N * vg, &q.res_block_b, &q.res_vecs_b);
+        }
+    }
     q.ws_partg_offset = size_t(round_up(q.jobs * C * 8, 256));
     q.ws_coefc_offset = q.ws_partg_offset + size_t(round_up(q.jobs * G * 8, 256));
     q.ws_coefg_offset = q.ws_coefc_offset + size_t(round_up(N * C * 8, 256));

@@ -129,6 +129,16 @@ constexpr int kClBlock = 256;
 #endif
 constexpr int64_t kClTargetJobs = GN_CL_TARGET_JOBS;
 constexpr int kClRounds = 4;        // voxel rounds a reduction lane holds per step
+// Channels-last resident path: at most this many vectors of a group per voxel, at most this
+// many (sample, channel) rows in a backward workgroup, and at most this many vectors per
+// workgroup. A group's channels are 16-64 bytes of every voxel, C*2 bytes apart, so its
+// loads are narrow; measured on MI355X (bf16, fwd+bwd): 8^3 x 512 channels, G=32 (1024
+// vectors a group) 28 -> 18 us a step against the three-kernel path, while 16^3 x 256
+// channels (4096 vectors) went 28 -> 72 us and a backward over 4 samples of 1024 vectors
+// 29 -> 37 us.
+constexpr int kClResMaxGroupVecs = 8;
+constexpr int kClResMaxRows = 512;
+constexpr int64_t kClResMaxVecs = 1024;
 constexpr int kClApplyRounds = 4;   // voxel rounds of a streaming job
 
 struct PlanCL {
@@ -141,6 +151,12 @@ struct PlanCL {
     int64_t chunk = 0, K = 0, jobs = 0;
     // streaming jobs
     int64_t chunk_a = 0, K_a = 0, jobs_a = 0;
+    // resident path (C/G a multiple of 8 with cvg = C/(8G) a power of two up to
+    // kClResMaxGroupVecs): forward per group (n, g), backward per g across all samples
+    bool res_fwd = false, res_bwd = false;
+    int res_block_f = 0, res_vecs_f = 0;
+    int res_block_b = 0, res_vecs_b = 0;
+    int lcvg = 0;        // log2 of the group's vectors per voxel
     // workspace: [partials: float2 * jobs * C][group partials: float2 * jobs * G]
     // [per-channel: float2 * N*C][per-group: float4 * N*G]
     size_t ws_partg_offset = 0, ws_coefc_offset = 0, ws_coefg_offset = 0, ws_bytes = 0;
