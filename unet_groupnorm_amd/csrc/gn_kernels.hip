@@ -1066,7 +1066,7 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
 // ------------------------------------------------------------------ launchers
 
 // Calls f with std::bool_constant<NT> for the streamed loads of a reduction or folded
-// streaming kernel: plain loads (false) when the launch was judged to fit the last-level
+// streaming kernel: plain loads (false) when the host found that x fits the last-level
 // cache, so that the step's later kernels find x there, else the kernel's streaming policy
 // Stream. The policy moves no bit of any result.
 template <bool Stream, typename F>
