@@ -616,6 +616,23 @@ def test_channels_last_bitwise_properties():
     assert torch.equal(yc.contiguous(), inp["beta"].to(torch.bfloat16).view(1, -1, 1, 1, 1).expand_as(yc).contiguous())
 
 
+@pytest.mark.parametrize("case", [CL_CASES[0], CL_CASES[4], CL_CASES[6]], ids=lambda c: c.name)
+def test_channels_last_optional_backward_outputs(case):
+    """The channels-last backward with dx only, and with dgamma/dbeta only, gives the bits of
+    the full call."""
+    say(f"{case.name} channels-last: backward with dx only, and with dgamma/dbeta only")
+    inp = workloads.make(case, DEV)
+    x, G = gn.as_layout(inp["x"], "ndhwc"), inp["G"]
+    dy = gn.as_layout(inp["dy"], "ndhwc")
+    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], inp["out_dtype"])
+    dx, dg, db = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G)
+    n1, dg2, db2 = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G, need_dx=False)
+    dx3, n2, n3 = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G, need_dgamma=False, need_dbeta=False)
+    torch.cuda.synchronize()
+    assert n1 is None and n2 is None and n3 is None
+    assert torch.equal(dg, dg2) and torch.equal(db, db2) and torch.equal(_bits(dx), _bits(dx3))
+
+
 def test_channels_last_autograd_keeps_the_layout():
     say("group_norm on a channels_last_3d tensor through autograd")
     inp = workloads.make(workloads.custom(2, 32, 8, (8, 8, 8), torch.bfloat16, dist="unet", seed=73), DEV)
