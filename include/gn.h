@@ -12,9 +12,10 @@
  *     a corrected two-pass per tile merged with Chan's parallel formula, register-only
  *     reductions in a fixed order with no float atomics (bitwise reproducible).
  *   - Same page, paragraph folding seven launches into four: grid, split count, tile
- *     sizes and reduction order are pure functions of the shape. (That page folds the
- *     finalize into the elementwise kernels; here it is a small kernel of its own, run
- *     once per group, so that the streaming kernels can be a very large grid.)
+ *     sizes and reduction order are pure functions of the shape. That page also folds
+ *     the finalize into the elementwise kernels; gn_forward and gn_backward do the same,
+ *     while the split-phase entry points (which must leave the statistics in between)
+ *     and the channels-last entry points run it as a small kernel of its own.
  *   - "Preserve GroupNorm dtype" (LBANN/ScaFFold pull 105), first paragraph: the
  *     normalized value is computed in fp32 and only the store narrows, so the output
  *     is the fp32 answer rounded once; an fp32 output is available on request. Second
