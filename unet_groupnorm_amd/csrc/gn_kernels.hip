@@ -864,12 +864,18 @@ res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
     const int64_t vb = row0 * (a.S / kVec);  // the group's first vector
     const float K = group_shift(x, a, n, g);
     float e[V * kVec];
+    float gms[V], bts[V];  // the vector's gamma_c and beta_c, requested with its loads
 #pragma unroll
     for (int u = 0; u < V; ++u) {
         const int w = u * blk + tid;
         float v[kVec];
+        gms[u] = 1.0f;
+        bts[u] = 0.0f;
         if (w < vg) {
             Io<TX>::template load8<kNtApply>(x + (vb + w) * kVec, v);
+            const int64_t c = g * a.Cg + fdiv(uint32_t(w), a.div_W);
+            if (gamma) gms[u] = gamma[c];
+            if (beta) bts[u] = beta[c];
         } else {
 #pragma unroll
             for (int i = 0; i < kVec; ++i) v[i] = K;  // contributes exact zeros below
@@ -906,9 +912,8 @@ res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
         for (int u = 0; u < V; ++u) {
             const int w = u * blk + tid;
             if (w < vg) {
-                const int64_t c = g * a.Cg + fdiv(uint32_t(w), a.div_W);
-                const float scale = (gamma ? gamma[c] : 1.0f) * rstd;
-                const float shift = beta ? beta[c] : 0.0f;
+                const float scale = gms[u] * rstd;
+                const float shift = bts[u];
                 float o[kVec];
 #pragma unroll
                 for (int i = 0; i < kVec; ++i) {
@@ -952,11 +957,14 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
         return (int64_t(n) * a.C + c) * W;
     };
     float xs[V * kVec], gs[V * kVec];
+    float mus[V], As[V];  // the vector's mean and rstd*gamma_c, kept for the dx
     int rows[V];
 #pragma unroll
     for (int u = 0; u < V; ++u) {
         const int w = u * blk + tid;
         rows[u] = -1;
+        mus[u] = 0.0f;
+        As[u] = 0.0f;
         if (w < nvt) {
             const int rho = int(fdiv(uint32_t(w), a.div_W));
             int n, c;
@@ -968,6 +976,8 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
             const float mu = mean[ng];
             const float A = rstd[ng] * (gamma ? gamma[c] : 1.0f);
             const float bt = beta ? beta[c] : 0.0f;
+            mus[u] = mu;
+            As[u] = A;
 #pragma unroll
             for (int i = 0; i < kVec; ++i) {
                 d[i] = e[i] - mu;
@@ -982,6 +992,8 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
     }
     __syncthreads();
     for (int rho = wave; rho < nrows; rho += nw) {
+        const int n = int(fdiv(uint32_t(rho), a.div_Cg));
+        const float rsn = rstd[int64_t(n) * a.G + g];  // requested before the sums
         float p1 = 0.0f, p2 = 0.0f;
         for (int k = lane; k < W; k += 64) {
             p1 = p1 + s_v1[rho * W + k];
@@ -990,13 +1002,13 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
         p1 = wave_allsum(p1);
         p2 = wave_allsum(p2);
         if (lane == 0) {
-            const int n = int(fdiv(uint32_t(rho), a.div_Cg));
             s_r1[rho] = p1;
-            s_r2[rho] = p2 * rstd[int64_t(n) * a.G + g];
+            s_r2[rho] = p2 * rsn;
         }
     }
     __syncthreads();
     for (int n = wave; n < N; n += nw) {
+        const float rs = rstd[int64_t(n) * a.G + g];  // requested before the sums
         float t1 = 0.0f, t2 = 0.0f;
         for (int i = lane; i < Cg; i += 64) {
             const float gm = gamma ? gamma[g * Cg + i] : 1.0f;
@@ -1006,7 +1018,6 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
         t1 = wave_allsum(t1);
         t2 = wave_allsum(t2);
         if (lane == 0) {
-            const float rs = rstd[int64_t(n) * a.G + g];
             const float c1 = float(double(t1) / double(a.M));
             const float c2 = float(double(t2) / double(a.M));
             s_v1[n] = -(rs * c1);
@@ -1045,9 +1056,8 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
                 const int w = u * blk + tid;
                 int n, c;
                 const int64_t gv = row_base(rho, n, c) + (w - rho * W);
-                const int64_t ng = int64_t(n) * a.G + g;
-                const float mu = mean[ng];
-                const float A = rstd[ng] * (gamma ? gamma[c] : 1.0f);
+                const float mu = mus[u];
+                const float A = As[u];
                 const float B = s_v1[n], E = s_v2[n];
                 float o[kVec];
 #pragma unroll
