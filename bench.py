@@ -30,6 +30,18 @@ KERNEL_SOURCES = ["unet_groupnorm_amd/csrc/gn_kernels.hip", "unet_groupnorm_amd/
                   "unet_groupnorm_amd/csrc/gn_launch.hpp", "unet_groupnorm_amd/csrc/gn_api.cpp"]
 
 
+# Workloads --trace-case runs: name -> (case, layout, activation); "census" runs the 18 sites.
+TRACE_CASES = {
+    "tiny": ("TINY", "ncdhw", None),
+    "deep": ("DEEP", "ncdhw", None),
+    "deep_f32out": ("DEEP_F32OUT", "ncdhw", None),
+    "scale7_ndhwc": ("SCALE7", "ndhwc", None),
+    "scale7_fp16": ("SCALE7_F16", "ncdhw", None),
+    "scale7_relu": ("SCALE7", "ncdhw", "relu"),
+    "census": (None, "ncdhw", None),
+}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -42,6 +54,9 @@ def parse():
     ap.add_argument("--settle", type=float, default=1.0,
                     help="seconds of untimed steps before the warmup steps (the first timed window "
                          "otherwise reads 2-4%% slow on a GPU that was idle a moment before)")
+    ap.add_argument("--trace-case", choices=sorted(TRACE_CASES),
+                    help="only run --steps steps (after --warmup) of this workload and print its "
+                         "time per step: a short program for a profiler's kernel trace")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB bf16 device copy 5 times (a kernel of known traffic "
                          "for scaling profiler byte counters)")
@@ -374,6 +389,38 @@ def load_traffic(workload):
     return rec, "ok"
 
 
+def trace_case(args):
+    """--trace-case: W warmup steps, then K timed steps of one workload (all 18 sites back to
+    back for "census"); prints one JSON line with the time per step."""
+    import torch
+
+    import workloads
+    name, layout, act = TRACE_CASES[args.trace_case]
+    cases = workloads.census_cases() if name is None else [getattr(workloads, name)]
+    runs = [Runner(c, activation=act, layout=layout) for c in cases]
+    log(f"trace case {args.trace_case}: {len(runs)} workload(s), {args.warmup} warmup and {args.steps} timed steps")
+    for _ in range(args.warmup):
+        for r in runs:
+            r.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        for r in runs:
+            r.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    total = sum(r.step_bytes for r in runs)
+    if args.copy_probe:
+        log("copy probe: 5 copies of 1 GiB")
+        copy_ceiling_gbps(reps=5)
+    print(json.dumps({"trace_case": args.trace_case, "workloads": [c.name for c in cases], "layout": layout,
+                      "activation": act, "steps": args.steps, "us_per_step": round(ms * 1e3, 2),
+                      "method_bytes_per_step": total,
+                      "gbps": round(total / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -387,6 +434,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
 
+    if args.trace_case:
+        trace_case(args)
+        return
     case = workloads.SCALE7 if args.workload == "scale7" else workloads.SCALE8
     log(f"workload {case.name} {case.shape}; generating inputs on the GPU")
     run = Runner(case)
