@@ -67,3 +67,36 @@ def test_two_processes_agree_bitwise():
     theirs = child.stdout.strip().splitlines()[-1]
     ours = digest(CASES)
     assert ours == theirs
+
+
+def test_concurrent_streams_match_one_stream():
+    """Two workloads enqueued on two streams at once (each with its own workspace, kernels of
+    both in flight together) give the bits each gives alone: the library keeps no state
+    between calls and touches nothing but its arguments."""
+    cases = [workloads.custom(1, 64, 8, (48, 48, 48), torch.bfloat16, dist="unet", seed=95),
+             workloads.custom(2, 256, 32, (8, 8, 8), torch.bfloat16, dist="deep", seed=96)]
+    print("[gpu-determinism] two streams: " + ", ".join(c.name for c in cases), flush=True)
+    inps = [workloads.make(c, "cuda") for c in cases]
+    alone = [[_bits(t).clone() for t in _run_inputs(i)] for i in inps]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    outs = [None, None]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for k in (0, 1):
+            streams[k].wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(streams[k]):
+                outs[k] = _run_inputs(inps[k], sync=False)
+        torch.cuda.synchronize()
+        for k in (0, 1):
+            for a, t in zip(alone[k], outs[k]):
+                assert torch.equal(a, _bits(t)), f"stream {k}, repeat {rep}"
+
+
+def _run_inputs(inp, sync=True):
+    x, G = inp["x"], inp["G"]
+    ws = gn.workspace_for(x, G)
+    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], inp["out_dtype"], workspace=ws)
+    dx, dg, db = gn.gn_backward(inp["dy"], x, mean, rstd, inp["gamma"], G, workspace=ws)
+    if sync:
+        torch.cuda.synchronize()
+    return [y, mean, rstd, dx, dg, db]
