@@ -39,6 +39,7 @@ TRACE_CASES = {
     "scale7_fp16": ("SCALE7_F16", "ncdhw", None),
     "scale7_relu": ("SCALE7", "ncdhw", "relu"),
     "census": (None, "ncdhw", None),
+    "shard8": (None, "ncdhw", None),  # one rank's share of the 256^3 site split in 8
 }
 
 
@@ -300,6 +301,58 @@ def census(steps=10, warmup=3):
             "bitwise_identical_10_repeats": identical, "per_shape": per_shape}
 
 
+def spatial_shard(steps=30, warmup=5, nshards=8):
+    """One rank's share of the 256^3, C=32, G=8 bf16 volume split in 8 along D
+    (1 x 32 x 32 x 256 x 256), run through the spatial-shard entry points as that rank would:
+    its statistics record, the shard-order merge of all ranks' records, the normalize; its
+    per-row backward sums, their merge, dx. The records of the other ranks (what an
+    all-gather of 128 B and 256 B would bring) are this shard's own, gathered once before
+    timing; the all-gather itself is not run (one GPU)."""
+    import torch
+
+    import unet_groupnorm_amd as gn
+    import workloads
+    case = workloads.custom(1, 32, 8, (256 // nshards, 256, 256), torch.bfloat16, dist="unet", seed=1208)
+    inp = workloads.make(case, "cuda")
+    x, dy, G, eps, gamma, beta = inp["x"], inp["dy"], inp["G"], inp["eps"], inp["gamma"], inp["beta"]
+    ws = gn.workspace_for(x, G)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    rec0 = gn.gn_forward_shard_stats(x, G, workspace=ws)
+    recs = torch.stack([rec0] * nshards).contiguous()
+    mean, rstd = gn.gn_forward_shard_merge(recs, gamma, beta, x.shape, G, eps, workspace=ws)
+    sums0 = gn.gn_backward_shard_sums(dy, x, mean, rstd, gamma, G, beta=beta, workspace=ws)
+    sums = torch.stack([sums0] * nshards).contiguous()
+    S_total = case.S * nshards
+    dg = torch.empty(case.C, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dg)
+
+    def step():
+        gn.gn_forward_shard_stats(x, G, moments=recs[0], workspace=ws)
+        gn.gn_forward_shard_merge(recs, gamma, beta, x.shape, G, eps, workspace=ws, mean=mean, rstd=rstd)
+        gn.gn_forward_apply(x, G, y, ws)
+        gn.gn_backward_shard_sums(dy, x, mean, rstd, gamma, G, beta=beta, sums=sums[0], workspace=ws)
+        gn.gn_backward_shard_merge(sums, mean, rstd, gamma, x.shape, S_total, G, workspace=ws, beta=beta,
+                                   dgamma=dg, dbeta=db)
+        gn.gn_backward_apply(dy, x, G, dx, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = 16 * case.numel
+    return {"workload": f"scale8_256cube_c32_g8 split in {nshards} along D, one rank's share "
+                        f"{tuple(case.shape)}, global statistics (records merged in shard order)",
+            "us_per_step": round(ms * 1e3, 2), "method_bytes_per_step": nbytes,
+            "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "note": "the all-gather of the records (N*G*16 B) and sums (N*C*8 B) is not run: one GPU"}
+
+
 def small_configs(steps=50, warmup=10):
     """The launch-bound configurations, timed as fwd+bwd microseconds per step: eager (one
     call per direction from Python) and replayed from a captured graph."""
@@ -395,6 +448,13 @@ def trace_case(args):
     import torch
 
     import workloads
+    if args.trace_case == "shard8":
+        r = spatial_shard(steps=args.steps, warmup=args.warmup)
+        if args.copy_probe:
+            log("copy probe: 5 copies of 1 GiB")
+            copy_ceiling_gbps(reps=5)
+        print(json.dumps({"trace_case": args.trace_case, **r}), flush=True)
+        return
     name, layout, act = TRACE_CASES[args.trace_case]
     cases = workloads.census_cases() if name is None else [getattr(workloads, name)]
     runs = [Runner(c, activation=act, layout=layout) for c in cases]
@@ -552,6 +612,8 @@ def main():
         out["census"] = census()
         log("small configurations (tiny, deep)")
         out["small_configs"] = small_configs()
+        log("one rank's share of the 256^3 site split in 8, global statistics")
+        out["spatial_shard"] = spatial_shard()
     print(json.dumps(out), flush=True)
 
 

@@ -32,12 +32,15 @@
 #ifndef GN_NT_STORE
 #define GN_NT_STORE 0
 #endif
-// Store policy of the streaming kernels with the finalize folded in (1: nontemporal). Their
-// workgroups each write a run of tens of KiB, and nontemporal stores measured about 7%
-// faster for them at 256^3 on MI355X (the one-step streaming kernels: no gain; the
-// channels-last ones: mixed), so the default differs from GN_NT_STORE's.
-#ifndef GN_NT_STORE_FOLD
-#define GN_NT_STORE_FOLD 1
+// Store policy of the NCDHW streaming kernels, folded and one-step (1: nontemporal), which
+// differs from GN_NT_STORE's default for the channels-last and resident kernels. Measured on
+// MI355X: the folded kernels about 7% faster at 256^3; on a step of one-step kernels (the
+// spatial-shard entry points, 1x32x32x256^2 bf16) plain stores left y and dx dirty in the
+// last-level cache for the next plain-load reduction to write back (239.8 -> 198.7 us a
+// step); the channels-last step went 189 -> 198 us and the resident deep config 15.9 ->
+// 16.7 us with nontemporal stores, so they keep plain ones.
+#ifndef GN_NT_STORE_STREAM
+#define GN_NT_STORE_STREAM 1
 #endif
 
 namespace gn {
@@ -47,7 +50,7 @@ namespace {
 constexpr bool kNtStats = GN_NT_STATS, kNtBwdReduce = GN_NT_BRED;
 constexpr bool kNtApply = GN_NT_APPLY, kNtBwdApply = GN_NT_BAPPLY;
 constexpr bool kReverseApply = GN_REVERSE_APPLY;
-constexpr bool kNtStore = GN_NT_STORE, kNtStoreFold = GN_NT_STORE_FOLD;
+constexpr bool kNtStore = GN_NT_STORE, kNtStoreStream = GN_NT_STORE_STREAM;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -397,7 +397,7 @@ __device__ __forceinline__ void apply_vec(const TX* __restrict__ x, TY* __restri
         Io<TX>::template load8<NT>(x + vi * kVec, e);
 #pragma unroll
         for (int i = 0; i < kVec; ++i) o[i] = f(e[i]);
-        Io<TY>::store8(y + vi * kVec, o);
+        Io<TY>::template store8<kNtStoreStream>(y + vi * kVec, o);
     } else {
         for (int i = 0; i < kVec; ++i) {
             const int64_t gi = vi * kVec + i;
@@ -406,7 +406,7 @@ __device__ __forceinline__ void apply_vec(const TX* __restrict__ x, TY* __restri
     }
 }
 
-template <typename TX, typename TY>
+template <typename TX, typename TY, bool NT>
 __global__ void __launch_bounds__(256)
 apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
              const float4* __restrict__ coef)
@@ -421,7 +421,7 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
         const Affine f = {cf.x, cf.y, cf.z, cf.w, a.act != 0};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
-            for (int u = 0; u < kApplyVecs; ++u) apply_vec<kNtApply>(x, y, jb, sv0 + int64_t(u) * blk + tid, f);
+            for (int u = 0; u < kApplyVecs; ++u) apply_vec<NT>(x, y, jb, sv0 + int64_t(u) * blk + tid, f);
         }
     }
 }
@@ -437,7 +437,7 @@ __device__ __forceinline__ void apply_full_step(const typename Io<TX>::Raw (&r)[
         Io<TX>::widen(r[u], e);
 #pragma unroll
         for (int i = 0; i < kVec; ++i) o[i] = f(e[i]);
-        Io<TY>::template store8<kNtStoreFold>(y + (sv0 + int64_t(u) * blk + tid) * kVec, o);
+        Io<TY>::template store8<kNtStoreStream>(y + (sv0 + int64_t(u) * blk + tid) * kVec, o);
     }
 }
 
@@ -717,7 +717,7 @@ __device__ __forceinline__ void dx_vec(const TD* __restrict__ dy, const TX* __re
         Io<TD>::template load8<NT>(dy + vi * kVec, gv);
 #pragma unroll
         for (int i = 0; i < kVec; ++i) o[i] = k(xv[i], gv[i]);
-        Io<TX>::store8(dx + vi * kVec, o);
+        Io<TX>::template store8<kNtStoreStream>(dx + vi * kVec, o);
     } else {
         for (int i = 0; i < kVec; ++i) {
             const int64_t gi = vi * kVec + i;
@@ -726,7 +726,7 @@ __device__ __forceinline__ void dx_vec(const TD* __restrict__ dy, const TX* __re
     }
 }
 
-template <typename TX, typename TD>
+template <typename TX, typename TD, bool NT>
 __global__ void __launch_bounds__(256)
 bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
                  const float4* __restrict__ coef, TX* __restrict__ dx)
@@ -742,7 +742,7 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
         const DxCoef k = {cf.x, cf.y, cf.z, cf.w, act ? coef[2 * jb.row + 1].x : 0.0f, act, a.M == 1};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
-            for (int u = 0; u < kApplyVecs; ++u) dx_vec<kNtBwdApply>(dy, x, dx, jb, sv0 + int64_t(u) * blk + tid, k);
+            for (int u = 0; u < kApplyVecs; ++u) dx_vec<NT>(dy, x, dx, jb, sv0 + int64_t(u) * blk + tid, k);
         }
     }
 }
@@ -760,7 +760,7 @@ __device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V]
         Io<TD>::widen(rd[u], gv);
 #pragma unroll
         for (int i = 0; i < kVec; ++i) o[i] = k(xv[i], gv[i]);
-        Io<TX>::template store8<kNtStoreFold>(dx + (sv0 + int64_t(u) * blk + tid) * kVec, o);
+        Io<TX>::template store8<kNtStoreStream>(dx + (sv0 + int64_t(u) * blk + tid) * kVec, o);
     }
 }
 
@@ -1148,10 +1148,13 @@ hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArg
     const dim3 grid = grid_of(a.jobs_a), block(unsigned(a.block_a));
     const float4* coef = ws.coef;
     return with_type(xdt, [&](auto tx) {
-        using TX = decltype(tx);
-        if (ydt == kF32)
-            return launch(apply_kernel<TX, float>, grid, block, st, cp<TX>(x), mp<float>(y), a, coef);
-        return launch(apply_kernel<TX, TX>, grid, block, st, cp<TX>(x), mp<TX>(y), a, coef);
+        return with_policy<kNtApply>(a, [&](auto nt) {
+            using TX = decltype(tx);
+            constexpr bool NT = decltype(nt)::value;
+            if (ydt == kF32)
+                return launch(apply_kernel<TX, float, NT>, grid, block, st, cp<TX>(x), mp<float>(y), a, coef);
+            return launch(apply_kernel<TX, TX, NT>, grid, block, st, cp<TX>(x), mp<TX>(y), a, coef);
+        });
     });
 }
 
@@ -1171,10 +1174,12 @@ hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, vo
     const float4* coef = ws.coef;
     return with_type(xdt, [&](auto tx) {
         return with_type(dydt, [&](auto td) {
-            using TX = decltype(tx);
-            using TD = decltype(td);
-            return launch(bwd_apply_kernel<TX, TD>, grid, block, st, cp<TD>(dy), cp<TX>(x), a, coef,
-                          mp<TX>(dx));
+            return with_policy<kNtBwdApply>(a, [&](auto nt) {
+                using TX = decltype(tx);
+                using TD = decltype(td);
+                return launch(bwd_apply_kernel<TX, TD, decltype(nt)::value>, grid, block, st, cp<TD>(dy),
+                              cp<TX>(x), a, coef, mp<TX>(dx));
+            });
         });
     });
 }
