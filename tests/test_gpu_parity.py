@@ -170,6 +170,19 @@ def test_ragged_shapes_elementwise(case):
 CENSUS = workloads.census_cases()
 
 
+@pytest.mark.parametrize("case,layout", [
+    (workloads.custom(70000, 4, 2, (8,), torch.bfloat16, dist="unet", seed=19), "ncdhw"),
+    (workloads.custom(70000, 8, 8, (2,), torch.bfloat16, dist="normal", seed=20), "ndhwc"),
+], ids=lambda v: getattr(v, "name", str(v)))
+def test_many_samples_past_the_grid_y_limit(case, layout):
+    """More samples than a launch's y extent holds (65535): the plans leave the per-(n, g)
+    grids of the resident path and run the flat-grid kernels; every element checked."""
+    p = gn.gn_plan_query(case.N, case.C, case.S, case.G) if layout == "ncdhw" else \
+        gn.gn_plan_query_cl(case.N, case.C, case.S, case.G)
+    assert p["resident_forward"] == 0
+    full_check(workloads.make(case, "cpu"), case.name + "_" + layout, layout=layout)
+
+
 @pytest.mark.parametrize("case", CENSUS, ids=lambda c: c.name)
 def test_census_sites(case):
     if case.numel <= (1 << 23):
