@@ -329,8 +329,10 @@ int gn_plan_query_cl(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info_cl
  * The merges run the same fixed-order computation on every rank, so all ranks obtain
  * bitwise identical mean, rstd, dgamma and dbeta. The workspace is this shard's
  * (gn_workspace_bytes(N, C, S, G)). A record holds a group's element count in 32 bits, so
- * (C/G) * S must be below 2^32; a shard whose groups have a single element must be the
- * whole volume. Device pointers; moments and sums 16- and 8-byte aligned.
+ * (C/G) * S must be below 2^32. A shard is a volume in its own right for validation (so
+ * N * (C/G) * S == 1 is rejected), but its piece of a group may be a single element: the
+ * backward merge records whether the whole group is one, and gn_backward_apply answers
+ * dx = 0 only then. Device pointers; moments and sums 16- and 8-byte aligned.
  */
 typedef struct gn_moments {
     float mean_hi;   /* the shard's group mean as mean_hi + mean_lo */

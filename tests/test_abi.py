@@ -211,8 +211,9 @@ def test_shard_entry_points_validate_before_launch():
     s = U(0x50000)
     assert lib.gn_backward_shard_merge(s, 2, A, B, None, None, 1, 8, 64, 32, 4, None, None, A, 1 << 20, None) == 2
     assert lib.gn_backward_shard_merge(s, 0, A, B, None, None, 1, 8, 64, 64, 4, None, None, A, 1 << 20, None) == 2
-    # a shard of single-element groups must be the whole volume
-    assert lib.gn_backward_shard_merge(s, 2, A, B, None, None, 2, 4, 1, 2, 4, None, None, A, 1 << 20, None) == 2
+    # a shard whose groups are single elements of larger groups is a valid shape (it gets as far as
+    # the device check, which host memory fails)
+    assert lib.gn_backward_shard_merge(s, 2, A, B, None, None, 2, 4, 1, 2, 4, None, None, A, 1 << 20, None) == 8
     assert lib.gn_backward_shard_merge(s, 2, A, B, None, None, 1, 8, 64, 128, 4, None, None, A, 8, None) == 6
 
 

@@ -163,3 +163,16 @@ def test_top_site_in_eight_shards():
                              P.stats_slack(b["mean"], b["rstd"], a_dy, b["dgamma"], x.shape[1])))
     rep.update(P.check_param("dbeta", P.to_np(r["dbeta"]), b["dbeta"], a_dy, depth))
     say(f"{case.name}_p8: ok {rep}")
+
+
+def test_one_voxel_shards_of_single_channel_groups():
+    """Groups of one channel (C/G = 1) split into one-voxel shards: each shard's piece of a
+    group is a single element, but the group is not; dx must be the whole group's, not the
+    exact zero that a single-element group gets."""
+    case = workloads.custom(2, 4, 4, (3, 1, 1), torch.float32, dist="unet", seed=86)
+    say(f"{case.name}: 3 one-voxel shards, C/G = 1")
+    inp = workloads.make(case, DEV)
+    r = run_sharded(inp, 3)
+    check_ranks_agree(r)
+    assert torch.count_nonzero(r["dx"]) > 0
+    full_compare(inp, r, "one_voxel_shards_p3", 3)

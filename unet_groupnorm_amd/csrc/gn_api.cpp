@@ -514,8 +514,6 @@ int gn_backward_shard_merge(const float* sums, int64_t P, const float* mean, con
     int rc = plan_or_error(N, C, S, G, &p);
     if (rc) return rc;
     if (S_total > gn::kMaxNumel / (N * C) || P > ((int64_t(1) << 62) / (N * C))) return GN_ERR_SHAPE;
-    // The dx kernel decides single-element groups from this shard's own size.
-    if (p.M == 1 && S_total != S) return GN_ERR_SHAPE;
     if (!aligned(sums, 8) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(gamma, 4) ||
         !aligned(beta, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4))
         return GN_ERR_ALIGN;

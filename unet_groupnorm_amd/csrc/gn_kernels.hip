@@ -657,7 +657,7 @@ __device__ __forceinline__ void publish_dx_coef(float mu, float rs, float2 c12, 
         const int64_t c = g * a.Cg + i;
         const DxCoef k = dx_coef(mu, rs, gamma ? gamma[c] : 1.0f, c12, 0.0f, a);
         coef[2 * (n * a.C + c)] = make_float4(mu, k.A, k.B, k.E);
-        coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, 0.0f, 0.0f, 0.0f);
+        coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, a.M == 1 ? 1.0f : 0.0f, 0.0f, 0.0f);
     }
 }
 
@@ -737,9 +737,11 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
         const int64_t jx = xcd_job(jj, a.jobs_a, GN_XCD_REMAP);
         const int64_t j = kReverseApply ? a.jobs_a - 1 - jx : jx;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
-        const float4 cf = coef[2 * jb.row];
+        const float4 cf = coef[2 * jb.row], cg = coef[2 * jb.row + 1];
         const bool act = a.act != 0;
-        const DxCoef k = {cf.x, cf.y, cf.z, cf.w, act ? coef[2 * jb.row + 1].x : 0.0f, act, a.M == 1};
+        // Whether the whole group is one element comes from the record: a spatial shard's
+        // piece of a group can be one element when the group is not.
+        const DxCoef k = {cf.x, cf.y, cf.z, cf.w, act ? cg.x : 0.0f, act, cg.y != 0.0f};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
             for (int u = 0; u < kApplyVecs; ++u) dx_vec<NT>(dy, x, dx, jb, sv0 + int64_t(u) * blk + tid, k);
@@ -1031,7 +1033,7 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
         const int64_t ng = int64_t(n) * a.G + g, row = int64_t(n) * a.C + c;
         const float gm = gamma ? gamma[c] : 1.0f;
         coef[2 * row] = make_float4(mean[ng], rstd[ng] * gm, s_v1[n], s_v2[n]);
-        coef[2 * row + 1] = make_float4(beta ? beta[c] : 0.0f, 0.0f, 0.0f, 0.0f);
+        coef[2 * row + 1] = make_float4(beta ? beta[c] : 0.0f, a.M == 1 ? 1.0f : 0.0f, 0.0f, 0.0f);
     }
     if (dgamma || dbeta) {
         for (int i = wave; i < Cg; i += nw) {

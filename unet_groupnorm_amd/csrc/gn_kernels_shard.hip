@@ -117,8 +117,8 @@ shard_sums_kernel(const float2* __restrict__ part, KArgs a, float2* __restrict__
 // Workgroups [0, ngroups): group (n, g). Thread 0 sums each channel's (s1, s2) over shards
 // 0..P-1 in order, then c1 = (1/M) sum gamma_c s1 and c2 = (1/M) sum gamma_c s2 over the
 // group's channels in order, M the group's element count over all shards; the group's rows
-// get the dx coefficients (mean, rstd*gamma_c, -rstd*c1, -rstd^2*c2) and (beta_c) for
-// gn_backward_apply. Workgroups [ngroups, ngroups + nchan): channel c, whose dgamma and
+// get the dx coefficients (mean, rstd*gamma_c, -rstd*c1, -rstd^2*c2) and (beta_c, 1 if M is
+// 1 else 0) for gn_backward_apply. Workgroups [ngroups, ngroups + nchan): channel c, whose dgamma and
 // dbeta are the sums over samples (outer) and shards (inner), in order.
 __global__ void __launch_bounds__(64)
 shard_merge_bwd_kernel(const float2* __restrict__ sums, int64_t P, const float* __restrict__ mean,
@@ -157,7 +157,7 @@ shard_merge_bwd_kernel(const float2* __restrict__ sums, int64_t P, const float* 
             const int64_t c = g * a.Cg + i;
             const float gm = gamma ? gamma[c] : 1.0f;
             coef[2 * (n * a.C + c)] = make_float4(mu, rs * gm, B, E);
-            coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, 0.0f, 0.0f, 0.0f);
+            coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, M_total == 1 ? 1.0f : 0.0f, 0.0f, 0.0f);
         }
     } else if (w < ngroups + nchan && threadIdx.x == 0) {
         const int64_t c = w - ngroups;
