@@ -365,7 +365,10 @@ int gn_backward_shard_merge(const float* sums /* [P][N*C][2] */, int64_t P,
                             float* dgamma, float* dbeta,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* ABI version of this header (incremented on any incompatible change). */
+/* ABI version of this header (incremented on any incompatible change); gn_abi_version()
+ * returns the version the library was built with, so a caller can check that the two
+ * agree before the first call. */
+#define GN_ABI_VERSION 9
 int gn_abi_version(void);
 
 #ifdef __cplusplus

@@ -220,7 +220,7 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     return GN_OK;
 }
 
-int gn_abi_version(void) { return 9; }
+int gn_abi_version(void) { return GN_ABI_VERSION; }
 
 const char* gn_status_string(int status)
 {
