@@ -44,7 +44,28 @@ def _draw(i):
     return case, relu, layout
 
 
-CASES = [_draw(i) for i in range(32)]
+def _draw_large(i):
+    """Volumes of 0.5-4 million elements and wider groups: many reduction jobs per row,
+    folded jobs split across rows, both sides of the resident limit."""
+    rng = np.random.default_rng(9500 + i)
+    G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    cg = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    C = G * cg
+    N = int(rng.integers(1, 5))
+    nd = int(rng.integers(1, 4))
+    budget = max(1, int(rng.choice([500000, 1500000, 4000000])) // (N * C))
+    spatial = [int(max(1, round(budget ** (1.0 / nd) * rng.uniform(0.7, 1.3)))) for _ in range(nd)]
+    x_dtype = DTYPES[int(rng.integers(0, 3))]
+    dy_dtype = DTYPES[int(rng.integers(0, 3))]
+    dist = str(rng.choice(["unet", "normal", "deep"]))
+    relu = bool(rng.random() < 0.3)
+    cl_ok = C % 8 == 0 and 256 % (C // 8) == 0 and (cg % 8 == 0 or 8 % cg == 0)
+    layout = "ndhwc" if (cl_ok and rng.random() < 0.5) else "ncdhw"
+    case = workloads.custom(N, C, G, tuple(spatial), x_dtype, dy_dtype, dist=dist, seed=9500 + i)
+    return case, relu, layout
+
+
+CASES = [_draw(i) for i in range(32)] + [_draw_large(i) for i in range(16)]
 
 
 def _id(v):
