@@ -254,6 +254,10 @@ typedef struct gn_plan_info {
     int64_t fold_chunk;           /* elements per streaming job with the finalize folded in */
     int64_t fold_chunks_per_row;
     int64_t fold_jobs;            /* rows * fold_chunks_per_row */
+    /* Resident backward over N > 1 samples split into one workgroup per (n, g): each also
+     * sums the other samples' rows of its channels i (i mod N == n), so that dgamma and
+     * dbeta keep the bits of the one-workgroup-per-g form. */
+    int32_t resident_backward_split;
 } gn_plan_info;
 
 /* Fills *out for a valid shape and returns GN_OK; otherwise returns the shape error. */
@@ -368,7 +372,7 @@ int gn_backward_shard_merge(const float* sums /* [P][N*C][2] */, int64_t P,
 /* ABI version of this header (incremented on any incompatible change); gn_abi_version()
  * returns the version the library was built with, so a caller can check that the two
  * agree before the first call. */
-#define GN_ABI_VERSION 9
+#define GN_ABI_VERSION 10
 int gn_abi_version(void);
 
 #ifdef __cplusplus

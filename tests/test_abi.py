@@ -37,7 +37,7 @@ def test_status_enum_matches_header():
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == int(re.search(r"#define GN_ABI_VERSION (\d+)", text).group(1)) == 9
+    assert lib.gn_abi_version() == int(re.search(r"#define GN_ABI_VERSION (\d+)", text).group(1)) == 10
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every

@@ -258,7 +258,21 @@ def test_resident_choice_and_shape(N, C, S, G):
     if ef:
         _check_res_shape(M // VEC, p["resident_block_forward"], p["resident_vectors_forward"])
     if eb:
-        _check_res_shape(N * M // VEC, p["resident_block_backward"], p["resident_vectors_backward"])
+        assert p["resident_backward_split"] == int(N > 1)
+        nv = _split_max_vectors(N, C, S, G) if N > 1 else N * M // VEC
+        _check_res_shape(nv, p["resident_block_backward"], p["resident_vectors_backward"])
+    else:
+        assert p["resident_backward_split"] == 0
+
+
+def _split_ncol(N, Cg, n):
+    """Channels i of a group with i mod N == n."""
+    return (Cg - 1 - n) // N + 1 if Cg > n else 0
+
+
+def _split_max_vectors(N, C, S, G):
+    Cg, W = C // G, S // VEC
+    return Cg * W + (N - 1) * _split_ncol(N, Cg, 0) * W
 
 
 @pytest.mark.parametrize("N,C,S,G", [s for s in RES_SHAPES if s[0] * s[1] * s[2] <= 2 ** 22])
@@ -280,7 +294,9 @@ def test_resident_workgroups_cover_every_element_once_and_stay_in_bounds(N, C, S
             assert 0 <= (w // W).max() < Cg
             np.add.at(seen, vb + w, 1)
         assert (seen == 1).all()
-    if p["resident_backward"]:
+    if p["resident_backward"] and p["resident_backward_split"]:
+        _check_split_backward(N, C, S, G, p)
+    elif p["resident_backward"]:
         B, V = p["resident_block_backward"], p["resident_vectors_backward"]
         vg, W = M // VEC, S // VEC
         nvt, nrows = N * vg, N * Cg
@@ -295,6 +311,58 @@ def test_resident_workgroups_cover_every_element_once_and_stay_in_bounds(N, C, S
             gv = (n * C + gg * Cg) * W + r
             np.add.at(seen, gv, 1)
         assert (seen == 1).all()
+
+
+def _check_split_backward(N, C, S, G, p):
+    """res_bwd_split_kernel restated: workgroup (g, n) holds its own rows (n, g*Cg + rho),
+    vector rho*W + k, then column rows crow = idx(n')*ncol + j for each other sample n' (idx:
+    its rank among the others) and channel i = n + j*N, vector (Cg + crow)*W + k. Own
+    vectors cover the volume once; every (sample, channel) row of a group is summed for
+    dgamma exactly once, by the workgroup whose n is the channel's index mod N, in sample
+    order; every index stays inside the volume and the LDS arrays."""
+    Cg, W = C // G, S // VEC
+    B, V = p["resident_block_backward"], p["resident_vectors_backward"]
+    total = N * C * S // VEC
+    own = np.zeros(total, dtype=np.int32)
+    for gg in range(G):
+        dg_rows = {}
+        for n in range(N):
+            ncol = _split_ncol(N, Cg, n)
+            nrows = Cg + (N - 1) * ncol
+            nvt = nrows * W
+            assert nvt <= B * V and nvt <= RES_MAX_VECS and nrows <= RES_MAX_VECS
+            w = (np.arange(V)[:, None] * B + np.arange(B)[None, :]).reshape(-1)
+            w = w[w < nvt]
+            R, k = w // W, w % W
+            nr = np.where(R < Cg, n, 0)
+            c = np.where(R < Cg, gg * Cg + R, 0)
+            col = R >= Cg
+            if col.any():
+                crow = R[col] - Cg
+                ni, j = crow // ncol, crow % ncol
+                nr[col] = np.where(ni < n, ni, ni + 1)
+                c[col] = gg * Cg + n + j * N
+                assert ((n + j * N) < Cg).all() and (nr[col] != n).all()
+            gv = (nr * C + c) * W + k
+            assert gv.min() >= 0 and gv.max() < total
+            np.add.at(own, gv[~col], 1)
+            # rows each dgamma sum reads, in sample order
+            for jj in range(ncol):
+                i = n + jj * N
+                rows = [i if np_ == n else Cg + (np_ if np_ < n else np_ - 1) * ncol + jj for np_ in range(N)]
+                assert max(rows) < nrows
+                # the row index maps back to (np_, channel i)
+                for np_, Rr in enumerate(rows):
+                    if Rr < Cg:
+                        assert np_ == n and Rr == i
+                    else:
+                        cr = Rr - Cg
+                        ni2, j2 = cr // ncol, cr % ncol
+                        assert (ni2 if ni2 < n else ni2 + 1) == np_ and n + j2 * N == i
+                assert i not in dg_rows
+                dg_rows[i] = n
+        assert sorted(dg_rows) == list(range(Cg)) and all(dg_rows[i] == i % N for i in dg_rows)
+    assert (own == 1).all()
 
 
 # ----------------------------------------------------------------------------- channels-last

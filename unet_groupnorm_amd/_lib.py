@@ -44,6 +44,7 @@ class GnPlanInfo(ctypes.Structure):
         ("fold_chunk", ctypes.c_int64),
         ("fold_chunks_per_row", ctypes.c_int64),
         ("fold_jobs", ctypes.c_int64),
+        ("resident_backward_split", ctypes.c_int32),
     ]
 
 

@@ -170,7 +170,8 @@ int bwd_finish(const void* dy, int dy_dtype, const void* x, int x_dtype, const f
 {
     if (p.res_bwd)
         return launch_status(gn::launch_res_bwd(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
-                                                dbeta, dx, a, w, st, p.res_block_b, p.res_vecs_b));
+                                                dbeta, dx, a, w, st, p.res_block_b, p.res_vecs_b,
+                                                p.res_bwd_split));
     if (kFoldFinalize && dx)
         return launch_status(gn::launch_bwd_apply_fin(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
                                                       dbeta, dx, a, w, st));
@@ -217,6 +218,7 @@ int gn_plan_query(int64_t N, int64_t C, int64_t S, int64_t G, gn_plan_info* out)
     out->fold_chunk = p.chunk_f;
     out->fold_chunks_per_row = p.K_f;
     out->fold_jobs = p.jobs_f;
+    out->resident_backward_split = p.res_bwd_split ? 1 : 0;
     return GN_OK;
 }
 
@@ -354,7 +356,8 @@ int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p.res_bwd)
         return launch_status(gn::launch_res_bwd(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
-                                                dbeta, nullptr, a, w, st, p.res_block_b, p.res_vecs_b));
+                                                dbeta, nullptr, a, w, st, p.res_block_b, p.res_vecs_b,
+                                                p.res_bwd_split));
     return launch_status(gn::launch_bwd_reduce(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta,
                                                dgamma, dbeta, a, w, st));
 }

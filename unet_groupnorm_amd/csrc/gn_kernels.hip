@@ -1073,6 +1073,163 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
     }
 }
 
+// Backward split over samples, one workgroup per (g, n) = (blockIdx.x, blockIdx.y): the
+// results of res_bwd_kernel, bit for bit, from N times as many workgroups. The workgroup's
+// vectors are its own group (n, g), rows rho = 0 .. C/G - 1 (vector rho*W + k), then the
+// "column" rows: for each channel i of the group with i mod N == n (ncol of them) and each
+// other sample n' in order, row (n', g*C/G + i), at vector (C/G + crow)*W + k with
+// crow = (index of n' among the other samples)*ncol + (i - n)/N. Every row's per-vector
+// sums and row sums are computed exactly as res_bwd_kernel computes them, so the rows
+// both kernels sum agree bitwise; the workgroup then takes sample n's c1, c2 and dx, and
+// dgamma/dbeta of its channels over all samples, in the same order as res_bwd_kernel.
+template <int V, typename TX, typename TD>
+__global__ void __launch_bounds__(kResMaxBlock)
+res_bwd_split_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
+                     const float* __restrict__ rstd, const float* __restrict__ gamma,
+                     const float* __restrict__ beta, KArgs a, float4* __restrict__ coef,
+                     float* __restrict__ dgamma, float* __restrict__ dbeta, TX* __restrict__ dx)
+{
+    __shared__ float s_v1[kResMaxVecs], s_v2[kResMaxVecs];  // per vector
+    __shared__ float s_r1[kResMaxVecs], s_r2[kResMaxVecs];  // per row: own rows, then column rows
+    __shared__ float s_be[2];
+    const int tid = threadIdx.x, blk = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nw = blk >> 6;
+    const int W = int(a.S / kVec), Cg = int(a.Cg), N = int(a.N);
+    const int64_t g = blockIdx.x;
+    const int n = int(blockIdx.y);
+    const int ncol = Cg > n ? (Cg - 1 - n) / N + 1 : 0;
+    const int vg = Cg * W;
+    const int nrows = Cg + (N - 1) * ncol;
+    const int nvt = nrows * W;  // <= the plan's bound, within kResMaxVecs
+    const bool act = a.act != 0;
+    // Sample and channel of workgroup row R.
+    auto row_of = [&](int R, int& nr, int& c) {
+        if (R < Cg) {
+            nr = n;
+            c = int(g * Cg) + R;
+        } else {
+            const int crow = R - Cg, ni = crow / ncol, j = crow - ni * ncol;
+            nr = ni < n ? ni : ni + 1;
+            c = int(g * Cg) + n + j * N;
+        }
+    };
+    float xs[V * kVec], gs[V * kVec];
+    float mus[V], As[V];
+    int rows[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+        const int w = u * blk + tid;
+        rows[u] = -1;
+        mus[u] = 0.0f;
+        As[u] = 0.0f;
+        if (w < nvt) {
+            const int R = int(fdiv(uint32_t(w), a.div_W));
+            int nr, c;
+            row_of(R, nr, c);
+            const int64_t gv = (int64_t(nr) * a.C + c) * W + (w - R * W);
+            const int64_t ng = int64_t(nr) * a.G + g;
+            float e[kVec], f[kVec], d[kVec], q[kVec];
+            Io<TX>::template load8<kNtBwdApply>(x + gv * kVec, e);
+            Io<TD>::template load8<kNtBwdApply>(dy + gv * kVec, f);
+            const float mu = mean[ng];
+            const float A = rstd[ng] * (gamma ? gamma[c] : 1.0f);
+            const float bt = beta ? beta[c] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) {
+                d[i] = e[i] - mu;
+                q[i] = act ? relu_gate(fmaf(d[i], A, bt), f[i]) : f[i];
+                xs[u * kVec + i] = e[i];
+                gs[u * kVec + i] = q[i];
+            }
+            s_v1[w] = tree_sum(q);
+            s_v2[w] = tree_sumprod(q, d);
+            if (w < vg) {  // own vectors: kept for the dx
+                rows[u] = R;
+                mus[u] = mu;
+                As[u] = A;
+            }
+        }
+    }
+    __syncthreads();
+    for (int R = wave; R < nrows; R += nw) {
+        int nr, c;
+        row_of(R, nr, c);
+        const float rsn = rstd[int64_t(nr) * a.G + g];
+        float p1 = 0.0f, p2 = 0.0f;
+        for (int k = lane; k < W; k += 64) {
+            p1 = p1 + s_v1[R * W + k];
+            p2 = p2 + s_v2[R * W + k];
+        }
+        p1 = wave_allsum(p1);
+        p2 = wave_allsum(p2);
+        if (lane == 0) {
+            s_r1[R] = p1;
+            s_r2[R] = p2 * rsn;
+        }
+    }
+    __syncthreads();
+    const int64_t ngo = int64_t(n) * a.G + g;
+    if (wave == 0) {
+        const float rs = rstd[ngo];
+        float t1 = 0.0f, t2 = 0.0f;
+        for (int i = lane; i < Cg; i += 64) {
+            const float gm = gamma ? gamma[g * Cg + i] : 1.0f;
+            t1 = t1 + gm * s_r1[i];
+            t2 = t2 + gm * s_r2[i];
+        }
+        t1 = wave_allsum(t1);
+        t2 = wave_allsum(t2);
+        if (lane == 0) {
+            const float c1 = float(double(t1) / double(a.M));
+            const float c2 = float(double(t2) / double(a.M));
+            s_be[0] = -(rs * c1);
+            s_be[1] = -((rs * rs) * c2);
+        }
+    }
+    __syncthreads();
+    const float B = s_be[0], E = s_be[1];
+    for (int rho = tid; rho < Cg; rho += blk) {
+        const int64_t c = g * Cg + rho, row = int64_t(n) * a.C + c;
+        const float gm = gamma ? gamma[c] : 1.0f;
+        coef[2 * row] = make_float4(mean[ngo], rstd[ngo] * gm, B, E);
+        coef[2 * row + 1] = make_float4(beta ? beta[c] : 0.0f, a.M == 1 ? 1.0f : 0.0f, 0.0f, 0.0f);
+    }
+    if (dgamma || dbeta) {
+        for (int j = wave; j < ncol; j += nw) {
+            const int i = n + j * N;
+            float q1 = 0.0f, q2 = 0.0f;
+            for (int np = lane; np < N; np += 64) {
+                const int R = np == n ? i : Cg + (np < n ? np : np - 1) * ncol + j;
+                q1 = q1 + s_r2[R];
+                q2 = q2 + s_r1[R];
+            }
+            q1 = wave_allsum(q1);
+            q2 = wave_allsum(q2);
+            if (lane == 0) {
+                if (dgamma) dgamma[g * Cg + i] = q1;
+                if (dbeta) dbeta[g * Cg + i] = q2;
+            }
+        }
+    }
+    if (dx) {
+#pragma unroll
+        for (int u = 0; u < V; ++u) {
+            const int rho = rows[u];
+            if (rho >= 0) {
+                const int w = u * blk + tid;
+                const int64_t gv = (int64_t(n) * a.C + g * Cg + rho) * W + (w - rho * W);
+                float o[kVec];
+#pragma unroll
+                for (int i = 0; i < kVec; ++i) {
+                    const float d = xs[u * kVec + i] - mus[u];
+                    o[i] = fmaf(As[u], gs[u * kVec + i], fmaf(E, d, B));
+                }
+                Io<TX>::store8(dx + gv * kVec, o);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launchers
@@ -1252,7 +1409,7 @@ hipError_t launch_res_fwd(const void* x, int xdt, const float* gamma, const floa
 hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, const float* mean,
                           const float* rstd, const float* gamma, const float* beta, float* dgamma,
                           float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st,
-                          int block, int vecs)
+                          int block, int vecs, bool split)
 {
     return with_type(xdt, [&](auto tx) {
         return with_type(dydt, [&](auto td) {
@@ -1260,6 +1417,10 @@ hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, cons
                 using TX = decltype(tx);
                 using TD = decltype(td);
                 constexpr int V = decltype(v)::value;
+                if (split)
+                    return launch(res_bwd_split_kernel<V, TX, TD>, dim3(unsigned(a.G), unsigned(a.N)),
+                                  dim3(unsigned(block)), st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a,
+                                  ws.coef, dgamma, dbeta, mp<TX>(dx));
                 return launch(res_bwd_kernel<V, TX, TD>, dim3(unsigned(a.G)), dim3(unsigned(block)), st,
                               cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.coef, dgamma, dbeta,
                               mp<TX>(dx));

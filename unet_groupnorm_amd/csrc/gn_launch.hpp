@@ -107,11 +107,12 @@ hipError_t launch_res_fwd(const void* x, int xdt, const float* gamma, const floa
                           float* mean, float* rstd, void* y, int ydt, const KArgs& a, Workspace ws,
                           hipStream_t st, int block, int vecs);
 // Resident path, backward: dgamma/dbeta (either may be null), the per-row dx coefficients,
-// and dx unless dx is null.
+// and dx unless dx is null; one workgroup per g over all samples, or with split one per
+// (n, g) (the same bits).
 hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, const float* mean,
                           const float* rstd, const float* gamma, const float* beta, float* dgamma,
                           float* dbeta, void* dx, const KArgs& a, Workspace ws, hipStream_t st,
-                          int block, int vecs);
+                          int block, int vecs, bool split);
 
 // The partial reductions alone (one float2 per reduction job in ws.part).
 hipError_t launch_stats_partials(const void* x, int xdt, const KArgs& a, Workspace ws, hipStream_t st);

@@ -104,7 +104,14 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
         }
         if (N <= kResMaxVecs / vg) {
             q.res_bwd = true;
-            resident_shape(N * vg, &q.res_block_b, &q.res_vecs_b);
+            if (GN_RES_SPLIT && N > 1) {
+                // the largest workgroup: its own vg vectors plus, for n = 0, ceil(Cg/N)
+                // channels of each of the other N - 1 samples
+                q.res_bwd_split = true;
+                resident_shape(vg + (N - 1) * ceil_div(Cg, N) * (S / kVec), &q.res_block_b, &q.res_vecs_b);
+            } else {
+                resident_shape(N * vg, &q.res_block_b, &q.res_vecs_b);
+            }
         }
     }
 

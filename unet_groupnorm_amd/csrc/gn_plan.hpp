@@ -63,6 +63,9 @@ constexpr int kApplyVecs = GN_APPLY_VECS;
 #ifndef GN_RESIDENT
 #define GN_RESIDENT 1
 #endif
+#ifndef GN_RES_SPLIT
+#define GN_RES_SPLIT 1
+#endif
 constexpr int kResMaxBlock = 1024;
 constexpr int kResMaxLaneVecs = 4;
 constexpr int64_t kResMaxVecs = int64_t(kResMaxBlock) * kResMaxLaneVecs;  // 32768 elements
@@ -105,6 +108,10 @@ struct Plan {
     bool res_fwd = false, res_bwd = false;
     int res_block_f = 0, res_vecs_f = 0;   // threads, vectors per lane (1, 2 or 4)
     int res_block_b = 0, res_vecs_b = 0;
+    // backward split over samples (N > 1): one workgroup per (n, g) instead of per g, which
+    // also sums the rows of the other samples for its share of the group's channels
+    // (channels i with i mod N == n), so that dgamma/dbeta still come from one workgroup
+    bool res_bwd_split = false;
     // workspace: [partials: float2 * jobs][row coefficients: 2 float4 * rows], 256-byte aligned
     size_t ws_coef_offset = 0;
     size_t ws_bytes = 0;
