@@ -683,6 +683,10 @@ RESIDENT = [
     (workloads.custom(2, 64, 1, (2, 2, 2), torch.float32, dist="tiny", seed=46), True, True),       # one vector per row
     (workloads.custom(2, 16, 16, (2, 2, 2), torch.bfloat16, dist="deep", seed=47, out_dtype=torch.float32), True, True),
     (workloads.custom(3, 12, 4, (4, 4, 6), torch.bfloat16, torch.float32, dist="deep", seed=48), True, True),
+    # backward split over samples: one workgroup gathers all 511 other samples' rows of its channel
+    (workloads.custom(512, 2, 2, (8,), torch.bfloat16, dist="unet", seed=49), True, True),
+    # C/G = 2 < N = 64: most (n, g) workgroups own no dgamma channel
+    (workloads.custom(64, 4, 2, (2, 2, 2), torch.float32, dist="normal", seed=50), True, True),
 ]
 
 
