@@ -15,6 +15,9 @@ namespace gn {
 
 namespace {
 
+// Records or sums a merge workgroup stages in LDS before its thread 0 merges them in order.
+constexpr int64_t kShardStage = 256;
+
 // The shift of group (n, g) within the shard: its first element, 0 if not finite.
 template <typename T>
 __device__ __forceinline__ float shard_shift(const T* __restrict__ x, const KArgs& a, int64_t n, int64_t g)
@@ -68,15 +71,23 @@ shard_merge_fwd_kernel(const Moments16* __restrict__ rec, int64_t P, const float
                        float* __restrict__ rstd_out, KArgs a, float4* __restrict__ coef)
 {
     __shared__ float s_stat[3];
+    __shared__ Moments16 s_rec[kShardStage];
     const int64_t ng = blockIdx.x;
     const int64_t n = ng / a.G, g = ng - n * a.G;
     const int64_t NG = a.N * a.G;
+    // The group's records staged in LDS by all threads at once (thread 0's merge then reads
+    // them in order without waiting on one global load at a time).
+    const bool staged = P <= kShardStage;
+    if (staged) {
+        for (int64_t p = threadIdx.x; p < P; p += blockDim.x) s_rec[p] = rec[p * NG + ng];
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
-        const float k0 = rec[ng].mean_hi;
+        const float k0 = staged ? s_rec[0].mean_hi : rec[ng].mean_hi;
         const float K = __builtin_isfinite(k0) ? k0 : 0.0f;
         Moments<uint64_t> acc = {0ull, 0.0f, 0.0f};
         for (int64_t p = 0; p < P; ++p) {
-            const Moments16 r = rec[p * NG + ng];
+            const Moments16 r = staged ? s_rec[p] : rec[p * NG + ng];
             chan_merge(acc, uint64_t(r.count), (r.mean_hi - K) + r.mean_lo, r.m2);
         }
         float var = float(double(acc.M2) / double(acc.n));
@@ -128,22 +139,34 @@ shard_merge_bwd_kernel(const float2* __restrict__ sums, int64_t P, const float* 
                        float* __restrict__ dbeta)
 {
     __shared__ float s_coef[2];
+    __shared__ float2 s_sum[kShardStage];
+    __shared__ float s_gm[kShardStage];
     const int64_t w = blockIdx.x;
     const int64_t NC = a.N * a.C;
     if (w < ngroups) {
         const int64_t n = w / a.G, g = w - n * a.G;
         const float mu = mean[w], rs = rstd[w];
+        // The group's (shard, channel) sums and gammas staged in LDS, [i][p], by all threads.
+        const bool staged = a.Cg * P <= kShardStage;
+        if (staged) {
+            for (int64_t q = threadIdx.x; q < a.Cg * P; q += blockDim.x) {
+                const int64_t i = q / P, p = q - i * P;
+                s_sum[q] = sums[p * NC + n * a.C + g * a.Cg + i];
+            }
+            for (int64_t i = threadIdx.x; i < a.Cg; i += blockDim.x) s_gm[i] = gamma ? gamma[g * a.Cg + i] : 1.0f;
+            __syncthreads();
+        }
         if (threadIdx.x == 0) {
             float t1 = 0.0f, t2 = 0.0f;
             for (int64_t i = 0; i < a.Cg; ++i) {
                 const int64_t c = g * a.Cg + i;
                 float s1 = 0.0f, s2 = 0.0f;
                 for (int64_t p = 0; p < P; ++p) {
-                    const float2 v = sums[p * NC + n * a.C + c];
+                    const float2 v = staged ? s_sum[i * P + p] : sums[p * NC + n * a.C + c];
                     s1 = s1 + v.x;
                     s2 = s2 + v.y;
                 }
-                const float gm = gamma ? gamma[c] : 1.0f;
+                const float gm = staged ? s_gm[i] : (gamma ? gamma[c] : 1.0f);
                 t1 = t1 + gm * s1;
                 t2 = t2 + gm * s2;
             }
@@ -159,18 +182,29 @@ shard_merge_bwd_kernel(const float2* __restrict__ sums, int64_t P, const float* 
             coef[2 * (n * a.C + c)] = make_float4(mu, rs * gm, B, E);
             coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, M_total == 1 ? 1.0f : 0.0f, 0.0f, 0.0f);
         }
-    } else if (w < ngroups + nchan && threadIdx.x == 0) {
+    } else if (w < ngroups + nchan) {
         const int64_t c = w - ngroups;
-        float q1 = 0.0f, q2 = 0.0f;
-        for (int64_t n = 0; n < a.N; ++n) {
-            for (int64_t p = 0; p < P; ++p) {
-                const float2 v = sums[p * NC + n * a.C + c];
-                q1 = q1 + v.y;
-                q2 = q2 + v.x;
+        // The channel's (sample, shard) sums staged in LDS, [n][p], by all threads.
+        const bool staged = a.N * P <= kShardStage;
+        if (staged) {
+            for (int64_t q = threadIdx.x; q < a.N * P; q += blockDim.x) {
+                const int64_t n = q / P, p = q - n * P;
+                s_sum[q] = sums[p * NC + n * a.C + c];
             }
+            __syncthreads();
         }
-        if (dgamma) dgamma[c] = q1;
-        if (dbeta) dbeta[c] = q2;
+        if (threadIdx.x == 0) {
+            float q1 = 0.0f, q2 = 0.0f;
+            for (int64_t n = 0; n < a.N; ++n) {
+                for (int64_t p = 0; p < P; ++p) {
+                    const float2 v = staged ? s_sum[n * P + p] : sums[p * NC + n * a.C + c];
+                    q1 = q1 + v.y;
+                    q2 = q2 + v.x;
+                }
+            }
+            if (dgamma) dgamma[c] = q1;
+            if (dbeta) dbeta[c] = q2;
+        }
     }
 }
 
