@@ -11,6 +11,7 @@ gn_forward and gn_backward take either and return outputs in the input's layout;
 split-phase entry points take NCDHW only.
 """
 import ctypes
+import math
 
 import torch
 
@@ -34,13 +35,10 @@ def _check(fn, status):
 
 
 def _dims(x, G):
-    if x.dim() < 2:
+    sh = x.shape
+    if len(sh) < 2:
         raise ValueError("GroupNorm input needs at least (N, C)")
-    N, C = int(x.shape[0]), int(x.shape[1])
-    S = 1
-    for d in x.shape[2:]:
-        S *= int(d)
-    return N, C, S, int(G)
+    return sh[0], sh[1], math.prod(sh[2:]), int(G)
 
 
 def _act(activation):
@@ -121,6 +119,24 @@ def _vec(name, t, C, dev):
     return _contig(name, t)
 
 
+# The per-step calls (gn_forward, gn_backward) check devices by index (x.get_device(): the
+# GPU's ordinal, -1 on the host), which costs less than building torch.device objects.
+def _vec_ptr(name, t, C, didx):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() != C or t.get_device() != didx or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of {C} elements on x's device")
+    return t.data_ptr()
+
+
+def _stream_of(didx):
+    if didx < 0:
+        return None
+    if _raw_stream is not None:
+        return _raw_stream(didx)
+    return torch.cuda.current_stream(didx).cuda_stream
+
+
 def gn_workspace_bytes(N, C, S, G, layout="ncdhw"):
     fn = lib.gn_workspace_bytes if layout == "ncdhw" else lib.gn_workspace_bytes_cl
     return int(fn(N, C, S, G))
@@ -159,19 +175,19 @@ def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, activation=None, 
     narrowing store). layout: None (from x's strides), "ncdhw" or "ndhwc"."""
     layout = _layout_arg(x, layout)
     N, C, S, G = _dims(x, G)
-    dev = x.device
+    didx = x.get_device()
     out_dtype = out_dtype or x.dtype
     y = out if out is not None else torch.empty_like(x, dtype=out_dtype)
     if y.shape != x.shape or y.stride() != x.stride():
         raise ValueError("out must have x's shape and layout")
-    mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
-    rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
+    mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
+    rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
     ws = workspace if workspace is not None else workspace_for(x, G, layout)
     fn, name = (lib.gn_forward, "gn_forward") if layout == "ncdhw" else (lib.gn_forward_cl, "gn_forward_cl")
     _check(name, fn(
-        _ptr(x), _dtype(x), _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
-        N, C, S, G, float(eps), _act(activation), _ptr(y), _dtype(y), _ptr(mean),
-        _ptr(rstd), _ptr(ws), ws.numel(), _stream(dev)))
+        x.data_ptr(), _dtype(x), _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx),
+        N, C, S, G, float(eps), _act(activation), y.data_ptr(), _dtype(y), mean.data_ptr(),
+        rstd.data_ptr(), ws.data_ptr(), ws.numel(), _stream_of(didx)))
     return y, mean, rstd
 
 
@@ -204,23 +220,23 @@ def gn_backward(dy, x, mean, rstd, gamma, G, *, beta=None, activation=None, need
     if dy.shape != x.shape or dy.stride() != x.stride():
         raise ValueError("dy must have x's shape and layout")
     N, C, S, G = _dims(x, G)
-    dev = x.device
+    didx = x.get_device()
     if need_dx and dx is None:
         dx = torch.empty_like(x)
     if need_dx and dx.stride() != x.stride():
         raise ValueError("dx must have x's layout")
     if need_dgamma and dgamma is None:
-        dgamma = torch.empty(C, dtype=torch.float32, device=dev)
+        dgamma = torch.empty(C, dtype=torch.float32, device=x.device)
     if need_dbeta and dbeta is None:
-        dbeta = torch.empty(C, dtype=torch.float32, device=dev)
+        dbeta = torch.empty(C, dtype=torch.float32, device=x.device)
     ws = workspace if workspace is not None else workspace_for(x, G, layout)
     fn, name = (lib.gn_backward, "gn_backward") if layout == "ncdhw" else (lib.gn_backward_cl, "gn_backward_cl")
     _check(name, fn(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
+        dy.data_ptr(), _dtype(dy), x.data_ptr(), _dtype(x), _ptr(mean), _ptr(rstd),
+        _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), _act(activation),
         N, C, S, G,
         _ptr(dx if need_dx else None), _ptr(dgamma if need_dgamma else None),
-        _ptr(dbeta if need_dbeta else None), _ptr(ws), ws.numel(), _stream(dev)))
+        _ptr(dbeta if need_dbeta else None), ws.data_ptr(), ws.numel(), _stream_of(didx)))
     return (dx if need_dx else None, dgamma if need_dgamma else None, dbeta if need_dbeta else None)
 
 
