@@ -146,7 +146,7 @@ constexpr int kClRounds = 4;        // voxel rounds a reduction lane holds per s
 constexpr int kClResMaxGroupVecs = 8;
 constexpr int kClResMaxRows = 512;
 constexpr int64_t kClResMaxVecs = 1024;
-constexpr int kClApplyRounds = 4;   // voxel rounds of a streaming job
+constexpr int kClApplyRounds = 2;   // voxel rounds of a streaming job (measured: 1, 4, 8 and 16 slower)
 
 struct PlanCL {
     int64_t N = 0, C = 0, S = 0, G = 0;
