@@ -37,8 +37,11 @@ constexpr int kVec = 8;
 #ifndef GN_LONG_CHUNK
 #define GN_LONG_CHUNK 262144
 #endif
+// Vectors per lane of the one-step streaming kernels (split-phase and spatial-shard calls).
+// Measured on one rank's share of the 256^3 site split in 8: 1 vector 187.3 us a step,
+// 2 vectors 176.0, 4 vectors 181.2.
 #ifndef GN_APPLY_VECS
-#define GN_APPLY_VECS 1
+#define GN_APPLY_VECS 2
 #endif
 // Largest reduction workgroup (threads); the plan sizes smaller ones to short rows.
 #ifndef GN_RED_BLOCK
