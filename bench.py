@@ -440,7 +440,45 @@ def cpu_baseline(runner, min_seconds=10.0, max_reps=40):
         "seconds_per_step": round(per, 3),
         "host_cpu": _cpu_model(),
         "host_cores_available": os.cpu_count(),
+        "threads": _oracle_threads(runner),
     }
+
+
+def _oracle_threads(runner, min_seconds=5.0, max_reps=60):
+    """The same oracle spread over the host's cores: each (n, g) group, taken as its channel
+    slice, is a GroupNorm with one group, so one oracle call per group (forward, then
+    backward) runs in a thread pool (the oracle's C calls release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from oracle import oracle as O
+    x, dy = runner.x.cpu(), runner.dy.cpu()
+    gamma, beta = runner.gamma.cpu(), runner.beta.cpu()
+    G, eps, N, C = runner.G, runner.eps, runner.case.N, runner.case.C
+    Cg = C // G
+    units = [(n, g) for n in range(N) for g in range(G)]
+    slices = [(x[n:n + 1, g * Cg:(g + 1) * Cg].contiguous(), dy[n:n + 1, g * Cg:(g + 1) * Cg].contiguous(),
+               gamma[g * Cg:(g + 1) * Cg], beta[g * Cg:(g + 1) * Cg]) for n, g in units]
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    workers = max(1, min(cores, 16, len(units)))
+
+    def one(u):
+        xs, ds, gs, bs = u
+        O.forward(xs, 1, gs, bs, eps=eps)
+        O.backward(ds, xs, 1, gs, eps=eps)
+
+    reps, t_total = 0, 0.0
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        while reps < max_reps and (reps == 0 or t_total < min_seconds):
+            t0 = time.perf_counter()
+            list(pool.map(one, slices))
+            t_total += time.perf_counter() - t0
+            reps += 1
+    per = t_total / reps
+    return {"value": round(runner.step_bytes / per / 1e9, 3), "unit": "GB/s", "cores": workers,
+            "sample": (f"the same volume as {len(units)} one-group oracle calls (one per (n, g) "
+                       f"group), forward + backward, on {workers} threads, {reps} repetition(s), "
+                       f"{per:.3f} s each"),
+            "seconds_per_step": round(per, 3)}
 
 
 def _cpu_model():
