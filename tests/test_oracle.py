@@ -417,3 +417,47 @@ def test_relu_keeps_negative_zero_and_nan_group_gradient():
     assert np.isfinite(db_t).all() and np.allclose(b["dbeta"], db_t, rtol=1e-12)
     assert np.array_equal(np.isnan(b["dx"]), np.isnan(dx_t))
     assert np.array_equal(np.isnan(b["dgamma"]), np.isnan(dg_t))
+
+
+# ----------------------------------------------------------------------------- gradient magnitudes
+
+def _abs_sums_torch(x, dy, G, gamma, beta, eps, relu):
+    """sum |g| and sum |g * xhat| per channel, entirely in torch float64: the statistics from
+    torch's mean and biased var, and with relu the gradient that reaches the affine output
+    taken from torch's autograd through relu."""
+    N, C = x.shape[:2]
+    x64, dy64 = x.to(torch.float64), dy.to(torch.float64)
+    xg = x64.reshape(N, G, -1)
+    mean = xg.mean(-1)
+    rstd = 1.0 / torch.sqrt(xg.var(-1, unbiased=False) + float(np.float32(eps)))
+    xhat = ((xg - mean[..., None]) * rstd[..., None]).reshape(x.shape)
+    bshape = (1, C) + (1,) * (x.dim() - 2)
+    g = dy64
+    if relu:
+        pre = (xhat * gamma.to(torch.float64).view(bshape) + beta.to(torch.float64).view(bshape))
+        pre.requires_grad_(True)
+        (g,) = torch.autograd.grad(torch.relu(pre), pre, dy64)
+    dims = (0,) + tuple(range(2, x.dim()))
+    return (g.abs().sum(dims).numpy(), (g * xhat).abs().sum(dims).numpy(), mean.numpy(), rstd.numpy(),
+            float((g == 0).double().mean()))
+
+
+@pytest.mark.parametrize("relu", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
+def test_channel_abs_sums_against_torch_autograd(dtype, relu):
+    """The magnitudes that scale every dgamma/dbeta tolerance: per channel sum |g| and
+    sum |g * xhat| over the samples and voxels, g = dy or the relu-gated dy. Checked against
+    torch float64 with its own statistics (passed to the oracle as its mean/rstd inputs) and,
+    with relu, torch autograd's gate; channels of one group and samples all differ."""
+    case = workloads.custom(3, 12, 4, (5, 6, 7), dtype, dist="tiny", seed=77)
+    inp = workloads.make(case, "cpu")
+    x, dy, G, eps = inp["x"], inp["dy"], inp["G"], inp["eps"]
+    gamma, beta = inp["gamma"], inp["beta"]
+    ea, eb, mean, rstd, zero_frac = _abs_sums_torch(x, dy, G, gamma, beta, eps, relu)
+    a, b = O.channel_abs_sums(dy, x, G, mean, rstd, gamma=gamma, beta=beta, relu=relu)
+    assert a.shape == b.shape == (12,)
+    assert np.allclose(a, ea, rtol=1e-12, atol=0.0)
+    assert np.allclose(b, eb, rtol=1e-12, atol=0.0)
+    # the gate did something, and every channel's magnitude is distinct
+    assert (zero_frac > 0.2) if relu else (zero_frac == 0.0)
+    assert len(set(np.round(a, 9))) == 12 and len(set(np.round(b, 9))) == 12

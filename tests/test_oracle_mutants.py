@@ -11,6 +11,7 @@ import os
 import subprocess
 
 import pytest
+import torch
 
 import tests.test_oracle as pins
 from oracle import oracle as O
@@ -47,6 +48,22 @@ MUTANTS = {
     "f16_no_subnormals": ("if (e == 0) v = ldexp((double)f, -24);", "if (e == 0) v = 0.0;"),
     "f16_precision": ("int q = (e - 1) - 10;    /* quantum", "int q = (e - 1) - 9;    /* quantum"),
     "f16_overflow_edge": ("if (r >= 65536.0) return", "if (r >= 65504.0) return"),
+    # the per-channel magnitudes behind every dgamma/dbeta bar (gno_channel_abs_sums)
+    "abs_sums_times_2": ("a += fabs(g_);", "a += 2.0 * fabs(g_);"),
+    "abs_sums_times_100": ("abs_dy[c] += a;\n            abs_dyxhat[c] += b;",
+                           "abs_dy[c] += 100.0 * a;\n            abs_dyxhat[c] += 100.0 * b;"),
+    "abs_sums_gate_dropped": ("if (act) g_ = gno_gate(gno_relu(gno_gamma(gamma, c) * xhat + gno_beta(beta, c)), g_);\n"
+                              "                a +=", "a +="),
+    "abs_sums_no_rstd": ("(gno_load(x, x_dt, base + s) - mean[ng]) * rstd[ng];",
+                         "(gno_load(x, x_dt, base + s) - mean[ng]);"),
+    "abs_sums_channel_index": ("const int64_t ng = n * G + c / Cg;\n            const int64_t base = (n * C + c) * S;\n"
+                               "            double a = 0.0, b = 0.0;",
+                               "const int64_t ng = n * G + c / Cg;\n            const int64_t base = (n * C + (c + 1) % C) * S;\n"
+                               "            double a = 0.0, b = 0.0;"),
+    "abs_sums_group_index": ("const int64_t ng = n * G + c / Cg;\n            const int64_t base = (n * C + c) * S;\n"
+                             "            double a = 0.0, b = 0.0;",
+                             "const int64_t ng = n * G + c % G;\n            const int64_t base = (n * C + c) * S;\n"
+                             "            double a = 0.0, b = 0.0;"),
 }
 
 PINS = [
@@ -67,6 +84,8 @@ PINS = [
     lambda: pins.test_against_torch_float64_group_norm("f16"),
     pins.test_relu_option_against_torch_autograd,
     pins.test_relu_keeps_negative_zero_and_nan_group_gradient,
+    lambda: pins.test_channel_abs_sums_against_torch_autograd(torch.bfloat16, False),
+    lambda: pins.test_channel_abs_sums_against_torch_autograd(torch.float16, True),
 ]
 
 
