@@ -12,45 +12,22 @@
 
 #include "gn_launch.hpp"
 
-// Load cache policy per kernel (1: nontemporal) and the order of the streaming grid
-// (1: last row first); compile-time overridable for measurement builds.
-#ifndef GN_NT_STATS
-#define GN_NT_STATS 1
-#endif
-#ifndef GN_NT_BRED
-#define GN_NT_BRED 1
-#endif
-#ifndef GN_NT_APPLY
-#define GN_NT_APPLY 1
-#endif
-#ifndef GN_NT_BAPPLY
-#define GN_NT_BAPPLY 1
-#endif
-#ifndef GN_REVERSE_APPLY
-#define GN_REVERSE_APPLY 0
-#endif
-#ifndef GN_NT_STORE
-#define GN_NT_STORE 0
-#endif
-// Store policy of the NCDHW streaming kernels, folded and one-step (1: nontemporal), which
-// differs from GN_NT_STORE's default for the channels-last and resident kernels. Measured on
-// MI355X: the folded kernels about 7% faster at 256^3; on a step of one-step kernels (the
-// spatial-shard entry points, 1x32x32x256^2 bf16) plain stores left y and dx dirty in the
-// last-level cache for the next plain-load reduction to write back (239.8 -> 198.7 us a
-// step); the channels-last step went 189 -> 198 us and the resident deep config 15.9 ->
-// 16.7 us with nontemporal stores, so they keep plain ones.
-#ifndef GN_NT_STORE_STREAM
-#define GN_NT_STORE_STREAM 1
-#endif
-
 namespace gn {
 
 namespace {
 
-constexpr bool kNtStats = GN_NT_STATS, kNtBwdReduce = GN_NT_BRED;
-constexpr bool kNtApply = GN_NT_APPLY, kNtBwdApply = GN_NT_BAPPLY;
-constexpr bool kReverseApply = GN_REVERSE_APPLY;
-constexpr bool kNtStore = GN_NT_STORE, kNtStoreStream = GN_NT_STORE_STREAM;
+// Load policy of the streamed tensors per kernel (true: nontemporal), used where the host
+// has not chosen plain loads for a volume that fits the last-level cache.
+constexpr bool kNtStats = true, kNtBwdReduce = true;
+constexpr bool kNtApply = true, kNtBwdApply = true;
+// Store policy: plain stores by default (the channels-last and resident kernels), and
+// nontemporal ones in the NCDHW streaming kernels, folded and one-step. Measured on MI355X:
+// the folded kernels about 7% faster at 256^3 with nontemporal stores; on a step of one-step
+// kernels (the spatial-shard entry points, 1x32x32x256^2 bf16) plain stores left y and dx
+// dirty in the last-level cache for the next plain-load reduction to write back (239.8 ->
+// 198.7 us a step); the channels-last step went 189 -> 198 us and the resident deep config
+// 15.9 -> 16.7 us with nontemporal stores, so they keep plain ones.
+constexpr bool kNtStore = false, kNtStoreStream = true;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

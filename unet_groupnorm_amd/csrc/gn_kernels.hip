@@ -40,9 +40,9 @@
 // tile (tile mean, then sum of squared deviations minus the squared sum of deviations over
 // n), merges tiles with Chan's parallel formula, then lanes merge in a fixed shuffle tree
 // and waves in a fixed order through LDS ("Optimize GroupNorm", paragraph introducing the
-// NDHWC kernel: corrected two-pass per tile combined by Chan's formula, register-only
-// reductions, fixed order, no float atomics). No atomics are used anywhere, so every
-// result is bitwise reproducible run to run.
+// NDHWC kernel, which takes the same route: per-tile two-pass moments, Chan merges, sums
+// kept in registers and combined in one order, no floating-point atomics). No atomics are
+// used anywhere, so every result is bitwise reproducible run to run.
 #include "gn_device.hpp"
 
 namespace gn {
@@ -50,21 +50,6 @@ namespace gn {
 namespace {
 
 // ------------------------------------------------------------------ job geometry
-
-// Workgroup -> job order. The dispatcher hands consecutive workgroups to the 8 XCDs in
-// turn; with GN_XCD_REMAP the workgroups of one XCD take one contiguous eighth of the jobs
-// (a bijection when the grid covers the jobs exactly and their count is a multiple of 8).
-#ifndef GN_XCD_REMAP
-#define GN_XCD_REMAP 0
-#endif
-#ifndef GN_XCD_REMAP_RED
-#define GN_XCD_REMAP_RED 0
-#endif
-__device__ __forceinline__ int64_t xcd_job(int64_t b, int64_t jobs, bool on)
-{
-    if (!on || (jobs & 7) != 0 || int64_t(gridDim.x) != jobs) return b;
-    return (b & 7) * (jobs >> 3) + (b >> 3);
-}
 
 struct Job {
     int64_t row, k;   // row = n*C + c, job index within the row
@@ -226,19 +211,8 @@ __device__ __forceinline__ void stats_masked_step(const TX* __restrict__ x, cons
 // The full steps are software-pipelined: the next step's vectors are requested before
 // the current step is reduced, alternating between two register sets so that waiting for
 // one set leaves the other in flight.
-// Waves per SIMD the statistics kernel is compiled for (0: the compiler's choice);
-// compile-time overridable for measurement builds.
-#ifndef GN_STATS_WAVES
-#define GN_STATS_WAVES 0
-#endif
-#if GN_STATS_WAVES > 0
-#define GN_STATS_BOUNDS __launch_bounds__(kRedBlock, GN_STATS_WAVES)
-#else
-#define GN_STATS_BOUNDS __launch_bounds__(kRedBlock)
-#endif
-
 template <typename TX, bool NT>
-__global__ void GN_STATS_BOUNDS
+__global__ void __launch_bounds__(kRedBlock)
 stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
 {
     using Raw = typename Io<TX>::Raw;
@@ -248,7 +222,7 @@ stats_kernel(const TX* __restrict__ x, KArgs a, float2* __restrict__ part)
     const int64_t stepv = int64_t(blk) * kStepVecs;
 
     for (int64_t wb = blockIdx.x; wb < a.jobs; wb += gridDim.x) {
-        const int64_t j = xcd_job(wb, a.jobs, GN_XCD_REMAP_RED);
+        const int64_t j = wb;
         const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, g = (jb.row - n * a.C) / a.Cg;
         const float K = group_shift(x, a, n, g);
@@ -363,17 +337,8 @@ fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
 }
 
 // Vectors per lane per step of the folded streaming kernels, and the waves per SIMD they
-// are compiled for (their register cap).
-#ifndef GN_FIN_VECS
-#define GN_FIN_VECS 2
-#endif
-constexpr int kFinVecs = GN_FIN_VECS;
-#ifndef GN_FIN_WAVES_F
-#define GN_FIN_WAVES_F 4
-#endif
-#ifndef GN_FIN_WAVES_B
-#define GN_FIN_WAVES_B 3
-#endif
+// are compiled for (their register cap): forward 4, backward 3.
+constexpr int kFinVecs = 2;
 
 // The normalize of one element: ((x - hi) - lo) * gamma*rstd + beta, then the relu.
 struct Affine {
@@ -414,8 +379,7 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kApplyVecs;
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
-        const int64_t jx = xcd_job(jj, a.jobs_a, GN_XCD_REMAP);
-        const int64_t j = kReverseApply ? a.jobs_a - 1 - jx : jx;
+        const int64_t j = jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row];
         const Affine f = {cf.x, cf.y, cf.z, cf.w, a.act != 0};
@@ -451,7 +415,7 @@ __device__ __forceinline__ void apply_full_step(const typename Io<TX>::Raw (&r)[
 // coefficients. The job's first full step is requested before the merge so that its
 // latency overlaps it; the full steps are software-pipelined as in stats_kernel.
 template <typename TX, typename TY, bool NT>
-__global__ void __launch_bounds__(256, GN_FIN_WAVES_F)
+__global__ void __launch_bounds__(256, 4)
 apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
                  float eps, const float2* __restrict__ part, float* __restrict__ mean_out,
                  float* __restrict__ rstd_out, KArgs a, float4* __restrict__ coef, TY* __restrict__ y)
@@ -462,7 +426,7 @@ apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, cons
     constexpr int V = kFinVecs;
     const int64_t stepv = int64_t(blk) * V;
     for (int64_t jj = blockIdx.x; jj < a.jobs_f; jj += gridDim.x) {
-        const int64_t j = kReverseApply ? a.jobs_f - 1 - jj : jj;
+        const int64_t j = jj;
         const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg;
         int64_t fs, fe, nsteps;
@@ -560,7 +524,7 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
     const int64_t stepv = int64_t(blk) * kStepVecs;
 
     for (int64_t wb = blockIdx.x; wb < a.jobs; wb += gridDim.x) {
-        const int64_t j = xcd_job(wb, a.jobs, GN_XCD_REMAP_RED);
+        const int64_t j = wb;
         const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, ng = n * a.G + c / a.Cg;
         const float mu = mean[ng];
@@ -734,8 +698,7 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kApplyVecs;
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
-        const int64_t jx = xcd_job(jj, a.jobs_a, GN_XCD_REMAP);
-        const int64_t j = kReverseApply ? a.jobs_a - 1 - jx : jx;
+        const int64_t j = jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row], cg = coef[2 * jb.row + 1];
         const bool act = a.act != 0;
@@ -772,7 +735,7 @@ __device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V]
 // rows' coefficient records; the first job of channel c in sample 0 writes dgamma_c and
 // dbeta_c, summed exactly as fin_bwd_kernel sums them.
 template <typename TX, typename TD, bool NT>
-__global__ void __launch_bounds__(256, GN_FIN_WAVES_B)
+__global__ void __launch_bounds__(256, 3)
 bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                      const float* __restrict__ rstd, const float* __restrict__ gamma,
                      const float* __restrict__ beta, const float2* __restrict__ part, KArgs a,
@@ -787,7 +750,7 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
     constexpr int V = kFinVecs;
     const int64_t stepv = int64_t(blk) * V;
     for (int64_t jj = blockIdx.x; jj < a.jobs_f; jj += gridDim.x) {
-        const int64_t j = kReverseApply ? a.jobs_f - 1 - jj : jj;
+        const int64_t j = jj;
         const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg, ng = n * a.G + g;
         int64_t fs, fe, nsteps;

@@ -1,9 +1,9 @@
 // gn_kernels_cl.hip -- GroupNorm over channels-last (NDHWC) activations on gfx950.
 //
 // "Optimize GroupNorm" (LBANN/ScaFFold pull 93), paragraph introducing the NDHWC kernel:
-// a dense run of voxels, all channels of each, yields the statistics of every group in
-// one coalesced pass, where walking the logical NCDHW order over channels-last memory is
-// a gather with a stride of C.
+// reading a contiguous span of voxels with every channel of each gives all groups'
+// statistics in one coalesced sweep; visiting channels-last memory channel by channel
+// instead would read with a stride of C.
 //
 // x[n][s][c] sits at (n*S + s)*C + c with C a multiple of 8, so a voxel is C/8 whole
 // vectors. Lane t of a workgroup owns channel vector cv = t mod (C/8) (channels 8cv ..

@@ -96,7 +96,7 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
     // Resident path: rows of whole vectors (so every vector lies in one row and every row
     // starts on a vector) and a workgroup's share within kResMaxVecs.
     // The forward's grid is (G, N), so N stays within the y extent every device accepts.
-    if (GN_RESIDENT && S % kVec == 0 && G <= (int64_t(1) << 30)) {
+    if (S % kVec == 0 && G <= (int64_t(1) << 30)) {
         const int64_t vg = q.M / kVec;
         if (vg <= kResMaxVecs && N <= 65535) {
             q.res_fwd = true;
@@ -104,7 +104,7 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p)
         }
         if (N <= kResMaxVecs / vg) {
             q.res_bwd = true;
-            if (GN_RES_SPLIT && N > 1) {
+            if (N > 1) {
                 // the largest workgroup: its own vg vectors plus, for n = 0, ceil(Cg/N)
                 // channels of each of the other N - 1 samples
                 q.res_bwd_split = true;
@@ -167,7 +167,7 @@ int make_plan_cl(int64_t N, int64_t C, int64_t S, int64_t G, PlanCL* p)
     // workgroup; the backward's workgroup also holds all samples, whose vectors start on
     // wave boundaries (S * C/(8G) a multiple of 64), within kClResMaxRows rows.
     const int64_t cvg = Cg / kVec;
-    if (GN_RESIDENT && Cg % kVec == 0 && cvg <= kClResMaxGroupVecs && (cvg & (cvg - 1)) == 0) {
+    if (Cg % kVec == 0 && cvg <= kClResMaxGroupVecs && (cvg & (cvg - 1)) == 0) {
         const int64_t vg = S * cvg;
         int l = 0;
         while ((int64_t(1) << l) < cvg) ++l;

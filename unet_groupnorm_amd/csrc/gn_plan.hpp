@@ -1,9 +1,10 @@
 // gn_plan.hpp -- launch plan for the GroupNorm kernels: a pure function of the shape.
 //
 // "Optimize GroupNorm" (LBANN/ScaFFold pull 93), paragraph folding seven launches into
-// four: grid, split count, tile sizes and reduction order are pure functions of the
-// shape; "Preserve GroupNorm dtype" (pull 105), second paragraph: the plan takes no
-// dtype, which is what makes the fp32 and bf16 backward bitwise identical.
+// four: the way the work is split -- launch shapes, partials per group, tiles and the
+// order partials are combined in -- is decided by the shape and nothing else; "Preserve
+// GroupNorm dtype" (pull 105), second paragraph: the plan takes no dtype, which is what
+// makes the fp32 and bf16 backward bitwise identical.
 //
 // Two decompositions of the volume, both into "jobs" that are contiguous runs of one
 // row (row = n*C + c):
@@ -27,48 +28,25 @@ namespace gn {
 // Elements per lane vector: one 16-byte load of bf16, two of fp32. The element -> lane
 // assignment is defined in these units, so it is the same for both dtypes.
 constexpr int kVec = 8;
-// Tuning constants (compile-time overridable for measurement builds).
-#ifndef GN_STEP_VECS
-#define GN_STEP_VECS 4
-#endif
-#ifndef GN_TARGET_JOBS
-#define GN_TARGET_JOBS 512
-#endif
-#ifndef GN_LONG_CHUNK
-#define GN_LONG_CHUNK 262144
-#endif
-// Vectors per lane of the one-step streaming kernels (split-phase and spatial-shard calls).
-// Measured on one rank's share of the 256^3 site split in 8: 1 vector 187.3 us a step,
-// 2 vectors 176.0, 4 vectors 181.2.
-#ifndef GN_APPLY_VECS
-#define GN_APPLY_VECS 2
-#endif
 // Largest reduction workgroup (threads); the plan sizes smaller ones to short rows.
-#ifndef GN_RED_BLOCK
-#define GN_RED_BLOCK 256
-#endif
-constexpr int kRedBlock = GN_RED_BLOCK;
+constexpr int kRedBlock = 256;
 // Vectors each lane holds per step of a reduction job (register tile = kVec * kStepVecs).
-constexpr int kStepVecs = GN_STEP_VECS;
+constexpr int kStepVecs = 4;
 // Reduction workgroups a launch aims for (512: 2 per CU on the 256 CUs of an MI355X), and
 // the job length (elements) for which it settles for half as many, but at least 256 (one
 // per CU). Measured on MI355X, bf16, fwd+bwd steps: against 2048 jobs, 512 is 1-2% faster
 // at 128^3-256^3 and 10% at 96^3 (C=32), and fewer, longer jobs also shorten the folded
 // kernels' partials merge; 256 jobs of 256K elements are another 1.5% at 128^3 (C=32), while
 // 256 jobs are 1-11% slower at 256^3, at 2x128^3 and at the 32^3 UNet site.
-constexpr int64_t kTargetJobs = GN_TARGET_JOBS;
-constexpr int64_t kLongChunk = GN_LONG_CHUNK;
+constexpr int64_t kTargetJobs = 512;
+constexpr int64_t kLongChunk = 262144;
 constexpr int64_t kMinJobs = 256;
-// Vectors each lane moves in a streaming job.
-constexpr int kApplyVecs = GN_APPLY_VECS;
+// Vectors each lane moves in a one-step streaming job (split-phase and spatial-shard calls).
+// Measured on one rank's share of the 256^3 site split in 8: 1 vector 187.3 us a step,
+// 2 vectors 176.0, 4 vectors 181.2.
+constexpr int kApplyVecs = 2;
 // Resident path: one workgroup holds a whole group in registers (at most kResMaxBlock
-// threads with kResMaxLaneVecs vectors each). GN_RESIDENT=0 turns it off (measurement).
-#ifndef GN_RESIDENT
-#define GN_RESIDENT 1
-#endif
-#ifndef GN_RES_SPLIT
-#define GN_RES_SPLIT 1
-#endif
+// threads with kResMaxLaneVecs vectors each).
 constexpr int kResMaxBlock = 1024;
 constexpr int kResMaxLaneVecs = 4;
 constexpr int64_t kResMaxVecs = int64_t(kResMaxBlock) * kResMaxLaneVecs;  // 32768 elements
@@ -77,10 +55,7 @@ constexpr int64_t kResMaxVecs = int64_t(kResMaxBlock) * kResMaxLaneVecs;  // 327
 // is long enough to amortize that and short enough that the grid stays large (measured on
 // MI355X, bf16, 128^3 and 256^3 with C=32 and the 32^3-64^3 UNet sites: 8192-12288 best;
 // 4096 about 20% slower, 32768 and more up to 9% slower at 256^3).
-#ifndef GN_FOLD_CHUNK
-#define GN_FOLD_CHUNK 8192
-#endif
-constexpr int64_t kFoldChunk = GN_FOLD_CHUNK;
+constexpr int64_t kFoldChunk = 8192;
 // Upper bound on a reduction job's element count (in-job counts stay within 32 bits).
 constexpr int64_t kMaxChunk = int64_t(1) << 30;
 // Upper bound on N*C*S accepted (indices stay far from int64 overflow).
@@ -134,10 +109,7 @@ constexpr int kClBlock = 256;
 // NCDHW plan's: each job ends in per-channel shuffle trees and three workgroup barriers,
 // and its K partials per group feed the finalize (measured on MI355X, 128^3 and 256^3,
 // C=32: 256-512 jobs best, 2048 about 5% slower, 128 too few).
-#ifndef GN_CL_TARGET_JOBS
-#define GN_CL_TARGET_JOBS 512
-#endif
-constexpr int64_t kClTargetJobs = GN_CL_TARGET_JOBS;
+constexpr int64_t kClTargetJobs = 512;
 constexpr int kClRounds = 4;        // voxel rounds a reduction lane holds per step
 // Channels-last resident path: at most this many vectors of a group per voxel, at most this
 // many (sample, channel) rows in a backward workgroup, and at most this many vectors per
