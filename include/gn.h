@@ -8,19 +8,22 @@
  *   - Same page, paragraph on the independent review: rstd = 1/sqrt(var + eps) with
  *     the biased variance (a single-element group has rstd = 316 at eps = 1e-5, and
  *     its input gradient is exactly zero); mean/rstd are outputs, not differentiable.
- *   - Same page, paragraph introducing the NDHWC Triton kernel: fp32 statistics from
- *     a corrected two-pass per tile merged with Chan's parallel formula, register-only
- *     reductions in a fixed order with no float atomics (bitwise reproducible).
- *   - Same page, paragraph folding seven launches into four: grid, split count, tile
- *     sizes and reduction order are pure functions of the shape. That page also folds
- *     the finalize into the elementwise kernels; gn_forward and gn_backward do the same,
+ *   - Same page, paragraph introducing the NDHWC Triton kernel: the statistics are fp32;
+ *     each tile's mean and squared deviations come from a two-pass form with a correction
+ *     term, tiles are combined with Chan's merge of (count, mean, M2), and every sum runs in
+ *     registers in one fixed order without floating-point atomics, so repeated calls give
+ *     the same bits.
+ *   - Same page, paragraph folding seven launches into four: how the work is split (the
+ *     launch shapes, the number of partial results per group, the tiles and the order in
+ *     which partials are combined) depends on the shape alone. That page also moves the
+ *     finalize into the elementwise kernels; gn_forward and gn_backward do the same,
  *     while the split-phase entry points (which must leave the statistics in between)
  *     and the channels-last entry points run it as a small kernel of its own.
- *   - "Preserve GroupNorm dtype" (LBANN/ScaFFold pull 105), first paragraph: the
- *     normalized value is computed in fp32 and only the store narrows, so the output
- *     is the fp32 answer rounded once; an fp32 output is available on request. Second
- *     paragraph: the plan takes no dtype, so the backward on the same values in fp32
- *     and in bf16 gives bitwise identical dx/dgamma/dbeta.
+ *   - "Preserve GroupNorm dtype" (LBANN/ScaFFold pull 105), first paragraph: everything
+ *     up to the output is fp32 arithmetic and the narrowing happens once, in the final
+ *     store, so a bf16 output equals the fp32 result rounded a single time; fp32 output
+ *     stays available. Second paragraph: the plan takes no dtype, so the backward on the
+ *     same values in fp32 and in bf16 gives bitwise identical dx/dgamma/dbeta.
  *
  * Layout. Every tensor argument is contiguous NCDHW: element (n, c, s) of a volume
  * with S = D*H*W voxels lives at flat index (n*C + c)*S + s. Group (n, g) is the
@@ -40,9 +43,11 @@
  *
  * Pointers. x, y, dy, dx and the workspace must be 16-byte aligned device pointers;
  * mean, rstd, gamma, beta, dgamma, dbeta 4-byte aligned device pointers. All of them
- * must live on one device, the device that owns x; the kernels are launched on x's
- * device whatever device is current, and a stream that belongs to another device is
- * rejected.
+ * must live on one device, the device that owns x: every pointer argument is checked
+ * (GN_ERR_DEVICE for host memory, pinned host memory or another device's memory). The
+ * kernels are launched on x's device whatever device is current, and a stream that belongs
+ * to another device is rejected. Buffer sizes cannot be checked through plain pointers: each
+ * must hold the elements stated for it.
  *
  * Errors. Every entry point returns an int status (gn_status). All validation runs
  * before anything is enqueued; on any error other than GN_ERR_LAUNCH nothing has been
@@ -76,7 +81,8 @@ typedef enum gn_status {
     GN_ERR_EPS = 5,       /* eps is negative or not finite */
     GN_ERR_WORKSPACE = 6, /* workspace smaller than gn_workspace_bytes(N, C, S, G) */
     GN_ERR_ALIGN = 7,     /* a pointer is not aligned as stated above */
-    GN_ERR_DEVICE = 8,    /* x is not device memory, or the stream belongs to another device */
+    GN_ERR_DEVICE = 8,    /* a pointer argument is not device memory of x's device, or the
+                             stream belongs to another device */
     GN_ERR_LAUNCH = 9,    /* the HIP runtime refused a launch; outputs are undefined */
     GN_ERR_ACTIVATION = 10, /* unknown activation code */
     GN_ERR_LAYOUT = 11      /* channels-last: C not a multiple of 8, C/8 not dividing 256, or

@@ -1,0 +1,98 @@
+"""The binding's checks of caller-supplied tensors, on the host: a buffer of the wrong
+size, dtype, layout or device is refused before any pointer reaches the library, which can
+check where memory lives but not how large a buffer is. With every tensor right, the call
+does reach the library, which then refuses host memory (GN_ERR_DEVICE)."""
+import pytest
+import torch
+
+import unet_groupnorm_amd as gn
+from unet_groupnorm_amd.gn import GnError
+
+N, C, G, SP = 2, 8, 4, (4, 4, 4)
+
+
+def _x(dtype=torch.bfloat16):
+    return torch.randn((N, C) + SP, generator=torch.Generator().manual_seed(3)).to(dtype)
+
+
+def _vec(n=C):
+    return torch.ones(n, dtype=torch.float32)
+
+
+def test_forward_reaches_the_library_when_every_tensor_is_right():
+    x = _x()
+    with pytest.raises(GnError) as e:
+        gn.gn_forward(x, _vec(), _vec(), G, out=torch.empty_like(x), mean=torch.empty(N, G),
+                      rstd=torch.empty(N, G), workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    assert e.value.status == 8
+
+
+@pytest.mark.parametrize("bad", ["mean_numel", "rstd_dtype", "out_dtype", "out_shape", "out_layout",
+                                 "gamma_numel", "ws_layout"])
+def test_forward_refuses_bad_buffers(bad):
+    x = _x()
+    kw = dict(out=torch.empty_like(x), mean=torch.empty(N, G), rstd=torch.empty(N, G),
+              workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    gamma = _vec()
+    if bad == "mean_numel":
+        kw["mean"] = torch.empty(N * G - 1)
+    elif bad == "rstd_dtype":
+        kw["rstd"] = torch.empty(N, G, dtype=torch.float64)
+    elif bad == "out_dtype":
+        kw["out"] = torch.empty_like(x, dtype=torch.int16)
+    elif bad == "out_shape":
+        kw["out"] = torch.empty((N, C, 4, 4, 3), dtype=x.dtype)
+    elif bad == "out_layout":
+        kw["out"] = torch.empty_like(x).transpose(2, 3).contiguous().transpose(2, 3)
+    elif bad == "gamma_numel":
+        gamma = _vec(C - 1)
+    elif bad == "ws_layout":
+        kw["workspace"] = torch.empty(1 << 17, dtype=torch.uint8)[::2]
+    with pytest.raises((ValueError, TypeError)):
+        gn.gn_forward(x, gamma, _vec(), G, **kw)
+
+
+@pytest.mark.parametrize("bad", ["dy_shape", "dy_dtype", "dx_dtype", "dx_shape", "mean_numel",
+                                 "dgamma_numel", "dbeta_dtype"])
+def test_backward_refuses_bad_buffers(bad):
+    x = _x()
+    kw = dict(dx=torch.empty_like(x), dgamma=torch.empty(C), dbeta=torch.empty(C),
+              workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    dy, mean = _x(), torch.empty(N, G)
+    if bad == "dy_shape":
+        dy = torch.empty((N, C, 4, 4, 5), dtype=x.dtype)
+    elif bad == "dy_dtype":
+        dy = dy.to(torch.float64)
+    elif bad == "dx_dtype":
+        kw["dx"] = torch.empty_like(x, dtype=torch.float32)   # dx is written in x's dtype
+    elif bad == "dx_shape":
+        kw["dx"] = torch.empty((N - 1, C) + SP, dtype=x.dtype)
+    elif bad == "mean_numel":
+        mean = torch.empty(N * G + 1)
+    elif bad == "dgamma_numel":
+        kw["dgamma"] = torch.empty(C - 2)
+    elif bad == "dbeta_dtype":
+        kw["dbeta"] = torch.empty(C, dtype=torch.float16)
+    with pytest.raises((ValueError, TypeError)):
+        gn.gn_backward(dy, x, mean, torch.empty(N, G), _vec(), G, **kw)
+
+
+def test_backward_reaches_the_library_when_every_tensor_is_right():
+    x = _x()
+    with pytest.raises(GnError) as e:
+        gn.gn_backward(_x(), x, torch.empty(N, G), torch.empty(N, G), _vec(), G, dx=torch.empty_like(x),
+                       dgamma=torch.empty(C), dbeta=torch.empty(C),
+                       workspace=torch.empty(1 << 16, dtype=torch.uint8))
+    assert e.value.status == 8
+
+
+def test_split_phase_refuses_bad_buffers():
+    x = _x()
+    ws = torch.empty(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        gn.gn_forward_stats(x, _vec(), _vec(), G, 1e-5, torch.empty(N * G - 1), torch.empty(N, G), ws)
+    with pytest.raises(TypeError):
+        gn.gn_backward_apply(_x(), x, G, torch.empty_like(x, dtype=torch.int32), ws)
+    with pytest.raises(ValueError):
+        gn.gn_backward_finish(_x(), x, torch.empty(N, G), torch.empty(N, G), _vec(), G, None,
+                              torch.empty(C + 1), None, ws)

@@ -460,7 +460,13 @@ def test_binding_rejects_bad_arguments():
         gn.gn_forward(x.transpose(2, 3), None, None, 2)
     with pytest.raises(ValueError, match="activation"):
         gn.gn_forward(x, None, None, 2, activation="gelu")
+    # every tensor in pinned host memory: the binding's checks pass, the library refuses
     with pytest.raises(gn.GnError, match="GN_ERR_DEVICE"):
+        gn.gn_forward(x.cpu().pin_memory(), None, None, 2, out=torch.empty_like(x, device="cpu").pin_memory(),
+                      mean=torch.empty(1, 2).pin_memory(), rstd=torch.empty(1, 2).pin_memory(),
+                      workspace=gn.workspace_for(x, 2).cpu().pin_memory())
+    # outputs on another device than x: the binding refuses before the library is called
+    with pytest.raises(ValueError, match="device"):
         gn.gn_forward(x.cpu().pin_memory(), None, None, 2, out=torch.empty_like(x),
                       mean=torch.empty(1, 2, device=DEV), rstd=torch.empty(1, 2, device=DEV),
                       workspace=gn.workspace_for(x, 2))

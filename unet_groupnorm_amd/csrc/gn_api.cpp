@@ -6,31 +6,20 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "gn.h"
 #include "gn_launch.hpp"
 #include "gn_plan.hpp"
 
-// Whether gn_forward and gn_backward (with dx) run the finalize inside the streaming pass
-// (two launches per direction) or as a kernel of its own (three); compile-time
-// overridable for measurement builds. The split-phase entry points always run it alone.
-#ifndef GN_FOLD_FINALIZE
-#define GN_FOLD_FINALIZE 1
-#endif
-
 namespace {
-
-constexpr bool kFoldFinalize = GN_FOLD_FINALIZE;
 
 // Volumes of x up to this many bytes are streamed with plain (cacheable) loads, others with
 // nontemporal ones. A step reads x four times and dy twice; when x fits well inside MI355X's
 // 256 MiB last-level cache the later reads find it there (measured: 128^3 x 32 channels of
 // bf16, 128 MiB, 3-4% faster a step; 256 MiB and more, and 1 GiB by 7%, slower than
 // nontemporal). Loads only: no result depends on it.
-#ifndef GN_CACHED_BYTES
-#define GN_CACHED_BYTES (int64_t(160) << 20)
-#endif
-constexpr int64_t kCachedBytes = GN_CACHED_BYTES;
+constexpr int64_t kCachedBytes = int64_t(160) << 20;
 
 gn::KArgs kargs_for(const gn::Plan& p, int activation, int x_dtype)
 {
@@ -57,20 +46,29 @@ int workspace_check(const void* ws, size_t bytes, const gn::Plan& p)
     return GN_OK;
 }
 
+// The device that owns p, or -1 if p is not device memory (host, pinned or unknown).
+int device_of(const void* p)
+{
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return -1;
+    return attr.device;
+}
+
 // Makes x's device current for the duration of a call ("Optimize GroupNorm", paragraph on
 // the independent review: launching on the current device instead of the input's device
-// faulted on a tensor living on another GPU). A stream of another device is rejected.
+// faulted on a tensor living on another GPU). A stream of another device is rejected, and so
+// is any other pointer argument that is not device memory of that device (a kernel would
+// otherwise read or write host memory, or another GPU's).
 class DeviceScope {
   public:
     int enter(const void* x, void* stream)
     {
-        hipPointerAttribute_t attr;
-        if (hipPointerGetAttributes(&attr, x) != hipSuccess) {
-            (void)hipGetLastError();
-            return GN_ERR_DEVICE;
-        }
-        if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return GN_ERR_DEVICE;
-        const int dev = attr.device;
+        const int dev = device_of(x);
+        if (dev < 0) return GN_ERR_DEVICE;
         int cur = -1;
         if (hipGetDevice(&cur) != hipSuccess) return GN_ERR_DEVICE;
         if (stream) {
@@ -85,8 +83,17 @@ class DeviceScope {
             if (hipSetDevice(dev) != hipSuccess) return GN_ERR_DEVICE;
             prev_ = cur;
         }
+        dev_ = dev;
         return GN_OK;
     }
+    // GN_OK if every non-NULL pointer lives on the call's device.
+    int same_device(std::initializer_list<const void*> ptrs) const
+    {
+        for (const void* p : ptrs)
+            if (p && device_of(p) != dev_) return GN_ERR_DEVICE;
+        return GN_OK;
+    }
+    int device() const { return dev_; }
     ~DeviceScope()
     {
         if (prev_ >= 0) (void)hipSetDevice(prev_);
@@ -94,13 +101,15 @@ class DeviceScope {
 
   private:
     int prev_ = -1;
+    int dev_ = -1;
 };
 
-int fwd_check(const void* x, int x_dtype, const float* gamma, const float* beta, int64_t N,
-              int64_t C, int64_t S, int64_t G, float eps, int activation, const void* y, int y_dtype,
-              const float* mean, const float* rstd, const void* ws, size_t ws_bytes, gn::Plan* p)
+// gn_forward's checks of everything but the workspace.
+int fwd_args_check(const void* x, int x_dtype, const float* gamma, const float* beta, int64_t N,
+                   int64_t C, int64_t S, int64_t G, float eps, int activation, const void* y, int y_dtype,
+                   const float* mean, const float* rstd, gn::Plan* p)
 {
-    if (!x || !y || !mean || !rstd || !ws) return GN_ERR_NULL;
+    if (!x || !y || !mean || !rstd) return GN_ERR_NULL;
     int rc = plan_or_error(N, C, S, G, p);
     if (rc) return rc;
     if (!dtype_ok(x_dtype) || !(y_dtype == x_dtype || y_dtype == GN_F32)) return GN_ERR_DTYPE;
@@ -109,6 +118,16 @@ int fwd_check(const void* x, int x_dtype, const float* gamma, const float* beta,
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(mean, 4) || !aligned(rstd, 4) ||
         !aligned(gamma, 4) || !aligned(beta, 4))
         return GN_ERR_ALIGN;
+    return GN_OK;
+}
+
+int fwd_check(const void* x, int x_dtype, const float* gamma, const float* beta, int64_t N,
+              int64_t C, int64_t S, int64_t G, float eps, int activation, const void* y, int y_dtype,
+              const float* mean, const float* rstd, const void* ws, size_t ws_bytes, gn::Plan* p)
+{
+    if (!ws) return GN_ERR_NULL;
+    const int rc = fwd_args_check(x, x_dtype, gamma, beta, N, C, S, G, eps, activation, y, y_dtype, mean, rstd, p);
+    if (rc) return rc;
     return workspace_check(ws, ws_bytes, *p);
 }
 
@@ -132,7 +151,8 @@ int bwd_check(const void* dy, int dy_dtype, const void* x, int x_dtype, const fl
 int launch_status(hipError_t e) { return e == hipSuccess ? GN_OK : GN_ERR_LAUNCH; }
 
 // The two halves of gn_forward. On the resident path the first does nothing and the
-// second runs the whole forward.
+// second runs the whole forward; otherwise the second is the normalize with the finalize
+// folded into each of its workgroups (the split-phase entry points run it alone).
 int fwd_partials(const void* x, int x_dtype, const gn::Plan& p, const gn::KArgs& a, gn::Workspace w,
                  hipStream_t st)
 {
@@ -147,12 +167,8 @@ int fwd_finish(const void* x, int x_dtype, const float* gamma, const float* beta
     if (p.res_fwd)
         return launch_status(gn::launch_res_fwd(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype, a, w,
                                                 st, p.res_block_f, p.res_vecs_f));
-    if (kFoldFinalize)
-        return launch_status(gn::launch_fwd_apply_fin(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype, a,
-                                                      w, st));
-    const int rc = launch_status(gn::launch_fin_fwd(x, x_dtype, gamma, beta, eps, mean, rstd, a, w, st));
-    if (rc) return rc;
-    return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, a, w, st));
+    return launch_status(gn::launch_fwd_apply_fin(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype, a,
+                                                  w, st));
 }
 
 // The two halves of gn_backward, likewise.
@@ -172,12 +188,10 @@ int bwd_finish(const void* dy, int dy_dtype, const void* x, int x_dtype, const f
         return launch_status(gn::launch_res_bwd(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
                                                 dbeta, dx, a, w, st, p.res_block_b, p.res_vecs_b,
                                                 p.res_bwd_split));
-    if (kFoldFinalize && dx)
+    if (dx)
         return launch_status(gn::launch_bwd_apply_fin(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dgamma,
                                                       dbeta, dx, a, w, st));
-    const int rc = launch_status(gn::launch_fin_bwd(mean, rstd, gamma, beta, dgamma, dbeta, a, w, st));
-    if (rc || !dx) return rc;
-    return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, a, w, st));
+    return launch_status(gn::launch_fin_bwd(mean, rstd, gamma, beta, dgamma, dbeta, a, w, st));
 }
 
 }  // namespace
@@ -235,7 +249,7 @@ const char* gn_status_string(int status)
         case GN_ERR_EPS: return "eps must be finite and >= 0";
         case GN_ERR_WORKSPACE: return "workspace smaller than gn_workspace_bytes()";
         case GN_ERR_ALIGN: return "misaligned pointer (tensors and workspace need 16 bytes, fp32 vectors 4)";
-        case GN_ERR_DEVICE: return "x is not device memory or the stream belongs to another device";
+        case GN_ERR_DEVICE: return "a pointer argument is not device memory of x's device, or the stream belongs to another device";
         case GN_ERR_LAUNCH: return "kernel launch failed";
         case GN_ERR_ACTIVATION: return "unknown activation (GN_ACT_NONE or GN_ACT_RELU)";
         case GN_ERR_LAYOUT: return "shape not supported channels-last (C a multiple of 8 with C/8 dividing 256; C/G dividing 8 or a multiple of 8)";
@@ -260,6 +274,7 @@ int gn_forward_stats(const void* x, int x_dtype, const float* gamma, const float
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({gamma, beta, mean, rstd, workspace}))) return rc;
     const gn::KArgs a = kargs_for(p, 0, x_dtype);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -283,6 +298,7 @@ int gn_forward_apply(const void* x, int x_dtype, int64_t N, int64_t C, int64_t S
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({y, workspace}))) return rc;
     return launch_status(gn::launch_fwd_apply(x, x_dtype, y, y_dtype, kargs_for(p, activation, x_dtype),
                                               gn::workspace_of(workspace, p),
                                               static_cast<hipStream_t>(stream)));
@@ -299,6 +315,7 @@ int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({gamma, beta, y, mean, rstd, workspace}))) return rc;
     const gn::KArgs a = kargs_for(p, activation, x_dtype);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -318,6 +335,7 @@ int gn_forward_partials(const void* x, int x_dtype, int64_t N, int64_t C, int64_
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({workspace}))) return rc;
     return fwd_partials(x, x_dtype, p, kargs_for(p, 0, x_dtype), gn::workspace_of(workspace, p),
                         static_cast<hipStream_t>(stream));
 }
@@ -333,6 +351,7 @@ int gn_forward_finish(const void* x, int x_dtype, const float* gamma, const floa
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({gamma, beta, y, mean, rstd, workspace}))) return rc;
     return fwd_finish(x, x_dtype, gamma, beta, eps, y, y_dtype, mean, rstd, p,
                       kargs_for(p, activation, x_dtype),
                       gn::workspace_of(workspace, p), static_cast<hipStream_t>(stream));
@@ -351,6 +370,7 @@ int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({dy, mean, rstd, gamma, beta, dgamma, dbeta, workspace}))) return rc;
     const gn::KArgs a = kargs_for(p, activation, x_dtype);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -376,6 +396,7 @@ int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({dy, dx, workspace}))) return rc;
     return launch_status(gn::launch_bwd_apply(dy, dy_dtype, x, x_dtype, dx, kargs_for(p, activation, x_dtype),
                                               gn::workspace_of(workspace, p),
                                               static_cast<hipStream_t>(stream)));
@@ -394,6 +415,7 @@ int gn_backward(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({dy, mean, rstd, gamma, beta, dx, dgamma, dbeta, workspace}))) return rc;
     const gn::KArgs a = kargs_for(p, activation, x_dtype);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -413,6 +435,7 @@ int gn_backward_partials(const void* dy, int dy_dtype, const void* x, int x_dtyp
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({dy, mean, rstd, gamma, beta, workspace}))) return rc;
     return bwd_partials(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, p,
                         kargs_for(p, activation, x_dtype),
                         gn::workspace_of(workspace, p), static_cast<hipStream_t>(stream));
@@ -431,6 +454,7 @@ int gn_backward_finish(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if (rc) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({dy, mean, rstd, gamma, beta, dx, dgamma, dbeta, workspace}))) return rc;
     return bwd_finish(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx, dgamma, dbeta, p,
                       kargs_for(p, activation, x_dtype), gn::workspace_of(workspace, p),
                       static_cast<hipStream_t>(stream));
@@ -453,6 +477,7 @@ int gn_forward_shard_stats(const void* x, int x_dtype, int64_t N, int64_t C, int
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({moments, workspace}))) return rc;
     const gn::KArgs a = kargs_for(p, 0, x_dtype);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -477,6 +502,7 @@ int gn_forward_shard_merge(const gn_moments* moments, int64_t P, const float* ga
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(moments, stream))) return rc;
+    if ((rc = ds.same_device({gamma, beta, mean, rstd, workspace}))) return rc;
     return launch_status(gn::launch_shard_merge_fwd(reinterpret_cast<const gn::Moments16*>(moments), P, gamma,
                                                     beta, eps, mean, rstd, gn::kargs_of(p),
                                                     gn::workspace_of(workspace, p),
@@ -498,6 +524,7 @@ int gn_backward_shard_sums(const void* dy, int dy_dtype, const void* x, int x_dt
     if (N > ((int64_t(1) << 31) - 1) / C) return GN_ERR_SHAPE;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({dy, mean, rstd, gamma, beta, sums, workspace}))) return rc;
     const gn::KArgs a = kargs_for(p, activation, x_dtype);
     const gn::Workspace w = gn::workspace_of(workspace, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -523,6 +550,7 @@ int gn_backward_shard_merge(const float* sums, int64_t P, const float* mean, con
     if ((rc = workspace_check(workspace, workspace_bytes, p))) return rc;
     DeviceScope ds;
     if ((rc = ds.enter(sums, stream))) return rc;
+    if ((rc = ds.same_device({mean, rstd, gamma, beta, dgamma, dbeta, workspace}))) return rc;
     return launch_status(gn::launch_shard_merge_bwd(reinterpret_cast<const float2*>(sums), P, mean, rstd, gamma,
                                                     beta, p.Cg * S_total, dgamma, dbeta, gn::kargs_of(p),
                                                     gn::workspace_of(workspace, p),
@@ -587,6 +615,7 @@ int gn_forward_cl(const void* x, int x_dtype, const float* gamma, const float* b
     if (workspace_bytes < p.ws_bytes) return GN_ERR_WORKSPACE;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({gamma, beta, y, mean, rstd, workspace}))) return rc;
     if (p.res_fwd)
         return launch_status(gn::launch_cl_res_forward(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype,
                                                        gn::clargs_of(p, activation),
@@ -613,6 +642,7 @@ int gn_backward_cl(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if (workspace_bytes < p.ws_bytes) return GN_ERR_WORKSPACE;
     DeviceScope ds;
     if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({dy, mean, rstd, gamma, beta, dx, dgamma, dbeta, workspace}))) return rc;
     if (p.res_bwd)
         return launch_status(gn::launch_cl_res_backward(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx,
                                                         dgamma, dbeta, gn::clargs_of(p, activation),

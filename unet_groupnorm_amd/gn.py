@@ -55,11 +55,6 @@ def _dtype(t):
         raise TypeError(f"unsupported dtype {t.dtype} (float32, bfloat16 or float16)") from None
 
 
-def _ptr(t):
-    # ctypes takes a plain int for a c_void_p argument
-    return None if t is None else t.data_ptr()
-
-
 def layout_of(t):
     """"ncdhw" for a contiguous tensor, "ndhwc" for one that is contiguous with the channel
     dimension last (and not also contiguous), else ValueError."""
@@ -102,31 +97,51 @@ def _contig(name, t):
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
-def _stream(dev):
-    # A tensor that is not on a GPU gets the null stream; the library then rejects it.
-    if dev.type != "cuda":
-        return None
-    if _raw_stream is not None:
-        return _raw_stream(dev.index if dev.index is not None else torch.cuda.current_device())
-    return torch.cuda.current_stream(dev).cuda_stream
-
-
-def _vec(name, t, C, dev):
-    if t is None:
-        return None
-    if t.dtype != torch.float32 or t.numel() != C or t.device != dev:
-        raise ValueError(f"{name} must be a float32 tensor of {C} elements on {dev}")
-    return _contig(name, t)
-
-
-# The per-step calls (gn_forward, gn_backward) check devices by index (x.get_device(): the
-# GPU's ordinal, -1 on the host), which costs less than building torch.device objects.
+# Every tensor a caller passes is checked here before its pointer reaches the library, which
+# can check where memory lives but not how large a buffer is: device by index (get_device():
+# the GPU's ordinal, -1 on the host, cheaper than torch.device objects), dtype, element count
+# and layout. Tensors the binding allocates itself are right by construction.
 def _vec_ptr(name, t, C, didx):
     if t is None:
         return None
-    if t.dtype != torch.float32 or t.numel() != C or t.get_device() != didx or not t.is_contiguous():
+    if t.dtype is not torch.float32 or t.numel() != C or t.get_device() != didx or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous float32 tensor of {C} elements on x's device")
     return t.data_ptr()
+
+
+def _buf_ptr(name, t, numel, didx, dtype=torch.float32):
+    """A contiguous `dtype` tensor of `numel` elements on device didx (None passes as NULL)."""
+    if t is None:
+        return None
+    if t.dtype is not dtype or t.numel() != numel or t.get_device() != didx or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of {numel} elements on x's device")
+    return t.data_ptr()
+
+
+def _sig(x):
+    """x's shape and strides, which the tensors of _like_ptr must share."""
+    return x.shape, x.stride()
+
+
+def _like_ptr(name, t, xsig, didx, dtypes):
+    """A tensor with x's shape and strides (xsig = _sig(x)), one of `dtypes`, on x's device."""
+    if t.shape != xsig[0] or t.stride() != xsig[1]:
+        raise ValueError(f"{name} must have x's shape and layout")
+    if t.get_device() != didx:
+        raise ValueError(f"{name} must be on x's device")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _ws_args(ws, didx):
+    """(pointer, size in bytes) of a workspace tensor on x's device."""
+    if ws.get_device() != didx or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on x's device")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+_IN_DTYPES = (torch.float32, torch.bfloat16, torch.float16)
 
 
 def _stream_of(didx):
@@ -176,39 +191,47 @@ def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, activation=None, 
     layout = _layout_arg(x, layout)
     N, C, S, G = _dims(x, G)
     didx = x.get_device()
+    xsig = _sig(x)
     out_dtype = out_dtype or x.dtype
     y = out if out is not None else torch.empty_like(x, dtype=out_dtype)
-    if y.shape != x.shape or y.stride() != x.stride():
-        raise ValueError("out must have x's shape and layout")
+    y_ptr = _like_ptr("out", y, xsig, didx, _IN_DTYPES)
+    m_ptr = _buf_ptr("mean", mean, N * G, didx)
+    r_ptr = _buf_ptr("rstd", rstd, N * G, didx)
     mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
     rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
-    ws = workspace if workspace is not None else workspace_for(x, G, layout)
+    ws_ptr, ws_bytes = _ws_args(workspace if workspace is not None else workspace_for(x, G, layout), didx)
     fn, name = (lib.gn_forward, "gn_forward") if layout == "ncdhw" else (lib.gn_forward_cl, "gn_forward_cl")
     _check(name, fn(
         x.data_ptr(), _dtype(x), _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx),
-        N, C, S, G, float(eps), _act(activation), y.data_ptr(), _dtype(y), mean.data_ptr(),
-        rstd.data_ptr(), ws.data_ptr(), ws.numel(), _stream_of(didx)))
+        N, C, S, G, float(eps), _act(activation), y_ptr, _dtype(y), m_ptr or mean.data_ptr(),
+        r_ptr or rstd.data_ptr(), ws_ptr, ws_bytes, _stream_of(didx)))
     return y, mean, rstd
+
+
+def _split_args(x, G):
+    """(N, C, S, G, didx, _sig(x)) of an NCDHW x for the split-phase entry points."""
+    _contig("x", x)
+    N, C, S, G = _dims(x, G)
+    return N, C, S, G, x.get_device(), _sig(x)
 
 
 def gn_forward_stats(x, gamma, beta, G, eps, mean, rstd, workspace):
     """First half of gn_forward: mean/rstd, and coefficients left in the workspace."""
-    _contig("x", x)
-    N, C, S, G = _dims(x, G)
-    dev = x.device
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_forward_stats", lib.gn_forward_stats(
-        _ptr(x), _dtype(x), _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
-        N, C, S, G, float(eps), _ptr(mean), _ptr(rstd), _ptr(workspace), workspace.numel(),
-        _stream(dev)))
+        x.data_ptr(), _dtype(x), _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx),
+        N, C, S, G, float(eps), _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx),
+        ws, nb, _stream_of(didx)))
 
 
 def gn_forward_apply(x, G, y, workspace, activation=None):
     """Second half of gn_forward: y from x and the workspace coefficients."""
-    _contig("x", x)
-    N, C, S, G = _dims(x, G)
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_forward_apply", lib.gn_forward_apply(
-        _ptr(x), _dtype(x), N, C, S, G, _act(activation), _ptr(_contig("y", y)), _dtype(y),
-        _ptr(workspace), workspace.numel(), _stream(x.device)))
+        x.data_ptr(), _dtype(x), N, C, S, G, _act(activation), _like_ptr("y", y, xsig, didx, _IN_DTYPES),
+        _dtype(y), ws, nb, _stream_of(didx)))
 
 
 def gn_backward(dy, x, mean, rstd, gamma, G, *, beta=None, activation=None, need_dx=True,
@@ -217,26 +240,25 @@ def gn_backward(dy, x, mean, rstd, gamma, G, *, beta=None, activation=None, need
     """Returns (dx or None, dgamma or None, dbeta or None); dx has x's dtype and layout. With
     activation="relu", dy is the gradient of relu(GroupNorm(x)) and beta is needed."""
     layout = _layout_arg(x, layout)
-    if dy.shape != x.shape or dy.stride() != x.stride():
-        raise ValueError("dy must have x's shape and layout")
     N, C, S, G = _dims(x, G)
     didx = x.get_device()
+    xsig = _sig(x)
+    dy_ptr = _like_ptr("dy", dy, xsig, didx, _IN_DTYPES)
     if need_dx and dx is None:
         dx = torch.empty_like(x)
-    if need_dx and dx.stride() != x.stride():
-        raise ValueError("dx must have x's layout")
+    dx_ptr = _like_ptr("dx", dx, xsig, didx, (x.dtype,)) if need_dx else None
     if need_dgamma and dgamma is None:
         dgamma = torch.empty(C, dtype=torch.float32, device=x.device)
     if need_dbeta and dbeta is None:
         dbeta = torch.empty(C, dtype=torch.float32, device=x.device)
-    ws = workspace if workspace is not None else workspace_for(x, G, layout)
+    ws_ptr, ws_bytes = _ws_args(workspace if workspace is not None else workspace_for(x, G, layout), didx)
     fn, name = (lib.gn_backward, "gn_backward") if layout == "ncdhw" else (lib.gn_backward_cl, "gn_backward_cl")
     _check(name, fn(
-        dy.data_ptr(), _dtype(dy), x.data_ptr(), _dtype(x), _ptr(mean), _ptr(rstd),
+        dy_ptr, _dtype(dy), x.data_ptr(), _dtype(x), _buf_ptr("mean", mean, N * G, didx),
+        _buf_ptr("rstd", rstd, N * G, didx),
         _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), _act(activation),
-        N, C, S, G,
-        _ptr(dx if need_dx else None), _ptr(dgamma if need_dgamma else None),
-        _ptr(dbeta if need_dbeta else None), ws.data_ptr(), ws.numel(), _stream_of(didx)))
+        N, C, S, G, dx_ptr, _vec_ptr("dgamma", dgamma if need_dgamma else None, C, didx),
+        _vec_ptr("dbeta", dbeta if need_dbeta else None, C, didx), ws_ptr, ws_bytes, _stream_of(didx)))
     return (dx if need_dx else None, dgamma if need_dgamma else None, dbeta if need_dbeta else None)
 
 
@@ -244,66 +266,66 @@ def gn_backward_reduce(dy, x, mean, rstd, gamma, G, dgamma, dbeta, workspace, be
                        activation=None):
     """First half of gn_backward: dgamma/dbeta (either may be None), coefficients left in
     the workspace."""
-    _contig("x", x); _contig("dy", dy)
-    N, C, S, G = _dims(x, G)
-    dev = x.device
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_backward_reduce", lib.gn_backward_reduce(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
-        N, C, S, G, _ptr(dgamma), _ptr(dbeta), _ptr(workspace), workspace.numel(), _stream(dev)))
+        _like_ptr("dy", dy, xsig, didx, _IN_DTYPES), _dtype(dy), x.data_ptr(), _dtype(x),
+        _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx),
+        _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), _act(activation),
+        N, C, S, G, _vec_ptr("dgamma", dgamma, C, didx), _vec_ptr("dbeta", dbeta, C, didx), ws, nb,
+        _stream_of(didx)))
 
 
 def gn_backward_apply(dy, x, G, dx, workspace, activation=None):
     """Second half of gn_backward: dx from x, dy and the workspace coefficients."""
-    _contig("x", x); _contig("dy", dy)
-    N, C, S, G = _dims(x, G)
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_backward_apply", lib.gn_backward_apply(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), N, C, S, G, _act(activation), _ptr(dx),
-        _ptr(workspace), workspace.numel(), _stream(x.device)))
+        _like_ptr("dy", dy, xsig, didx, _IN_DTYPES), _dtype(dy), x.data_ptr(), _dtype(x), N, C, S, G,
+        _act(activation), _like_ptr("dx", dx, xsig, didx, (x.dtype,)), ws, nb, _stream_of(didx)))
 
 
 def gn_forward_partials(x, G, workspace):
     """gn_forward's first launch: the partial statistics of x, left in the workspace."""
-    _contig("x", x)
-    N, C, S, G = _dims(x, G)
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_forward_partials", lib.gn_forward_partials(
-        _ptr(x), _dtype(x), N, C, S, G, _ptr(workspace), workspace.numel(), _stream(x.device)))
+        x.data_ptr(), _dtype(x), N, C, S, G, ws, nb, _stream_of(didx)))
 
 
 def gn_forward_finish(x, gamma, beta, G, eps, y, mean, rstd, workspace, activation=None):
     """gn_forward's second launch: the finalize, then y (after gn_forward_partials)."""
-    _contig("x", x)
-    N, C, S, G = _dims(x, G)
-    dev = x.device
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_forward_finish", lib.gn_forward_finish(
-        _ptr(x), _dtype(x), _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
-        N, C, S, G, float(eps), _act(activation), _ptr(_contig("y", y)), _dtype(y), _ptr(mean),
-        _ptr(rstd), _ptr(workspace), workspace.numel(), _stream(dev)))
+        x.data_ptr(), _dtype(x), _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx),
+        N, C, S, G, float(eps), _act(activation), _like_ptr("y", y, xsig, didx, _IN_DTYPES), _dtype(y),
+        _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx), ws, nb, _stream_of(didx)))
 
 
 def gn_backward_partials(dy, x, mean, rstd, gamma, G, workspace, beta=None, activation=None):
     """gn_backward's first launch: the per-job sums, left in the workspace."""
-    _contig("x", x); _contig("dy", dy)
-    N, C, S, G = _dims(x, G)
-    dev = x.device
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_backward_partials", lib.gn_backward_partials(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
-        N, C, S, G, _ptr(workspace), workspace.numel(), _stream(dev)))
+        _like_ptr("dy", dy, xsig, didx, _IN_DTYPES), _dtype(dy), x.data_ptr(), _dtype(x),
+        _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx),
+        _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), _act(activation),
+        N, C, S, G, ws, nb, _stream_of(didx)))
 
 
 def gn_backward_finish(dy, x, mean, rstd, gamma, G, dx, dgamma, dbeta, workspace, beta=None,
                        activation=None):
     """gn_backward's second launch: dx, dgamma, dbeta (each may be None) after
     gn_backward_partials."""
-    _contig("x", x); _contig("dy", dy)
-    N, C, S, G = _dims(x, G)
-    dev = x.device
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_backward_finish", lib.gn_backward_finish(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
-        N, C, S, G, _ptr(dx), _ptr(dgamma), _ptr(dbeta), _ptr(workspace), workspace.numel(),
-        _stream(dev)))
+        _like_ptr("dy", dy, xsig, didx, _IN_DTYPES), _dtype(dy), x.data_ptr(), _dtype(x),
+        _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx),
+        _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), _act(activation),
+        N, C, S, G, None if dx is None else _like_ptr("dx", dx, xsig, didx, (x.dtype,)),
+        _vec_ptr("dgamma", dgamma, C, didx), _vec_ptr("dbeta", dbeta, C, didx), ws, nb, _stream_of(didx)))
 
 
 # ----------------------------------------------------------------------------- spatial shards
@@ -326,13 +348,12 @@ def _dims_of_shape(shape, G):
 def gn_forward_shard_stats(x, G, *, moments=None, workspace=None):
     """This shard's record per group, a [N*G, 4] float32 tensor of rows (mean head, mean
     tail, M2, element count as uint32 bits) -- the gn_moments layout."""
-    _contig("x", x)
-    N, C, S, G = _dims(x, G)
+    N, C, S, G, didx, xsig = _split_args(x, G)
     moments = moments if moments is not None else torch.empty((N * G, 4), dtype=torch.float32, device=x.device)
-    ws = workspace if workspace is not None else workspace_for(x, G)
+    ws, nb = _ws_args(workspace if workspace is not None else workspace_for(x, G), didx)
     _check("gn_forward_shard_stats", lib.gn_forward_shard_stats(
-        _ptr(x), _dtype(x), N, C, S, G, _ptr(_contig("moments", moments)), _ptr(ws), ws.numel(),
-        _stream(x.device)))
+        x.data_ptr(), _dtype(x), N, C, S, G, _buf_ptr("moments", moments, N * G * 4, didx), ws, nb,
+        _stream_of(didx)))
     return moments
 
 
@@ -343,14 +364,16 @@ def gn_forward_shard_merge(moments, gamma, beta, shape, G, eps=1e-5, *, workspac
     N, C, S, G = _dims_of_shape(shape, G)
     _contig("moments", moments)
     P = moments.numel() // (N * G * 4)
-    if moments.numel() != P * N * G * 4 or P < 1:
-        raise ValueError("moments must be [P, N*G, 4]")
-    dev = moments.device
-    mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
-    rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=dev)
+    if moments.numel() != P * N * G * 4 or P < 1 or moments.dtype != torch.float32:
+        raise ValueError("moments must be a float32 [P, N*G, 4] tensor")
+    didx = moments.get_device()
+    mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=moments.device)
+    rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=moments.device)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_forward_shard_merge", lib.gn_forward_shard_merge(
-        _ptr(moments), P, _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)),
-        N, C, S, G, float(eps), _ptr(mean), _ptr(rstd), _ptr(workspace), workspace.numel(), _stream(dev)))
+        moments.data_ptr(), P, _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx),
+        N, C, S, G, float(eps), _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx),
+        ws, nb, _stream_of(didx)))
     return mean, rstd
 
 
@@ -358,15 +381,14 @@ def gn_backward_shard_sums(dy, x, mean, rstd, gamma, G, *, beta=None, activation
                            workspace=None):
     """This shard's (sum g, rstd * sum g*(x - mean)) per row (n, c), [N*C, 2] float32, with
     the whole volume's mean and rstd."""
-    _contig("x", x); _contig("dy", dy)
-    N, C, S, G = _dims(x, G)
-    dev = x.device
-    sums = sums if sums is not None else torch.empty((N * C, 2), dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else workspace_for(x, G)
+    N, C, S, G, didx, xsig = _split_args(x, G)
+    sums = sums if sums is not None else torch.empty((N * C, 2), dtype=torch.float32, device=x.device)
+    ws, nb = _ws_args(workspace if workspace is not None else workspace_for(x, G), didx)
     _check("gn_backward_shard_sums", lib.gn_backward_shard_sums(
-        _ptr(dy), _dtype(dy), _ptr(x), _dtype(x), _ptr(mean), _ptr(rstd),
-        _ptr(_vec("gamma", gamma, C, dev)), _ptr(_vec("beta", beta, C, dev)), _act(activation),
-        N, C, S, G, _ptr(_contig("sums", sums)), _ptr(ws), ws.numel(), _stream(dev)))
+        _like_ptr("dy", dy, xsig, didx, _IN_DTYPES), _dtype(dy), x.data_ptr(), _dtype(x),
+        _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx),
+        _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), _act(activation),
+        N, C, S, G, _buf_ptr("sums", sums, N * C * 2, didx), ws, nb, _stream_of(didx)))
     return sums
 
 
@@ -379,18 +401,19 @@ def gn_backward_shard_merge(sums, mean, rstd, gamma, shape, S_total, G, *, works
     N, C, S, G = _dims_of_shape(shape, G)
     _contig("sums", sums)
     P = sums.numel() // (N * C * 2)
-    if sums.numel() != P * N * C * 2 or P < 1:
-        raise ValueError("sums must be [P, N*C, 2]")
-    dev = sums.device
+    if sums.numel() != P * N * C * 2 or P < 1 or sums.dtype != torch.float32:
+        raise ValueError("sums must be a float32 [P, N*C, 2] tensor")
+    didx = sums.get_device()
     if need_dgamma and dgamma is None:
-        dgamma = torch.empty(C, dtype=torch.float32, device=dev)
+        dgamma = torch.empty(C, dtype=torch.float32, device=sums.device)
     if need_dbeta and dbeta is None:
-        dbeta = torch.empty(C, dtype=torch.float32, device=dev)
+        dbeta = torch.empty(C, dtype=torch.float32, device=sums.device)
+    ws, nb = _ws_args(workspace, didx)
     _check("gn_backward_shard_merge", lib.gn_backward_shard_merge(
-        _ptr(sums), P, _ptr(mean), _ptr(rstd), _ptr(_vec("gamma", gamma, C, dev)),
-        _ptr(_vec("beta", beta, C, dev)), N, C, S, int(S_total), G,
-        _ptr(dgamma if need_dgamma else None), _ptr(dbeta if need_dbeta else None),
-        _ptr(workspace), workspace.numel(), _stream(dev)))
+        sums.data_ptr(), P, _buf_ptr("mean", mean, N * G, didx), _buf_ptr("rstd", rstd, N * G, didx),
+        _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), N, C, S, int(S_total), G,
+        _vec_ptr("dgamma", dgamma if need_dgamma else None, C, didx),
+        _vec_ptr("dbeta", dbeta if need_dbeta else None, C, didx), ws, nb, _stream_of(didx)))
     return (dgamma if need_dgamma else None, dbeta if need_dbeta else None)
 
 
