@@ -15,6 +15,15 @@ requested device so that 256^3 volumes are generated in place):
   dy ~ N(0, 1) bf16.
 - ``normal``: z ~ N(0, 1) for both x and dy (the whole-UNet census sites).
 
+dy has zero mean in every recipe above, so each channel's sums of dy and dy * xhat
+cancel to about sqrt(S) of their terms' size. A case with ``dy_mode="offset"`` instead
+draws dy = sigma * (u_c + z' + v_c * z), with per-channel u_c ~ U(1, 2) and v_c ~ U(4, 6)
+drawn after beta, z' a fresh N(0, 1) draw and z the standard normal draw that x was made
+from. Both channel sums then grow with S instead of cancelling: dbeta_c ~ sigma * u_c * S,
+and dgamma_c ~ sigma * S * (v_c * s_c + u_c * (o_c - mu_g)) / sigma_g, where v_c * s_c >= 2
+outweighs the channel offset term (|o_c - mu_g| < 2); so the parameter gradients can be
+held to a relative bar that means something.
+
 In every recipe gamma ~ N(1, 0.1), beta ~ N(0, 0.1) in fp32 and eps = 1e-5.
 Values are drawn in fp32 and rounded once (nearest-even) to bf16 or fp16 where the
 case asks for a 16-bit dtype. The pages' real activations come from a trained UNet on a fractal
@@ -41,6 +50,7 @@ class Case:
     out_dtype: torch.dtype = None  # None: the input's dtype
     eps: float = 1e-5
     tags: Tuple[str, ...] = field(default_factory=tuple)
+    dy_mode: str = "zero_mean"  # or "offset": channel sums of dy and dy * xhat that do not cancel
 
     @property
     def S(self) -> int:
@@ -64,6 +74,11 @@ SCALE8 = Case("scale8_256cube_c32_g8", 1, 32, 8, (256, 256, 256), BF16, BF16, "u
 DEEP = Case("deep_n4_c512_g32_8cube", 4, 512, 32, (8, 8, 8), BF16, BF16, "deep", 1004)
 # The 128^3 site with fp16 activations (the pages list fp16 among the input dtypes).
 SCALE7_F16 = Case("scale7_128cube_c32_g8_fp16", 1, 32, 8, (128, 128, 128), F16, F16, "unet", 1017)
+# The two top-level sites with a dy whose channel sums do not cancel (dy_mode "offset").
+SCALE7_DY_OFFSET = Case("scale7_128cube_c32_g8_dy_offset", 1, 32, 8, (128, 128, 128), BF16, BF16, "unet", 1027,
+                        dy_mode="offset")
+SCALE8_DY_OFFSET = Case("scale8_256cube_c32_g8_dy_offset", 1, 32, 8, (256, 256, 256), BF16, BF16, "unet", 1028,
+                        dy_mode="offset")
 # fp32-output mode: y in fp32, dy arrives in fp32 (holding bf16-representable values).
 DEEP_F32OUT = Case("deep_n4_c512_g32_8cube_f32out", 4, 512, 32, (8, 8, 8), BF16, F32, "deep", 1004,
                    out_dtype=F32)
@@ -114,6 +129,11 @@ def make(case: Case, device="cpu", with_dy=True):
     scale, offset = _channel_params(rng, case)
     gamma = rng.normal(1.0, 0.1, case.C).astype(np.float32)
     beta = rng.normal(0.0, 0.1, case.C).astype(np.float32)
+    if case.dy_mode not in ("zero_mean", "offset"):
+        raise ValueError(case.dy_mode)
+    if case.dy_mode == "offset":
+        u = rng.uniform(1.0, 2.0, case.C)
+        v = rng.uniform(4.0, 6.0, case.C)
 
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -122,12 +142,16 @@ def make(case: Case, device="cpu", with_dy=True):
     bshape = (1, case.C) + (1,) * len(case.spatial)
     sc = torch.tensor(scale, dtype=torch.float32, device=dev).view(bshape)
     of = torch.tensor(offset, dtype=torch.float32, device=dev).view(bshape)
-    x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
-    x.mul_(sc).add_(of)
-    x = x.to(case.x_dtype)
+    z = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    x = (z * sc).add_(of).to(case.x_dtype)
     dy = None
     if with_dy:
         dy = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        if case.dy_mode == "offset":
+            uc = torch.tensor(u, dtype=torch.float32, device=dev).view(bshape)
+            vc = torch.tensor(v, dtype=torch.float32, device=dev).view(bshape)
+            dy.add_(uc).add_(z.mul_(vc))
+        del z
         dy.mul_(_dy_sigma(case))
         # dy carries the output's values; in the fp32-output mode it holds values of x's
         # 16-bit dtype stored as fp32, so that both dy dtypes describe the same numbers.
@@ -143,7 +167,8 @@ def make(case: Case, device="cpu", with_dy=True):
     }
 
 
-def custom(N, C, G, spatial, x_dtype=BF16, dy_dtype=None, dist="normal", seed=0, out_dtype=None):
+def custom(N, C, G, spatial, x_dtype=BF16, dy_dtype=None, dist="normal", seed=0, out_dtype=None,
+           dy_mode="zero_mean"):
     """A Case for an arbitrary test shape (ragged sizes, edge cases)."""
     return Case(f"custom_n{N}_c{C}_g{G}_{'x'.join(map(str, spatial))}", N, C, G, tuple(spatial),
-                x_dtype, dy_dtype or (out_dtype or x_dtype), dist, seed, out_dtype=out_dtype)
+                x_dtype, dy_dtype or (out_dtype or x_dtype), dist, seed, out_dtype=out_dtype, dy_mode=dy_mode)
