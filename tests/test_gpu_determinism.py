@@ -100,3 +100,37 @@ def _run_inputs(inp, sync=True):
     if sync:
         torch.cuda.synchronize()
     return [y, mean, rstd, dx, dg, db]
+
+
+def test_negative_control_atomic_order_accumulation_is_caught():
+    """The check above can fail: a test-only reduction outside libgn.so (libgn_probe.so's
+    gnp_atomic_group_sums) that reduces each job of the 128^3 site in a fixed order but adds
+    the jobs' partials to its group's total with global atomic adds, in the order the
+    workgroups finish, gives more than one bit pattern over 10 identical calls; libgn.so's
+    group statistics on the same input give exactly one ("Make loss calculation deterministic
+    and sync-free", first paragraph: atomically ordered sums drift between identical calls)."""
+    import ctypes
+
+    sys.path.insert(0, ROOT)
+    import bench
+    probe = bench.probe_lib()
+    case = workloads.SCALE7
+    inp = workloads.make(case, "cuda", with_dy=False)
+    x, G = inp["x"], inp["G"]
+    groups, M = case.N * G, (case.C // G) * case.S
+    sums = torch.empty(groups, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    atomic, ours = set(), set()
+    for _ in range(10):
+        assert probe.gnp_atomic_group_sums(x.data_ptr(), groups, M, 4096, sums.data_ptr(), stream) == 0
+        _, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"])
+        torch.cuda.synchronize()
+        atomic.add(_bits(sums).cpu().numpy().tobytes())
+        ours.add(_bits(mean).cpu().numpy().tobytes() + _bits(rstd).cpu().numpy().tobytes())
+    # the control computes the right thing: its sums are the group sums to fp32 accuracy
+    ref = x.double().view(groups, M).sum(dim=1)
+    assert torch.allclose(sums.double(), ref, rtol=1e-5, atol=1e-3 * M ** 0.5)
+    print(f"[determinism] atomic-order sums: {len(atomic)} bit patterns in 10 calls; libgn.so: {len(ours)}",
+          flush=True)
+    assert len(atomic) >= 2
+    assert len(ours) == 1
