@@ -24,12 +24,11 @@ def test_trace_cases_are_listed():
         assert name in r.stdout, name
 
 
-def test_threaded_oracle_baseline_splits_into_independent_groups():
-    """The CPU baseline's threaded run calls the oracle once per (n, g) group on its channel
-    slice; a group's slice with one group must give the whole call's outputs for it, bitwise
-    (groups share nothing in the definition), and the run reports the threads it used."""
-    import types
-
+def test_all_core_oracle_gives_the_whole_calls_bits():
+    """The CPU baseline's all-core run splits each direction into per-(n, g) group calls and
+    per-(n, c) row calls of the oracle; every output must be the whole-volume call's, bitwise
+    (the definition's sums run over the same elements in the same order), on a ragged shape
+    with several samples and groups."""
     import numpy as np
     import torch
 
@@ -41,17 +40,12 @@ def test_threaded_oracle_baseline_splits_into_independent_groups():
     x = (torch.randn(N, C, 4, 6, 5, generator=gen) * 2 + 0.5).to(torch.bfloat16)
     dy = torch.randn(N, C, 4, 6, 5, generator=gen).to(torch.bfloat16)
     gm, bt = torch.randn(C, generator=gen), torch.randn(C, generator=gen)
-    whole_y = O.forward(x, G, gm, bt, eps=1e-5)["y"]
-    whole = O.backward(dy, x, G, gm, eps=1e-5)
-    Cg = C // G
-    for n in range(N):
-        for g in range(G):
-            sl = slice(g * Cg, (g + 1) * Cg)
-            xs, ds = x[n:n + 1, sl].contiguous(), dy[n:n + 1, sl].contiguous()
-            assert np.array_equal(O.forward(xs, 1, gm[sl], bt[sl], eps=1e-5)["y"], whole_y[n:n + 1, sl])
-            part = O.backward(ds, xs, 1, gm[sl], eps=1e-5)
-            assert np.array_equal(part["dx"], whole["dx"][n:n + 1, sl])
-    r = types.SimpleNamespace(x=x, dy=dy, gamma=gm, beta=bt, G=G, eps=1e-5,
-                              case=types.SimpleNamespace(N=N, C=C), step_bytes=16 * x.numel())
-    out = bench._oracle_threads(r, min_seconds=0.0, max_reps=2)
-    assert 1 <= out["cores"] <= min(16, N * G) and out["value"] > 0
+    f = O.forward(x, G, gm, bt, eps=1e-5)
+    b = O.backward(dy, x, G, gm, eps=1e-5)
+    out = bench.oracle_all_cores(x, dy, gm, bt, G, 1e-5, min_seconds=0.0, max_reps=1, workers=3)
+    o = out["_outputs"]
+    for k in ("mean", "rstd", "y"):
+        assert np.array_equal(o[k], f[k]), k
+    for k in ("dx", "dgamma", "dbeta"):
+        assert np.array_equal(o[k], b[k]), k
+    assert out["cores"] == 3 and out["forward"]["seconds"] > 0 and out["backward"]["seconds"] > 0
