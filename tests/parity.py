@@ -193,8 +193,11 @@ WELL_CONDITIONED = 0.1
 
 
 def well_conditioned(ref, abs_terms):
+    """Channels whose sum keeps at least WELL_CONDITIONED of its terms' magnitude (a channel
+    whose terms are all zero has nothing to be relative to: its floor is zero anyway)."""
     ref = np.asarray(ref, dtype=np.float64)
-    return np.isfinite(ref) & (np.abs(ref) >= WELL_CONDITIONED * np.asarray(abs_terms))
+    abs_terms = np.asarray(abs_terms, dtype=np.float64)
+    return np.isfinite(ref) & (abs_terms > 0) & (np.abs(ref) >= WELL_CONDITIONED * abs_terms)
 
 
 def check_param(name, got, ref, abs_terms, depth, slack=0.0):
