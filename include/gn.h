@@ -31,8 +31,9 @@
  * are [N*G] fp32, indexed n*G + g. gamma, beta, dgamma, dbeta are [C] fp32.
  *
  * Ownership and ordering. The caller owns and allocates every buffer, including the
- * workspace (gn_workspace_bytes). The library never allocates device memory, never
- * synchronizes the device or the stream, and never copies device-to-host. All work is
+ * workspace (gn_workspace_bytes). The library never allocates device memory (the static
+ * scratch array of gn_forward_noalloc is part of its code object), never synchronizes the
+ * device or the stream, and never copies device-to-host. All work is
  * enqueued on `stream` (a hipStream_t; NULL means the null stream of the current
  * device) in stream order, and the call returns as soon as it is enqueued. Outputs are
  * fully overwritten (dgamma/dbeta are written, not accumulated). The workspace holds
@@ -52,7 +53,8 @@
  * Errors. Every entry point returns an int status (gn_status). All validation runs
  * before anything is enqueued; on any error other than GN_ERR_LAUNCH nothing has been
  * enqueued and no output is touched. After GN_ERR_LAUNCH outputs are undefined.
- * Nothing is thrown across the ABI and no state is kept between calls.
+ * Nothing is thrown across the ABI and no state is kept between calls, apart from the
+ * contents of gn_forward_noalloc's scratch.
  */
 #ifndef GN_H
 #define GN_H
@@ -85,8 +87,10 @@ typedef enum gn_status {
                              stream belongs to another device */
     GN_ERR_LAUNCH = 9,    /* the HIP runtime refused a launch; outputs are undefined */
     GN_ERR_ACTIVATION = 10, /* unknown activation code */
-    GN_ERR_LAYOUT = 11      /* channels-last: C not a multiple of 8, C/8 not dividing 256, or
+    GN_ERR_LAYOUT = 11,     /* channels-last: C not a multiple of 8, C/8 not dividing 256, or
                                C/G neither dividing 8 nor a multiple of 8 */
+    GN_ERR_SCRATCH = 12     /* gn_forward_noalloc: gn_workspace_bytes(N, C, S, G) exceeds
+                               GN_NOALLOC_SCRATCH_BYTES */
 } gn_status;
 
 /*
@@ -186,6 +190,23 @@ int gn_backward_reduce(const void* dy, int dy_dtype, const void* x, int x_dtype,
 int gn_backward_apply(const void* dy, int dy_dtype, const void* x, int x_dtype,
                       int64_t N, int64_t C, int64_t S, int64_t G, int activation, void* dx,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gn_forward for callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation. Same arguments,
+ * semantics, results (bitwise those of gn_forward) and errors, without the workspace: the
+ * library's own static scratch array of GN_NOALLOC_SCRATCH_BYTES per device serves as the
+ * workspace. Shapes whose gn_workspace_bytes exceeds that size return GN_ERR_SCRATCH before
+ * anything is enqueued. The call allocates nothing. Every call on one device shares that
+ * device's scratch, which keeps the last call's contents: calls that overlap on one device
+ * (two streams at once, or a graph replayed beside another call) race, and must be ordered
+ * by the caller. Nothing in the scratch needs to start at zero.
+ */
+#define GN_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+int gn_forward_noalloc(const void* x, int x_dtype, const float* gamma, const float* beta,
+                       int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
+                       void* y, int y_dtype, float* mean, float* rstd, void* stream);
 
 /*
  * The two launches of gn_forward as two calls, stream-ordered on one workspace, so that
@@ -378,7 +399,7 @@ int gn_backward_shard_merge(const float* sums /* [P][N*C][2] */, int64_t P,
 /* ABI version of this header (incremented on any incompatible change); gn_abi_version()
  * returns the version the library was built with, so a caller can check that the two
  * agree before the first call. */
-#define GN_ABI_VERSION 10
+#define GN_ABI_VERSION 11
 int gn_abi_version(void);
 
 #ifdef __cplusplus

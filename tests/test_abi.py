@@ -21,7 +21,7 @@ def _declared_functions():
 
 def test_every_declared_function_is_exported():
     names = _declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for name in names:
         assert hasattr(lib, name), name
 
@@ -37,7 +37,7 @@ def test_status_enum_matches_header():
     for code in STATUS_NAMES:
         assert lib.gn_status_string(code)
     assert lib.gn_status_string(1234) == b"unknown status"
-    assert lib.gn_abi_version() == int(re.search(r"#define GN_ABI_VERSION (\d+)", text).group(1)) == 10
+    assert lib.gn_abi_version() == int(re.search(r"#define GN_ABI_VERSION (\d+)", text).group(1)) == 11
 
 
 # Fake but aligned, non-null addresses: validation never dereferences them, and every
@@ -222,3 +222,33 @@ def test_moments_record_layout():
     text = (pathlib.Path(__file__).resolve().parents[1] / "include" / "gn.h").read_text()
     assert [(n, t) for n, t in _struct_fields(text, "gn_moments")] == [
         ("mean_hi", "float"), ("mean_lo", "float"), ("m2", "float"), ("count", "uint32_t")]
+
+
+def fwd_noalloc(**kw):
+    args = dict(x=A, xdt=GN_BF16, gamma=None, beta=None, N=1, C=8, S=64, G=4, eps=1e-5, act=0, y=B,
+                ydt=GN_BF16, mean=A, rstd=B, stream=None)
+    args.update(kw)
+    return lib.gn_forward_noalloc(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(y=None), 1), (dict(rstd=None), 1),
+    (dict(N=0), 2), (dict(C=8, G=8, S=1), 2), (dict(C=6, G=4), 3),
+    (dict(xdt=7), 4), (dict(xdt=GN_F32, ydt=GN_BF16), 4), (dict(eps=float("nan")), 5),
+    (dict(x=ctypes.c_void_p(0x10002)), 7), (dict(act=5), 10),
+    # a shape whose workspace exceeds the static scratch (65536 rows need 2 MiB of row records)
+    (dict(N=64, C=1024, S=8, G=32), 12),
+    # a valid shape that fits gets as far as the device check, which host addresses fail
+    (dict(), 8), (dict(N=32, C=256, S=8, G=32), 8),
+])
+def test_noalloc_forward_validation(kw, status):
+    assert fwd_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size_in_header_and_binding():
+    from unet_groupnorm_amd._lib import GN_NOALLOC_SCRATCH_BYTES
+    text = open(HEADER).read()
+    m = re.search(r"#define GN_NOALLOC_SCRATCH_BYTES \(1u << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == GN_NOALLOC_SCRATCH_BYTES
+    # the largest case above that fits, and the one that does not
+    assert lib.gn_workspace_bytes(32, 256, 8, 32) <= GN_NOALLOC_SCRATCH_BYTES < lib.gn_workspace_bytes(64, 1024, 8, 32)

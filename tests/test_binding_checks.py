@@ -86,7 +86,7 @@ def test_backward_reaches_the_library_when_every_tensor_is_right():
     assert e.value.status == 8
 
 
-def test_split_phase_refuses_bad_buffers():
+def test_split_phase_and_noalloc_refuse_bad_buffers():
     x = _x()
     ws = torch.empty(1 << 16, dtype=torch.uint8)
     with pytest.raises(ValueError):
@@ -96,3 +96,8 @@ def test_split_phase_refuses_bad_buffers():
     with pytest.raises(ValueError):
         gn.gn_backward_finish(_x(), x, torch.empty(N, G), torch.empty(N, G), _vec(), G, None,
                               torch.empty(C + 1), None, ws)
+    with pytest.raises(ValueError):
+        gn.gn_forward_noalloc(x, _vec(), _vec(), G, mean=torch.empty(3), rstd=torch.empty(N, G))
+    with pytest.raises(GnError) as e:
+        gn.gn_forward_noalloc(x, _vec(), _vec(), G)
+    assert e.value.status == 8

@@ -17,6 +17,7 @@ from .gn import (  # noqa: F401
     gn_forward,
     gn_forward_apply,
     gn_forward_finish,
+    gn_forward_noalloc,
     gn_forward_partials,
     gn_forward_shard_merge,
     gn_forward_shard_stats,

@@ -16,8 +16,10 @@ GN_ACT_NONE, GN_ACT_RELU = 0, 1
 STATUS_NAMES = {
     0: "GN_OK", 1: "GN_ERR_NULL", 2: "GN_ERR_SHAPE", 3: "GN_ERR_GROUPS", 4: "GN_ERR_DTYPE",
     5: "GN_ERR_EPS", 6: "GN_ERR_WORKSPACE", 7: "GN_ERR_ALIGN", 8: "GN_ERR_DEVICE", 9: "GN_ERR_LAUNCH",
-    10: "GN_ERR_ACTIVATION", 11: "GN_ERR_LAYOUT",
+    10: "GN_ERR_ACTIVATION", 11: "GN_ERR_LAYOUT", 12: "GN_ERR_SCRATCH",
 }
+# Size of the static scratch array that gn_forward_noalloc uses as its workspace.
+GN_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 
 class GnPlanInfo(ctypes.Structure):
@@ -76,6 +78,7 @@ def _declare(lib):
     sig = {
         "gn_workspace_bytes": (SZ, [I64, I64, I64, I64]),
         "gn_forward": (I, [P, I, P, P, I64, I64, I64, I64, F, I, P, I, P, P, P, SZ, P]),
+        "gn_forward_noalloc": (I, [P, I, P, P, I64, I64, I64, I64, F, I, P, I, P, P, P]),
         "gn_forward_stats": (I, [P, I, P, P, I64, I64, I64, I64, F, P, P, P, SZ, P]),
         "gn_forward_apply": (I, [P, I, I64, I64, I64, I64, I, P, I, P, SZ, P]),
         "gn_backward": (I, [P, I, P, I, P, P, P, P, I, I64, I64, I64, I64, P, P, P, P, SZ, P]),

@@ -1,12 +1,14 @@
 // gn_api.cpp -- the C ABI declared in include/gn.h: validation, planning, launches.
 //
-// Every check runs before anything is enqueued. The library keeps no state, allocates
-// nothing, never synchronizes and never reads device memory from the host.
+// Every check runs before anything is enqueued. The library allocates nothing, never
+// synchronizes and never reads device memory from the host. Its only state is, per
+// device, the address of the static scratch array that gn_forward_noalloc uses.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <mutex>
 
 #include "gn.h"
 #include "gn_launch.hpp"
@@ -150,6 +152,36 @@ int bwd_check(const void* dy, int dy_dtype, const void* x, int x_dtype, const fl
 
 int launch_status(hipError_t e) { return e == hipSuccess ? GN_OK : GN_ERR_LAUNCH; }
 
+// ------------------------------------------------------------------ static scratch
+//
+// The workspace of gn_forward_noalloc: device memory of the library itself, one copy per
+// device (each device the library runs on holds it until the process ends). In host code
+// `scratch` names a host-side stand-in, not a device address; its address on a device is
+// queried once per device, with that device current, and only that address is handed to
+// kernels. Every call on a device shares that device's copy: calls that overlap on one
+// device (two streams at once) race on it.
+static __device__ __align__(256) unsigned char scratch[GN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on device dev, which must be current; nullptr if the
+// runtime cannot give it.
+void* scratch_on(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            ptr = nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
 // The two halves of gn_forward. On the resident path the first does nothing and the
 // second runs the whole forward; otherwise the second is the normalize with the finalize
 // folded into each of its workgroups (the split-phase entry points run it alone).
@@ -253,6 +285,7 @@ const char* gn_status_string(int status)
         case GN_ERR_LAUNCH: return "kernel launch failed";
         case GN_ERR_ACTIVATION: return "unknown activation (GN_ACT_NONE or GN_ACT_RELU)";
         case GN_ERR_LAYOUT: return "shape not supported channels-last (C a multiple of 8 with C/8 dividing 256; C/G dividing 8 or a multiple of 8)";
+        case GN_ERR_SCRATCH: return "gn_forward_noalloc: the shape needs a larger workspace than its static scratch holds (gn_workspace_bytes > GN_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -318,6 +351,26 @@ int gn_forward(const void* x, int x_dtype, const float* gamma, const float* beta
     if ((rc = ds.same_device({gamma, beta, y, mean, rstd, workspace}))) return rc;
     const gn::KArgs a = kargs_for(p, activation, x_dtype);
     const gn::Workspace w = gn::workspace_of(workspace, p);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = fwd_partials(x, x_dtype, p, a, w, st))) return rc;
+    return fwd_finish(x, x_dtype, gamma, beta, eps, y, y_dtype, mean, rstd, p, a, w, st);
+}
+
+int gn_forward_noalloc(const void* x, int x_dtype, const float* gamma, const float* beta,
+                       int64_t N, int64_t C, int64_t S, int64_t G, float eps, int activation,
+                       void* y, int y_dtype, float* mean, float* rstd, void* stream)
+{
+    gn::Plan p;
+    int rc = fwd_args_check(x, x_dtype, gamma, beta, N, C, S, G, eps, activation, y, y_dtype, mean, rstd, &p);
+    if (rc) return rc;
+    if (p.ws_bytes > GN_NOALLOC_SCRATCH_BYTES) return GN_ERR_SCRATCH;
+    DeviceScope ds;
+    if ((rc = ds.enter(x, stream))) return rc;
+    if ((rc = ds.same_device({gamma, beta, y, mean, rstd}))) return rc;
+    void* ws = scratch_on(ds.device());
+    if (!ws) return GN_ERR_DEVICE;
+    const gn::KArgs a = kargs_for(p, activation, x_dtype);
+    const gn::Workspace w = gn::workspace_of(ws, p);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = fwd_partials(x, x_dtype, p, a, w, st))) return rc;
     return fwd_finish(x, x_dtype, gamma, beta, eps, y, y_dtype, mean, rstd, p, a, w, st);

@@ -208,6 +208,26 @@ def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, activation=None, 
     return y, mean, rstd
 
 
+def gn_forward_noalloc(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, activation=None, out=None, mean=None,
+                       rstd=None):
+    """gn_forward through the allocation-free entry point (NCDHW): the library's static
+    scratch serves as the workspace. Outputs not given are allocated here by torch; pass
+    out, mean and rstd for a call that allocates nothing at all."""
+    _contig("x", x)
+    N, C, S, G = _dims(x, G)
+    didx = x.get_device()
+    xsig = _sig(x)
+    y = out if out is not None else torch.empty_like(x, dtype=out_dtype or x.dtype)
+    y_ptr = _like_ptr("out", y, xsig, didx, _IN_DTYPES)
+    mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
+    rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
+    _check("gn_forward_noalloc", lib.gn_forward_noalloc(
+        x.data_ptr(), _dtype(x), _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx),
+        N, C, S, G, float(eps), _act(activation), y_ptr, _dtype(y), _buf_ptr("mean", mean, N * G, didx),
+        _buf_ptr("rstd", rstd, N * G, didx), _stream_of(didx)))
+    return y, mean, rstd
+
+
 def _split_args(x, G):
     """(N, C, S, G, didx, _sig(x)) of an NCDHW x for the split-phase entry points."""
     _contig("x", x)
