@@ -120,9 +120,9 @@ def probe_lib():
             raise ImportError(f"{path} is missing; build first (python -c 'import __graft_entry__ as g; g.build()')")
         lib = ctypes.CDLL(path)
         P, I, I64, SZ, U32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint32
-        lib.gnp_read.argtypes = [P, SZ, I, U32, P, I64, P]
-        lib.gnp_write.argtypes = [P, SZ, I, U32, I64, P]
-        lib.gnp_copy.argtypes = [P, P, SZ, I, I, I64, P]
+        lib.gnp_read.argtypes = [P, SZ, I, I, U32, P, I64, P]
+        lib.gnp_write.argtypes = [P, SZ, I, I, U32, I64, P]
+        lib.gnp_copy.argtypes = [P, P, SZ, I, I, I, I64, P]
         lib.gnp_atomic_group_sums.argtypes = [P, I64, I64, I64, P, P]
         for f in (lib.gnp_read, lib.gnp_write, lib.gnp_copy, lib.gnp_atomic_group_sums):
             f.restype = I
@@ -135,51 +135,59 @@ def _stream_ptr():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def ceiling(nbytes=1 << 30, reps=10, grids=(1024, 2048, 4096, 8192)):
+def ceiling(nbytes=1 << 30, reps=10, grids=(1024, 2048, 4096, 8192, 16384, 32768), vecs=(2, 4, 8, 16)):
     """HBM rates of pure streams over `nbytes` buffers (far larger than the 256 MiB last-level
-    cache), with plain and nontemporal loads and stores, each at the best of a few grid sizes:
-    the rates the device delivers for the traffic the GroupNorm kernels generate."""
+    cache), with plain and nontemporal loads and stores, each at the best of a sweep of grid
+    sizes and vectors in flight per lane: the rates the device delivers for the traffic the
+    GroupNorm kernels generate."""
     import torch
     lib = probe_lib()
     src = torch.full((nbytes // 4,), 7, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
     st = _stream_ptr()
+    magic = 0x5EED5EED
     variants = {
-        "read_nontemporal": (lambda g: lib.gnp_read(src.data_ptr(), nbytes, 1, 0x5EED5EED, sink.data_ptr(), g, st), nbytes),
-        "read_plain": (lambda g: lib.gnp_read(src.data_ptr(), nbytes, 0, 0x5EED5EED, sink.data_ptr(), g, st), nbytes),
-        "write_nontemporal": (lambda g: lib.gnp_write(dst.data_ptr(), nbytes, 1, 3, g, st), nbytes),
-        "write_plain": (lambda g: lib.gnp_write(dst.data_ptr(), nbytes, 0, 3, g, st), nbytes),
-        "copy_nontemporal": (lambda g: lib.gnp_copy(src.data_ptr(), dst.data_ptr(), nbytes, 1, 1, g, st), 2 * nbytes),
-        "copy_plain": (lambda g: lib.gnp_copy(src.data_ptr(), dst.data_ptr(), nbytes, 0, 0, g, st), 2 * nbytes),
+        "read_nontemporal": (lambda g, v: lib.gnp_read(src.data_ptr(), nbytes, 1, v, magic, sink.data_ptr(), g, st),
+                             nbytes),
+        "read_plain": (lambda g, v: lib.gnp_read(src.data_ptr(), nbytes, 0, v, magic, sink.data_ptr(), g, st), nbytes),
+        "write_nontemporal": (lambda g, v: lib.gnp_write(dst.data_ptr(), nbytes, 1, v, 3, g, st), nbytes),
+        "write_plain": (lambda g, v: lib.gnp_write(dst.data_ptr(), nbytes, 0, v, 3, g, st), nbytes),
+        "copy_nontemporal": (lambda g, v: lib.gnp_copy(src.data_ptr(), dst.data_ptr(), nbytes, 1, 1, v, g, st),
+                             2 * nbytes),
+        "copy_plain": (lambda g, v: lib.gnp_copy(src.data_ptr(), dst.data_ptr(), nbytes, 0, 0, v, g, st), 2 * nbytes),
+        "copy_nt_loads_plain_stores": (lambda g, v: lib.gnp_copy(src.data_ptr(), dst.data_ptr(), nbytes, 1, 0, v, g,
+                                                                 st), 2 * nbytes),
     }
     out = {}
     for name, (fn, moved) in variants.items():
         best = None
-        for g in grids:
-            for _ in range(2):
-                assert fn(g) == 0, name
-            e0, e1 = _events(2)
-            e0.record()
-            for _ in range(reps):
-                fn(g)
-            e1.record()
-            torch.cuda.synchronize()
-            gbps = moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
-            if best is None or gbps > best[0]:
-                best = (gbps, g)
-        out[name] = {"gbps": round(best[0], 1), "grid": best[1]}
+        for v in vecs:
+            for g in grids:
+                for _ in range(2):
+                    assert fn(g, v) == 0, name
+                e0, e1 = _events(2)
+                e0.record()
+                for _ in range(reps):
+                    fn(g, v)
+                e1.record()
+                torch.cuda.synchronize()
+                gbps = moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+                if best is None or gbps > best[0]:
+                    best = (gbps, g, v)
+        out[name] = {"gbps": round(best[0], 1), "grid": best[1], "vecs": best[2]}
     assert int(sink.sum().item()) == 0  # the magic value was never read, so nothing was written
     read = max(out["read_nontemporal"]["gbps"], out["read_plain"]["gbps"])
     write = max(out["write_nontemporal"]["gbps"], out["write_plain"]["gbps"])
-    copy = max(out["copy_nontemporal"]["gbps"], out["copy_plain"]["gbps"])
+    copy = max(out[k]["gbps"] for k in out if k.startswith("copy"))
     del src, dst
     torch.cuda.empty_cache()
     return {"bytes": nbytes, "read_gbps": read, "write_gbps": write, "copy_gbps": copy,
             # a copy moves equal bytes each way: what pricing reads and writes separately predicts
             "copy_predicted_gbps": round(2 / (1 / read + 1 / write), 1),
             "variants": out, "kernels": "libgn_probe.so gnp_read / gnp_write / gnp_copy (16-byte vectors, "
-                                        "8 per lane in flight, 256-thread workgroups)"}
+                                        "256-thread workgroups; best of 2-16 vectors a lane in flight and "
+                                        "1024-32768 workgroups)"}
 
 
 def kernel_bounds(rw, numel, kernel_us, ceil):
@@ -621,7 +629,7 @@ def probe_copy(nbytes=1 << 30, reps=5):
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(reps):
-        assert probe_lib().gnp_copy(src.data_ptr(), dst.data_ptr(), nbytes, 1, 1, 4096, _stream_ptr()) == 0
+        assert probe_lib().gnp_copy(src.data_ptr(), dst.data_ptr(), nbytes, 1, 1, 8, 4096, _stream_ptr()) == 0
     torch.cuda.synchronize()
 
 

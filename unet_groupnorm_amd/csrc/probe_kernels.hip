@@ -17,16 +17,18 @@
 // C ABI (all pointers are device pointers; `stream` is a hipStream_t, NULL for the null
 // stream; every function returns 0 on success, 1 for arguments it rejects before launching
 // anything, 2 when the runtime refuses the launch):
-//   int gnp_read (const void* src, size_t bytes, int nontemporal, uint32_t magic,
+//   int gnp_read (const void* src, size_t bytes, int nontemporal, int vecs, uint32_t magic,
 //                 uint32_t* sink, int64_t grid, void* stream);
-//       reads `bytes` (a multiple of 16 * 256 * kProbeVecs) once; sink[0..63] is written
-//       only by a lane whose xor of everything it read equals `magic` (so the loads cannot
-//       be dropped; pass a value the data cannot produce and sink stays untouched).
-//   int gnp_write(void* dst, size_t bytes, int nontemporal, uint32_t value, int64_t grid,
-//                 void* stream);
+//       reads `bytes` (a multiple of 16 * 256 * vecs) once; sink[0..63] is written only by
+//       a lane whose xor of everything it read equals `magic` (so the loads cannot be
+//       dropped; pass a value the data cannot produce and sink stays untouched).
+//   int gnp_write(void* dst, size_t bytes, int nontemporal, int vecs, uint32_t value,
+//                 int64_t grid, void* stream);
 //       fills `bytes` with the 32-bit `value`.
 //   int gnp_copy (const void* src, void* dst, size_t bytes, int nontemporal_loads,
-//                 int nontemporal_stores, int64_t grid, void* stream);
+//                 int nontemporal_stores, int vecs, int64_t grid, void* stream);
+//   `vecs` (2, 4, 8 or 16) is the number of 16-byte vectors each lane has in flight per
+//   tile; workgroups (256 threads) stride over the tiles, `grid` of them.
 //   int gnp_atomic_group_sums(const uint16_t* x_bf16, int64_t groups, int64_t group_elems,
 //                             int64_t chunk, float* sums, void* stream);
 //       sums[g] = sum of the group's bf16 values, g < groups, each group `group_elems`
@@ -35,13 +37,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kProbeBlock = 256;
-constexpr int kProbeVecs = 8;  // 16-byte vectors each lane has in flight per tile
-constexpr int64_t kTileBytes = int64_t(16) * kProbeBlock * kProbeVecs;
 
 template <bool NT>
 __device__ __forceinline__ u32x4 ld(const u32x4* p)
@@ -61,50 +63,65 @@ __device__ __forceinline__ void st(u32x4* p, u32x4 v)
 // Tile t covers vectors [t * 256 * V, (t + 1) * 256 * V); lane `tid` takes vectors
 // tid, tid + 256, ... of it, so every load and store instruction of a wave is one contiguous
 // 1 KiB. Workgroups stride over the tiles.
-template <bool NT>
+template <int V, bool NT>
 __global__ void __launch_bounds__(kProbeBlock)
 read_kernel(const u32x4* __restrict__ src, int64_t tiles, uint32_t magic, uint32_t* __restrict__ sink)
 {
     const int tid = threadIdx.x;
     uint32_t acc = 0;
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const u32x4* p = src + t * (kProbeBlock * kProbeVecs) + tid;
-        u32x4 v[kProbeVecs];
+        const u32x4* p = src + t * (kProbeBlock * V) + tid;
+        u32x4 v[V];
 #pragma unroll
-        for (int u = 0; u < kProbeVecs; ++u) v[u] = ld<NT>(p + u * kProbeBlock);
+        for (int u = 0; u < V; ++u) v[u] = ld<NT>(p + u * kProbeBlock);
 #pragma unroll
-        for (int u = 0; u < kProbeVecs; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        for (int u = 0; u < V; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
     if (acc == magic) sink[tid & 63] = acc;
 }
 
-template <bool NT>
+template <int V, bool NT>
 __global__ void __launch_bounds__(kProbeBlock)
 write_kernel(u32x4* __restrict__ dst, int64_t tiles, uint32_t value)
 {
     const int tid = threadIdx.x;
     const u32x4 v = {value, value, value, value};
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        u32x4* p = dst + t * (kProbeBlock * kProbeVecs) + tid;
+        u32x4* p = dst + t * (kProbeBlock * V) + tid;
 #pragma unroll
-        for (int u = 0; u < kProbeVecs; ++u) st<NT>(p + u * kProbeBlock, v);
+        for (int u = 0; u < V; ++u) st<NT>(p + u * kProbeBlock, v);
     }
 }
 
-template <bool NTL, bool NTS>
+template <int V, bool NTL, bool NTS>
 __global__ void __launch_bounds__(kProbeBlock)
 copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t tiles)
 {
     const int tid = threadIdx.x;
     for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-        const int64_t o = t * (kProbeBlock * kProbeVecs) + tid;
-        u32x4 v[kProbeVecs];
+        const int64_t o = t * (kProbeBlock * V) + tid;
+        u32x4 v[V];
 #pragma unroll
-        for (int u = 0; u < kProbeVecs; ++u) v[u] = ld<NTL>(src + o + u * kProbeBlock);
+        for (int u = 0; u < V; ++u) v[u] = ld<NTL>(src + o + u * kProbeBlock);
 #pragma unroll
-        for (int u = 0; u < kProbeVecs; ++u) st<NTS>(dst + o + u * kProbeBlock, v[u]);
+        for (int u = 0; u < V; ++u) st<NTS>(dst + o + u * kProbeBlock, v[u]);
     }
 }
+
+// Calls f with std::integral_constant<int, V> for V in {2, 4, 8, 16}; -1 for other values.
+template <typename F>
+int with_vecs(int vecs, F&& f)
+{
+    switch (vecs) {
+        case 2: return f(std::integral_constant<int, 2>{});
+        case 4: return f(std::integral_constant<int, 4>{});
+        case 8: return f(std::integral_constant<int, 8>{});
+        case 16: return f(std::integral_constant<int, 16>{});
+        default: return -1;
+    }
+}
+
+int64_t tile_bytes(int vecs) { return int64_t(16) * kProbeBlock * vecs; }
 
 // ------------------------------------------------------------------ negative control
 
@@ -157,58 +174,70 @@ unsigned grid_for(int64_t grid, int64_t tiles)
 
 extern "C" {
 
-int gnp_read(const void* src, size_t bytes, int nontemporal, uint32_t magic, uint32_t* sink, int64_t grid,
-             void* stream)
+int gnp_read(const void* src, size_t bytes, int nontemporal, int vecs, uint32_t magic, uint32_t* sink,
+             int64_t grid, void* stream)
 {
-    if (!src || !sink || bytes == 0 || bytes % kTileBytes != 0 || grid < 1) return 1;
-    const int64_t tiles = int64_t(bytes / kTileBytes);
+    if (!src || !sink || bytes == 0 || grid < 1 || vecs < 1 || bytes % tile_bytes(vecs) != 0) return 1;
+    const int64_t tiles = int64_t(bytes / tile_bytes(vecs));
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const u32x4* s = static_cast<const u32x4*>(src);
-    if (nontemporal)
-        read_kernel<true><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(s, tiles, magic, sink);
-    else
-        read_kernel<false><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(s, tiles, magic, sink);
-    return status(hipGetLastError());
+    const int rc = with_vecs(vecs, [&](auto v) {
+        constexpr int V = decltype(v)::value;
+        if (nontemporal)
+            read_kernel<V, true><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(s, tiles, magic, sink);
+        else
+            read_kernel<V, false><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(s, tiles, magic, sink);
+        return status(hipGetLastError());
+    });
+    return rc < 0 ? 1 : rc;
 }
 
-int gnp_write(void* dst, size_t bytes, int nontemporal, uint32_t value, int64_t grid, void* stream)
+int gnp_write(void* dst, size_t bytes, int nontemporal, int vecs, uint32_t value, int64_t grid, void* stream)
 {
-    if (!dst || bytes == 0 || bytes % kTileBytes != 0 || grid < 1) return 1;
-    const int64_t tiles = int64_t(bytes / kTileBytes);
+    if (!dst || bytes == 0 || grid < 1 || vecs < 1 || bytes % tile_bytes(vecs) != 0) return 1;
+    const int64_t tiles = int64_t(bytes / tile_bytes(vecs));
     const hipStream_t st = static_cast<hipStream_t>(stream);
     u32x4* d = static_cast<u32x4*>(dst);
-    if (nontemporal)
-        write_kernel<true><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(d, tiles, value);
-    else
-        write_kernel<false><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(d, tiles, value);
-    return status(hipGetLastError());
+    const int rc = with_vecs(vecs, [&](auto v) {
+        constexpr int V = decltype(v)::value;
+        if (nontemporal)
+            write_kernel<V, true><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(d, tiles, value);
+        else
+            write_kernel<V, false><<<grid_for(grid, tiles), kProbeBlock, 0, st>>>(d, tiles, value);
+        return status(hipGetLastError());
+    });
+    return rc < 0 ? 1 : rc;
 }
 
-int gnp_copy(const void* src, void* dst, size_t bytes, int nontemporal_loads, int nontemporal_stores, int64_t grid,
-             void* stream)
+int gnp_copy(const void* src, void* dst, size_t bytes, int nontemporal_loads, int nontemporal_stores, int vecs,
+             int64_t grid, void* stream)
 {
-    if (!src || !dst || bytes == 0 || bytes % kTileBytes != 0 || grid < 1) return 1;
-    const int64_t tiles = int64_t(bytes / kTileBytes);
+    if (!src || !dst || bytes == 0 || grid < 1 || vecs < 1 || bytes % tile_bytes(vecs) != 0) return 1;
+    const int64_t tiles = int64_t(bytes / tile_bytes(vecs));
     const unsigned g = grid_for(grid, tiles);
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const u32x4* s = static_cast<const u32x4*>(src);
     u32x4* d = static_cast<u32x4*>(dst);
-    if (nontemporal_loads && nontemporal_stores)
-        copy_kernel<true, true><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
-    else if (nontemporal_loads)
-        copy_kernel<true, false><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
-    else if (nontemporal_stores)
-        copy_kernel<false, true><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
-    else
-        copy_kernel<false, false><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
-    return status(hipGetLastError());
+    const int rc = with_vecs(vecs, [&](auto v) {
+        constexpr int V = decltype(v)::value;
+        if (nontemporal_loads && nontemporal_stores)
+            copy_kernel<V, true, true><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
+        else if (nontemporal_loads)
+            copy_kernel<V, true, false><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
+        else if (nontemporal_stores)
+            copy_kernel<V, false, true><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
+        else
+            copy_kernel<V, false, false><<<g, kProbeBlock, 0, st>>>(s, d, tiles);
+        return status(hipGetLastError());
+    });
+    return rc < 0 ? 1 : rc;
 }
 
 int gnp_atomic_group_sums(const uint16_t* x_bf16, int64_t groups, int64_t group_elems, int64_t chunk,
                           float* sums, void* stream)
 {
     if (!x_bf16 || !sums || groups < 1 || chunk < 2048 || chunk % 2048 != 0 || group_elems < chunk ||
-        group_elems % chunk != 0)
+        group_elems % chunk != 0 || reinterpret_cast<uintptr_t>(x_bf16) % 16 != 0)
         return 1;
     const int64_t jobs_per_group = group_elems / chunk;
     const int64_t jobs = groups * jobs_per_group;
