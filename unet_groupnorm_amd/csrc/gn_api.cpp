@@ -31,6 +31,14 @@ gn::KArgs kargs_for(const gn::Plan& p, int activation, int x_dtype)
     return a;
 }
 
+gn::ClArgs clargs_for(const gn::PlanCL& p, int activation, int x_dtype)
+{
+    gn::ClArgs a = gn::clargs_of(p, activation);
+    const int64_t bytes = p.N * p.C * p.S * (x_dtype == GN_F32 ? 4 : 2);
+    a.cached = bytes <= kCachedBytes ? 1 : 0;
+    return a;
+}
+
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool dtype_ok(int d) { return d == GN_F32 || d == GN_BF16 || d == GN_F16; }
 bool act_ok(int a) { return a == GN_ACT_NONE || a == GN_ACT_RELU; }
@@ -671,11 +679,11 @@ int gn_forward_cl(const void* x, int x_dtype, const float* gamma, const float* b
     if ((rc = ds.same_device({gamma, beta, y, mean, rstd, workspace}))) return rc;
     if (p.res_fwd)
         return launch_status(gn::launch_cl_res_forward(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype,
-                                                       gn::clargs_of(p, activation),
+                                                       clargs_for(p, activation, x_dtype),
                                                        static_cast<hipStream_t>(stream), p.res_block_f,
                                                        p.res_vecs_f));
     return launch_status(gn::launch_cl_forward(x, x_dtype, gamma, beta, eps, mean, rstd, y, y_dtype,
-                                               gn::clargs_of(p, activation), gn::workspace_cl_of(workspace, p),
+                                               clargs_for(p, activation, x_dtype), gn::workspace_cl_of(workspace, p),
                                                static_cast<hipStream_t>(stream)));
 }
 
@@ -698,11 +706,11 @@ int gn_backward_cl(const void* dy, int dy_dtype, const void* x, int x_dtype,
     if ((rc = ds.same_device({dy, mean, rstd, gamma, beta, dx, dgamma, dbeta, workspace}))) return rc;
     if (p.res_bwd)
         return launch_status(gn::launch_cl_res_backward(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx,
-                                                        dgamma, dbeta, gn::clargs_of(p, activation),
+                                                        dgamma, dbeta, clargs_for(p, activation, x_dtype),
                                                         static_cast<hipStream_t>(stream), p.res_block_b,
                                                         p.res_vecs_b));
     return launch_status(gn::launch_cl_backward(dy, dy_dtype, x, x_dtype, mean, rstd, gamma, beta, dx, dgamma,
-                                                dbeta, gn::clargs_of(p, activation),
+                                                dbeta, clargs_for(p, activation, x_dtype),
                                                 gn::workspace_cl_of(workspace, p),
                                                 static_cast<hipStream_t>(stream)));
 }

@@ -166,7 +166,7 @@ __device__ __forceinline__ void cl_stats_full(const typename Io<TX>::Raw (&R)[kC
 // stored group-major: part[(g*N + n)*K + k]. The full steps are software-pipelined (the
 // next step's vectors are requested before the current one is reduced, alternating two
 // register sets); a last partial step is masked by voxel.
-template <int NGL, typename TX>
+template <int NGL, typename TX, bool NT>
 __global__ void __launch_bounds__(kClBlock)
 cl_stats_kernel(const TX* __restrict__ x, ClArgs a, float2* __restrict__ part)
 {
@@ -191,16 +191,16 @@ cl_stats_kernel(const TX* __restrict__ x, ClArgs a, float2* __restrict__ part)
         const int64_t nfull = (v1 - v0) / step;
         if (nfull > 0) {
             Raw A[kClRounds], B[kClRounds];
-            cl_load_step<kNtStats>(xs, v0, vps, a.C, A);
+            cl_load_step<NT>(xs, v0, vps, a.C, A);
             int64_t s = 0;
             for (; s + 2 < nfull; s += 2) {
-                cl_load_step<kNtStats>(xs, v0 + (s + 1) * step, vps, a.C, B);
+                cl_load_step<NT>(xs, v0 + (s + 1) * step, vps, a.C, B);
                 cl_stats_full<NGL, TX>(A, Ks, acc);
-                cl_load_step<kNtStats>(xs, v0 + (s + 2) * step, vps, a.C, A);
+                cl_load_step<NT>(xs, v0 + (s + 2) * step, vps, a.C, A);
                 cl_stats_full<NGL, TX>(B, Ks, acc);
             }
             if (s + 1 < nfull) {
-                cl_load_step<kNtStats>(xs, v0 + (s + 1) * step, vps, a.C, B);
+                cl_load_step<NT>(xs, v0 + (s + 1) * step, vps, a.C, B);
                 cl_stats_full<NGL, TX>(A, Ks, acc);
                 cl_stats_full<NGL, TX>(B, Ks, acc);
             } else {
@@ -215,7 +215,7 @@ cl_stats_kernel(const TX* __restrict__ x, ClArgs a, float2* __restrict__ part)
             for (int r = 0; r < kClRounds; ++r) {
                 const int64_t vox = st + int64_t(r) * vps + vo;
                 if (vox < v1) {
-                    Io<TX>::template load8<kNtStats>(xs + (st + int64_t(r) * vps) * a.C, e[r]);
+                    Io<TX>::template load8<NT>(xs + (st + int64_t(r) * vps) * a.C, e[r]);
                     valid |= 1u << r;
                 } else {
 #pragma unroll
@@ -319,7 +319,7 @@ __device__ __forceinline__ void cl_load_coefc(const float2* __restrict__ p, floa
 
 // y = ((x - head) - tail) * gamma_c*rstd + beta_c, optional relu, one narrowing store; a
 // streaming job is kClApplyRounds rounds of a workgroup over one sample's voxels.
-template <int NGL, typename TX, typename TY>
+template <int NGL, typename TX, typename TY, bool NT>
 __global__ void __launch_bounds__(kClBlock)
 cl_apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, ClArgs a, const float2* __restrict__ coefc,
                 const float4* __restrict__ coefg)
@@ -345,7 +345,7 @@ cl_apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, ClArgs a, const fl
             if (vox < v1) {
                 const int64_t off = (n * a.S + vox) * a.C + int64_t(cv) * kVec;
                 float e[kVec], o[kVec];
-                Io<TX>::template load8<kNtApply>(x + off, e);
+                Io<TX>::template load8<NT>(x + off, e);
 #pragma unroll
                 for (int i = 0; i < kVec; ++i) {
                     const float v = fmaf((e[i] - hi[i / W]) - lo[i / W], sc[i], sh[i]);
@@ -405,7 +405,7 @@ __device__ __forceinline__ void cl_bwd_full(const typename Io<TX>::Raw (&RX)[kCl
 // part[(c*N + n)*K + k]. A lane sums its rounds in order within a step and the steps in
 // order (full steps software-pipelined as in cl_stats_kernel); lanes sharing a channel
 // vector in the shuffle tree; waves in order.
-template <int NGL, bool ACT, typename TX, typename TD>
+template <int NGL, bool ACT, typename TX, typename TD, bool NT>
 __global__ void __launch_bounds__(kClBlock)
 cl_bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                      const float* __restrict__ rstd, const float* __restrict__ gamma,
@@ -444,20 +444,20 @@ cl_bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
         if (nfull > 0) {
             RawX AX[kClRounds], BX[kClRounds];
             RawD AD[kClRounds], BD[kClRounds];
-            cl_load_step<kNtBwdReduce>(xs, v0, vps, a.C, AX);
-            cl_load_step<kNtBwdReduce>(ds, v0, vps, a.C, AD);
+            cl_load_step<NT>(xs, v0, vps, a.C, AX);
+            cl_load_step<NT>(ds, v0, vps, a.C, AD);
             int64_t s = 0;
             for (; s + 2 < nfull; s += 2) {
-                cl_load_step<kNtBwdReduce>(xs, v0 + (s + 1) * step, vps, a.C, BX);
-                cl_load_step<kNtBwdReduce>(ds, v0 + (s + 1) * step, vps, a.C, BD);
+                cl_load_step<NT>(xs, v0 + (s + 1) * step, vps, a.C, BX);
+                cl_load_step<NT>(ds, v0 + (s + 1) * step, vps, a.C, BD);
                 cl_bwd_full<NGL, ACT, TX, TD>(AX, AD, mu, A, bt, s1, s2);
-                cl_load_step<kNtBwdReduce>(xs, v0 + (s + 2) * step, vps, a.C, AX);
-                cl_load_step<kNtBwdReduce>(ds, v0 + (s + 2) * step, vps, a.C, AD);
+                cl_load_step<NT>(xs, v0 + (s + 2) * step, vps, a.C, AX);
+                cl_load_step<NT>(ds, v0 + (s + 2) * step, vps, a.C, AD);
                 cl_bwd_full<NGL, ACT, TX, TD>(BX, BD, mu, A, bt, s1, s2);
             }
             if (s + 1 < nfull) {
-                cl_load_step<kNtBwdReduce>(xs, v0 + (s + 1) * step, vps, a.C, BX);
-                cl_load_step<kNtBwdReduce>(ds, v0 + (s + 1) * step, vps, a.C, BD);
+                cl_load_step<NT>(xs, v0 + (s + 1) * step, vps, a.C, BX);
+                cl_load_step<NT>(ds, v0 + (s + 1) * step, vps, a.C, BD);
                 cl_bwd_full<NGL, ACT, TX, TD>(AX, AD, mu, A, bt, s1, s2);
                 cl_bwd_full<NGL, ACT, TX, TD>(BX, BD, mu, A, bt, s1, s2);
             } else {
@@ -474,8 +474,8 @@ cl_bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
                 const int64_t vox = st + int64_t(r) * vps + vo;
                 if (vox < v1) {
                     float e[kVec], f[kVec];
-                    Io<TX>::template load8<kNtBwdReduce>(xs + (st + int64_t(r) * vps) * a.C, e);
-                    Io<TD>::template load8<kNtBwdReduce>(ds + (st + int64_t(r) * vps) * a.C, f);
+                    Io<TX>::template load8<NT>(xs + (st + int64_t(r) * vps) * a.C, e);
+                    Io<TD>::template load8<NT>(ds + (st + int64_t(r) * vps) * a.C, f);
                     cl_bwd_round<NGL, ACT>(e, f, mu, A, bt, p1, p2);
                 }
             }
@@ -604,7 +604,7 @@ cl_fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd
 }
 
 // dx = A*g + (B + E*(x - mean)), g = dy or the relu-gated dy, narrowed once to x's dtype.
-template <int NGL, typename TX, typename TD>
+template <int NGL, typename TX, typename TD, bool NT>
 __global__ void __launch_bounds__(kClBlock)
 cl_bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, ClArgs a,
                     const float2* __restrict__ coefc, const float4* __restrict__ coefg, TX* __restrict__ dx)
@@ -632,8 +632,8 @@ cl_bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, ClArgs 
             if (vox < v1) {
                 const int64_t off = (n * a.S + vox) * a.C + int64_t(cv) * kVec;
                 float xv[kVec], gv[kVec], o[kVec];
-                Io<TX>::template load8<kNtBwdApply>(x + off, xv);
-                Io<TD>::template load8<kNtBwdApply>(dy + off, gv);
+                Io<TX>::template load8<NT>(x + off, xv);
+                Io<TD>::template load8<NT>(dy + off, gv);
 #pragma unroll
                 for (int i = 0; i < kVec; ++i) {
                     const int q = i / W;
@@ -643,7 +643,10 @@ cl_bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, ClArgs 
                     if (single) t = t - t;
                     o[i] = t;
                 }
-                Io<TX>::store8(dx + off, o);
+                // dx goes out with nontemporal stores, like y (MI355X, bf16, C=32, G=8, step with
+                // plain loads at 128^3: 181.9 -> 176.3 us; nontemporal loads at 256^3: 1388 ->
+                // 1354 us)
+                Io<TX>::template store8<true>(dx + off, o);
             }
         }
     }
@@ -857,6 +860,18 @@ cl_res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const flo
 }
 
 // Calls f with std::integral_constant<int, NGL> for the lane's slot count.
+// Calls f with std::bool_constant<NT> for the streamed loads: plain loads (false) when the
+// host found that x fits the last-level cache, so that the step's later kernels find x there,
+// else nontemporal ones (measured on MI355X, bf16, C=32, G=8, fwd+bwd: 128^3 185.2 -> 181.9 us
+// with plain loads, 176.3 with nontemporal dx stores as well; 256^3 1354 -> 1477 us with plain
+// loads). The policy moves no bit of any result.
+template <typename F>
+hipError_t with_cl_policy(const ClArgs& a, F&& f)
+{
+    if (a.cached) return f(std::bool_constant<false>{});
+    return f(std::bool_constant<true>{});
+}
+
 template <typename F>
 hipError_t with_ngl(int ngl, F&& f)
 {
@@ -875,10 +890,12 @@ hipError_t launch_cl_forward(const void* x, int xdt, const float* gamma, const f
                              WorkspaceCL ws, hipStream_t st)
 {
     return with_type(xdt, [&](auto tx) {
+      return with_cl_policy(a, [&](auto nt) {
         return with_ngl(a.ngl, [&](auto ng) {
             using TX = decltype(tx);
             constexpr int NGL = decltype(ng)::value;
-            hipError_t e = launch(cl_stats_kernel<NGL, TX>, grid_of(a.jobs), dim3(kClBlock), st, cp<TX>(x), a,
+            constexpr bool NT = decltype(nt)::value;
+            hipError_t e = launch(cl_stats_kernel<NGL, TX, NT>, grid_of(a.jobs), dim3(kClBlock), st, cp<TX>(x), a,
                                   ws.part);
             if (e != hipSuccess) return e;
             e = launch(cl_fin_fwd_kernel<TX>, dim3(unsigned(a.N * a.G)), dim3(256), st, cp<TX>(x), gamma, beta,
@@ -887,11 +904,12 @@ hipError_t launch_cl_forward(const void* x, int xdt, const float* gamma, const f
             const float2* cc = ws.coefc;
             const float4* cg = ws.coefg;
             if (ydt == kF32)
-                return launch(cl_apply_kernel<NGL, TX, float>, grid_of(a.jobs_a), dim3(kClBlock), st, cp<TX>(x),
-                              mp<float>(y), a, cc, cg);
-            return launch(cl_apply_kernel<NGL, TX, TX>, grid_of(a.jobs_a), dim3(kClBlock), st, cp<TX>(x),
+                return launch(cl_apply_kernel<NGL, TX, float, NT>, grid_of(a.jobs_a), dim3(kClBlock), st,
+                              cp<TX>(x), mp<float>(y), a, cc, cg);
+            return launch(cl_apply_kernel<NGL, TX, TX, NT>, grid_of(a.jobs_a), dim3(kClBlock), st, cp<TX>(x),
                           mp<TX>(y), a, cc, cg);
         });
+      });
     });
 }
 
@@ -901,15 +919,17 @@ hipError_t launch_cl_backward(const void* dy, int dydt, const void* x, int xdt, 
                               hipStream_t st)
 {
     return with_type(xdt, [&](auto tx) {
-        return with_type(dydt, [&](auto td) {
+      return with_type(dydt, [&](auto td) {
+        return with_cl_policy(a, [&](auto nt) {
             return with_ngl(a.ngl, [&](auto ng) {
                 using TX = decltype(tx);
                 using TD = decltype(td);
                 constexpr int NGL = decltype(ng)::value;
+                constexpr bool NT = decltype(nt)::value;
                 hipError_t e = a.act
-                    ? launch(cl_bwd_reduce_kernel<NGL, true, TX, TD>, grid_of(a.jobs), dim3(kClBlock), st,
+                    ? launch(cl_bwd_reduce_kernel<NGL, true, TX, TD, NT>, grid_of(a.jobs), dim3(kClBlock), st,
                              cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part, ws.partg)
-                    : launch(cl_bwd_reduce_kernel<NGL, false, TX, TD>, grid_of(a.jobs), dim3(kClBlock), st,
+                    : launch(cl_bwd_reduce_kernel<NGL, false, TX, TD, NT>, grid_of(a.jobs), dim3(kClBlock), st,
                              cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.part, ws.partg);
                 if (e != hipSuccess) return e;
                 const int64_t ngroups = a.N * a.G;
@@ -918,11 +938,12 @@ hipError_t launch_cl_backward(const void* dy, int dydt, const void* x, int xdt, 
                            beta, static_cast<const float2*>(ws.part), static_cast<const float2*>(ws.partg), a,
                            ngroups, nchan, ws.coefc, ws.coefg, dgamma, dbeta);
                 if (e != hipSuccess || !dx) return e;
-                return launch(cl_bwd_apply_kernel<NGL, TX, TD>, grid_of(a.jobs_a), dim3(kClBlock), st,
+                return launch(cl_bwd_apply_kernel<NGL, TX, TD, NT>, grid_of(a.jobs_a), dim3(kClBlock), st,
                               cp<TD>(dy), cp<TX>(x), a, static_cast<const float2*>(ws.coefc),
                               static_cast<const float4*>(ws.coefg), mp<TX>(dx));
             });
         });
+      });
     });
 }
 

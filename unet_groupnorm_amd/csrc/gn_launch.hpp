@@ -152,6 +152,7 @@ struct ClArgs {
     int64_t chunk, K, jobs;
     int64_t chunk_a, K_a, jobs_a;
     int32_t ngl, act;
+    int32_t cached;                   // host's choice: plain loads, the volume fits the LLC
     int32_t lcvg;                     // resident path: log2 of a group's vectors per voxel
     FastDiv div_vg;                   // resident path: S * C/(8G), a group's vectors
 };
@@ -164,6 +165,7 @@ inline ClArgs clargs_of(const PlanCL& p, int act = 0)
     a.chunk = p.chunk; a.K = p.K; a.jobs = p.jobs;
     a.chunk_a = p.chunk_a; a.K_a = p.K_a; a.jobs_a = p.jobs_a;
     a.ngl = p.ngl; a.act = act;
+    a.cached = 0;
     a.lcvg = p.lcvg;
     a.div_vg = fastdiv_of(p.res_bwd ? p.S << p.lcvg : 0);
     return a;
