@@ -34,6 +34,17 @@
 //       sums[g] = sum of the group's bf16 values, g < groups, each group `group_elems`
 //       contiguous elements split into jobs of `chunk` elements (chunk a multiple of 2048
 //       dividing group_elems); zeroes sums first, then accumulates with atomic adds.
+//   int gnp_barrier(int64_t grid, int group, int rounds, int kind, uint32_t* counters,
+//                   int* failed, void* stream);
+//       the cost of cross-workgroup synchronization: `grid` workgroups (256 threads),
+//       launched cooperatively so that all are resident at once, pass `rounds` barriers.
+//       kind 0: no barrier (the launch alone); 1: the grid-wide barrier of cooperative
+//       groups; 2: a barrier among each `group` consecutive workgroups on a counter per
+//       group (device-scope atomic add, then polling with device-scope atomic loads between
+//       a release and an acquire fence); 3: the same without the fences. counters holds
+//       grid / group zeroed words (the call zeroes them); a wait that polls more than 2^22
+//       times gives up, sets *failed and leaves, so every wave ends.
+#include <hip/hip_cooperative_groups.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -162,6 +173,39 @@ atomic_sums_kernel(const uint16_t* __restrict__ x, int64_t group_elems, int64_t 
     }
 }
 
+// ------------------------------------------------------------------ barrier cost
+
+constexpr int kSpinLimit = 1 << 22;
+
+template <int KIND>
+__global__ void __launch_bounds__(kProbeBlock)
+barrier_kernel(int group, int rounds, uint32_t* __restrict__ counters, int* __restrict__ failed)
+{
+    const int g = blockIdx.x / group;
+    for (int r = 0; r < rounds; ++r) {
+        if (KIND == 1) {
+            cooperative_groups::this_grid().sync();
+        } else if (KIND >= 2) {
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                if (KIND == 2) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __hip_atomic_fetch_add(counters + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t target = uint32_t(group) * uint32_t(r + 1);
+                int spins = 0;
+                while (__hip_atomic_load(counters + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+                    if (++spins > kSpinLimit) {
+                        __hip_atomic_store(failed, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                if (KIND == 2) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            }
+            __syncthreads();
+        }
+    }
+}
+
 int status(hipError_t e) { return e == hipSuccess ? 0 : 2; }
 
 unsigned grid_for(int64_t grid, int64_t tiles)
@@ -248,6 +292,21 @@ int gnp_atomic_group_sums(const uint16_t* x_bf16, int64_t groups, int64_t group_
     if (e != hipSuccess) return 2;
     atomic_sums_kernel<<<unsigned(jobs), kProbeBlock, 0, st>>>(x_bf16, group_elems, chunk, jobs_per_group, sums);
     return status(hipGetLastError());
+}
+
+int gnp_barrier(int64_t grid, int group, int rounds, int kind, uint32_t* counters, int* failed, void* stream)
+{
+    if (grid < 1 || grid > 65536 || group < 1 || grid % group != 0 || rounds < 0 || kind < 0 || kind > 3 ||
+        !counters || !failed)
+        return 1;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemsetAsync(counters, 0, size_t(grid / group) * sizeof(uint32_t), st) != hipSuccess) return 2;
+    void* args[] = {&group, &rounds, &counters, &failed};
+    const void* k = kind == 0 ? reinterpret_cast<const void*>(barrier_kernel<0>)
+                  : kind == 1 ? reinterpret_cast<const void*>(barrier_kernel<1>)
+                  : kind == 2 ? reinterpret_cast<const void*>(barrier_kernel<2>)
+                              : reinterpret_cast<const void*>(barrier_kernel<3>);
+    return status(hipLaunchCooperativeKernel(k, dim3(unsigned(grid)), dim3(kProbeBlock), args, 0, st));
 }
 
 }  // extern "C"
