@@ -102,8 +102,15 @@ def bytes_per_elem(x_dtype, y_dtype, dy_dtype):
 
 
 def _events(n):
+    """n timing events, each recorded once already: torch creates a HIP event at its first
+    record, and that creation, left inside a timed loop, could hold the host up long enough
+    for the GPU to run dry between two events."""
     import torch
-    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    return ev
 
 
 # ----------------------------------------------------------------------------- probe kernels
@@ -312,27 +319,34 @@ class Runner:
                 "median_ms": round(statistics.median(every), 5), "min_of_medians_ms": round(min(medians), 5),
                 "max_of_medians_ms": round(max(medians), 5)}
 
-    def in_step_kernels(self, steps=50):
+    def in_step_kernels(self, steps=50, backlog=4):
         """Each kernel's average duration inside the step: events between the step's four
         kernels (launched through the two-call halves of gn_forward and gn_backward, the
         same kernels as step()), over `steps` steps enqueued back to back. Each figure
-        includes one event packet's latency."""
+        includes one event packet's latency. The events exist before the first is recorded
+        and `backlog` untimed steps are queued ahead of them, so the GPU is never left
+        waiting on the host between two events (a wait would land in one kernel's figure)."""
         torch = self.torch
         ph = self.phases()
+        n = len(ph)
         for _ in range(3):
             for _, f in ph:
                 f()
         torch.cuda.synchronize()
-        rows = []
-        for _ in range(steps):
-            ev = _events(len(ph) + 1)
-            ev[0].record()
-            for i, (_, f) in enumerate(ph):
+        ev = _events(steps * n + 1)
+        for _ in range(backlog):
+            for _, f in ph:
                 f()
-                ev[i + 1].record()
-            rows.append(ev)
+        ev[0].record()
+        k = 0
+        for _ in range(steps):
+            for _, f in ph:
+                f()
+                k += 1
+                ev[k].record()
         torch.cuda.synchronize()
-        return {name: sum(ev[i].elapsed_time(ev[i + 1]) for ev in rows) / steps for i, (name, _) in enumerate(ph)}
+        return {name: sum(ev[s * n + i].elapsed_time(ev[s * n + i + 1]) for s in range(steps)) / steps
+                for i, (name, _) in enumerate(ph)}
 
     def back_to_back_kernels(self, reps):
         """Each kernel launched `reps` times back to back between two events, after one full
@@ -385,9 +399,9 @@ class Runner:
         torch = self.torch
         buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
         total = 0.0
+        e0, e1 = _events(2)
         for _ in range(steps):
             buf.fill_(1)
-            e0, e1 = _events(2)
             e0.record()
             self.step()
             e1.record()
@@ -403,9 +417,8 @@ class Runner:
         With fresh=False the same events bracket the same calls without the rewrites."""
         torch = self.torch
         xs, dys = (self.x.clone(), self.dy.clone()) if fresh else (None, None)
-        ev = []
-        for _ in range(steps + 1):
-            e = _events(4)
+        ev = [_events(4) for _ in range(steps + 1)]
+        for e in ev:
             if fresh:
                 self.x.copy_(xs)
             e[0].record()
@@ -416,7 +429,6 @@ class Runner:
             e[2].record()
             self.bwd()
             e[3].record()
-            ev.append(e)
         torch.cuda.synchronize()
         # the first step is dropped: the host enqueues it while the GPU is idle
         total = sum(e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in ev[1:])
@@ -431,10 +443,12 @@ def site_roofline(run, ceil, steps):
     each bracketed kernel reads long by that much: the latency is measured as the four
     bracketed kernels' sum minus the same steps timed without the inner events (step time
     between two events around `steps` steps), divided by four, and taken off each kernel.
-    The rocprofv3 kernel trace of the same command, which times the kernels themselves,
-    gives the same in-step averages."""
+    The in-step figures are the least of three measurements (by their sum). The rocprofv3
+    kernel trace of the same command, which times the kernels themselves, gives the same
+    in-step averages."""
     step_ms, _ = run.timed_steps(steps, 3)
-    ks = run.in_step_kernels(steps)
+    # three measurements; the one with the smallest total has the fewest host-side gaps
+    ks = min((run.in_step_kernels(steps) for _ in range(3)), key=lambda d: sum(d.values()))
     step_ms = (step_ms + run.timed_steps(steps, 0)[0]) / 2
     b2b = run.back_to_back_kernels(20)
     dom = "bwd_apply"
@@ -455,8 +469,8 @@ def site_roofline(run, ceil, steps):
         "algorithmic_bytes_per_launch": dom_bytes,
         "avg_launch_us": round(us[dom], 2),
         "timing": f"HIP events between the four kernels of each of {steps} back-to-back steps on the kernels' "
-                  "stream, less one event's latency (the bracketed kernels' sum minus the step timed without "
-                  "the inner events, over four)",
+                  "stream (queued behind untimed steps; the least of three runs), less one event's latency (the "
+                  "bracketed kernels' sum minus the step timed without the inner events, over four)",
         "event_latency_us": round(event_us, 2),
         "step_us_without_inner_events": round(step_ms * 1e3, 2),
         "ceiling_frac": kb[dom]["frac_of_bound"] if kb else None,

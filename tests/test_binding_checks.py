@@ -2,6 +2,8 @@
 size, dtype, layout or device is refused before any pointer reaches the library, which can
 check where memory lives but not how large a buffer is. With every tensor right, the call
 does reach the library, which then refuses host memory (GN_ERR_DEVICE)."""
+import os
+
 import pytest
 import torch
 
@@ -101,3 +103,44 @@ def test_split_phase_and_noalloc_refuse_bad_buffers():
     with pytest.raises(GnError) as e:
         gn.gn_forward_noalloc(x, _vec(), _vec(), G)
     assert e.value.status == 8
+
+
+def test_compiled_binding_is_the_in_tree_module_over_the_same_library():
+    from unet_groupnorm_amd import _gnbind
+    from unet_groupnorm_amd._lib import lib
+    assert _gnbind.abi_version() == lib.gn_abi_version()
+    here = os.path.dirname(os.path.abspath(gn.__file__))
+    assert os.path.dirname(os.path.abspath(_gnbind.__file__)) == here
+
+
+def test_compiled_binding_refuses_what_the_helpers_refuse():
+    x = _x()
+    with pytest.raises(ValueError, match="layout"):
+        gn.gn_forward(x, _vec(), _vec(), G, layout="nchw")
+    with pytest.raises(ValueError, match="layout"):
+        gn.gn_forward(x, _vec(), _vec(), G, layout="ndhwc")      # x is NCDHW-contiguous, C > 1
+    with pytest.raises(TypeError):
+        gn.gn_forward(x, _vec(), _vec(), G, out_dtype=torch.float64)
+    with pytest.raises(TypeError):
+        gn.gn_forward(x.to(torch.int32), _vec(), _vec(), G)
+    with pytest.raises(ValueError, match="activation"):
+        gn.gn_backward(_x(), x, torch.empty(N, G), torch.empty(N, G), _vec(), G, activation="gelu")
+    with pytest.raises(ValueError):
+        gn.gn_forward(torch.zeros(4), None, None, 1)
+    # a shape with no plan reports the planner's status under the size query's name
+    with pytest.raises(GnError, match="gn_workspace_bytes") as e:
+        gn.gn_forward(torch.zeros((1, 6, 2, 2, 2), dtype=torch.bfloat16), None, None, 4)
+    assert e.value.status == 3
+
+
+def test_compiled_binding_takes_the_layout_from_the_strides():
+    # every buffer right but in host memory: the outputs are allocated before the library
+    # refuses the call, so their absence cannot be what it reports
+    x = _x().contiguous(memory_format=torch.channels_last_3d)
+    with pytest.raises(GnError) as e:
+        gn.gn_forward(x, _vec(), _vec(), G)
+    assert e.value.status == 8 and "gn_forward_cl" in str(e.value)
+    with pytest.raises(GnError) as e:
+        gn.gn_backward(_x().contiguous(memory_format=torch.channels_last_3d), x, torch.empty(N, G),
+                       torch.empty(N, G), _vec(), G, need_dx=False)
+    assert e.value.status == 8 and "gn_backward_cl" in str(e.value)

@@ -3,7 +3,9 @@
 Every function here has the name of the C entry point it calls (include/gn.h). It
 allocates outputs and the workspace with torch on x's device, passes raw pointers and
 the current HIP stream of that device, and turns a non-zero status into an exception.
-All arithmetic happens in the HIP kernels.
+All arithmetic happens in the HIP kernels. The two per-step calls, gn_forward and
+gn_backward, do their marshalling in the compiled module _gnbind (csrc/gn_binding.cpp);
+the others go through ctypes.
 
 Tensors are contiguous NCDHW (any number of trailing spatial dims, flattened to S), or
 contiguous with the channel dimension last (NDHWC, torch's channels_last_3d for 5-D):
@@ -18,8 +20,15 @@ import torch
 from ._lib import (GN_ACT_NONE, GN_ACT_RELU, GN_BF16, GN_F16, GN_F32, GN_OK, STATUS_NAMES, GnPlanInfo,
                    GnPlanInfoCL, lib)
 
+try:
+    from . import _gnbind
+except ImportError as e:
+    raise ImportError("unet_groupnorm_amd._gnbind (the compiled binding of gn_forward and gn_backward) is "
+                      "not built: run python unet_groupnorm_amd/build.py") from e
+
 _DT = {torch.float32: GN_F32, torch.bfloat16: GN_BF16, torch.float16: GN_F16}
 _ACT = {None: GN_ACT_NONE, "none": GN_ACT_NONE, "relu": GN_ACT_RELU}
+_LAYOUT = {None: -1, "ncdhw": 0, "ndhwc": 1}
 
 
 class GnError(RuntimeError):
@@ -183,28 +192,34 @@ def workspace_for(x, G, layout=None):
     return torch.empty(nbytes, dtype=torch.uint8, device=x.device)
 
 
+def _out_code(out_dtype):
+    if out_dtype is None:
+        return -1
+    try:
+        return _DT[out_dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {out_dtype} (float32, bfloat16 or float16)") from None
+
+
+def _layout_code(layout):
+    try:
+        return _LAYOUT[layout]
+    except (KeyError, TypeError):
+        raise ValueError(f"tensor is not contiguous in layout {layout!r}") from None
+
+
 def gn_forward(x, gamma, beta, G, eps=1e-5, out_dtype=None, *, activation=None, workspace=None,
                out=None, mean=None, rstd=None, layout=None):
     """Returns (y, mean, rstd). y has out_dtype (default: x.dtype) and x's layout; mean/rstd
     are [N, G] fp32. activation: None or "relu" (applied in fp32 before the single
-    narrowing store). layout: None (from x's strides), "ncdhw" or "ndhwc"."""
-    layout = _layout_arg(x, layout)
-    N, C, S, G = _dims(x, G)
-    didx = x.get_device()
-    xsig = _sig(x)
-    out_dtype = out_dtype or x.dtype
-    y = out if out is not None else torch.empty_like(x, dtype=out_dtype)
-    y_ptr = _like_ptr("out", y, xsig, didx, _IN_DTYPES)
-    m_ptr = _buf_ptr("mean", mean, N * G, didx)
-    r_ptr = _buf_ptr("rstd", rstd, N * G, didx)
-    mean = mean if mean is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
-    rstd = rstd if rstd is not None else torch.empty((N, G), dtype=torch.float32, device=x.device)
-    ws_ptr, ws_bytes = _ws_args(workspace if workspace is not None else workspace_for(x, G, layout), didx)
-    fn, name = (lib.gn_forward, "gn_forward") if layout == "ncdhw" else (lib.gn_forward_cl, "gn_forward_cl")
-    _check(name, fn(
-        x.data_ptr(), _dtype(x), _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx),
-        N, C, S, G, float(eps), _act(activation), y_ptr, _dtype(y), m_ptr or mean.data_ptr(),
-        r_ptr or rstd.data_ptr(), ws_ptr, ws_bytes, _stream_of(didx)))
+    narrowing store). layout: None (from x's strides), "ncdhw" or "ndhwc".
+
+    The tensors are checked, outputs not given are allocated, and gn_forward or
+    gn_forward_cl is called by the compiled module _gnbind (the checks of the helpers
+    above, in C++)."""
+    y, mean, rstd, status, fn = _gnbind.forward(x, gamma, beta, int(G), float(eps), _out_code(out_dtype),
+                                                _act(activation), workspace, out, mean, rstd, _layout_code(layout))
+    _check(fn, status)
     return y, mean, rstd
 
 
@@ -258,28 +273,13 @@ def gn_backward(dy, x, mean, rstd, gamma, G, *, beta=None, activation=None, need
                 need_dgamma=True, need_dbeta=True, workspace=None, dx=None, dgamma=None, dbeta=None,
                 layout=None):
     """Returns (dx or None, dgamma or None, dbeta or None); dx has x's dtype and layout. With
-    activation="relu", dy is the gradient of relu(GroupNorm(x)) and beta is needed."""
-    layout = _layout_arg(x, layout)
-    N, C, S, G = _dims(x, G)
-    didx = x.get_device()
-    xsig = _sig(x)
-    dy_ptr = _like_ptr("dy", dy, xsig, didx, _IN_DTYPES)
-    if need_dx and dx is None:
-        dx = torch.empty_like(x)
-    dx_ptr = _like_ptr("dx", dx, xsig, didx, (x.dtype,)) if need_dx else None
-    if need_dgamma and dgamma is None:
-        dgamma = torch.empty(C, dtype=torch.float32, device=x.device)
-    if need_dbeta and dbeta is None:
-        dbeta = torch.empty(C, dtype=torch.float32, device=x.device)
-    ws_ptr, ws_bytes = _ws_args(workspace if workspace is not None else workspace_for(x, G, layout), didx)
-    fn, name = (lib.gn_backward, "gn_backward") if layout == "ncdhw" else (lib.gn_backward_cl, "gn_backward_cl")
-    _check(name, fn(
-        dy_ptr, _dtype(dy), x.data_ptr(), _dtype(x), _buf_ptr("mean", mean, N * G, didx),
-        _buf_ptr("rstd", rstd, N * G, didx),
-        _vec_ptr("gamma", gamma, C, didx), _vec_ptr("beta", beta, C, didx), _act(activation),
-        N, C, S, G, dx_ptr, _vec_ptr("dgamma", dgamma if need_dgamma else None, C, didx),
-        _vec_ptr("dbeta", dbeta if need_dbeta else None, C, didx), ws_ptr, ws_bytes, _stream_of(didx)))
-    return (dx if need_dx else None, dgamma if need_dgamma else None, dbeta if need_dbeta else None)
+    activation="relu", dy is the gradient of relu(GroupNorm(x)) and beta is needed. Checked,
+    allocated and called by _gnbind, as gn_forward."""
+    dx, dgamma, dbeta, status, fn = _gnbind.backward(
+        dy, x, mean, rstd, gamma, beta, _act(activation), int(G), bool(need_dx), bool(need_dgamma),
+        bool(need_dbeta), workspace, dx, dgamma, dbeta, _layout_code(layout))
+    _check(fn, status)
+    return dx, dgamma, dbeta
 
 
 def gn_backward_reduce(dy, x, mean, rstd, gamma, G, dgamma, dbeta, workspace, beta=None,
