@@ -105,11 +105,12 @@ int make_plan(int64_t N, int64_t C, int64_t S, int64_t G, Plan* p);
 // so C/8 must divide kClBlock. The lane's 8 channels lie in ngl = max(1, 8 / (C/G))
 // groups, which needs C/G to divide 8 or to be a multiple of 8.
 constexpr int kClBlock = 256;
-// Reduction workgroups a channels-last launch aims for. Fewer and longer jobs than the
-// NCDHW plan's: each job ends in per-channel shuffle trees and three workgroup barriers,
-// and its K partials per group feed the finalize (measured on MI355X, 128^3 and 256^3,
-// C=32: 256-512 jobs best, 2048 about 5% slower, 128 too few).
-constexpr int64_t kClTargetJobs = 512;
+// Reduction workgroups a channels-last launch aims for: one per CU. Each job ends in
+// per-channel shuffle trees and three workgroup barriers, and its K partials per group feed
+// the finalize. Measured on MI355X (bf16, fwd+bwd, plain loads and nontemporal stores):
+// 256 jobs against 512, 128^3 x 32 channels 175.7 -> 172.3 us, 256^3 1357 -> 1354, 64^3 x 64
+// 61.7 -> 61.4, 32^3 x 128 31.8 -> 31.2; 1024 slower at 128^3 and 256^3; 128 too few.
+constexpr int64_t kClTargetJobs = 256;
 constexpr int kClRounds = 4;        // voxel rounds a reduction lane holds per step
 // Channels-last resident path: at most this many vectors of a group per voxel, at most this
 // many (sample, channel) rows in a backward workgroup, and at most this many vectors per
