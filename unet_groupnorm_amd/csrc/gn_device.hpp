@@ -33,6 +33,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ element access
 
@@ -164,10 +165,12 @@ template <> struct Io<_Float16> {
     {
         return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16)));
     }
+    // One packed conversion of the pair (gfx950 converts two fp32 values to fp16 in one
+    // instruction, rounding each exactly as the scalar conversion does).
     static __device__ __forceinline__ uint32_t pack(float a, float b)
     {
-        return uint32_t(__builtin_bit_cast(uint16_t, _Float16(pin_f32(a)))) |
-               (uint32_t(__builtin_bit_cast(uint16_t, _Float16(pin_f32(b)))) << 16);
+        const f32x2 v = {pin_f32(a), pin_f32(b)};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
     }
     template <bool NT>
     static __device__ __forceinline__ Raw load_raw(const _Float16* p)
