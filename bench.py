@@ -487,8 +487,8 @@ def census(steps=10, warmup=3):
     """The 18 GroupNorm sites of a scale-7 UNet, fwd+bwd each, back to back: aggregate rate
     on method bytes, called eagerly and replayed from one captured HIP graph of the pass, the
     pass with every input just written (events around the GroupNorm calls, and the same
-    events without the rewrites for comparison), and whether 10 repeats of every site are
-    bitwise identical."""
+    events without the rewrites for comparison), every site's step after a last-level cache
+    flush, and whether 10 repeats of every site are bitwise identical."""
     import torch
 
     import workloads
@@ -531,6 +531,8 @@ def census(steps=10, warmup=3):
     # inputs just written, and the same event pattern on resident inputs
     fresh_ms = sum(r.produced_steps(3, fresh=True) for r in runs)
     warm_ev_ms = sum(r.produced_steps(3, fresh=False) for r in runs)
+    # every site's step after the last-level cache was flushed
+    flushed_ms = sum(r.flushed_steps(3) for r in runs)
     # determinism: 10 repeats per site, every output compared bitwise with the first
     identical = True
     for r in runs:
@@ -562,6 +564,9 @@ def census(steps=10, warmup=3):
                                     "value": round(total / (fresh_ms * 1e-3) / 1e9, 1),
                                     "same_events_resident_inputs_ms": round(warm_ev_ms, 4),
                                     "timing": "HIP events around each GroupNorm call (36 a pass)"},
+            "llc_flushed": {"ms_per_pass": round(flushed_ms, 4),
+                            "value": round(total / (flushed_ms * 1e-3) / 1e9, 1),
+                            "timing": "each site's fwd+bwd step timed alone after 512 MiB of writes"},
             "bitwise_identical_10_repeats": identical, "per_shape": per_shape}
 
 
@@ -619,7 +624,8 @@ def spatial_shard(steps=30, warmup=5, nshards=8):
 
 def small_configs(steps=50, warmup=10):
     """The launch-bound configurations, timed as fwd+bwd microseconds per step: eager (one
-    call per direction from Python) and replayed from a captured graph."""
+    call per direction from Python), replayed from a captured graph, and each step alone
+    after a last-level cache flush."""
     import workloads
     out = {}
     for case in (workloads.TINY, workloads.DEEP, workloads.DEEP_F32OUT):
@@ -627,11 +633,13 @@ def small_configs(steps=50, warmup=10):
         r.settle(0.25)
         sms, _ = r.timed_steps(steps, warmup)
         gms = r.graph_steps()
+        fms = r.flushed_steps(10)
         out[case.name] = {"us_per_step": round(sms * 1e3, 2),
                           "value": round(r.step_bytes / (sms * 1e-3) / 1e9, 1),
                           "bytes_per_step": r.step_bytes,
                           "graph_us_per_step": round(gms * 1e3, 2),
-                          "graph_value": round(r.step_bytes / (gms * 1e-3) / 1e9, 1)}
+                          "graph_value": round(r.step_bytes / (gms * 1e-3) / 1e9, 1),
+                          "llc_flushed_us_per_step": round(fms * 1e3, 2)}
         del r
     return out
 
