@@ -278,6 +278,36 @@ def test_large_mean_offset_keeps_variance(spatial):
     P.check_y(P.to_np(y).reshape(-1), f["y"].reshape(-1), *P.channel_params_at(np.arange(x.size), x.shape, None, None))
 
 
+@pytest.mark.parametrize("spatial", [(20, 18, 17), (16, 16, 16)])
+def test_eps_zero(spatial):
+    """eps = 0 is a valid argument: with spread in every group the statistics are 1/sigma
+    exactly as the definition has them, and a constant group (variance 0, rstd = inf) gives
+    NaN in that group's y and dx and nowhere else, as the fp64 definition does (0 * inf).
+    Two-pass kernels at the ragged shape, the resident path at 16^3."""
+    say(f"eps = 0, (2, 8, {spatial}), G=4, one constant group")
+    inp = workloads.make(workloads.custom(2, 8, 4, spatial, torch.float32, dist="unet", seed=23), "cpu")
+    inp["eps"] = 0.0
+    x = inp["x"].clone()
+    x[1, 2:4] = 0.75                     # group (1, 1): constant
+    inp["x"] = x
+    r = full_check(inp, "eps0")
+    assert torch.isnan(r["y"][1, 2:4]).all() and not torch.isnan(r["y"][0]).any()
+    assert torch.isnan(r["dx"][1, 2:4]).all() and not torch.isnan(r["dx"][1, 4:]).any()
+
+
+@pytest.mark.parametrize("scale", [1e-12, 1e12])
+def test_extreme_magnitudes(scale):
+    """Values of 1e-12 and 1e12 times the usual spread, around offsets ten times the spread,
+    fp32 throughout: every result stays within its relative bar (the statistics carry the
+    scale through the shift and the head/tail mean). The group's sum of squared deviations
+    is kept in fp32, so a group whose M * variance passes the fp32 range is out of the
+    domain (M * sigma^2 < 3.4e38)."""
+    say(f"fp32 input scaled by {scale:g}, (2, 16, 12, 11, 10), G=4")
+    inp = workloads.make(workloads.custom(2, 16, 4, (12, 11, 10), torch.float32, dist="unet", seed=29), "cpu")
+    inp["x"] = ((inp["x"].double() * scale) + 10 * scale).float()
+    full_check(inp, f"scale_{scale:g}")
+
+
 # ----------------------------------------------------------------------------- bitwise properties
 
 @pytest.mark.parametrize("case", [workloads.DEEP, workloads.SCALE7], ids=lambda c: c.name)
