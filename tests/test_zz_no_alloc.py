@@ -81,3 +81,37 @@ def test_noalloc_binding_and_oversize_shape():
     with pytest.raises(gn.GnError) as e:
         gn.gn_forward_noalloc(x, None, None, 32)
     assert e.value.status == 12
+
+
+def test_noalloc_forward_replayed_from_a_captured_graph():
+    """The callers the entry point is for include code under graph capture: one call captured
+    (outputs and inputs allocated before the capture, nothing allocated inside it), then the
+    graph replayed three times, new inputs copied in and the program's own eager work and a
+    synchronization between the replays, each replay bitwise equal to an eager gn_forward."""
+    case = workloads.custom(2, 32, 8, (20, 18, 16), torch.bfloat16, dist="unet", seed=64)
+    say(f"{case.name}: gn_forward_noalloc captured in a graph, replayed 3 times")
+    inp = workloads.make(case, "cuda", with_dy=False)
+    x, gamma, beta, G, eps = inp["x"].clone(), inp["gamma"], inp["beta"], inp["G"], inp["eps"]
+    y = torch.empty_like(x)
+    mean = torch.empty((x.shape[0], G), dtype=torch.float32, device="cuda")
+    rstd = torch.empty_like(mean)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gn.gn_forward_noalloc(x, gamma, beta, G, eps, out=y, mean=mean, rstd=rstd)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gn.gn_forward_noalloc(x, gamma, beta, G, eps, out=y, mean=mean, rstd=rstd)
+    for seed in (65, 66, 67):
+        x.copy_(workloads.make(workloads.custom(2, 32, 8, (20, 18, 16), torch.bfloat16, dist="unet", seed=seed),
+                               "cuda", with_dy=False)["x"])
+        y_ref, m_ref, r_ref = gn.gn_forward(x, gamma, beta, G, eps)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(mean), _bits(m_ref)) and torch.equal(_bits(rstd), _bits(r_ref))
+        assert torch.equal(_bits(y), _bits(y_ref))
+        say(f"replay with inputs of seed {seed}: bitwise equal")
+    del graph
