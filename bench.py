@@ -393,21 +393,57 @@ class Runner:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (replays * per_graph)
 
-    def flushed_steps(self, steps, flush_bytes=512 << 20):
-        """Each step timed alone after overwriting a buffer twice the size of the 256 MiB
-        last-level cache, so that no input starts the step in that cache."""
+    def _flush(self, mode, flush_bytes):
+        """A callable that evicts the 256 MiB last-level cache by touching a buffer twice its
+        size: mode "read" reads it (the cache is left holding clean lines, and whatever a
+        step left dirty is written back inside the flush), mode "write" overwrites it (the
+        cache is left full of dirty lines that the next kernel's misses must write back)."""
         torch = self.torch
-        buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        buf = torch.ones(flush_bytes // 4, dtype=torch.int32, device="cuda")
+        if mode == "read":
+            sink = torch.empty((), dtype=torch.int64, device="cuda")
+            return lambda: torch.sum(buf, dim=0, out=sink)
+        if mode == "write":
+            return lambda: buf.fill_(1)
+        raise ValueError(mode)
+
+    def flushed_steps(self, steps, flush_bytes=512 << 20, mode="read"):
+        """Each step timed alone after a flush of the last-level cache (see _flush), so that
+        no input starts the step in that cache."""
+        torch = self.torch
+        flush = self._flush(mode, flush_bytes)
         total = 0.0
         e0, e1 = _events(2)
         for _ in range(steps):
-            buf.fill_(1)
+            flush()
             e0.record()
             self.step()
             e1.record()
             torch.cuda.synchronize()
             total += e0.elapsed_time(e1)
         return total / steps
+
+    def flushed_kernels(self, steps, flush_bytes=512 << 20, mode="read"):
+        """The step's four kernels (the two-call halves of gn_forward and gn_backward, as
+        in_step_kernels launches them) timed one by one after the same flush as
+        flushed_steps: each step starts with no input in the last-level cache, and its
+        kernels then see what the earlier ones left there. Mean milliseconds per kernel."""
+        torch = self.torch
+        ph = self.phases()
+        n = len(ph)
+        flush = self._flush(mode, flush_bytes)
+        ev = _events(n + 1)
+        total = [0.0] * n
+        for _ in range(steps):
+            flush()
+            ev[0].record()
+            for i, (_, f) in enumerate(ph):
+                f()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            for i in range(n):
+                total[i] += ev[i].elapsed_time(ev[i + 1])
+        return {name: total[i] / steps for i, (name, _) in enumerate(ph)}
 
     def produced_steps(self, steps, fresh=True):
         """Steps whose inputs were just written, as in a training step where a convolution
@@ -566,7 +602,7 @@ def census(steps=10, warmup=3):
                                     "timing": "HIP events around each GroupNorm call (36 a pass)"},
             "llc_flushed": {"ms_per_pass": round(flushed_ms, 4),
                             "value": round(total / (flushed_ms * 1e-3) / 1e9, 1),
-                            "timing": "each site's fwd+bwd step timed alone after 512 MiB of writes"},
+                            "timing": "each site's fwd+bwd step timed alone after a 512 MiB read"},
             "bitwise_identical_10_repeats": identical, "per_shape": per_shape}
 
 
@@ -997,9 +1033,24 @@ def main():
     if not args.no_extras:
         out["compulsory_bytes_gbps"] = round(10 * case.numel / (ms * 1e-3) / 1e9, 1)
         log("timing steps with the last-level cache flushed before each")
-        fms = run.flushed_steps(max(10, args.steps // 5))
-        out["llc_flushed"] = {"ms_per_step": round(fms, 5),
-                              "value": round(run.step_bytes / (fms * 1e-3) / 1e9, 1)}
+        nfl = max(10, args.steps // 5)
+
+        def flushed(mode):
+            fms = run.flushed_steps(nfl, mode=mode)
+            fk = run.flushed_kernels(nfl, mode=mode)
+            return {
+                "ms_per_step": round(fms, 5),
+                "value": round(run.step_bytes / (fms * 1e-3) / 1e9, 1),
+                "pct_of_peak": round(100 * run.step_bytes / (fms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 2),
+                "compulsory_bytes_gbps": round(10 * case.numel / (fms * 1e-3) / 1e9, 1),
+                "kernels": {name: {"us": round(1e3 * t, 2),
+                                   "gbps": round(run.phase_bytes[name] * case.numel / (t * 1e-3) / 1e9, 1)}
+                            for name, t in fk.items()},
+            }
+
+        out["llc_flushed"] = {"flush": "512 MiB read before each step (clean eviction)", **flushed("read")}
+        out["llc_flushed_dirty"] = {"flush": "512 MiB overwritten before each step (the cache left dirty)",
+                                    **flushed("write")}
         log("timing steps whose inputs were just rewritten (x before the forward, dy before the backward)")
         pms = run.produced_steps(max(10, args.steps // 5))
         out["inputs_just_written"] = {"ms_per_step": round(pms, 5),
