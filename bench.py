@@ -903,6 +903,112 @@ def accuracy(runner, f, b):
     return out
 
 
+def _bf16_ulp_dist(a, b):
+    """Distance in bf16 units in the last place between two arrays of bf16 bit patterns
+    (sign-magnitude mapped onto a line, so that +0 and -0 are 0 apart)."""
+    import numpy as np
+    a, b = a.astype(np.int32), b.astype(np.int32)
+    oa = np.where(a & 0x8000, -(a & 0x7FFF), a)
+    ob = np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(oa - ob)
+
+
+def accuracy_streamed(runner, workers=None):
+    """The GPU's outputs on a bf16 NCDHW volume too large to hold in fp64 at once, against
+    the oracle group by group and channel by channel, the calls oracle_all_cores makes:
+    mean and rstd of each (n, g) against the oracle's group statistics; y and dx of each
+    (n, c) row as bf16 ulp distances from the fp64 value rounded once (y beyond 1 ulp held
+    to the fp32 bar 1e-5 * max(|y|, |gamma_c| + |beta_c|), as on the headline site); dgamma
+    and dbeta against the sums of their terms' magnitudes (dy has zero mean, so the channel
+    sums cancel). Only per-row summaries are kept."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    import torch
+
+    from oracle import oracle as O
+    runner.act = None
+    runner.step()
+    torch.cuda.synchronize()
+    case = runner.case
+    N, C, G, S = case.N, case.C, runner.G, case.S
+    Cg = C // G
+    x, dy = runner.x.cpu().reshape(N, C, S), runner.dy.cpu().reshape(N, C, S)
+
+    def bits(t):
+        return t.detach().cpu().view(torch.int16).numpy().view(np.uint16).reshape(N, C, S)
+
+    ybits, dxbits = bits(runner.y), bits(runner.dx)
+    gam, bet = runner.gamma.cpu().numpy(), runner.beta.cpu().numpy()
+    m_gpu = runner.mean.cpu().numpy().astype(np.float64).reshape(-1)
+    r_gpu = runner.rstd.cpu().numpy().astype(np.float64).reshape(-1)
+    dg_gpu = runner.dgamma.cpu().numpy().astype(np.float64)
+    db_gpu = runner.dbeta.cpu().numpy().astype(np.float64)
+    idx = np.arange(S, dtype=np.int64)
+    groups = [(n, g) for n in range(N) for g in range(G)]
+    rows = [(n, c) for n in range(N) for c in range(C)]
+    workers = workers or max(1, min(_host_cores(), 16))
+
+    def group(u):
+        n, g = u
+        sl = slice(g * Cg, (g + 1) * Cg)
+        st = O.group_stats(x[n:n + 1, sl], 1, runner.eps)
+        b = O.backward(dy[n:n + 1, sl], x[n:n + 1, sl], 1, gam[sl], eps=runner.eps, want_dx=False)
+        a_dy, a_dyx = O.channel_abs_sums(dy[n:n + 1, sl], x[n:n + 1, sl], 1, b["mean"], b["rstd"])
+        return st, b, a_dy, a_dyx
+
+    def row(u, gs):
+        n, c = u
+        st, b, _, _ = gs[n * G + c // Cg]
+        xr, dyr = x[n:n + 1, c:c + 1], dy[n:n + 1, c:c + 1]
+        y64 = O.forward_at(xr, 1, idx, st[0], st[2], gam[c:c + 1], bet[c:c + 1])
+        yd = _bf16_ulp_dist(ybits[n, c], O.round_bf16(y64))
+        far = np.nonzero(yd > 1)[0]
+        yfb = 0.0
+        if far.size:
+            got = (ybits[n, c][far].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            bar = 1e-5 * np.maximum(np.abs(y64[far]), abs(float(gam[c])) + abs(float(bet[c])))
+            yfb = float(np.max(np.abs(got - y64[far]) / bar))
+        dx64 = O.backward_at(dyr, xr, 1, idx, b["mean"], b["rstd"], b["c1"], b["c2"], gam[c:c + 1])
+        dxd = _bf16_ulp_dist(dxbits[n, c], O.round_bf16(dx64))
+        dxg = (dxbits[n, c].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return {"y_max_ulp": int(yd.max()), "y_equal": int(np.sum(yd == 0)), "y_beyond_1": int(far.size),
+                "y_fallback": yfb, "dx_max_ulp": int(dxd.max()), "dx_max_err": float(np.max(np.abs(dxg - dx64))),
+                "dx_max_abs": float(np.max(np.abs(dx64)))}
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        gs = list(pool.map(group, groups))
+        rs = list(pool.map(lambda u: row(u, gs), rows))
+    mean64 = np.array([g[0][0][0, 0] for g in gs])
+    sigma64 = np.sqrt(np.array([g[0][1][0, 0] for g in gs]))
+    rstd64 = np.array([g[0][2][0, 0] for g in gs])
+    dg64, db64, a_dy, a_dyx = np.zeros(C), np.zeros(C), np.zeros(C), np.zeros(C)
+    for (n, g), (_, b, ad, adx) in zip(groups, gs):
+        sl = slice(g * Cg, (g + 1) * Cg)
+        dg64[sl] += b["dgamma"]
+        db64[sl] += b["dbeta"]
+        a_dy[sl] += ad
+        a_dyx[sl] += adx
+    return {
+        "workload": case.name,
+        "method": (f"the oracle per (n, g) group and per (n, c) row on {workers} threads "
+                   f"({len(groups)} groups, {len(rows)} rows, {time.perf_counter() - t0:.1f} s); no fp64 "
+                   "tensor of the whole volume is formed"),
+        "mean_max_rel_err": float(np.max(np.abs(m_gpu - mean64) / np.abs(mean64))),
+        "mean_max_err_of_sigma": float(np.max(np.abs(m_gpu - mean64) / sigma64)),
+        "rstd_max_rel_err": float(np.max(np.abs(r_gpu - rstd64) / rstd64)),
+        "y_max_ulp_from_fp64_rounded_once": max(r["y_max_ulp"] for r in rs),
+        "y_frac_equal_to_fp64_rounded_once": sum(r["y_equal"] for r in rs) / case.numel,
+        "y_beyond_1_ulp": sum(r["y_beyond_1"] for r in rs),
+        "y_beyond_1_ulp_max_err_of_fp32_bar": max(r["y_fallback"] for r in rs),
+        "dx_max_err_of_max_abs_dx": max(r["dx_max_err"] for r in rs) / max(r["dx_max_abs"] for r in rs),
+        "dx_max_ulp_from_fp64_rounded_once": max(r["dx_max_ulp"] for r in rs),
+        "zero_mean_dy": {"dgamma_max_err_of_sum_abs_terms": float(np.max(np.abs(dg_gpu - dg64) / a_dyx)),
+                         "dbeta_max_err_of_sum_abs_terms": float(np.max(np.abs(db_gpu - db64) / a_dy))},
+    }
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -1106,6 +1212,9 @@ def main():
             "inputs_just_written": {"ms_per_step": round(pms8, 4),
                                     "value": round(r8.step_bytes / (pms8 * 1e-3) / 1e9, 1)},
         }
+        if not args.no_cpu_baseline:
+            log(f"the GPU's accuracy on {c8.name} against the oracle, group by group and row by row")
+            out["scale8"]["accuracy"] = accuracy_streamed(r8)
         del r8
         torch.cuda.empty_cache()
         log("census: 18 GroupNorm sites of a scale-7 UNet")
