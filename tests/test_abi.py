@@ -62,7 +62,8 @@ def bwd(fn="gn_backward", **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), 1), (dict(y=None), 1), (dict(mean=None), 1), (dict(ws=None), 1),
-    (dict(N=0), 2), (dict(S=-1), 2), (dict(G=0), 2), (dict(C=8, G=8, S=1), 2),
+    (dict(N=0), 2), (dict(S=0), 2), (dict(S=-1), 2), (dict(G=0), 2), (dict(C=0), 2),
+    (dict(C=8, G=8, S=1), 2),
     (dict(C=6, G=4), 3),
     (dict(xdt=2), 4), (dict(xdt=GN_F32, ydt=GN_BF16), 4), (dict(ydt=7), 4),
     (dict(eps=-1e-5), 5), (dict(eps=float("nan")), 5), (dict(eps=float("inf")), 5),
@@ -78,7 +79,8 @@ def test_forward_validation(kw, status, fn):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dy=None), 1), (dict(x=None), 1), (dict(rstd=None), 1), (dict(ws=None), 1),
-    (dict(C=6, G=4), 3), (dict(N=-2), 2), (dict(dydt=5), 4), (dict(xdt=3), 4),
+    (dict(C=6, G=4), 3), (dict(N=-2), 2), (dict(N=0), 2), (dict(S=0), 2), (dict(dydt=5), 4),
+    (dict(xdt=3), 4),
     (dict(wsb=0), 6), (dict(dx=ctypes.c_void_p(0x10008)), 7),
     (dict(dgamma=ctypes.c_void_p(0x10002)), 7), (dict(beta=ctypes.c_void_p(0x10002)), 7),
     (dict(act=5), 10),
@@ -168,6 +170,7 @@ def cl_fwd(**kw):
     (dict(C=4096, G=8), 11),          # C/8 = 512 > 256
     (dict(C=32, G=5), 3),             # C % G
     (dict(N=0), 2),
+    (dict(S=0), 2),
     (dict(x=None), 1),
     (dict(wsb=16), 6),
     (dict(xdt=7), 4),
@@ -233,7 +236,7 @@ def fwd_noalloc(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), 1), (dict(y=None), 1), (dict(rstd=None), 1),
-    (dict(N=0), 2), (dict(C=8, G=8, S=1), 2), (dict(C=6, G=4), 3),
+    (dict(N=0), 2), (dict(S=0), 2), (dict(C=8, G=8, S=1), 2), (dict(C=6, G=4), 3),
     (dict(xdt=7), 4), (dict(xdt=GN_F32, ydt=GN_BF16), 4), (dict(eps=float("nan")), 5),
     (dict(x=ctypes.c_void_p(0x10002)), 7), (dict(act=5), 10),
     # a shape whose workspace exceeds the static scratch (65536 rows need 2 MiB of row records)
