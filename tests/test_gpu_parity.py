@@ -839,3 +839,53 @@ def test_volume_past_int32_indexing():
     S = (1 << 28) + 64
     case = workloads.custom(1, 8, 8, (S,), torch.bfloat16, dist="unet", seed=31)
     sampled_check(workloads.make(case, DEV), "int64_volume", n_random=1 << 16, seed=31)
+
+
+# ----------------------------------------------------------------------------- input addresses
+
+def _placed(arena, nbytes, bit31):
+    """A 256-byte aligned offset into `arena` where 2 * nbytes fit wholly on one side of bit 31
+    of the address's low 32-bit word (set if bit31, clear otherwise)."""
+    a0 = arena.data_ptr()
+    for o in range(0, arena.numel() - 2 * nbytes + 1, 1 << 24):
+        lo = (a0 + o) & 0xFFFFFFFF
+        if bit31 and lo < 0x80000000:
+            o += 0x80000000 - lo
+        elif not bit31 and lo >= 0x80000000:
+            o += 0x100000000 - lo
+        lo = (a0 + o) & 0xFFFFFFFF
+        if o + 2 * nbytes <= arena.numel() and bool(lo & 0x80000000) == bit31 \
+                and ((lo + 2 * nbytes - 1) & 0x80000000 != 0) == bit31 and lo + 2 * nbytes <= 0x100000000:
+            return o
+    raise AssertionError("no placement found")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_inputs_whose_addresses_have_bit31_set_in_the_low_word(dtype):
+    """The step loads of 16-bit inputs read through a buffer resource whose scalar base is the
+    step's address, assembled from two 32-bit words. x and dy placed where the low word has bit
+    31 set give the same bits as placed where it is clear (a low word sign-extended over the
+    high one would send every such load outside the address space)."""
+    case = workloads.custom(1, 32, 8, (64, 64, 48), dtype, dist="unet", seed=98)
+    inp = _on_gpu(workloads.make(case, "cpu"))
+    nbytes = inp["x"].numel() * inp["x"].element_size()
+    arena = torch.empty((3 << 30) + 4 * nbytes, dtype=torch.uint8, device=DEV)
+    outs = []
+    for bit31 in (False, True):
+        o = _placed(arena, nbytes, bit31)
+        x = arena[o:o + nbytes].view(dtype).view(inp["x"].shape)
+        dy = arena[o + nbytes:o + 2 * nbytes].view(dtype).view(inp["dy"].shape)
+        x.copy_(inp["x"])
+        dy.copy_(inp["dy"])
+        for t in (x, dy):
+            assert bool(t.data_ptr() & 0x80000000) == bit31
+        say(f"{case.name}: x at {x.data_ptr():#x}, dy at {dy.data_ptr():#x} (bit 31 of the low word "
+            f"{'set' if bit31 else 'clear'}) -> gn_forward + gn_backward")
+        r = _run({**inp, "x": x, "dy": dy})
+        outs.append({k: v.clone() for k, v in r.items()})
+    for k in outs[0]:
+        a, b = outs[0][k], outs[1][k]
+        bits = (lambda t: t.view(torch.int16)) if a.element_size() == 2 else (lambda t: t.view(torch.int32))
+        assert torch.equal(bits(a), bits(b)), k
+    del arena
+    torch.cuda.empty_cache()

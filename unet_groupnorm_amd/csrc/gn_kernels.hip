@@ -157,13 +157,45 @@ __device__ __forceinline__ uint32_t load_step_masked(const T* __restrict__ p, co
 
 // ------------------------------------------------------------------ forward
 
-// The lane's V raw vectors of one full step.
+// Dword 3 of a raw buffer resource (gfx9 layout): data format 32 bits, no swizzle, no
+// index stride. Raw loads ignore the format, but a zero format would make them return 0.
+constexpr int kBufWord3 = 0x00020000;
+
+// The lane's V raw vectors of one full step, plain global loads.
+template <bool NT, int V, typename T>
+__device__ __forceinline__ void load_raw_step_global(const T* __restrict__ p, int64_t sv0, int blk, int tid,
+                                                     typename Io<T>::Raw (&r)[V])
+{
+#pragma unroll
+    for (int u = 0; u < V; ++u) r[u] = Io<T>::template load_raw<NT>(p + (sv0 + int64_t(u) * blk + tid) * kVec);
+}
+
+// The same vectors. Plain 16-byte vectors (bf16, fp16) are read through a buffer resource
+// that spans just this step: the step's start is the same for every lane, so it goes into
+// the resource's scalar base and each load carries a 32-bit lane offset instead of a 64-bit
+// vector address (fewer VALU operations a vector), and the resource's range check keeps
+// every load inside the step. Same addresses, same bits. Measured on MI355X (bf16, C=32,
+// G=8, interleaved A/B): 128^3 168.2 -> 167.1 us a step (normalize 45.2 -> 44.5, dx 64.5 ->
+// 63.8), 64^3 56.0 -> 54.8, 32^3 23.4 -> 24.1. The backward sums, which stream x and dy side
+// by side, lost 2.3 us at 128^3 this way and use load_raw_step_global.
 template <bool NT, int V, typename T>
 __device__ __forceinline__ void load_raw_step(const T* __restrict__ p, int64_t sv0, int blk, int tid,
                                               typename Io<T>::Raw (&r)[V])
 {
+    if constexpr (!NT && sizeof(typename Io<T>::Raw) == 16) {
+        // readfirstlane returns a signed int: both words are kept unsigned, so that a low word
+        // with bit 31 set is not sign-extended over the high word.
+        const uint64_t a = reinterpret_cast<uint64_t>(p + sv0 * kVec);
+        const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a)));
+        const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32)));
+        const uint64_t base = (uint64_t(hi) << 32) | uint64_t(lo);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), 0, V * blk * 16, kBufWord3);
 #pragma unroll
-    for (int u = 0; u < V; ++u) r[u] = Io<T>::template load_raw<NT>(p + (sv0 + int64_t(u) * blk + tid) * kVec);
+        for (int u = 0; u < V; ++u) r[u].u = __builtin_amdgcn_raw_buffer_load_b128(rs, (u * blk + tid) * 16, 0, 0);
+    } else {
+        load_raw_step_global<NT>(p, sv0, blk, tid, r);
+    }
 }
 
 // Steps [fs, fe) of a job are full; step 0 when fs = 1 and step fe when fe < nsteps hold
@@ -538,20 +570,20 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
         if (fe > fs) {
             RawX AX[kStepVecs], BX[kStepVecs];
             RawD AD[kStepVecs], BD[kStepVecs];
-            load_raw_step<NT>(x, jb.v0 + fs * stepv, blk, tid, AX);
-            load_raw_step<NT>(dy, jb.v0 + fs * stepv, blk, tid, AD);
+            load_raw_step_global<NT>(x, jb.v0 + fs * stepv, blk, tid, AX);
+            load_raw_step_global<NT>(dy, jb.v0 + fs * stepv, blk, tid, AD);
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step_global<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step_global<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
-                load_raw_step<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
-                load_raw_step<NT>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
+                load_raw_step_global<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
+                load_raw_step_global<NT>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
                 bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
             }
             if (s + 1 < fe) {
-                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
-                load_raw_step<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
+                load_raw_step_global<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step_global<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
                 bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
             } else {
