@@ -176,8 +176,11 @@ __device__ __forceinline__ void load_raw_step_global(const T* __restrict__ p, in
 // vector address (fewer VALU operations a vector), and the resource's range check keeps
 // every load inside the step. Same addresses, same bits. Measured on MI355X (bf16, C=32,
 // G=8, interleaved A/B): 128^3 168.2 -> 167.1 us a step (normalize 45.2 -> 44.5, dx 64.5 ->
-// 63.8), 64^3 56.0 -> 54.8, 32^3 23.4 -> 24.1. The backward sums, which stream x and dy side
-// by side, lost 2.3 us at 128^3 this way and use load_raw_step_global.
+// 63.8), 64^3 56.0 -> 54.8, 32^3 23.4 -> 24.1. The backward sums read x this way and dy with
+// load_raw_step_global: with both through resources they lost 2.3 us at 128^3; with x alone
+// the resident-input step is unchanged (166.8 against 167.0 us) and the sums gain 3-5 us
+// when x and dy come from HBM (after a 512 MiB read 49.6 -> 44.6 us, with x and dy just
+// rewritten 58.8 -> 55.8).
 template <bool NT, int V, typename T>
 __device__ __forceinline__ void load_raw_step(const T* __restrict__ p, int64_t sv0, int blk, int tid,
                                               typename Io<T>::Raw (&r)[V])
@@ -570,19 +573,19 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
         if (fe > fs) {
             RawX AX[kStepVecs], BX[kStepVecs];
             RawD AD[kStepVecs], BD[kStepVecs];
-            load_raw_step_global<NT>(x, jb.v0 + fs * stepv, blk, tid, AX);
+            load_raw_step<NT>(x, jb.v0 + fs * stepv, blk, tid, AX);
             load_raw_step_global<NT>(dy, jb.v0 + fs * stepv, blk, tid, AD);
             int64_t s = fs;
             for (; s + 2 < fe; s += 2) {
-                load_raw_step_global<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
                 load_raw_step_global<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
-                load_raw_step_global<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
+                load_raw_step<NT>(x, jb.v0 + (s + 2) * stepv, blk, tid, AX);
                 load_raw_step_global<NT>(dy, jb.v0 + (s + 2) * stepv, blk, tid, AD);
                 bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
             }
             if (s + 1 < fe) {
-                load_raw_step_global<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
+                load_raw_step<NT>(x, jb.v0 + (s + 1) * stepv, blk, tid, BX);
                 load_raw_step_global<NT>(dy, jb.v0 + (s + 1) * stepv, blk, tid, BD);
                 bwd_full_step<TX, TD>(AX, AD, mu, act, scale, shift, s1, s2);
                 bwd_full_step<TX, TD>(BX, BD, mu, act, scale, shift, s1, s2);
