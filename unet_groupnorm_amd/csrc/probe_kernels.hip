@@ -4,7 +4,7 @@
 //  - Streaming probes: a read stream, a write fill and a copy over a device buffer, with
 //    plain or nontemporal loads and stores. They move bytes and do nothing else, so their
 //    rates are the HBM rates the device delivers for pure reads, pure writes and a 1:1 mix;
-//    the GroupNorm kernels' times are judged against the bound those rates give for each
+//    the GroupNorm kernels' times are compared with the bound those rates give for each
 //    kernel's own mix of reads and writes.
 //  - A negative control for the determinism tests: per-group sums of a bf16 volume in which
 //    each workgroup reduces its job in a fixed order and then adds its partial to the
