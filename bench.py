@@ -1199,6 +1199,9 @@ def main():
         ms8, _ = r8.timed_steps(max(5, args.steps // 5), 3)
         proto8 = r8.step_protocol(trials=7, per_trial=5)
         roof8 = site_roofline(r8, ceil, 10)
+        traffic8, note8 = load_traffic(c8.name)
+        roof8["traffic"] = (traffic8 or {}).get("bytes_per_launch")
+        roof8["traffic_note"] = note8 if traffic8 is None else traffic8.get("note", "ok")
         fms8 = r8.flushed_steps(5)
         pms8 = r8.produced_steps(5)
         out["scale8"] = {
