@@ -376,21 +376,21 @@ fin_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
 constexpr int kFinVecs = 2;
 
 // The normalize of one element: ((x - hi) - lo) * gamma*rstd + beta, then the relu.
+template <bool ACT>
 struct Affine {
     float hi, lo, scale, shift;
-    bool act;
     __device__ __forceinline__ float operator()(float e) const
     {
         const float v = fmaf((e - hi) - lo, scale, shift);
-        return act ? relu_f(v) : v;
+        return ACT ? relu_f(v) : v;
     }
 };
 
 // y for vector vi of job jb: one vector load and store when the vector lies wholly inside
 // the job, element-wise at its edges.
-template <bool NT, typename TX, typename TY>
+template <bool NT, typename TX, typename TY, typename F>
 __device__ __forceinline__ void apply_vec(const TX* __restrict__ x, TY* __restrict__ y, const Job& jb,
-                                          int64_t vi, const Affine& f)
+                                          int64_t vi, const F& f)
 {
     if (vi >= jb.vf0 && vi < jb.vf1) {
         float e[kVec], o[kVec];
@@ -406,7 +406,7 @@ __device__ __forceinline__ void apply_vec(const TX* __restrict__ x, TY* __restri
     }
 }
 
-template <typename TX, typename TY, bool NT>
+template <typename TX, typename TY, bool NT, bool ACT>
 __global__ void __launch_bounds__(256)
 apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
              const float4* __restrict__ coef)
@@ -417,7 +417,7 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
         const int64_t j = jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row];
-        const Affine f = {cf.x, cf.y, cf.z, cf.w, a.act != 0};
+        const Affine<ACT> f = {cf.x, cf.y, cf.z, cf.w};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
             for (int u = 0; u < kApplyVecs; ++u) apply_vec<NT>(x, y, jb, sv0 + int64_t(u) * blk + tid, f);
@@ -426,9 +426,9 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
 }
 
 // y for the lane's V vectors of one full step, from raw loads.
-template <typename TX, typename TY, int V>
+template <typename TX, typename TY, int V, typename F>
 __device__ __forceinline__ void apply_full_step(const typename Io<TX>::Raw (&r)[V], TY* __restrict__ y,
-                                                int64_t sv0, int blk, int tid, const Affine& f)
+                                                int64_t sv0, int blk, int tid, const F& f)
 {
 #pragma unroll
     for (int u = 0; u < V; ++u) {
@@ -449,7 +449,7 @@ __device__ __forceinline__ void apply_full_step(const typename Io<TX>::Raw (&r)[
 // finalize launch is gone. The group's first job publishes mean, rstd and the rows'
 // coefficients. The job's first full step is requested before the merge so that its
 // latency overlaps it; the full steps are software-pipelined as in stats_kernel.
-template <typename TX, typename TY, bool NT>
+template <typename TX, typename TY, bool NT, bool ACT>
 __global__ void __launch_bounds__(256, 4)
 apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
                  float eps, const float2* __restrict__ part, float* __restrict__ mean_out,
@@ -470,7 +470,7 @@ apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, cons
         if (fe > fs) load_raw_step<NT>(x, jb.v0 + fs * stepv, blk, tid, A);
         const GroupStat st = group_stat(x, part, a, eps, n, g, l);
         if (jb.k == 0 && c == g * a.Cg) publish_group_stat(st, gamma, beta, a, n, g, mean_out, rstd_out, coef);
-        const Affine f = {st.hi, st.lo, (gamma ? gamma[c] : 1.0f) * st.rstd, beta ? beta[c] : 0.0f, a.act != 0};
+        const Affine<ACT> f = {st.hi, st.lo, (gamma ? gamma[c] : 1.0f) * st.rstd, beta ? beta[c] : 0.0f};
         // The edge steps stay rolled: unrolled, their element-wise loads would set the
         // kernel's register count.
         if (fs > 0) {
@@ -544,8 +544,11 @@ __device__ __forceinline__ void bwd_masked_step(const TD* __restrict__ dy, const
 
 // Per job: s1 = sum dy and s2 = rstd * sum dy * (x - mean) over the job's elements, lanes
 // summing their tiles in step order, then the shuffle tree, then the waves in order. The
-// full steps are software-pipelined as in stats_kernel.
-template <typename TX, typename TD, bool NT>
+// full steps are software-pipelined as in stats_kernel. The relu gate is a template
+// parameter (with_act): read from the launch arguments at run time, it was evaluated on
+// every element and then discarded when off (an fma, two compares and two selects an
+// element).
+template <typename TX, typename TD, bool NT, bool ACT>
 __global__ void __launch_bounds__(kRedBlock)
 bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
                   const float* __restrict__ mean, const float* __restrict__ rstd,
@@ -563,7 +566,7 @@ bwd_reduce_kernel(const TD* __restrict__ dy, const TX* __restrict__ x,
         const Job jb = job_at(a.S, a.chunk, a.K, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, ng = n * a.G + c / a.Cg;
         const float mu = mean[ng];
-        const bool act = a.act != 0;
+        constexpr bool act = ACT;
         const float scale = act ? rstd[ng] * (gamma ? gamma[c] : 1.0f) : 0.0f;
         const float shift = act ? (beta ? beta[c] : 0.0f) : 0.0f;
         float s1 = 0.0f, s2 = 0.0f;  // sum dy, sum dy * (x - mu)
@@ -628,23 +631,31 @@ __device__ __forceinline__ float2 group_c12(const float2* __restrict__ part, con
 // The dx coefficients of row (n, c): mean, A = rstd*gamma_c, B = -rstd*c1, E = -rstd^2*c2, so
 // that dx = rstd*(gamma_c*g - c1 - xhat*c2) = A*g + (B + E*(x - mean)), where g is dy, or with
 // the relu dy gated on pre = (x - mean)*A + beta_c.
+template <bool ACT>
 struct DxCoef {
     float mu, A, B, E, bt;
-    bool act, single;
+    bool single;
     // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
     __device__ __forceinline__ float operator()(float xv, float gv) const
     {
-        const float d = xv - mu;
-        const float g = act ? relu_gate(fmaf(d, A, bt), gv) : gv;
-        float t = fmaf(A, g, fmaf(E, d, B));
+        float t = full(xv, gv);
         if (single) t = t - t;
         return t;
     }
+    // The same without the single-element rule, for full steps: a single-element group's
+    // rows are one element long, so no full step ever holds one.
+    __device__ __forceinline__ float full(float xv, float gv) const
+    {
+        const float d = xv - mu;
+        const float g = ACT ? relu_gate(fmaf(d, A, bt), gv) : gv;
+        return fmaf(A, g, fmaf(E, d, B));
+    }
 };
 
-__device__ __forceinline__ DxCoef dx_coef(float mu, float rs, float gm, float2 c12, float bt, const KArgs& a)
+template <bool ACT>
+__device__ __forceinline__ DxCoef<ACT> dx_coef(float mu, float rs, float gm, float2 c12, float bt, const KArgs& a)
 {
-    return DxCoef{mu, rs * gm, -(rs * c12.x), -((rs * rs) * c12.y), bt, a.act != 0, a.M == 1};
+    return DxCoef<ACT>{mu, rs * gm, -(rs * c12.x), -((rs * rs) * c12.y), bt, a.M == 1};
 }
 
 // Writes the dx coefficient records of group (n, g)'s rows for bwd_apply_kernel.
@@ -654,7 +665,7 @@ __device__ __forceinline__ void publish_dx_coef(float mu, float rs, float2 c12, 
 {
     for (int64_t i = threadIdx.x; i < a.Cg; i += blockDim.x) {
         const int64_t c = g * a.Cg + i;
-        const DxCoef k = dx_coef(mu, rs, gamma ? gamma[c] : 1.0f, c12, 0.0f, a);
+        const DxCoef<false> k = dx_coef<false>(mu, rs, gamma ? gamma[c] : 1.0f, c12, 0.0f, a);
         coef[2 * (n * a.C + c)] = make_float4(mu, k.A, k.B, k.E);
         coef[2 * (n * a.C + c) + 1] = make_float4(beta ? beta[c] : 0.0f, a.M == 1 ? 1.0f : 0.0f, 0.0f, 0.0f);
     }
@@ -706,9 +717,9 @@ fin_bwd_kernel(const float* __restrict__ mean, const float* __restrict__ rstd,
 
 // dx for vector vi of job jb: vector loads and store when the vector lies wholly inside the
 // job, element-wise at its edges.
-template <bool NT, typename TX, typename TD>
+template <bool NT, typename TX, typename TD, typename F>
 __device__ __forceinline__ void dx_vec(const TD* __restrict__ dy, const TX* __restrict__ x, TX* __restrict__ dx,
-                                       const Job& jb, int64_t vi, const DxCoef& k)
+                                       const Job& jb, int64_t vi, const F& k)
 {
     if (vi >= jb.vf0 && vi < jb.vf1) {
         float xv[kVec], gv[kVec], o[kVec];
@@ -725,7 +736,7 @@ __device__ __forceinline__ void dx_vec(const TD* __restrict__ dy, const TX* __re
     }
 }
 
-template <typename TX, typename TD, bool NT>
+template <typename TX, typename TD, bool NT, bool ACT>
 __global__ void __launch_bounds__(256)
 bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
                  const float4* __restrict__ coef, TX* __restrict__ dx)
@@ -736,10 +747,9 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
         const int64_t j = jj;
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row], cg = coef[2 * jb.row + 1];
-        const bool act = a.act != 0;
         // Whether the whole group is one element comes from the record: a spatial shard's
         // piece of a group can be one element when the group is not.
-        const DxCoef k = {cf.x, cf.y, cf.z, cf.w, act ? cg.x : 0.0f, act, cg.y != 0.0f};
+        const DxCoef<ACT> k = {cf.x, cf.y, cf.z, cf.w, ACT ? cg.x : 0.0f, cg.y != 0.0f};
         for (int64_t sv0 = jb.v0; sv0 < jb.v0 + jb.nvec; sv0 += stepv) {
 #pragma unroll
             for (int u = 0; u < kApplyVecs; ++u) dx_vec<NT>(dy, x, dx, jb, sv0 + int64_t(u) * blk + tid, k);
@@ -748,10 +758,10 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
 }
 
 // dx for the lane's V vectors of one full step, from raw loads.
-template <typename TX, typename TD, int V>
+template <typename TX, typename TD, int V, typename F>
 __device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V],
                                              const typename Io<TD>::Raw (&rd)[V], TX* __restrict__ dx,
-                                             int64_t sv0, int blk, int tid, const DxCoef& k)
+                                             int64_t sv0, int blk, int tid, const F& k)
 {
 #pragma unroll
     for (int u = 0; u < V; ++u) {
@@ -759,7 +769,7 @@ __device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V]
         Io<TX>::widen(rx[u], xv);
         Io<TD>::widen(rd[u], gv);
 #pragma unroll
-        for (int i = 0; i < kVec; ++i) o[i] = k(xv[i], gv[i]);
+        for (int i = 0; i < kVec; ++i) o[i] = k.full(xv[i], gv[i]);
         Io<TX>::template store8<kNtStoreStream>(dx + (sv0 + int64_t(u) * blk + tid) * kVec, o);
     }
 }
@@ -769,7 +779,7 @@ __device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V]
 // exactly as fin_bwd_kernel does, and streams the job. The group's first job writes the
 // rows' coefficient records; the first job of channel c in sample 0 writes dgamma_c and
 // dbeta_c, summed exactly as fin_bwd_kernel sums them.
-template <typename TX, typename TD, bool NT>
+template <typename TX, typename TD, bool NT, bool ACT>
 __global__ void __launch_bounds__(256, 3)
 bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                      const float* __restrict__ rstd, const float* __restrict__ gamma,
@@ -800,8 +810,8 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
         const float2 c12 = group_c12(part, gamma, a, n, g, s_a, s_b, s_coef);
         if (jb.k == 0 && c == g * a.Cg) publish_dx_coef(mu, rs, c12, gamma, beta, a, n, g, coef);
         if ((dgamma || dbeta) && jb.k == 0 && n == 0) channel_param_sums(part, a, c, s_a, s_b, dgamma, dbeta);
-        const bool act = a.act != 0;
-        const DxCoef k = dx_coef(mu, rs, gamma ? gamma[c] : 1.0f, c12, act ? (beta ? beta[c] : 0.0f) : 0.0f, a);
+        constexpr bool act = ACT;
+        const DxCoef<ACT> k = dx_coef<ACT>(mu, rs, gamma ? gamma[c] : 1.0f, c12, act ? (beta ? beta[c] : 0.0f) : 0.0f, a);
         if (fs > 0) {  // rolled, as in apply_fin_kernel
 #pragma unroll 1
             for (int u = 0; u < V; ++u) dx_vec<NT>(dy, x, dx, jb, jb.v0 + int64_t(u) * blk + tid, k);
@@ -1243,6 +1253,16 @@ hipError_t with_policy(const KArgs& a, F&& f)
     return f(std::bool_constant<Stream>{});
 }
 
+// Calls f with std::bool_constant<ACT>: whether the relu is fused, a template parameter of
+// the streaming and backward-sum kernels so that the plain path carries none of its
+// arithmetic.
+template <typename F>
+hipError_t with_act(const KArgs& a, F&& f)
+{
+    if (a.act) return f(std::bool_constant<true>{});
+    return f(std::bool_constant<false>{});
+}
+
 hipError_t launch_stats_partials(const void* x, int xdt, const KArgs& a, Workspace ws, hipStream_t st)
 {
     return with_type(xdt, [&](auto tx) {
@@ -1263,9 +1283,12 @@ hipError_t launch_bwd_partials(const void* dy, int dydt, const void* x, int xdt,
             return with_policy<kNtBwdReduce>(a, [&](auto nt) {
                 using TX = decltype(tx);
                 using TD = decltype(td);
-                return launch(bwd_reduce_kernel<TX, TD, decltype(nt)::value>, grid_of(a.jobs),
-                              dim3(unsigned(a.block)), st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a,
-                              ws.part);
+                constexpr bool NT = decltype(nt)::value;
+                return with_act(a, [&](auto act) {
+                    return launch(bwd_reduce_kernel<TX, TD, NT, decltype(act)::value>, grid_of(a.jobs),
+                                  dim3(unsigned(a.block)), st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a,
+                                  ws.part);
+                });
             });
         });
     });
@@ -1308,9 +1331,13 @@ hipError_t launch_fwd_apply(const void* x, int xdt, void* y, int ydt, const KArg
         return with_policy<kNtApply>(a, [&](auto nt) {
             using TX = decltype(tx);
             constexpr bool NT = decltype(nt)::value;
-            if (ydt == kF32)
-                return launch(apply_kernel<TX, float, NT>, grid, block, st, cp<TX>(x), mp<float>(y), a, coef);
-            return launch(apply_kernel<TX, TX, NT>, grid, block, st, cp<TX>(x), mp<TX>(y), a, coef);
+            return with_act(a, [&](auto act) {
+                constexpr bool ACT = decltype(act)::value;
+                if (ydt == kF32)
+                    return launch(apply_kernel<TX, float, NT, ACT>, grid, block, st, cp<TX>(x), mp<float>(y), a,
+                                  coef);
+                return launch(apply_kernel<TX, TX, NT, ACT>, grid, block, st, cp<TX>(x), mp<TX>(y), a, coef);
+            });
         });
     });
 }
@@ -1334,8 +1361,10 @@ hipError_t launch_bwd_apply(const void* dy, int dydt, const void* x, int xdt, vo
             return with_policy<kNtBwdApply>(a, [&](auto nt) {
                 using TX = decltype(tx);
                 using TD = decltype(td);
-                return launch(bwd_apply_kernel<TX, TD, decltype(nt)::value>, grid, block, st, cp<TD>(dy),
-                              cp<TX>(x), a, coef, mp<TX>(dx));
+                return with_act(a, [&](auto act) {
+                    return launch(bwd_apply_kernel<TX, TD, decltype(nt)::value, decltype(act)::value>, grid, block,
+                                  st, cp<TD>(dy), cp<TX>(x), a, coef, mp<TX>(dx));
+                });
             });
         });
     });
@@ -1350,11 +1379,14 @@ hipError_t launch_fwd_apply_fin(const void* x, int xdt, const float* gamma, cons
         return with_policy<kNtApply>(a, [&](auto nt) {
             using TX = decltype(tx);
             constexpr bool NT = decltype(nt)::value;
-            if (ydt == kF32)
-                return launch(apply_fin_kernel<TX, float, NT>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma,
-                              beta, eps, part, mean, rstd, a, ws.coef, mp<float>(y));
-            return launch(apply_fin_kernel<TX, TX, NT>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma, beta,
-                          eps, part, mean, rstd, a, ws.coef, mp<TX>(y));
+            return with_act(a, [&](auto act) {
+                constexpr bool ACT = decltype(act)::value;
+                if (ydt == kF32)
+                    return launch(apply_fin_kernel<TX, float, NT, ACT>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x),
+                                  gamma, beta, eps, part, mean, rstd, a, ws.coef, mp<float>(y));
+                return launch(apply_fin_kernel<TX, TX, NT, ACT>, grid_of(a.jobs_f), dim3(256), st, cp<TX>(x), gamma,
+                              beta, eps, part, mean, rstd, a, ws.coef, mp<TX>(y));
+            });
         });
     });
 }
@@ -1369,9 +1401,11 @@ hipError_t launch_bwd_apply_fin(const void* dy, int dydt, const void* x, int xdt
             return with_policy<kNtBwdApply>(a, [&](auto nt) {
                 using TX = decltype(tx);
                 using TD = decltype(td);
-                return launch(bwd_apply_fin_kernel<TX, TD, decltype(nt)::value>, grid_of(a.jobs_f), dim3(256), st,
-                              cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, part, a, ws.coef, dgamma, dbeta,
-                              mp<TX>(dx));
+                return with_act(a, [&](auto act) {
+                    return launch(bwd_apply_fin_kernel<TX, TD, decltype(nt)::value, decltype(act)::value>,
+                                  grid_of(a.jobs_f), dim3(256), st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta,
+                                  part, a, ws.coef, dgamma, dbeta, mp<TX>(dx));
+                });
             });
         });
     });
