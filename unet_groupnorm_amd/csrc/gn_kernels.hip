@@ -858,7 +858,7 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
 // per-row normalize coefficients (the record fin_fwd_kernel writes, so that
 // gn_forward_apply can follow) and y unless y is null, computed exactly as apply_kernel
 // computes it from those coefficients.
-template <int V, typename TX, typename TY>
+template <int V, typename TX, typename TY, bool ACT>
 __global__ void __launch_bounds__(kResMaxBlock)
 res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
                const float* __restrict__ beta, float eps, float* __restrict__ mean_out,
@@ -868,7 +868,7 @@ res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
     const int tid = threadIdx.x, blk = blockDim.x;
     const int vg = int(a.M / kVec);    // vectors per group (<= kResMaxVecs)
     const float fM = float(a.M);       // exact: M <= 8 * kResMaxVecs
-    const bool act = a.act != 0;
+    constexpr bool act = ACT;
     const int64_t g = blockIdx.x, n = blockIdx.y, ng = n * a.G + g;
     const int64_t row0 = n * a.C + g * a.Cg;
     const int64_t vb = row0 * (a.S / kVec);  // the group's first vector
@@ -944,7 +944,7 @@ res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma,
 // (the record fin_bwd_kernel writes, for gn_backward_apply); per channel: dgamma and dbeta
 // over the samples in order; then dx unless dx is null, computed exactly as
 // bwd_apply_kernel computes it from those coefficients.
-template <int V, typename TX, typename TD>
+template <int V, typename TX, typename TD, bool ACT>
 __global__ void __launch_bounds__(kResMaxBlock)
 res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                const float* __restrict__ rstd, const float* __restrict__ gamma,
@@ -958,7 +958,7 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
     const int W = int(a.S / kVec), Cg = int(a.Cg), N = int(a.N);
     const int nvt = N * int(a.M / kVec);  // vectors of the workgroup (<= kResMaxVecs)
     const int nrows = N * Cg;             // rows of the workgroup
-    const bool act = a.act != 0;
+    constexpr bool act = ACT;
     const int64_t g = blockIdx.x;
     // The global vector index of workgroup row rho, and its sample and channel.
     auto row_base = [&](int rho, int& n, int& c) {
@@ -1090,7 +1090,7 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
 // sums and row sums are computed exactly as res_bwd_kernel computes them, so the rows
 // both kernels sum agree bitwise; the workgroup then takes sample n's c1, c2 and dx, and
 // dgamma/dbeta of its channels over all samples, in the same order as res_bwd_kernel.
-template <int V, typename TX, typename TD>
+template <int V, typename TX, typename TD, bool ACT>
 __global__ void __launch_bounds__(kResMaxBlock)
 res_bwd_split_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                      const float* __restrict__ rstd, const float* __restrict__ gamma,
@@ -1109,7 +1109,7 @@ res_bwd_split_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
     const int vg = Cg * W;
     const int nrows = Cg + (N - 1) * ncol;
     const int nvt = nrows * W;  // <= the plan's bound, within kResMaxVecs
-    const bool act = a.act != 0;
+    constexpr bool act = ACT;
     // Sample and channel of workgroup row R.
     auto row_of = [&](int R, int& nr, int& c) {
         if (R < Cg) {
@@ -1429,11 +1429,14 @@ hipError_t launch_res_fwd(const void* x, int xdt, const float* gamma, const floa
         return with_vecs(vecs, [&](auto v) {
             using TX = decltype(tx);
             constexpr int V = decltype(v)::value;
-            if (y && ydt == kF32)
-                return launch(res_fwd_kernel<V, TX, float>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean,
-                              rstd, a, ws.coef, mp<float>(y));
-            return launch(res_fwd_kernel<V, TX, TX>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd,
-                          a, ws.coef, mp<TX>(y));
+            return with_act(a, [&](auto act) {
+                constexpr bool ACT = decltype(act)::value;
+                if (y && ydt == kF32)
+                    return launch(res_fwd_kernel<V, TX, float, ACT>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean,
+                                  rstd, a, ws.coef, mp<float>(y));
+                return launch(res_fwd_kernel<V, TX, TX, ACT>, grid, blk, st, cp<TX>(x), gamma, beta, eps, mean, rstd,
+                              a, ws.coef, mp<TX>(y));
+            });
         });
     });
 }
@@ -1449,13 +1452,16 @@ hipError_t launch_res_bwd(const void* dy, int dydt, const void* x, int xdt, cons
                 using TX = decltype(tx);
                 using TD = decltype(td);
                 constexpr int V = decltype(v)::value;
-                if (split)
-                    return launch(res_bwd_split_kernel<V, TX, TD>, dim3(unsigned(a.G), unsigned(a.N)),
-                                  dim3(unsigned(block)), st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a,
-                                  ws.coef, dgamma, dbeta, mp<TX>(dx));
-                return launch(res_bwd_kernel<V, TX, TD>, dim3(unsigned(a.G)), dim3(unsigned(block)), st,
-                              cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.coef, dgamma, dbeta,
-                              mp<TX>(dx));
+                return with_act(a, [&](auto act) {
+                    constexpr bool ACT = decltype(act)::value;
+                    if (split)
+                        return launch(res_bwd_split_kernel<V, TX, TD, ACT>, dim3(unsigned(a.G), unsigned(a.N)),
+                                      dim3(unsigned(block)), st, cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a,
+                                      ws.coef, dgamma, dbeta, mp<TX>(dx));
+                    return launch(res_bwd_kernel<V, TX, TD, ACT>, dim3(unsigned(a.G)), dim3(unsigned(block)), st,
+                                  cp<TD>(dy), cp<TX>(x), mean, rstd, gamma, beta, a, ws.coef, dgamma, dbeta,
+                                  mp<TX>(dx));
+                });
             });
         });
     });
