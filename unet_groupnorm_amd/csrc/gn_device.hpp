@@ -53,7 +53,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
 // NaN-correct ReLU): relu is 0 where v < 0 and v otherwise, so NaN, +Inf and -0.0 pass;
 // its gradient is blocked where the relu result is <= 0 and passes otherwise (NaN too).
 __device__ __forceinline__ float relu_f(float v) { return v < 0.0f ? 0.0f : v; }
-__device__ __forceinline__ float relu_gate(float pre, float g) { return relu_f(pre) <= 0.0f ? 0.0f : g; }
+// The backward gate of the relu: closed where relu(pre) <= 0. relu(pre) <= 0 holds exactly
+// where pre <= 0 does (negatives and both zeros; a NaN pre gives a NaN relu, and both
+// comparisons are false for it, so the gate stays open), so the gate tests pre directly.
+__device__ __forceinline__ float relu_gate(float pre, float g) { return pre <= 0.0f ? 0.0f : g; }
 
 // Loads of the streamed tensors are marked nontemporal: each element is read once per
 // kernel, and on MI355X this lifts a streaming read from about 6.2 to about 7 TB/s.
