@@ -65,7 +65,25 @@ def _draw_large(i):
     return case, relu, layout
 
 
-CASES = [_draw(i) for i in range(32)] + [_draw_large(i) for i in range(16)]
+def _draw_large16(i):
+    """Large volumes of 16-bit inputs (whose full steps are read through buffer resources)
+    with the relu on half the time (the relu and plain builds of every kernel)."""
+    rng = np.random.default_rng(9700 + i)
+    G = int(rng.choice([2, 4, 8, 16]))
+    cg = int(rng.choice([1, 2, 4, 8]))
+    C = G * cg
+    N = int(rng.integers(1, 4))
+    nd = int(rng.integers(1, 4))
+    budget = max(1, int(rng.choice([1000000, 3000000])) // (N * C))
+    spatial = [int(max(1, round(budget ** (1.0 / nd) * rng.uniform(0.7, 1.3)))) for _ in range(nd)]
+    x_dtype = [torch.bfloat16, torch.float16][int(rng.integers(0, 2))]
+    dy_dtype = DTYPES[int(rng.integers(0, 3))]
+    relu = bool(rng.random() < 0.5)
+    case = workloads.custom(N, C, G, tuple(spatial), x_dtype, dy_dtype, dist="unet", seed=9700 + i)
+    return case, relu, "ncdhw"
+
+
+CASES = [_draw(i) for i in range(32)] + [_draw_large(i) for i in range(16)] + [_draw_large16(i) for i in range(8)]
 
 
 def _id(v):
