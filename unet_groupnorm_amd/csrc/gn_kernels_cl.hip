@@ -319,7 +319,7 @@ __device__ __forceinline__ void cl_load_coefc(const float2* __restrict__ p, floa
 
 // y = ((x - head) - tail) * gamma_c*rstd + beta_c, optional relu, one narrowing store; a
 // streaming job is kClApplyRounds rounds of a workgroup over one sample's voxels.
-template <int NGL, typename TX, typename TY, bool NT>
+template <int NGL, typename TX, typename TY, bool NT, bool ACT>
 __global__ void __launch_bounds__(kClBlock)
 cl_apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, ClArgs a, const float2* __restrict__ coefc,
                 const float4* __restrict__ coefg)
@@ -328,7 +328,7 @@ cl_apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, ClArgs a, const fl
     const int tid = threadIdx.x;
     const int Cv = int(a.Cv), cv = tid % Cv, vo = tid / Cv, vps = int(a.vps);
     const int64_t g0 = (int64_t(cv) * kVec) / a.Cg;
-    const bool act = a.act != 0;
+    constexpr bool act = ACT;  // a template parameter, as in the NCDHW streaming kernels
     for (int64_t j = blockIdx.x; j < a.jobs_a; j += gridDim.x) {
         const int64_t n = j / a.K_a, k = j - n * a.K_a;
         const int64_t v0 = k * a.chunk_a, v1 = (v0 + a.chunk_a < a.S) ? v0 + a.chunk_a : a.S;
@@ -904,10 +904,14 @@ hipError_t launch_cl_forward(const void* x, int xdt, const float* gamma, const f
             const float2* cc = ws.coefc;
             const float4* cg = ws.coefg;
             if (ydt == kF32)
-                return launch(cl_apply_kernel<NGL, TX, float, NT>, grid_of(a.jobs_a), dim3(kClBlock), st,
-                              cp<TX>(x), mp<float>(y), a, cc, cg);
-            return launch(cl_apply_kernel<NGL, TX, TX, NT>, grid_of(a.jobs_a), dim3(kClBlock), st, cp<TX>(x),
-                          mp<TX>(y), a, cc, cg);
+                return a.act ? launch(cl_apply_kernel<NGL, TX, float, NT, true>, grid_of(a.jobs_a), dim3(kClBlock),
+                                      st, cp<TX>(x), mp<float>(y), a, cc, cg)
+                             : launch(cl_apply_kernel<NGL, TX, float, NT, false>, grid_of(a.jobs_a), dim3(kClBlock),
+                                      st, cp<TX>(x), mp<float>(y), a, cc, cg);
+            return a.act ? launch(cl_apply_kernel<NGL, TX, TX, NT, true>, grid_of(a.jobs_a), dim3(kClBlock), st,
+                                  cp<TX>(x), mp<TX>(y), a, cc, cg)
+                         : launch(cl_apply_kernel<NGL, TX, TX, NT, false>, grid_of(a.jobs_a), dim3(kClBlock), st,
+                                  cp<TX>(x), mp<TX>(y), a, cc, cg);
         });
       });
     });
