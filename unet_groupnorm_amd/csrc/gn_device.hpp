@@ -240,24 +240,68 @@ __device__ __forceinline__ void chan_merge(Moments<CT>& a, CT nb, float mb, floa
     a.n = n;
 }
 
+// Lane i receives lane i + OFF's value, for the offsets of the fixed trees below (32, 16,
+// 8, 4, 2, 1), in registers rather than through LDS: OFF = 32 and 16 exchange halves and
+// rows of the wave (gfx950's v_permlane32_swap and v_permlane16_swap), smaller offsets
+// shift within each row of 16 lanes (DPP row_shl). Only lanes i < OFF are guaranteed lane
+// i + OFF's value, and only those lanes' results reach lane 0 in the trees. Every lane of
+// the wave must be active.
+template <int OFF>
+__device__ __forceinline__ uint32_t lane_down(uint32_t v)
+{
+    static_assert(OFF == 1 || OFF == 2 || OFF == 4 || OFF == 8 || OFF == 16 || OFF == 32, "tree offset");
+    if constexpr (OFF == 32) {
+        return __builtin_amdgcn_permlane32_swap(v, v, false, false)[1];
+    } else if constexpr (OFF == 16) {
+        return __builtin_amdgcn_permlane16_swap(v, v, false, false)[1];
+    } else {
+        return uint32_t(__builtin_amdgcn_update_dpp(int(v), int(v), 0x100 | OFF, 0xF, 0xF, false));
+    }
+}
+
+template <int OFF>
+__device__ __forceinline__ float lane_down(float v)
+{
+    return __uint_as_float(lane_down<OFF>(__float_as_uint(v)));
+}
+
+template <int OFF>
+__device__ __forceinline__ uint64_t lane_down(uint64_t v)
+{
+    return (uint64_t(lane_down<OFF>(uint32_t(v >> 32))) << 32) | uint64_t(lane_down<OFF>(uint32_t(v)));
+}
+
+template <int OFF, typename CT>
+__device__ __forceinline__ void wave_merge_level(Moments<CT>& a)
+{
+    const CT nb = lane_down<OFF>(a.n);
+    const float mb = lane_down<OFF>(a.m);
+    const float Mb = lane_down<OFF>(a.M2);
+    chan_merge(a, nb, mb, Mb);
+}
+
 // Lane 0 ends up with the merge of all 64 lanes, combined in a fixed tree: lane i takes
 // lane i + off for off = 32, 16, ..., 1 (left operand always the lower lane).
 template <typename CT>
 __device__ __forceinline__ void wave_merge(Moments<CT>& a)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const CT nb = __shfl_down(a.n, off);
-        const float mb = __shfl_down(a.m, off);
-        const float Mb = __shfl_down(a.M2, off);
-        chan_merge(a, nb, mb, Mb);
-    }
+    wave_merge_level<32>(a);
+    wave_merge_level<16>(a);
+    wave_merge_level<8>(a);
+    wave_merge_level<4>(a);
+    wave_merge_level<2>(a);
+    wave_merge_level<1>(a);
 }
 
+// Lane 0 ends up with the sum of all 64 lanes, in the same tree.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_down(v, off);
+    v = v + lane_down<32>(v);
+    v = v + lane_down<16>(v);
+    v = v + lane_down<8>(v);
+    v = v + lane_down<4>(v);
+    v = v + lane_down<2>(v);
+    v = v + lane_down<1>(v);
     return v;
 }
 

@@ -44,21 +44,28 @@ __device__ __forceinline__ int64_t cl_job_voxels(const ClArgs& a, int64_t k)
 
 // Lanes of a wave that own the same channel vector are Cv apart (Cv a power of two). Lane
 // i takes lane i + off for off = 32, 16, ..., Cv; lanes 0 .. min(Cv, 64) - 1 then hold the
-// merge over their channel vector's lanes of the wave.
+// merge over their channel vector's lanes of the wave. At each level only lanes i < off
+// feed those lanes, which is what lane_down guarantees. Cv is the same for every lane, so
+// the level tests are scalar branches and every lane stays active.
 template <typename CT>
 __device__ __forceinline__ void wave_merge_stride(Moments<CT>& a, int Cv)
 {
-    for (int off = 32; off >= Cv; off >>= 1) {
-        const CT nb = __shfl_down(a.n, off);
-        const float mb = __shfl_down(a.m, off);
-        const float Mb = __shfl_down(a.M2, off);
-        chan_merge(a, nb, mb, Mb);
-    }
+    if (Cv <= 32) wave_merge_level<32>(a);
+    if (Cv <= 16) wave_merge_level<16>(a);
+    if (Cv <= 8) wave_merge_level<8>(a);
+    if (Cv <= 4) wave_merge_level<4>(a);
+    if (Cv <= 2) wave_merge_level<2>(a);
+    if (Cv <= 1) wave_merge_level<1>(a);
 }
 
 __device__ __forceinline__ float wave_sum_stride(float v, int Cv)
 {
-    for (int off = 32; off >= Cv; off >>= 1) v = v + __shfl_down(v, off);
+    if (Cv <= 32) v = v + lane_down<32>(v);
+    if (Cv <= 16) v = v + lane_down<16>(v);
+    if (Cv <= 8) v = v + lane_down<8>(v);
+    if (Cv <= 4) v = v + lane_down<4>(v);
+    if (Cv <= 2) v = v + lane_down<2>(v);
+    if (Cv <= 1) v = v + lane_down<1>(v);
     return v;
 }
 
