@@ -400,21 +400,13 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f)
     return uint32_t((uint64_t(x) * f.m) >> 32);
 }
 
-// Butterfly sum over the wave; every lane returns the same value (a + b == b + a).
-__device__ __forceinline__ float wave_allsum(float v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off);
-    return v;
-}
-
 // Block-wide sums of a and b; waves are added in wave order and every thread returns
 // the result. s holds 2 * kResMaxWaves floats and may be reused on return.
 __device__ __forceinline__ float2 block_allsum2(float a, float b, float* s)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    a = wave_allsum(a);
-    b = wave_allsum(b);
+    a = wave_sum(a);
+    b = wave_sum(b);
     if (lane == 0) { s[wave] = a; s[kResMaxWaves + wave] = b; }
     __syncthreads();
     float ra = s[0], rb = s[kResMaxWaves];

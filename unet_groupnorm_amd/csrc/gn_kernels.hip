@@ -1009,8 +1009,8 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
             p1 = p1 + s_v1[rho * W + k];
             p2 = p2 + s_v2[rho * W + k];
         }
-        p1 = wave_allsum(p1);
-        p2 = wave_allsum(p2);
+        p1 = wave_sum(p1);
+        p2 = wave_sum(p2);
         if (lane == 0) {
             s_r1[rho] = p1;
             s_r2[rho] = p2 * rsn;
@@ -1025,8 +1025,8 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
             t1 = t1 + gm * s_r1[n * Cg + i];
             t2 = t2 + gm * s_r2[n * Cg + i];
         }
-        t1 = wave_allsum(t1);
-        t2 = wave_allsum(t2);
+        t1 = wave_sum(t1);
+        t2 = wave_sum(t2);
         if (lane == 0) {
             const float c1 = float(double(t1) / double(a.M));
             const float c2 = float(double(t2) / double(a.M));
@@ -1050,8 +1050,8 @@ res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float*
                 q1 = q1 + s_r2[n * Cg + i];
                 q2 = q2 + s_r1[n * Cg + i];
             }
-            q1 = wave_allsum(q1);
-            q2 = wave_allsum(q2);
+            q1 = wave_sum(q1);
+            q2 = wave_sum(q2);
             if (lane == 0) {
                 if (dgamma) dgamma[g * Cg + i] = q1;
                 if (dbeta) dbeta[g * Cg + i] = q2;
@@ -1168,8 +1168,8 @@ res_bwd_split_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
             p1 = p1 + s_v1[R * W + k];
             p2 = p2 + s_v2[R * W + k];
         }
-        p1 = wave_allsum(p1);
-        p2 = wave_allsum(p2);
+        p1 = wave_sum(p1);
+        p2 = wave_sum(p2);
         if (lane == 0) {
             s_r1[R] = p1;
             s_r2[R] = p2 * rsn;
@@ -1185,8 +1185,8 @@ res_bwd_split_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
             t1 = t1 + gm * s_r1[i];
             t2 = t2 + gm * s_r2[i];
         }
-        t1 = wave_allsum(t1);
-        t2 = wave_allsum(t2);
+        t1 = wave_sum(t1);
+        t2 = wave_sum(t2);
         if (lane == 0) {
             const float c1 = float(double(t1) / double(a.M));
             const float c2 = float(double(t2) / double(a.M));
@@ -1211,8 +1211,8 @@ res_bwd_split_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
                 q1 = q1 + s_r2[R];
                 q2 = q2 + s_r1[R];
             }
-            q1 = wave_allsum(q1);
-            q2 = wave_allsum(q2);
+            q1 = wave_sum(q1);
+            q2 = wave_sum(q2);
             if (lane == 0) {
                 if (dgamma) dgamma[g * Cg + i] = q1;
                 if (dbeta) dbeta[g * Cg + i] = q2;

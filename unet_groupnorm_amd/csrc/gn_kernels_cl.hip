@@ -745,11 +745,11 @@ cl_res_fwd_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, con
 // Backward, one workgroup per g covering the groups (n, g) of all N samples: vector w of
 // the workgroup is vector w mod vg of sample w / vg (vg = S * cvg, a multiple of 64, so
 // every wave lies in one sample). Per vector and channel: g (dy, or dy gated by the relu)
-// and g*(x - mean); lanes of a wave that share a channel vector add them in a butterfly
-// over the lane bits above log2(cvg); per (sample, channel) row the waves' sums in (vector
-// set, wave) order, then s2 times rstd; per sample c1, c2 over the group's channels in
-// order; per channel dgamma, dbeta over the samples in order; then dx from the registers as
-// bwd_apply computes it (dx = A*g + (B + E*(x - mean))).
+// and g*(x - mean); lanes of a wave that share a channel vector add them in the strided
+// lane tree (lane i takes lane i + off, off = 32 down to cvg); per (sample, channel) row
+// the waves' sums in (vector set, wave) order, then s2 times rstd; per sample c1, c2 over
+// the group's channels in order; per channel dgamma, dbeta over the samples in order; then
+// dx from the registers as bwd_apply computes it (dx = A*g + (B + E*(x - mean))).
 template <int V, typename TX, typename TD>
 __global__ void __launch_bounds__(kResMaxBlock)
 cl_res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
@@ -790,10 +790,8 @@ cl_res_bwd_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const flo
                 p[i] = q;
                 p[kVec + i] = q * d;
             }
-            for (int o = 32; o >= cvg; o >>= 1) {
 #pragma unroll
-                for (int j = 0; j < kSlot; ++j) p[j] = p[j] + __shfl_xor(p[j], o);
-            }
+            for (int j = 0; j < kSlot; ++j) p[j] = wave_sum_stride(p[j], cvg);
             if (lane < cvg) {
                 float* dst = s_part + ((u * kResMaxWaves + wave) * kClResMaxGroupVecs + lane) * kSlot;
 #pragma unroll
