@@ -589,6 +589,7 @@ CL_CASES = [
     workloads.custom(2, 32, 8, (4, 4, 4), torch.float16, torch.float32, dist="unet", seed=68),
     workloads.custom(2, 8, 8, (1, 1, 1), torch.float32, dist="normal", seed=69),           # M = 1
     workloads.custom(1, 16, 4, (40, 41, 42), torch.bfloat16, dist="unet", seed=70),        # many jobs, ragged
+    workloads.custom(1, 128, 16, (9, 10, 11), torch.bfloat16, dist="unet", seed=91),       # C/8 = 16: two tree levels
 ]
 
 
