@@ -441,6 +441,51 @@ def test_split_phase_entry_points_match_fused(case):
         assert torch.equal(u, v)
 
 
+FOLD_ORDER_CASES = [
+    workloads.SCALE7,                                                                        # 32 folded jobs a reduction job
+    workloads.custom(1, 32, 8, (64, 64, 64), torch.bfloat16, dist="unet", seed=95),          # 2
+    workloads.custom(1, 48, 8, (64, 64, 64), torch.bfloat16, dist="unet", seed=97),          # 2, 768 of them
+    workloads.custom(1, 32, 8, (61, 64, 64), torch.float16, dist="normal", seed=96),         # short last job: index order
+]
+
+
+@pytest.mark.parametrize("case", FOLD_ORDER_CASES, ids=lambda c: c.name)
+def test_folded_jobs_in_tail_first_order_write_every_element(case):
+    """Where each reduction job is a whole number of folded jobs, the folded kernels take their
+    jobs in a permuted order (the last folded job of every reduction job first). Every
+    element of y and dx must still be written exactly as the split-phase kernels, which
+    stream in index order, write it: the fused outputs start as NaN and must come out
+    bitwise equal to the split-phase ones."""
+    inp = workloads.make(case, DEV)
+    x, G, gamma, beta, dy = inp["x"], inp["G"], inp["gamma"], inp["beta"], inp["dy"]
+    N, C = x.shape[:2]
+    S = x.numel() // (N * C)
+    p = gn.gn_plan_query(N, C, S, G)
+    nested = p["chunk"] % p["fold_chunk"] == 0 and \
+        p["fold_chunks_per_row"] == p["chunks_per_row"] * (p["chunk"] // p["fold_chunk"])
+    F = p["chunk"] // p["fold_chunk"] if nested else 1
+    say(f"{case.name}: {F} folded jobs a reduction job, fused outputs poisoned with NaN")
+    if case is not FOLD_ORDER_CASES[-1]:
+        assert F > 1
+    y = torch.full_like(x, float("nan"))
+    dx = torch.full_like(x, float("nan"))
+    mean = torch.full((N, G), float("nan"), device=DEV)
+    rstd = torch.full((N, G), float("nan"), device=DEV)
+    gn.gn_forward(x, gamma, beta, G, inp["eps"], out=y, mean=mean, rstd=rstd)
+    gn.gn_backward(dy, x, mean, rstd, gamma, G, dx=dx)
+    ws = gn.workspace_for(x, G)
+    y2, mean2, rstd2, dx2 = torch.empty_like(y), torch.empty_like(mean), torch.empty_like(rstd), torch.empty_like(dx)
+    dg2, db2 = torch.empty(C, device=DEV), torch.empty(C, device=DEV)
+    gn.gn_forward_stats(x, gamma, beta, G, inp["eps"], mean2, rstd2, ws)
+    gn.gn_forward_apply(x, G, y2, ws)
+    gn.gn_backward_reduce(dy, x, mean2, rstd2, gamma, G, dg2, db2, ws)
+    gn.gn_backward_apply(dy, x, G, dx2, ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any() and not torch.isnan(dx).any()
+    for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2)):
+        assert torch.equal(_bits(u), _bits(v))
+
+
 def test_optional_backward_outputs():
     case = workloads.DEEP
     say(f"{case.name}: backward with dx only, and with dgamma/dbeta only")

@@ -400,6 +400,28 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f)
     return uint32_t((uint64_t(x) * f.m) >> 32);
 }
 
+// The folded job that workgroup slot w (0 <= w < jobs_f) of a folded streaming kernel
+// takes. With fold_nest = F > 1 (every reduction job is exactly F folded jobs, the inputs
+// stay in the last-level cache) the slots take the last folded job of every reduction job
+// first, then the second-to-last, and so on, so that each pass over x (and dy) runs against
+// the direction of the reduction pass before it, whose most recently read lines are the
+// ones the cache still holds, and the next reduction pass finds the lines this one read
+// last. The map c*F + (F - 1 - p), over c < jobs_f / F and p < F with w = p * (jobs_f / F)
+// + c, is a permutation of [0, jobs_f), so the results do not depend on it.
+__device__ __forceinline__ int64_t folded_job(int64_t w, const KArgs& a)
+{
+    if (a.fold_nest <= 1) return w;
+    uint32_t p, c;
+    if (a.fold_shift >= 0) {
+        p = uint32_t(w) >> a.fold_shift;
+        c = uint32_t(w) & ((1u << a.fold_shift) - 1u);
+    } else {
+        p = fdiv(uint32_t(w), a.div_fold_R);
+        c = uint32_t(w) - p * uint32_t(a.fold_R);
+    }
+    return int64_t(c) * a.fold_nest + (a.fold_nest - 1 - int64_t(p));
+}
+
 // Block-wide sums of a and b; waves are added in wave order and every thread returns
 // the result. s holds 2 * kResMaxWaves floats and may be reused on return.
 __device__ __forceinline__ float2 block_allsum2(float a, float b, float* s)

@@ -38,6 +38,12 @@ struct KArgs {
     int32_t act;                      // 0: none, 1: relu after the affine
     int32_t cached;                   // host's choice: plain loads, the volume fits the LLC
     FastDiv div_W, div_vg, div_Cg;    // resident path: S/8, M/8 and C/G as divisors
+    // Folded-job order (folded_job): fold_nest = F > 1 when every reduction job is exactly F
+    // folded jobs, the inputs are cached and jobs_f < 2^16; then fold_R = jobs_f / F, and
+    // fold_shift = log2(fold_R) when that is a power of two (else -1). Else F = 1.
+    int32_t fold_nest, fold_R;
+    FastDiv div_fold_R;
+    int32_t fold_shift;
 };
 
 inline KArgs kargs_of(const Plan& p, int act = 0)
@@ -54,6 +60,15 @@ inline KArgs kargs_of(const Plan& p, int act = 0)
     a.div_W = fastdiv_of(p.S % kVec == 0 ? p.S / kVec : 0);
     a.div_vg = fastdiv_of(p.S % kVec == 0 ? p.M / kVec : 0);
     a.div_Cg = fastdiv_of(p.Cg);
+    const bool nest = p.chunk_f > 0 && p.chunk % p.chunk_f == 0 && p.K_f == p.K * (p.chunk / p.chunk_f);
+    const int64_t F = nest ? p.chunk / p.chunk_f : 1;
+    const bool permute = F > 1 && p.jobs_f < 65536;  // slots then fit fdiv's exact range
+    a.fold_nest = permute ? int32_t(F) : 1;
+    a.fold_R = permute ? int32_t(p.jobs_f / F) : 1;
+    a.div_fold_R = fastdiv_of(a.fold_R);
+    a.fold_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((int64_t(1) << sh) == a.fold_R) a.fold_shift = sh;
     return a;
 }
 
