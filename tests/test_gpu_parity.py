@@ -486,6 +486,31 @@ def test_folded_jobs_in_tail_first_order_write_every_element(case):
         assert torch.equal(_bits(u), _bits(v))
 
 
+@pytest.mark.parametrize("shape", [(2, 64, 8, (16, 16, 20)), (1, 32, 8, (32, 32, 32))], ids=str)
+def test_channels_last_streaming_jobs_in_tail_first_order_write_every_element(shape):
+    """The channels-last normalize and dx kernels take their jobs in the same tail-first
+    order where the streaming jobs nest in the reduction jobs (80 and 128 reduction jobs of
+    2 streaming jobs here, through the multiply-shift and the shift forms of the map):
+    outputs poisoned with NaN come out finite and bitwise equal to a second call's."""
+    N, C, G, sp = shape
+    case = workloads.custom(N, C, G, sp, torch.bfloat16, dist="unet", seed=98)
+    inp = workloads.make(case, DEV)
+    x, dy = gn.as_layout(inp["x"], "ndhwc"), gn.as_layout(inp["dy"], "ndhwc")
+    p = gn.gn_plan_query_cl(N, C, x.numel() // (N * C), G)
+    assert p["chunk"] == 2 * p["apply_chunk"] and p["apply_jobs_per_sample"] == 2 * p["jobs_per_sample"]
+    assert not p["resident_forward"] and not p["resident_backward"]
+    say(f"channels-last {shape}: {p['jobs']} reduction jobs of 2 streaming jobs, outputs poisoned with NaN")
+    y = torch.full_like(x, float("nan"))
+    dx = torch.full_like(x, float("nan"))
+    y, mean, rstd = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"], out=y)
+    dx = gn.gn_backward(dy, x, mean, rstd, inp["gamma"], G, dx=dx)[0]
+    y2, mean2, rstd2 = gn.gn_forward(x, inp["gamma"], inp["beta"], G, inp["eps"])
+    dx2 = gn.gn_backward(dy, x, mean2, rstd2, inp["gamma"], G)[0]
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any() and not torch.isnan(dx).any()
+    assert torch.equal(_bits(y), _bits(y2)) and torch.equal(_bits(dx), _bits(dx2))
+
+
 def test_optional_backward_outputs():
     case = workloads.DEEP
     say(f"{case.name}: backward with dx only, and with dgamma/dbeta only")

@@ -40,6 +40,7 @@ gn::ClArgs clargs_for(const gn::PlanCL& p, int activation, int x_dtype)
     gn::ClArgs a = gn::clargs_of(p, activation);
     const int64_t bytes = p.N * p.C * p.S * (x_dtype == GN_F32 ? 4 : 2);
     a.cached = bytes <= kCachedBytes ? 1 : 0;
+    if (!a.cached) a.fold_nest = 1;  // as for NCDHW: index order over nontemporal streams
     return a;
 }
 

@@ -400,15 +400,17 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f)
     return uint32_t((uint64_t(x) * f.m) >> 32);
 }
 
-// The folded job that workgroup slot w (0 <= w < jobs_f) of a folded streaming kernel
-// takes. With fold_nest = F > 1 (every reduction job is exactly F folded jobs, the inputs
-// stay in the last-level cache) the slots take the last folded job of every reduction job
-// first, then the second-to-last, and so on, so that each pass over x (and dy) runs against
-// the direction of the reduction pass before it, whose most recently read lines are the
-// ones the cache still holds, and the next reduction pass finds the lines this one read
-// last. The map c*F + (F - 1 - p), over c < jobs_f / F and p < F with w = p * (jobs_f / F)
-// + c, is a permutation of [0, jobs_f), so the results do not depend on it.
-__device__ __forceinline__ int64_t folded_job(int64_t w, const KArgs& a)
+// The streaming job that workgroup slot w (0 <= w < jobs) of a folded (or channels-last)
+// streaming kernel takes. With A.fold_nest = F > 1 (every reduction job is exactly F
+// streaming jobs, and the inputs stay in the last-level cache) the slots take the last
+// streaming job of every reduction job first, then the second-to-last, and so on, so that
+// each pass over x (and dy) runs against the direction of the reduction pass before it,
+// whose most recently read lines are the ones the cache still holds, and the next
+// reduction pass finds the lines this one read last. The map c*F + (F - 1 - p), over
+// c < R = jobs / F and p < F with w = p*R + c, is a permutation of [0, jobs), so the
+// results do not depend on it.
+template <typename A>
+__device__ __forceinline__ int64_t job_in_order(int64_t w, const A& a)
 {
     if (a.fold_nest <= 1) return w;
     uint32_t p, c;

@@ -468,7 +468,7 @@ apply_fin_kernel(const TX* __restrict__ x, const float* __restrict__ gamma, cons
     constexpr int V = kFinVecs;
     const int64_t stepv = int64_t(blk) * V;
     for (int64_t jj = blockIdx.x; jj < a.jobs_f; jj += gridDim.x) {
-        const int64_t j = folded_job(jj, a);
+        const int64_t j = job_in_order(jj, a);
         const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg;
         int64_t fs, fe, nsteps;
@@ -802,7 +802,7 @@ bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const 
     constexpr int V = kFinVecs;
     const int64_t stepv = int64_t(blk) * V;
     for (int64_t jj = blockIdx.x; jj < a.jobs_f; jj += gridDim.x) {
-        const int64_t j = folded_job(jj, a);
+        const int64_t j = job_in_order(jj, a);
         const Job jb = job_at(a.S, a.chunk_f, a.K_f, j);
         const int64_t n = jb.row / a.C, c = jb.row - n * a.C, g = c / a.Cg, ng = n * a.G + g;
         int64_t fs, fe, nsteps;

@@ -336,7 +336,8 @@ cl_apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, ClArgs a, const fl
     const int Cv = int(a.Cv), cv = tid % Cv, vo = tid / Cv, vps = int(a.vps);
     const int64_t g0 = (int64_t(cv) * kVec) / a.Cg;
     constexpr bool act = ACT;  // a template parameter, as in the NCDHW streaming kernels
-    for (int64_t j = blockIdx.x; j < a.jobs_a; j += gridDim.x) {
+    for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
+        const int64_t j = job_in_order(jj, a);
         const int64_t n = j / a.K_a, k = j - n * a.K_a;
         const int64_t v0 = k * a.chunk_a, v1 = (v0 + a.chunk_a < a.S) ? v0 + a.chunk_a : a.S;
         float sc[kVec], sh[kVec], hi[NGL], lo[NGL];
@@ -623,7 +624,8 @@ cl_bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, ClArgs 
     const bool act = a.act != 0;
     // A single-element group is answered as t - t: +0 for finite t, NaN otherwise.
     const bool single = (a.M == 1);
-    for (int64_t j = blockIdx.x; j < a.jobs_a; j += gridDim.x) {
+    for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
+        const int64_t j = job_in_order(jj, a);
         const int64_t n = j / a.K_a, k = j - n * a.K_a;
         const int64_t v0 = k * a.chunk_a, v1 = (v0 + a.chunk_a < a.S) ? v0 + a.chunk_a : a.S;
         float A[kVec], bt[kVec], mu[NGL], B[NGL], E[NGL];

@@ -27,6 +27,21 @@ inline FastDiv fastdiv_of(int64_t d)
     return FastDiv{(d >= 1 && d <= 65536) ? (uint64_t(1) << 32) / uint64_t(d) + 1 : 0};
 }
 
+// The streaming jobs' order (job_in_order, gn_device.hpp): with F > 1 streaming jobs in
+// each reduction job and fewer than 2^16 of them (fdiv's exact range), nest = F,
+// R = jobs / F (the reduction jobs) and shift = log2(R) when R is a power of two, else -1;
+// otherwise nest = 1 (index order).
+inline void set_job_order(int64_t F, int64_t jobs, int32_t& nest, int32_t& R, int32_t& shift, FastDiv& divR)
+{
+    const bool permute = F > 1 && jobs < 65536;
+    nest = permute ? int32_t(F) : 1;
+    R = permute ? int32_t(jobs / F) : 1;
+    shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((int64_t(1) << sh) == R) shift = sh;
+    divR = fastdiv_of(R);
+}
+
 // Plain-old-data view of a Plan, passed by value to every kernel.
 struct KArgs {
     int64_t N, C, S, G;
@@ -38,9 +53,8 @@ struct KArgs {
     int32_t act;                      // 0: none, 1: relu after the affine
     int32_t cached;                   // host's choice: plain loads, the volume fits the LLC
     FastDiv div_W, div_vg, div_Cg;    // resident path: S/8, M/8 and C/G as divisors
-    // Folded-job order (folded_job): fold_nest = F > 1 when every reduction job is exactly F
-    // folded jobs, the inputs are cached and jobs_f < 2^16; then fold_R = jobs_f / F, and
-    // fold_shift = log2(fold_R) when that is a power of two (else -1). Else F = 1.
+    // Folded-job order (job_in_order, set by set_job_order): folded jobs nested in the
+    // reduction jobs.
     int32_t fold_nest, fold_R;
     FastDiv div_fold_R;
     int32_t fold_shift;
@@ -62,13 +76,7 @@ inline KArgs kargs_of(const Plan& p, int act = 0)
     a.div_Cg = fastdiv_of(p.Cg);
     const bool nest = p.chunk_f > 0 && p.chunk % p.chunk_f == 0 && p.K_f == p.K * (p.chunk / p.chunk_f);
     const int64_t F = nest ? p.chunk / p.chunk_f : 1;
-    const bool permute = F > 1 && p.jobs_f < 65536;  // slots then fit fdiv's exact range
-    a.fold_nest = permute ? int32_t(F) : 1;
-    a.fold_R = permute ? int32_t(p.jobs_f / F) : 1;
-    a.div_fold_R = fastdiv_of(a.fold_R);
-    a.fold_shift = -1;
-    for (int sh = 0; sh < 31; ++sh)
-        if ((int64_t(1) << sh) == a.fold_R) a.fold_shift = sh;
+    set_job_order(F, p.jobs_f, a.fold_nest, a.fold_R, a.fold_shift, a.div_fold_R);
     return a;
 }
 
@@ -170,6 +178,11 @@ struct ClArgs {
     int32_t cached;                   // host's choice: plain loads, the volume fits the LLC
     int32_t lcvg;                     // resident path: log2 of a group's vectors per voxel
     FastDiv div_vg;                   // resident path: S * C/(8G), a group's vectors
+    // Streaming-job order (job_in_order): as in KArgs, with the streaming jobs of chunk_a
+    // voxels nested in the reduction jobs of chunk voxels.
+    int32_t fold_nest, fold_R;
+    FastDiv div_fold_R;
+    int32_t fold_shift;
 };
 
 inline ClArgs clargs_of(const PlanCL& p, int act = 0)
@@ -183,6 +196,8 @@ inline ClArgs clargs_of(const PlanCL& p, int act = 0)
     a.cached = 0;
     a.lcvg = p.lcvg;
     a.div_vg = fastdiv_of(p.res_bwd ? p.S << p.lcvg : 0);
+    const bool nest = p.chunk_a > 0 && p.chunk % p.chunk_a == 0 && p.K_a == p.K * (p.chunk / p.chunk_a);
+    set_job_order(nest ? p.chunk / p.chunk_a : 1, p.jobs_a, a.fold_nest, a.fold_R, a.fold_shift, a.div_fold_R);
     return a;
 }
 
