@@ -452,10 +452,10 @@ FOLD_ORDER_CASES = [
 @pytest.mark.parametrize("case", FOLD_ORDER_CASES, ids=lambda c: c.name)
 def test_folded_jobs_in_tail_first_order_write_every_element(case):
     """Where each reduction job is a whole number of folded jobs, the folded kernels take their
-    jobs in a permuted order (the last folded job of every reduction job first). Every
-    element of y and dx must still be written exactly as the split-phase kernels, which
-    stream in index order, write it: the fused outputs start as NaN and must come out
-    bitwise equal to the split-phase ones."""
+    jobs in a permuted order (the last folded job of every reduction job first), and the
+    split-phase one-step kernels likewise over their own jobs. Every element of y and dx
+    must still be written once: both paths' outputs start as NaN and must come out finite
+    and bitwise equal to each other."""
     inp = workloads.make(case, DEV)
     x, G, gamma, beta, dy = inp["x"], inp["G"], inp["gamma"], inp["beta"], inp["dy"]
     N, C = x.shape[:2]
@@ -474,7 +474,8 @@ def test_folded_jobs_in_tail_first_order_write_every_element(case):
     gn.gn_forward(x, gamma, beta, G, inp["eps"], out=y, mean=mean, rstd=rstd)
     gn.gn_backward(dy, x, mean, rstd, gamma, G, dx=dx)
     ws = gn.workspace_for(x, G)
-    y2, mean2, rstd2, dx2 = torch.empty_like(y), torch.empty_like(mean), torch.empty_like(rstd), torch.empty_like(dx)
+    y2, dx2 = torch.full_like(y, float("nan")), torch.full_like(dx, float("nan"))
+    mean2, rstd2 = torch.empty_like(mean), torch.empty_like(rstd)
     dg2, db2 = torch.empty(C, device=DEV), torch.empty(C, device=DEV)
     gn.gn_forward_stats(x, gamma, beta, G, inp["eps"], mean2, rstd2, ws)
     gn.gn_forward_apply(x, G, y2, ws)
@@ -482,6 +483,7 @@ def test_folded_jobs_in_tail_first_order_write_every_element(case):
     gn.gn_backward_apply(dy, x, G, dx2, ws)
     torch.cuda.synchronize()
     assert not torch.isnan(y).any() and not torch.isnan(dx).any()
+    assert not torch.isnan(y2).any() and not torch.isnan(dx2).any()
     for u, v in ((y, y2), (mean, mean2), (rstd, rstd2), (dx, dx2)):
         assert torch.equal(_bits(u), _bits(v))
 

@@ -31,7 +31,7 @@ gn::KArgs kargs_for(const gn::Plan& p, int activation, int x_dtype)
     // The folded-job order pays where the inputs stay in the last-level cache; over
     // nontemporal streams it spreads each moment's accesses over every reduction job's span
     // (256^3: 1309 -> 1413 us a step), so they keep index order.
-    if (!a.cached) a.fold_nest = 1;
+    if (!a.cached) a.fold_nest = a.step_nest = 1;
     return a;
 }
 

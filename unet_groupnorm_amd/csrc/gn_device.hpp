@@ -409,19 +409,31 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f)
 // reduction pass finds the lines this one read last. The map c*F + (F - 1 - p), over
 // c < R = jobs / F and p < F with w = p*R + c, is a permutation of [0, jobs), so the
 // results do not depend on it.
+__device__ __forceinline__ int64_t permuted_job(int64_t w, int32_t F, int32_t R, int32_t shift, FastDiv divR)
+{
+    if (F <= 1) return w;
+    uint32_t p, c;
+    if (shift >= 0) {
+        p = uint32_t(w) >> shift;
+        c = uint32_t(w) & ((1u << shift) - 1u);
+    } else {
+        p = fdiv(uint32_t(w), divR);
+        c = uint32_t(w) - p * uint32_t(R);
+    }
+    return int64_t(c) * F + (F - 1 - int64_t(p));
+}
+
+// The folded (NCDHW) or streaming (channels-last) jobs' order.
 template <typename A>
 __device__ __forceinline__ int64_t job_in_order(int64_t w, const A& a)
 {
-    if (a.fold_nest <= 1) return w;
-    uint32_t p, c;
-    if (a.fold_shift >= 0) {
-        p = uint32_t(w) >> a.fold_shift;
-        c = uint32_t(w) & ((1u << a.fold_shift) - 1u);
-    } else {
-        p = fdiv(uint32_t(w), a.div_fold_R);
-        c = uint32_t(w) - p * uint32_t(a.fold_R);
-    }
-    return int64_t(c) * a.fold_nest + (a.fold_nest - 1 - int64_t(p));
+    return permuted_job(w, a.fold_nest, a.fold_R, a.fold_shift, a.div_fold_R);
+}
+
+// The one-step streaming jobs' order (NCDHW split-phase and spatial-shard calls).
+__device__ __forceinline__ int64_t step_job_in_order(int64_t w, const KArgs& a)
+{
+    return permuted_job(w, a.step_nest, a.step_R, a.step_shift, a.div_step_R);
 }
 
 // Block-wide sums of a and b; waves are added in wave order and every thread returns

@@ -421,7 +421,7 @@ apply_kernel(const TX* __restrict__ x, TY* __restrict__ y, KArgs a,
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kApplyVecs;
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
-        const int64_t j = jj;
+        const int64_t j = step_job_in_order(jj, a);
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row];
         const Affine<ACT> f = {cf.x, cf.y, cf.z, cf.w};
@@ -751,7 +751,7 @@ bwd_apply_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, KArgs a,
     const int tid = threadIdx.x, blk = blockDim.x;
     const int64_t stepv = int64_t(blk) * kApplyVecs;
     for (int64_t jj = blockIdx.x; jj < a.jobs_a; jj += gridDim.x) {
-        const int64_t j = jj;
+        const int64_t j = step_job_in_order(jj, a);
         const Job jb = job_at(a.S, a.chunk_a, a.K_a, j);
         const float4 cf = coef[2 * jb.row], cg = coef[2 * jb.row + 1];
         // Whether the whole group is one element comes from the record: a spatial shard's

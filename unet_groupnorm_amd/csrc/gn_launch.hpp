@@ -58,6 +58,10 @@ struct KArgs {
     int32_t fold_nest, fold_R;
     FastDiv div_fold_R;
     int32_t fold_shift;
+    // The same for the one-step streaming jobs (chunk_a) nested in the reduction jobs.
+    int32_t step_nest, step_R;
+    FastDiv div_step_R;
+    int32_t step_shift;
 };
 
 inline KArgs kargs_of(const Plan& p, int act = 0)
@@ -77,6 +81,8 @@ inline KArgs kargs_of(const Plan& p, int act = 0)
     const bool nest = p.chunk_f > 0 && p.chunk % p.chunk_f == 0 && p.K_f == p.K * (p.chunk / p.chunk_f);
     const int64_t F = nest ? p.chunk / p.chunk_f : 1;
     set_job_order(F, p.jobs_f, a.fold_nest, a.fold_R, a.fold_shift, a.div_fold_R);
+    const bool nest_a = p.chunk_a > 0 && p.chunk % p.chunk_a == 0 && p.K_a == p.K * (p.chunk / p.chunk_a);
+    set_job_order(nest_a ? p.chunk / p.chunk_a : 1, p.jobs_a, a.step_nest, a.step_R, a.step_shift, a.div_step_R);
     return a;
 }
 
