@@ -786,8 +786,20 @@ __device__ __forceinline__ void dx_full_step(const typename Io<TX>::Raw (&rx)[V]
 // exactly as fin_bwd_kernel does, and streams the job. The group's first job writes the
 // rows' coefficient records; the first job of channel c in sample 0 writes dgamma_c and
 // dbeta_c, summed exactly as fin_bwd_kernel sums them.
+// Workgroups a CU the folded dx kernel is compiled for, which sets its register budget:
+// 3 in general; 6 (at most 80 VGPRs, six waves a SIMD) for the cached relu build with
+// bf16 x and 16-bit dy, which otherwise took 95 VGPRs and ran five waves a SIMD. With the
+// cap it takes 78, spills none and moves SGPRs to VGPR lanes instead: relu step at 128^3
+// 163.2 -> 162.1 us, 64^3 x 64 49.5 -> 48.4 (interleaved A/B, same bits). The other input
+// types spill to memory under that cap, so they keep 3.
 template <typename TX, typename TD, bool NT, bool ACT>
-__global__ void __launch_bounds__(256, 3)
+constexpr int bwd_apply_fin_blocks()
+{
+    return (ACT && !NT && std::is_same<TX, uint16_t>::value && sizeof(TD) == 2) ? 6 : 3;
+}
+
+template <typename TX, typename TD, bool NT, bool ACT>
+__global__ void __launch_bounds__(256, (bwd_apply_fin_blocks<TX, TD, NT, ACT>()))
 bwd_apply_fin_kernel(const TD* __restrict__ dy, const TX* __restrict__ x, const float* __restrict__ mean,
                      const float* __restrict__ rstd, const float* __restrict__ gamma,
                      const float* __restrict__ beta, const float2* __restrict__ part, KArgs a,
