@@ -400,13 +400,13 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t x, FastDiv f)
     return uint32_t((uint64_t(x) * f.m) >> 32);
 }
 
-// The streaming job that workgroup slot w (0 <= w < jobs) of a folded (or channels-last)
-// streaming kernel takes. With A.fold_nest = F > 1 (every reduction job is exactly F
-// streaming jobs, and the inputs stay in the last-level cache) the slots take the last
-// streaming job of every reduction job first, then the second-to-last, and so on, so that
-// each pass over x (and dy) runs against the direction of the reduction pass before it,
-// whose most recently read lines are the ones the cache still holds, and the next
-// reduction pass finds the lines this one read last. The map c*F + (F - 1 - p), over
+// The streaming job that workgroup slot w (0 <= w < jobs) of a streaming kernel takes,
+// with the order's parameters from set_job_order. With F > 1 (every reduction job is
+// exactly F streaming jobs, and the inputs stay in the last-level cache) the slots take
+// the last streaming job of every reduction job first, then the second-to-last, and so
+// on, so that each pass over x (and dy) runs against the direction of the reduction pass
+// before it, whose most recently read lines are the ones the cache still holds, and the
+// next reduction pass finds the lines this one read last. The map c*F + (F - 1 - p), over
 // c < R = jobs / F and p < F with w = p*R + c, is a permutation of [0, jobs), so the
 // results do not depend on it.
 __device__ __forceinline__ int64_t permuted_job(int64_t w, int32_t F, int32_t R, int32_t shift, FastDiv divR)
